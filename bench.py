@@ -1,0 +1,205 @@
+#!/usr/bin/env python3
+"""Throughput of the DeepSeekMoE layer on one MI355X.
+
+One step = one pass of the whole hot path over one batch: moe_forward (router
+GEMM + top-K + gates, expert grouping, grouped gate/up GEMM with SwiGLU,
+grouped down GEMM, combine) followed by the aux-loss-free bias update from the
+step's expert counts.  Inputs are seeded synthetic tensors resident in HBM
+before timing starts.  Prints ONE JSON line on stdout.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload bf16_d7168]
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer tokens/sec + grouped-GEMM % MFMA peak, d=7168 N_r=256 K=8, 1 GPU"
+PEAK_TFLOPS = {"bf16": 2500.0, "e4m3": 5000.0, "f32": 157.3}
+PEAK_HBM_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    csrc = os.path.join(ROOT, "mixture_experts_layer_deepseekmoe_amd", "csrc")
+    h = hashlib.sha256()
+    for f in ("gemm_core.hpp", "ggemm.hip", "moe_common.hpp", "kernels.hpp"):
+        h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per gate/up launch from the committed rocprofv3 counter runs, if
+    they were taken on the current grouped-GEMM source; else None."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    table = json.load(open(TRAFFIC_FILE))
+    rec = table.get(workload)
+    if not rec or rec.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return rec.get("gate_up_bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="bf16_d7168")
+    ap.add_argument("--cpu-sample-tokens", type=int, default=256)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(sharding is described in DESIGN.md, not implemented); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import mixture_experts_layer_deepseekmoe_amd as moe
+    from mixture_experts_layer_deepseekmoe_amd.binding import HipEvents
+    from moe_workloads import get_config, make_inputs
+
+    cfg = get_config(args.workload)
+    torch.cuda.set_device(0)
+    log(f"[bench] workload {cfg.name}: generating seeded inputs")
+    inp = make_inputs(cfg, 0, weights_device="cuda")
+    shape = moe.LayerShape.from_config(cfg)
+    u = inp.u.cuda().contiguous()
+    cen = inp.centroids.cuda().contiguous()
+    bias = inp.bias.cuda().contiguous()
+    weights = moe.prepare_weights(cfg, inp)
+    ws = moe.alloc_workspace(shape)
+    routing = moe.alloc_routing(shape)
+    y = torch.empty((cfg.T, cfg.d), dtype=torch.float32 if cfg.out_dtype == "f32" else torch.bfloat16,
+                    device="cuda")
+    TK = cfg.T * cfg.top_k
+    torch.cuda.synchronize()
+
+    def step(trace=None):
+        moe.moe_forward(shape, u, cen, bias, weights, y=y, routing=routing, workspace=ws, trace=trace)
+        moe.moe_update_bias(bias, routing["expert_counts"], TK, 0.001)
+
+    log(f"[bench] warmup {args.warmup} steps")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    events = [HipEvents() for _ in range(args.steps)]
+    log(f"[bench] timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(events[k].trace)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    elapsed = t1 - t0
+    stages = {}
+    for ev in events:
+        for name, ms in ev.elapsed_ms().items():
+            stages[name] = stages.get(name, 0.0) + ms / args.steps
+    for ev in events:
+        ev.close()
+    counts = routing["expert_counts"].cpu().numpy()
+    log(f"[bench] {elapsed / args.steps * 1e3:.3f} ms/step; stages (ms): "
+        + ", ".join(f"{k} {v:.4f}" for k, v in stages.items()))
+
+    # ---------------- roofline of the dominant kernel (grouped gate/up GEMM)
+    rows = TK + cfg.n_shared * cfg.T
+    es = {"bf16": 2, "e4m3": 1, "f32": 4}[cfg.w_dtype]
+    gu_flops = 2.0 * rows * 2 * cfg.inter * cfg.d
+    dn_flops = 2.0 * rows * cfg.d * cfg.inter
+    gu_s = stages["gate_up"] * 1e-3
+    dn_s = stages["down"] * 1e-3
+    peak = PEAK_TFLOPS[cfg.w_dtype]
+    gu_tflops = gu_flops / gu_s / 1e12
+    touched = int((counts > 0).sum())
+    gu_bytes = (touched + cfg.n_shared) * 2 * cfg.inter * cfg.d * es + cfg.T * cfg.d * es + rows * cfg.inter * es
+    roofline = {"bound": "mfma", "kernel": "gateup_kernel (grouped gate/up GEMM + SwiGLU)",
+                "achieved": round(gu_tflops, 2), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(gu_tflops / peak, 4), "traffic": measured_traffic(cfg.name),
+                "flops_per_launch": gu_flops, "algorithmic_bytes_per_launch": gu_bytes,
+                "avg_launch_ms": round(stages["gate_up"], 4)}
+    grouped_frac = (gu_flops + dn_flops) / (gu_s + dn_s) / 1e12 / peak
+
+    xs = 4 if cfg.x_dtype == "f32" else 2
+    os_ = 4 if cfg.out_dtype == "f32" else 2
+    ys = 4 if cfg.w_dtype == "f32" else 2
+    hbm = {
+        "route": (cfg.T * cfg.d * xs + cfg.n_routed * cfg.d * xs + TK * 8) / (stages["route"] * 1e-3) / 1e9,
+        "group": (TK * 4 * 3 + TK * 8) / (stages["group"] * 1e-3) / 1e9,
+        "combine": (cfg.T * cfg.d * xs + rows * cfg.d * ys + cfg.T * cfg.d * os_ + TK * 8)
+                   / (stages["combine"] * 1e-3) / 1e9,
+    }
+
+    result = {
+        "metric": METRIC,
+        "value": round(cfg.T * args.steps / elapsed, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(elapsed / args.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.w_dtype,
+        "data": "synthetic (seeded N(0,1) activations, N(0,0.006) weights, N(0,0.02) centroids, random init)",
+        "config": {"workload": cfg.name, "T": cfg.T, "d": cfg.d, "n_routed": cfg.n_routed,
+                   "n_shared": cfg.n_shared, "inter": cfg.inter, "top_k": cfg.top_k,
+                   "x_dtype": cfg.x_dtype, "w_dtype": cfg.w_dtype, "out_dtype": cfg.out_dtype,
+                   "parallelism": "single GPU"},
+        "roofline": roofline,
+        "grouped_gemm_mfma_frac": round(grouped_frac, 4),
+        "stage_ms": {k: round(v, 4) for k, v in stages.items()},
+        "stage_hbm_frac": {k: round(v / PEAK_HBM_GBS, 4) for k, v in hbm.items()},
+        "load": {"max_over_mean": round(float(counts.max() / counts.mean()), 3), "experts_touched": touched},
+    }
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_sample_tokens, result)
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(cfg, inp, n_tokens, result):
+    """The CPU oracle, as it stands, on the first n_tokens tokens of the batch."""
+    import numpy as np
+    import threadpoolctl
+
+    from moe_workloads import to_numpy_f32
+    from oracle import moe_oracle as O
+
+    n = min(n_tokens, cfg.T)
+    u = to_numpy_f32(inp.u[:n])
+    E = to_numpy_f32(inp.centroids)
+    b = inp.bias.numpy()
+    routed = lambda e: (to_numpy_f32(inp.w_gate_up[e]), to_numpy_f32(inp.w_down[e]))
+    shared = [(to_numpy_f32(inp.ws_gate_up[s]), to_numpy_f32(inp.ws_down[s])) for s in range(cfg.n_shared)]
+    threads = max([p.get("num_threads", 1) for p in threadpoolctl.threadpool_info()], default=1)
+    log(f"[bench] cpu baseline: oracle on {n} tokens, {threads} BLAS threads")
+    t0 = time.perf_counter()
+    O.layer_forward(u, E, b, cfg.top_k, routed, cfg.n_routed, shared, fp8=cfg.fp8)
+    dt = time.perf_counter() - t0
+    return {"value": round(n / dt, 3), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {n} of the {cfg.T} tokens of the same seeded batch, full layer (fp64 NumPy; "
+                      f"expert weights streamed from HBM per expert inside the timed region)",
+            "seconds": round(dt, 2)}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,215 @@
+/*
+ * moe.h - C ABI of the DeepSeekMoE layer for AMD Instinct MI355X (gfx950).
+ *
+ * What is computed (pages about the DeepSeek-V3 Technical Report):
+ *   - "DeepSeek-V3 Technical Report" summary (xyznot.com), section 2,
+ *     "DeepSeekMoE with Auxiliary-Loss-Free Balancing":
+ *       h'_t    = u_t + sum_{i<=N_s} FFN^(s)_i(u_t) + sum_{i<=N_r} g_{i,t} FFN^(r)_i(u_t)
+ *       s_{i,t} = Sigmoid(u_t^T e_i)
+ *       g'_{i,t}= s_{i,t} if s_{i,t} + b_i is among the K_r largest of {s_{j,t} + b_j}, else 0
+ *       g_{i,t} = g'_{i,t} normalised over the token's selected experts
+ *       b_i    -= gamma when expert i is overloaded, += gamma when underloaded (gamma = 0.001)
+ *     and, in its key-ideas list, the FP8 granularity: E4M3 for all tensors,
+ *     1x128 activation tiles, 128x128 weight blocks, FP32 promotion every 128.
+ *   - The same h' and g' formulas in the wenxiaobai explainer ("DeepSeek-V3深度解析"),
+ *     items on DeepSeekMoE and on auxiliary-loss-free load balancing.
+ *   - The expert FFN is the SwiGLU operator (the report's FP8 training section,
+ *     as paraphrased on why-be.co.kr): FFN(x) = W_down (SiLU(W_gate x) * (W_up x)).
+ *
+ * Conventions for every entry point:
+ *   - All tensor pointers are DEVICE pointers (HBM of the current HIP device),
+ *     owned by the caller; the library never allocates, frees, synchronises
+ *     or keeps state between calls.  Work is enqueued on `stream` (0 = the
+ *     null stream) and the call returns without waiting for it.
+ *   - Matrices are row-major and the reduction dimension is innermost
+ *     ("K-contiguous").  Pointers must be 16-byte aligned.
+ *   - Every call returns a moe_status.  Arguments are validated before any
+ *     work is enqueued: on an error nothing is launched and no output is
+ *     touched.  MOE_ERR_LAUNCH reports a failed kernel launch (the outputs
+ *     are then undefined).
+ *   - Inputs are expected to be finite.  Should a score be NaN the router
+ *     still returns K distinct in-range experts per token.
+ *   - Repeated calls with the same inputs give bit-identical outputs.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_DTYPE_F32 = 0,   /* IEEE binary32 */
+  MOE_DTYPE_BF16 = 1,  /* bfloat16 (values rounded to nearest even) */
+  MOE_DTYPE_E4M3 = 2   /* OCP FP8 E4M3 (bias 7, max 448, no inf) with fp32 block scales */
+} moe_dtype;
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = 1,  /* null pointer, bad shape, bad dtype combination, misalignment */
+  MOE_ERR_UNSUPPORTED = 2,  /* valid but outside the library's limits (see moe_shape) */
+  MOE_ERR_WORKSPACE = 3,    /* workspace missing or smaller than moe_workspace_size() */
+  MOE_ERR_LAUNCH = 4        /* a kernel launch failed */
+} moe_status;
+
+/*
+ * Layer shape and dtypes.
+ *   T         tokens in the batch (>= 0; 0 is a no-op)
+ *   d         hidden size
+ *   n_routed  N_r routed experts, 1..512
+ *   n_shared  N_s shared experts, 0..8
+ *   inter     I, the intermediate size of every expert (shared and routed)
+ *   top_k     K_r experts chosen per token, 1..min(N_r, 16)
+ *   x_dtype   dtype of u and of the centroids e_i: F32 or BF16
+ *   w_dtype   dtype of the expert weights and of the expert GEMMs:
+ *               F32  (requires x_dtype F32)
+ *               BF16 (requires x_dtype BF16)
+ *               E4M3 (requires x_dtype BF16): the FP8 path.  u is quantised
+ *                    per 1x128 tile and h per 1x128 tile on the fly, weights
+ *                    come pre-quantised per 128x128 block (moe_quantize_weight_e4m3).
+ *                    The router and the residual use the unquantised bf16 u.
+ *   out_dtype dtype of y: F32 or BF16
+ * Limits: d and inter multiples of 64 (F32: 32 is enough; E4M3: 128);
+ * T * top_k and (top_k + n_shared) * T below 2^31.
+ */
+typedef struct {
+  int32_t T, d, n_routed, n_shared, inter, top_k;
+  int32_t x_dtype, w_dtype, out_dtype;
+} moe_shape;
+
+/*
+ * Expert weights.  Gate and up projections of one expert are one [2I][d]
+ * matrix, the I gate rows first.
+ *   w_gate_up   [N_r][2I][d]     w_dtype
+ *   w_down      [N_r][d][I]      w_dtype
+ *   ws_gate_up  [N_s][2I][d]     w_dtype (may be null when N_s = 0)
+ *   ws_down     [N_s][d][I]      w_dtype
+ * E4M3 only (fp32 block scales, one per 128x128 block of the matrix above):
+ *   s_gate_up   [N_r][2I/128][d/128]
+ *   s_down      [N_r][d/128][I/128]
+ *   ss_gate_up  [N_s][2I/128][d/128]
+ *   ss_down     [N_s][d/128][I/128]
+ */
+typedef struct {
+  const void* w_gate_up;
+  const void* w_down;
+  const void* ws_gate_up;
+  const void* ws_down;
+  const float* s_gate_up;
+  const float* s_down;
+  const float* ss_gate_up;
+  const float* ss_down;
+} moe_weights;
+
+/*
+ * Routing results.
+ *   topk_idx       [T][K] int32  selected experts, by descending s + b
+ *                                (exact ties: lower index first)
+ *   topk_gate      [T][K] fp32   g = s / (sum of the K selected s), same order
+ *   expert_counts  [N_r]  int32  assignments per expert (sum = T*K)
+ *   expert_offsets [N_r+1] int32 exclusive prefix sum of expert_counts
+ *   perm_token     [T*K]  int32  token of each grouped row; grouped rows are
+ *                                expert-major, tokens ascending within an expert
+ *   pos            [T][K] int32  grouped row of assignment (t, k)
+ */
+typedef struct {
+  int32_t* topk_idx;
+  float* topk_gate;
+  int32_t* expert_counts;
+  int32_t* expert_offsets;
+  int32_t* perm_token;
+  int32_t* pos;
+} moe_routing;
+
+/* Human-readable name of a status code (static string). */
+const char* moe_status_str(int status);
+
+/* Library version string (static). */
+const char* moe_version(void);
+
+/*
+ * Bytes of device workspace moe_route / moe_forward need for `shape`
+ * (written to *bytes).  The same workspace serves both calls.
+ */
+int moe_workspace_size(const moe_shape* shape, size_t* bytes);
+
+/*
+ * Routing only: affinities, biased top-K, normalised gates, and the stable
+ * grouping of assignments by expert.  Computes every field of `out` (all
+ * must be non-null).  u: [T][d] x_dtype; centroids: [N_r][d] x_dtype;
+ * bias: [N_r] fp32.  The affinity GEMM accumulates in fp32.
+ */
+int moe_route(const moe_shape* shape, const void* u, const void* centroids, const float* bias,
+              const moe_routing* out, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Optional per-stage timing: when a moe_trace is passed to moe_forward, the
+ * library records start[i] on `stream` before stage i and stop[i] after it
+ * (hipEventRecord; the events are created and owned by the caller).  A stage
+ * that does not run for the given dtypes gets both events back to back.
+ */
+#define MOE_NUM_STAGES 6
+typedef enum {
+  MOE_STAGE_ROUTE = 0,    /* affinity GEMM + sigmoid + bias + top-K + gates */
+  MOE_STAGE_GROUP = 1,    /* expert histogram, scan, stable permutation, m-tile list */
+  MOE_STAGE_QUANT = 2,    /* FP8 only: 1x128 quantisation of u */
+  MOE_STAGE_GATE_UP = 3,  /* grouped gate/up GEMM with the SwiGLU epilogue */
+  MOE_STAGE_DOWN = 4,     /* grouped down-projection GEMM */
+  MOE_STAGE_COMBINE = 5   /* residual + shared + gate-weighted routed sum */
+} moe_stage;
+typedef struct {
+  hipEvent_t start[MOE_NUM_STAGES];
+  hipEvent_t stop[MOE_NUM_STAGES];
+} moe_trace;
+
+/*
+ * The layer forward: y[T][d] (out_dtype) = h'.  `routing` may be null, and so
+ * may any of its fields; non-null fields receive the routing results.
+ * Expert outputs are accumulated in fp32 and stored in bf16 between the
+ * kernels (fp32 when w_dtype is F32); the final sum is fp32.  `trace` may be
+ * null.
+ */
+int moe_forward(const moe_shape* shape, const void* u, const void* centroids, const float* bias,
+                const moe_weights* weights, void* y, const moe_routing* routing, void* workspace,
+                size_t workspace_bytes, const moe_trace* trace, hipStream_t stream);
+
+/*
+ * Aux-loss-free bias update, in place:
+ *   bias[i] += gamma if n_routed * counts[i] <  total_assignments   (underloaded)
+ *   bias[i] -= gamma if n_routed * counts[i] >  total_assignments   (overloaded)
+ *   unchanged        if equal
+ * total_assignments is T*K of the batch the counts were taken over (so the
+ * threshold is the mean load T*K/N_r).  fp32 arithmetic; gamma = 0.001 in
+ * DeepSeek-V3.
+ */
+int moe_update_bias(float* bias, const int32_t* counts, int32_t n_routed, int64_t total_assignments, float gamma,
+                    hipStream_t stream);
+
+/*
+ * FP8 weight preparation (done once, offline): quantise `n` row-major
+ * [rows][cols] matrices (src_dtype F32 or BF16) to OCP E4M3 with one fp32
+ * scale per 128x128 block: scale = amax/448, code = E4M3(x * (448/amax))
+ * rounded to nearest even and saturated; scale 1 and zero codes for an
+ * all-zero block.  codes: [n][rows][cols] uint8; scales: [n][rows/128][cols/128].
+ * rows and cols must be multiples of 128.
+ */
+int moe_quantize_weight_e4m3(const void* src, int32_t src_dtype, int64_t n, int32_t rows, int32_t cols,
+                             uint8_t* codes, float* scales, hipStream_t stream);
+
+/*
+ * FP8 activation quantisation, as moe_forward applies it to u: per row, per
+ * 1x128 tile, scale = amax/448 and E4M3 codes (same rounding as above).
+ * src: [rows][cols] bf16; codes: [rows][cols]; scales: [rows][cols/128].
+ */
+int moe_quantize_act_e4m3(const void* src, int32_t rows, int32_t cols, uint8_t* codes, float* scales,
+                          hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_MI355X_H */

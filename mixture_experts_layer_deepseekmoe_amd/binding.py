@@ -1,0 +1,308 @@
+"""ctypes binding over libmoe_mi355x.so (the C ABI in include/moe.h).
+
+Argument marshalling only: every step of the layer runs in the library's HIP
+kernels.  torch tensors provide device memory and the current HIP stream;
+outputs and the workspace are allocated here with torch when the caller does
+not pass them.  There is no fallback: if the library is missing, loading
+fails with an error telling how to build it.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Dict, Optional
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmoe_mi355x.so")
+
+# moe_dtype
+F32, BF16, E4M3 = 0, 1, 2
+DTYPE_CODE = {"f32": F32, "bf16": BF16, "e4m3": E4M3}
+_TORCH_DT = {F32: torch.float32, BF16: torch.bfloat16}
+
+# moe_status
+MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_LAUNCH = range(5)
+
+EXPORTED = ("moe_status_str", "moe_version", "moe_workspace_size", "moe_route", "moe_forward",
+            "moe_update_bias", "moe_quantize_weight_e4m3", "moe_quantize_act_e4m3")
+
+
+class MoEError(RuntimeError):
+    def __init__(self, code: int, what: str):
+        super().__init__(f"{what}: {status_str(code)} ({code})")
+        self.code = code
+
+
+class Shape(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in
+                ("T", "d", "n_routed", "n_shared", "inter", "top_k", "x_dtype", "w_dtype", "out_dtype")]
+
+
+class Weights(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in
+                ("w_gate_up", "w_down", "ws_gate_up", "ws_down", "s_gate_up", "s_down", "ss_gate_up", "ss_down")]
+
+
+NUM_STAGES = 6
+STAGES = ("route", "group", "quant", "gate_up", "down", "combine")
+
+
+class Trace(ctypes.Structure):
+    _fields_ = [("start", ctypes.c_void_p * NUM_STAGES), ("stop", ctypes.c_void_p * NUM_STAGES)]
+
+
+class Routing(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in
+                ("topk_idx", "topk_gate", "expert_counts", "expert_offsets", "perm_token", "pos")]
+
+
+_lib = None
+
+
+def load_library() -> ctypes.CDLL:
+    """Load the HIP library (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                           "`python -m mixture_experts_layer_deepseekmoe_amd.build` (hipcc, gfx950)")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    lib.moe_status_str.restype = ctypes.c_char_p
+    lib.moe_status_str.argtypes = [ctypes.c_int]
+    lib.moe_version.restype = ctypes.c_char_p
+    lib.moe_version.argtypes = []
+    lib.moe_workspace_size.restype = ctypes.c_int
+    lib.moe_workspace_size.argtypes = [ctypes.POINTER(Shape), ctypes.POINTER(sz)]
+    lib.moe_route.restype = ctypes.c_int
+    lib.moe_route.argtypes = [ctypes.POINTER(Shape), vp, vp, vp, ctypes.POINTER(Routing), vp, sz, vp]
+    lib.moe_forward.restype = ctypes.c_int
+    lib.moe_forward.argtypes = [ctypes.POINTER(Shape), vp, vp, vp, ctypes.POINTER(Weights), vp,
+                                ctypes.POINTER(Routing), vp, sz, ctypes.POINTER(Trace), vp]
+    lib.moe_update_bias.restype = ctypes.c_int
+    lib.moe_update_bias.argtypes = [vp, vp, i32, i64, ctypes.c_float, vp]
+    lib.moe_quantize_weight_e4m3.restype = ctypes.c_int
+    lib.moe_quantize_weight_e4m3.argtypes = [vp, i32, i64, i32, i32, vp, vp, vp]
+    lib.moe_quantize_act_e4m3.restype = ctypes.c_int
+    lib.moe_quantize_act_e4m3.argtypes = [vp, i32, i32, vp, vp, vp]
+    _lib = lib
+    return lib
+
+
+def status_str(code: int) -> str:
+    return load_library().moe_status_str(code).decode()
+
+
+def version() -> str:
+    return load_library().moe_version().decode()
+
+
+def _check(code: int, what: str):
+    if code != MOE_OK:
+        raise MoEError(code, what)
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensors passed to the MoE library must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to the MoE library must be contiguous")
+    return t.data_ptr()
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+@dataclass
+class LayerShape:
+    T: int
+    d: int
+    n_routed: int
+    n_shared: int
+    inter: int
+    top_k: int
+    x_dtype: str = "bf16"
+    w_dtype: str = "bf16"
+    out_dtype: str = "f32"
+
+    @classmethod
+    def from_config(cls, cfg, T: Optional[int] = None) -> "LayerShape":
+        return cls(cfg.T if T is None else T, cfg.d, cfg.n_routed, cfg.n_shared, cfg.inter, cfg.top_k,
+                   cfg.x_dtype, cfg.w_dtype, cfg.out_dtype)
+
+    def c(self) -> Shape:
+        return Shape(self.T, self.d, self.n_routed, self.n_shared, self.inter, self.top_k,
+                     DTYPE_CODE[self.x_dtype], DTYPE_CODE[self.w_dtype], DTYPE_CODE[self.out_dtype])
+
+
+def workspace_size(shape: LayerShape) -> int:
+    n = ctypes.c_size_t(0)
+    _check(load_library().moe_workspace_size(ctypes.byref(shape.c()), ctypes.byref(n)), "moe_workspace_size")
+    return n.value
+
+
+def alloc_workspace(shape: LayerShape, device="cuda") -> torch.Tensor:
+    return torch.empty(max(workspace_size(shape), 1), dtype=torch.uint8, device=device)
+
+
+def alloc_routing(shape: LayerShape, device="cuda") -> Dict[str, torch.Tensor]:
+    T, K, N = shape.T, shape.top_k, shape.n_routed
+    i32 = torch.int32
+    return {
+        "topk_idx": torch.empty((T, K), dtype=i32, device=device),
+        "topk_gate": torch.empty((T, K), dtype=torch.float32, device=device),
+        "expert_counts": torch.empty((N,), dtype=i32, device=device),
+        "expert_offsets": torch.empty((N + 1,), dtype=i32, device=device),
+        "perm_token": torch.empty((T * K,), dtype=i32, device=device),
+        "pos": torch.empty((T, K), dtype=i32, device=device),
+    }
+
+
+def _routing_struct(r: Optional[Dict[str, torch.Tensor]]) -> Optional[Routing]:
+    if r is None:
+        return None
+    return Routing(*[_ptr(r.get(n)) for n, _ in Routing._fields_])
+
+
+def moe_route(shape: LayerShape, u: torch.Tensor, centroids: torch.Tensor, bias: torch.Tensor,
+              out: Optional[Dict[str, torch.Tensor]] = None,
+              workspace: Optional[torch.Tensor] = None) -> Dict[str, torch.Tensor]:
+    """Routing only (affinities, biased top-K, gates, grouping).  Returns the routing tensors."""
+    lib = load_library()
+    out = alloc_routing(shape, u.device) if out is None else out
+    ws = alloc_workspace(shape, u.device) if workspace is None else workspace
+    rc = lib.moe_route(ctypes.byref(shape.c()), _ptr(u), _ptr(centroids), _ptr(bias),
+                       ctypes.byref(_routing_struct(out)), _ptr(ws), ws.numel(), _stream())
+    _check(rc, "moe_route")
+    return out
+
+
+@dataclass
+class ExpertWeights:
+    """Device expert weights (bf16/f32), or e4m3 codes (uint8) plus fp32 block scales."""
+    w_gate_up: torch.Tensor
+    w_down: torch.Tensor
+    ws_gate_up: Optional[torch.Tensor] = None
+    ws_down: Optional[torch.Tensor] = None
+    s_gate_up: Optional[torch.Tensor] = None
+    s_down: Optional[torch.Tensor] = None
+    ss_gate_up: Optional[torch.Tensor] = None
+    ss_down: Optional[torch.Tensor] = None
+
+    def c(self) -> Weights:
+        f = lambda t: None if t is None or t.numel() == 0 else _ptr(t)
+        return Weights(f(self.w_gate_up), f(self.w_down), f(self.ws_gate_up), f(self.ws_down),
+                       f(self.s_gate_up), f(self.s_down), f(self.ss_gate_up), f(self.ss_down))
+
+
+def moe_forward(shape: LayerShape, u: torch.Tensor, centroids: torch.Tensor, bias: torch.Tensor,
+                weights: ExpertWeights, y: Optional[torch.Tensor] = None,
+                routing: Optional[Dict[str, torch.Tensor]] = None,
+                workspace: Optional[torch.Tensor] = None, trace: Optional[Trace] = None) -> torch.Tensor:
+    """The layer forward.  Returns y [T, d] in shape.out_dtype.  ``trace``: optional
+    per-stage hipEvent pairs (see HipEvents)."""
+    lib = load_library()
+    if y is None:
+        y = torch.empty((shape.T, shape.d), dtype=_TORCH_DT[DTYPE_CODE[shape.out_dtype]], device=u.device)
+    ws = alloc_workspace(shape, u.device) if workspace is None else workspace
+    rs = _routing_struct(routing)
+    rc = lib.moe_forward(ctypes.byref(shape.c()), _ptr(u), _ptr(centroids), _ptr(bias),
+                         ctypes.byref(weights.c()), _ptr(y), ctypes.byref(rs) if rs is not None else None,
+                         _ptr(ws), ws.numel(), ctypes.byref(trace) if trace is not None else None, _stream())
+    _check(rc, "moe_forward")
+    return y
+
+
+def moe_update_bias(bias: torch.Tensor, counts: torch.Tensor, total_assignments: int, gamma: float = 0.001):
+    """In-place aux-loss-free bias update on the GPU."""
+    rc = load_library().moe_update_bias(_ptr(bias), _ptr(counts), bias.numel(), int(total_assignments),
+                                        float(gamma), _stream())
+    _check(rc, "moe_update_bias")
+    return bias
+
+
+def moe_quantize_weight_e4m3(w: torch.Tensor):
+    """[n, rows, cols] (or [rows, cols]) f32/bf16 -> (uint8 codes, fp32 scales [n, rows/128, cols/128])."""
+    squeeze = w.dim() == 2
+    w3 = w.unsqueeze(0) if squeeze else w
+    n, rows, cols = w3.shape
+    codes = torch.empty((n, rows, cols), dtype=torch.uint8, device=w.device)
+    scales = torch.empty((n, rows // 128, cols // 128), dtype=torch.float32, device=w.device)
+    code = {torch.float32: F32, torch.bfloat16: BF16}[w.dtype]
+    rc = load_library().moe_quantize_weight_e4m3(_ptr(w3) if n else None, code, n, rows, cols,
+                                                 _ptr(codes) if n else None, _ptr(scales) if n else None, _stream())
+    _check(rc, "moe_quantize_weight_e4m3")
+    return (codes[0], scales[0]) if squeeze else (codes, scales)
+
+
+def moe_quantize_act_e4m3(x: torch.Tensor):
+    """[rows, cols] bf16 -> (uint8 codes, fp32 scales [rows, cols/128])."""
+    rows, cols = x.shape
+    codes = torch.empty((rows, cols), dtype=torch.uint8, device=x.device)
+    scales = torch.empty((rows, cols // 128), dtype=torch.float32, device=x.device)
+    rc = load_library().moe_quantize_act_e4m3(_ptr(x) if rows else None, rows, cols,
+                                              _ptr(codes) if rows else None, _ptr(scales) if rows else None,
+                                              _stream())
+    _check(rc, "moe_quantize_act_e4m3")
+    return codes, scales
+
+
+def prepare_weights(cfg, inputs) -> ExpertWeights:
+    """Device weights for moe_forward from seeded inputs (quantised on the GPU for e4m3 configs)."""
+    dev = torch.device("cuda")
+    mv = lambda t: t.to(dev).contiguous()
+    if cfg.w_dtype != "e4m3":
+        return ExpertWeights(mv(inputs.w_gate_up), mv(inputs.w_down),
+                             mv(inputs.ws_gate_up) if cfg.n_shared else None,
+                             mv(inputs.ws_down) if cfg.n_shared else None)
+    gq, gs = moe_quantize_weight_e4m3(mv(inputs.w_gate_up))
+    dq, ds = moe_quantize_weight_e4m3(mv(inputs.w_down))
+    if cfg.n_shared:
+        sgq, sgs = moe_quantize_weight_e4m3(mv(inputs.ws_gate_up))
+        sdq, sds = moe_quantize_weight_e4m3(mv(inputs.ws_down))
+    else:
+        sgq = sgs = sdq = sds = None
+    return ExpertWeights(gq, dq, sgq, sdq, gs, ds, sgs, sds)
+
+
+class HipEvents:
+    """Per-stage hipEvent pairs for moe_forward's trace argument, created
+    through the HIP runtime (the same events the library records on its
+    stream), with elapsed-time readout."""
+
+    def __init__(self):
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.trace = Trace()
+        for i in range(NUM_STAGES):
+            for arr in (self.trace.start, self.trace.stop):
+                ev = ctypes.c_void_p()
+                if self.hip.hipEventCreate(ctypes.byref(ev)) != 0:
+                    raise RuntimeError("hipEventCreate failed")
+                arr[i] = ev.value
+
+    def elapsed_ms(self) -> Dict[str, float]:
+        out = {}
+        for i, name in enumerate(STAGES):
+            self.hip.hipEventSynchronize(self.trace.stop[i])
+            ms = ctypes.c_float(0)
+            if self.hip.hipEventElapsedTime(ctypes.byref(ms), self.trace.start[i], self.trace.stop[i]) != 0:
+                raise RuntimeError("hipEventElapsedTime failed")
+            out[name] = ms.value
+        return out
+
+    def close(self):
+        for i in range(NUM_STAGES):
+            self.hip.hipEventDestroy(self.trace.start[i])
+            self.hip.hipEventDestroy(self.trace.stop[i])

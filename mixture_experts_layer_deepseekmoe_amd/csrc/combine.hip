@@ -1,0 +1,100 @@
+// Combine (DeepSeek-V3 Technical Report summary, section 2):
+//   h'_t = u_t + sum_s FFN^(s)_s(u_t) + sum_k g_{t,k} FFN^(r)_{idx[t,k]}(u_t)
+// Each token's expert outputs are read from the grouped rows (shared expert s
+// at row T*K + s*T + t, routed choice k at row pos[t,k]) and summed in fp32 in
+// a fixed order: u, then the shared experts in order, then the routed choices
+// in selection order.  No atomics: the result is bit-reproducible.
+// One wave per token, 8 columns per lane per step (16-byte bf16 loads).
+#include "kernels.hpp"
+#include "moe_common.hpp"
+
+namespace moe {
+
+namespace {
+
+template <int F>
+__device__ __forceinline__ void load8(const void* base, size_t off, float v[8]) {
+  if constexpr (F == FMT_F32) {
+    const float4 a = *reinterpret_cast<const float4*>(static_cast<const float*>(base) + off);
+    const float4 b = *reinterpret_cast<const float4*>(static_cast<const float*>(base) + off + 4);
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  } else {
+    const uint4 r = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + off);
+    const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = bf16_to_f32(static_cast<uint16_t>(w[i] & 0xffffu));
+      v[2 * i + 1] = bf16_to_f32(static_cast<uint16_t>(w[i] >> 16));
+    }
+  }
+}
+
+template <int XF, int YF, int OF>
+__global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= a.T) return;
+  float gk = 0.f;
+  int pk = 0;
+  if (lane < a.top_k) {
+    gk = a.gate[static_cast<size_t>(t) * a.top_k + lane];
+    pk = a.pos[static_cast<size_t>(t) * a.top_k + lane];
+  }
+  // Broadcast the K gates and rows while every lane is still active.
+  float gs[MAX_TOPK];
+  int ps[MAX_TOPK];
+#pragma unroll
+  for (int k = 0; k < MAX_TOPK; ++k) {
+    gs[k] = __shfl(gk, k);
+    ps[k] = __shfl(pk, k);
+  }
+  const size_t d = a.d;
+  for (int c = lane * 8; c < a.d; c += 64 * 8) {
+    float acc[8], v[8];
+    load8<XF>(a.u, static_cast<size_t>(t) * d + c, acc);
+    for (int s = 0; s < a.n_shared; ++s) {
+      load8<YF>(a.yrows, static_cast<size_t>(a.TK + static_cast<long long>(s) * a.T + t) * d + c, v);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] += v[i];
+    }
+#pragma unroll
+    for (int k = 0; k < MAX_TOPK; ++k) {
+      if (k >= a.top_k) break;
+      load8<YF>(a.yrows, static_cast<size_t>(ps[k]) * d + c, v);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] = fmaf(gs[k], v[i], acc[i]);
+    }
+    if constexpr (OF == FMT_F32) {
+      float* o = static_cast<float*>(a.out) + static_cast<size_t>(t) * d + c;
+      *reinterpret_cast<float4*>(o) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+      *reinterpret_cast<float4*>(o + 4) = make_float4(acc[4], acc[5], acc[6], acc[7]);
+    } else {
+      uint32_t w[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        w[i] = static_cast<uint32_t>(f32_to_bf16(acc[2 * i])) | (static_cast<uint32_t>(f32_to_bf16(acc[2 * i + 1])) << 16);
+      *reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.out) + static_cast<size_t>(t) * d + c) =
+          make_uint4(w[0], w[1], w[2], w[3]);
+    }
+  }
+}
+
+template <int XF, int YF>
+hipError_t launch_o(int ofmt, const CombineArgs& a, hipStream_t s) {
+  const dim3 grid(ceil_div(a.T, 4)), block(256);
+  if (ofmt == FMT_F32)
+    hipLaunchKernelGGL((combine_kernel<XF, YF, FMT_F32>), grid, block, 0, s, a);
+  else
+    hipLaunchKernelGGL((combine_kernel<XF, YF, FMT_BF16>), grid, block, 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_combine(int xfmt, int yfmt, int ofmt, const CombineArgs& a, hipStream_t s) {
+  if (a.T == 0) return hipSuccess;
+  if (xfmt == FMT_F32) return yfmt == FMT_F32 ? launch_o<FMT_F32, FMT_F32>(ofmt, a, s) : launch_o<FMT_F32, FMT_BF16>(ofmt, a, s);
+  return yfmt == FMT_F32 ? launch_o<FMT_BF16, FMT_F32>(ofmt, a, s) : launch_o<FMT_BF16, FMT_BF16>(ofmt, a, s);
+}
+
+}  // namespace moe

@@ -1,0 +1,259 @@
+// Grouping tokens by expert: a stable counting sort in three passes, plus the
+// small kernels around it (FP8 quantisers, the aux-loss-free bias update).
+//
+//   hist    per block of 256 tokens, per-expert assignment counts (LDS atomics
+//           only count, so the result is order independent)
+//   scan    one block: per-(block, expert) exclusive prefix over blocks, the
+//           expert counts and offsets (exclusive prefix over experts), and
+//           the m-tile list of the grouped GEMMs
+//   permute per token block again: a token's rank among the block's tokens
+//           routed to the same expert comes from a per-expert bitmask of the
+//           block's tokens (popcount of the lower bits), so grouped row
+//           p = offsets[e] + base[block][e] + rank is the stable
+//           (token-ascending) position.  No atomic decides any position.
+#include "kernels.hpp"
+#include "moe_common.hpp"
+
+namespace moe {
+
+namespace {
+
+__global__ __launch_bounds__(GROUP_TB) void hist_kernel(GroupArgs a) {
+  __shared__ int h[MAX_ROUTED];
+  for (int e = threadIdx.x; e < a.n_routed; e += GROUP_TB) h[e] = 0;
+  __syncthreads();
+  const int t = blockIdx.x * GROUP_TB + threadIdx.x;
+  if (t < a.T) {
+    for (int k = 0; k < a.top_k; ++k) atomicAdd(&h[a.idx[static_cast<size_t>(t) * a.top_k + k]], 1);
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < a.n_routed; e += GROUP_TB)
+    a.block_hist[static_cast<size_t>(blockIdx.x) * a.n_routed + e] = h[e];
+}
+
+constexpr int SCAN_THREADS = 1024;
+
+__global__ __launch_bounds__(SCAN_THREADS) void scan_kernel(GroupArgs a, int nblk) {
+  __shared__ int sc[MAX_ROUTED + MAX_SHARED + 1];
+  __shared__ int tmp[MAX_ROUTED + MAX_SHARED + 1];
+  const int tid = threadIdx.x;
+  const int nr = a.n_routed;
+  // 1. per-expert totals and per-block bases
+  for (int e = tid; e < nr; e += SCAN_THREADS) {
+    int run = 0;
+    for (int b = 0; b < nblk; ++b) {
+      int* p = a.block_hist + static_cast<size_t>(b) * nr + e;
+      const int h = *p;
+      *p = run;
+      run += h;
+    }
+    a.counts[e] = run;
+    sc[e] = run;
+  }
+  __syncthreads();
+  // 2. inclusive scan (Hillis-Steele) over experts, then offsets
+  for (int off = 1; off < nr; off <<= 1) {
+    for (int e = tid; e < nr; e += SCAN_THREADS) tmp[e] = sc[e] + (e >= off ? sc[e - off] : 0);
+    __syncthreads();
+    for (int e = tid; e < nr; e += SCAN_THREADS) sc[e] = tmp[e];
+    __syncthreads();
+  }
+  for (int e = tid; e <= nr; e += SCAN_THREADS) a.offsets[e] = e == 0 ? 0 : sc[e - 1];
+  if (a.mtiles == nullptr) return;
+  __syncthreads();
+  // 3. m-tiles: group g (routed experts, then shared experts over all T
+  //    tokens) is cut into ceil(M_g / BM) tiles of balanced size.
+  const int ng = nr + a.n_shared;
+  const long long TK = static_cast<long long>(a.T) * a.top_k;
+  for (int g = tid; g < ng; g += SCAN_THREADS) {
+    const int M = g < nr ? (sc[g] - (g ? sc[g - 1] : 0)) : a.T;
+    tmp[g] = ceil_div(M, GG_BM);
+  }
+  __syncthreads();
+  if (tid == 0) {   // at most 520 groups: a short serial scan
+    int run = 0;
+    for (int g = 0; g < ng; ++g) { const int n = tmp[g]; tmp[g] = run; run += n; }
+    tmp[ng] = run;
+    *a.mt_count = run;
+  }
+  __syncthreads();
+  for (int g = tid; g < ng; g += SCAN_THREADS) {
+    const long long M = g < nr ? (sc[g] - (g ? sc[g - 1] : 0)) : a.T;
+    const long long first = g < nr ? (g ? sc[g - 1] : 0) : TK + static_cast<long long>(g - nr) * a.T;
+    const int n = tmp[g + 1] - tmp[g];
+    for (int k = 0; k < n; ++k) {
+      const long long r0 = k * M / n, r1 = (k + 1) * M / n;
+      a.mtiles[tmp[g] + k] = make_int4(g, static_cast<int>(first + r0), static_cast<int>(r1 - r0), 0);
+    }
+  }
+}
+
+__global__ __launch_bounds__(GROUP_TB) void permute_kernel(GroupArgs a) {
+  __shared__ uint32_t mask[MAX_ROUTED][GROUP_TB / 32];
+  for (int i = threadIdx.x; i < a.n_routed * (GROUP_TB / 32); i += GROUP_TB) (&mask[0][0])[i] = 0;
+  __syncthreads();
+  const int tl = threadIdx.x;
+  const int t = blockIdx.x * GROUP_TB + tl;
+  const int word = tl >> 5;
+  const uint32_t bit = 1u << (tl & 31);
+  if (t < a.T) {
+    for (int k = 0; k < a.top_k; ++k) atomicOr(&mask[a.idx[static_cast<size_t>(t) * a.top_k + k]][word], bit);
+  }
+  __syncthreads();
+  if (t < a.T) {
+    for (int k = 0; k < a.top_k; ++k) {
+      const size_t ik = static_cast<size_t>(t) * a.top_k + k;
+      const int e = a.idx[ik];
+      int rank = __popc(mask[e][word] & (bit - 1u));
+      for (int wd = 0; wd < word; ++wd) rank += __popc(mask[e][wd]);
+      const int p = a.offsets[e] + a.block_hist[static_cast<size_t>(blockIdx.x) * a.n_routed + e] + rank;
+      a.pos[ik] = p;
+      a.perm_token[p] = t;
+    }
+  }
+}
+
+// FP8 activation quantiser: per row, per 1x128 tile, scale = amax / 448,
+// codes = E4M3(x * (448 / amax)); scale 1 and zero codes for an all-zero tile.
+// One wave per row; each 16-lane group handles one 128-column tile at a time.
+__global__ __launch_bounds__(256) void quant_act_kernel(const uint16_t* __restrict__ x, int rows, int cols,
+                                                        uint8_t* __restrict__ q, float* __restrict__ scale) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const int ntile = cols / 128;
+  const int grp = lane >> 4, gl = lane & 15;
+  for (int tb = 0; tb < ntile; tb += 4) {
+    const int tile = tb + grp;
+    const bool live = tile < ntile;
+    const size_t off = static_cast<size_t>(row) * cols + tile * 128 + gl * 8;
+    uint4 raw = make_uint4(0, 0, 0, 0);
+    if (live) raw = *reinterpret_cast<const uint4*>(x + off);
+    float v[8];
+    const uint32_t wds[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = bf16_to_f32(static_cast<uint16_t>(wds[i] & 0xffffu));
+      v[2 * i + 1] = bf16_to_f32(static_cast<uint16_t>(wds[i] >> 16));
+    }
+    float m = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(v[i]));
+    m = wave_max_16(m);
+    const float sc = m == 0.f ? 1.f : m / 448.f;
+    const float inv = m == 0.f ? 0.f : 448.f / m;
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) lo |= f32_to_e4m3(v[i] * inv) << (8 * i);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) hi |= f32_to_e4m3(v[4 + i] * inv) << (8 * i);
+    if (live) {
+      *reinterpret_cast<uint2*>(q + off) = make_uint2(lo, hi);
+      if (gl == 0) scale[static_cast<size_t>(row) * ntile + tile] = sc;
+    }
+  }
+}
+
+// FP8 weight quantiser: one block per 128x128 block of one matrix.
+template <int FMT>
+__global__ __launch_bounds__(256) void quant_weight_kernel(const void* __restrict__ w, int rows, int cols,
+                                                           uint8_t* __restrict__ q, float* __restrict__ scale) {
+  const int rb = rows / 128, cb = cols / 128;
+  const long long blk = blockIdx.x;
+  const long long mat = blk / (rb * cb);
+  const int bi = static_cast<int>((blk / cb) % rb), bj = static_cast<int>(blk % cb);
+  const size_t base = static_cast<size_t>(mat) * rows * cols + static_cast<size_t>(bi) * 128 * cols + bj * 128;
+  float v[8][8];
+  float m = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int c = threadIdx.x + 256 * i;
+    const size_t off = base + static_cast<size_t>(c >> 4) * cols + (c & 15) * 8;
+    if constexpr (FMT == FMT_BF16) {
+      const uint4 raw = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(w) + off);
+      const uint32_t wds[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        v[i][2 * j] = bf16_to_f32(static_cast<uint16_t>(wds[j] & 0xffffu));
+        v[i][2 * j + 1] = bf16_to_f32(static_cast<uint16_t>(wds[j] >> 16));
+      }
+    } else {
+      const float4 r0 = *reinterpret_cast<const float4*>(static_cast<const float*>(w) + off);
+      const float4 r1 = *reinterpret_cast<const float4*>(static_cast<const float*>(w) + off + 4);
+      v[i][0] = r0.x; v[i][1] = r0.y; v[i][2] = r0.z; v[i][3] = r0.w;
+      v[i][4] = r1.x; v[i][5] = r1.y; v[i][6] = r1.z; v[i][7] = r1.w;
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(v[i][j]));
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+  __shared__ float red[4];
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const float sc = m == 0.f ? 1.f : m / 448.f;
+  const float inv = m == 0.f ? 0.f : 448.f / m;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int c = threadIdx.x + 256 * i;
+    const size_t off = base + static_cast<size_t>(c >> 4) * cols + (c & 15) * 8;
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) lo |= f32_to_e4m3(v[i][j] * inv) << (8 * j);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) hi |= f32_to_e4m3(v[i][4 + j] * inv) << (8 * j);
+    *reinterpret_cast<uint2*>(q + off) = make_uint2(lo, hi);
+  }
+  if (threadIdx.x == 0) scale[blk] = sc;
+}
+
+// Aux-loss-free balancing (section 2 of the xyznot summary): an expert whose
+// load is above the batch mean T*K/N_r (decided as N_r * count > T*K) gets
+// b -= gamma, one below it b += gamma, one exactly at it is left alone.
+__global__ void bias_update_kernel(float* bias, const int32_t* counts, int n_routed, long long total, float gamma) {
+  const int e = blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= n_routed) return;
+  const long long diff = total - static_cast<long long>(n_routed) * counts[e];
+  const float step = diff > 0 ? gamma : (diff < 0 ? -gamma : 0.f);
+  bias[e] = bias[e] + step;
+}
+
+}  // namespace
+
+hipError_t launch_group(const GroupArgs& a, hipStream_t s) {
+  const int nblk = ceil_div(a.T, GROUP_TB);
+  if (nblk > 0) hipLaunchKernelGGL(hist_kernel, dim3(nblk), dim3(GROUP_TB), 0, s, a);
+  hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(SCAN_THREADS), 0, s, a, nblk);
+  if (nblk > 0) hipLaunchKernelGGL(permute_kernel, dim3(nblk), dim3(GROUP_TB), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_act(const void* x, int rows, int cols, uint8_t* q, float* scale, hipStream_t s) {
+  if (rows == 0) return hipSuccess;
+  hipLaunchKernelGGL(quant_act_kernel, dim3(ceil_div(rows, 4)), dim3(256), 0, s,
+                     static_cast<const uint16_t*>(x), rows, cols, q, scale);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_weight(int fmt, const void* w, long long n, int rows, int cols, uint8_t* q, float* scale,
+                               hipStream_t s) {
+  const long long nblk = n * (rows / 128) * (cols / 128);
+  if (nblk == 0) return hipSuccess;
+  if (fmt == FMT_BF16)
+    hipLaunchKernelGGL(quant_weight_kernel<FMT_BF16>, dim3(static_cast<unsigned>(nblk)), dim3(256), 0, s, w, rows,
+                       cols, q, scale);
+  else
+    hipLaunchKernelGGL(quant_weight_kernel<FMT_F32>, dim3(static_cast<unsigned>(nblk)), dim3(256), 0, s, w, rows,
+                       cols, q, scale);
+  return hipGetLastError();
+}
+
+hipError_t launch_bias_update(float* bias, const int32_t* counts, int n_routed, long long total, float gamma,
+                              hipStream_t s) {
+  hipLaunchKernelGGL(bias_update_kernel, dim3(ceil_div(n_routed, 256)), dim3(256), 0, s, bias, counts, n_routed,
+                     total, gamma);
+  return hipGetLastError();
+}
+
+}  // namespace moe

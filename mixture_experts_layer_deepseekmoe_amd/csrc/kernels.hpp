@@ -1,0 +1,102 @@
+// Internal launcher interface between the C-ABI layer and the kernel files.
+// Every launcher enqueues on the given stream and returns the launch status.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "moe_common.hpp"
+
+namespace moe {
+
+// Tile rows of the grouped GEMMs (m-tiles hold at most this many rows).
+constexpr int GG_BM = 256;
+// B rows per grouped-GEMM tile: 128 gate + 128 up rows (128 h columns), or
+// 256 output columns for the down projection.
+constexpr int GG_BNW = 256;
+constexpr int GG_HCOLS = 128;
+constexpr int ROUTE_BT = 32;      // tokens per router block
+constexpr int GROUP_TB = 256;     // tokens per histogram / permute block
+constexpr int MAX_ROUTED = 512;
+constexpr int MAX_SHARED = 8;
+constexpr int MAX_TOPK = 16;
+
+struct RouteArgs {
+  const void* u;          // [T][d] fmt
+  const void* centroids;  // [N_r][d] fmt
+  const float* bias;      // [N_r]
+  int T, d, n_routed, top_k;
+  int32_t* idx;           // [T][K]
+  float* gate;            // [T][K]
+};
+
+struct GroupArgs {
+  const int32_t* idx;     // [T][K]
+  int T, top_k, n_routed, n_shared;
+  int32_t* block_hist;    // [nblk][N_r] scratch
+  int32_t* counts;        // [N_r]
+  int32_t* offsets;       // [N_r + 1]
+  int32_t* perm_token;    // [T*K]
+  int32_t* pos;           // [T][K]
+  int4* mtiles;           // [max_mtiles] (group, first grouped row, rows, 0); null: routing only
+  int32_t* mt_count;      // [1]
+};
+
+struct GateUpArgs {
+  const void* x;          // GEMM input rows by token: u (f32/bf16) or its e4m3 codes
+  const float* x_scale;   // e4m3: [T][d/128]
+  const int32_t* perm_token;
+  int T, TK, n_routed, d, inter;
+  const void* w_routed;   // [N_r][2I][d]
+  const void* w_shared;   // [N_s][2I][d]
+  const float* sw_routed; // e4m3: [N_r][2I/128][d/128]
+  const float* sw_shared;
+  const int4* mtiles;
+  const int32_t* mt_count;
+  int max_mtiles;
+  void* h;                // [R][I]: f32 / bf16 / e4m3 codes
+  float* h_scale;         // e4m3: [R][I/128]
+};
+
+struct DownArgs {
+  const void* h;          // [R][I]
+  const float* h_scale;   // e4m3: [R][I/128]
+  int n_routed, d, inter;
+  const void* w_routed;   // [N_r][d][I]
+  const void* w_shared;   // [N_s][d][I]
+  const float* sw_routed; // e4m3: [N_r][d/128][I/128]
+  const float* sw_shared;
+  const int4* mtiles;
+  const int32_t* mt_count;
+  int max_mtiles;
+  void* y;                // [R][d]: f32 (f32 path) or bf16
+};
+
+struct CombineArgs {
+  const void* u;          // [T][d]
+  const void* yrows;      // [R][d] expert outputs in grouped row order
+  const float* gate;      // [T][K]
+  const int32_t* pos;     // [T][K]
+  int T, d, top_k, n_shared;
+  long long TK;
+  void* out;              // [T][d]
+};
+
+hipError_t launch_route(int fmt, const RouteArgs& a, hipStream_t s);
+hipError_t launch_group(const GroupArgs& a, hipStream_t s);
+hipError_t launch_quant_act(const void* x, int rows, int cols, uint8_t* q, float* scale, hipStream_t s);
+hipError_t launch_quant_weight(int fmt, const void* w, long long n, int rows, int cols, uint8_t* q, float* scale,
+                               hipStream_t s);
+hipError_t launch_bias_update(float* bias, const int32_t* counts, int n_routed, long long total, float gamma,
+                              hipStream_t s);
+hipError_t launch_gateup(int fmt, const GateUpArgs& a, hipStream_t s);
+hipError_t launch_down(int fmt, const DownArgs& a, hipStream_t s);
+hipError_t launch_combine(int xfmt, int yfmt, int ofmt, const CombineArgs& a, hipStream_t s);
+
+inline int max_mtiles(long long T, int K, int n_routed, int n_shared) {
+  // sum over groups of ceil(M_g / BM) <= (T*K)/BM + N_r + N_s * ceil(T/BM)
+  return static_cast<int>((T * K) / GG_BM + n_routed + n_shared * ((T + GG_BM - 1) / GG_BM));
+}
+
+}  // namespace moe

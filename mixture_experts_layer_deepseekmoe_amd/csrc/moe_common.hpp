@@ -1,0 +1,97 @@
+// Shared device helpers for the gfx950 (CDNA4) DeepSeekMoE kernels:
+// number formats, MFMA wrappers, wave reductions.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+// Element formats handled by the kernels.
+enum : int { FMT_F32 = 0, FMT_BF16 = 1, FMT_E4M3 = 2 };
+
+constexpr int WAVE = 64;
+
+// ---------------------------------------------------------------- bf16
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+  return __uint_as_float(static_cast<uint32_t>(h) << 16);
+}
+
+// Round to nearest, ties to even; NaN stays NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+// ---------------------------------------------------------------- OCP FP8 E4M3
+//
+// E4M3: 1 sign, 4 exponent (bias 7), 3 mantissa bits; largest finite 448,
+// no infinities, S.1111.111 is NaN, subnormals m/8 * 2^-6.  Encoding rounds
+// to nearest with ties to the even code and saturates at +-448 (values at
+// or above the 464 midpoint clamp to 448; non-finite input is outside the
+// contract and also clamps).  The sign is kept, so -0 encodes as 0x80.
+__device__ __forceinline__ uint32_t f32_to_e4m3(float x) {
+  const uint32_t sign = (__float_as_uint(x) >> 24) & 0x80u;
+  const float a = fabsf(x);
+  if (!(a < 464.0f)) return sign | 0x7Eu;
+  if (a < 0.015625f) {                       // below 2^-6: the subnormal grid, step 2^-9
+    const float q = __builtin_rintf(a * 512.0f);   // exact scaling, round half to even
+    return sign | static_cast<uint32_t>(q);        // q == 8 is the smallest normal, code 0x08
+  }
+  const uint32_t ua = __float_as_uint(a);
+  uint32_t e = (ua >> 23) - 127u + 7u;       // 1..15
+  uint32_t m = (ua >> 20) & 7u;
+  const uint32_t rest = ua & 0xFFFFFu;
+  if (rest > 0x80000u || (rest == 0x80000u && (m & 1u))) {
+    if (++m == 8u) { m = 0; ++e; }
+  }
+  return sign | (e << 3) | m;
+}
+
+// ---------------------------------------------------------------- MFMA
+//
+// 16x16 output tiles on one wave.  Operand fragments: lane l supplies row
+// (l & 15) of A (column (l & 15) of B) for a run of consecutive k chosen by
+// lane group l >> 4; A and B use the same k assignment, so any fixed
+// assignment gives the exact dot products.  Output: lane l holds rows
+// 4*(l >> 4) + r, r = 0..3, of column (l & 15).
+
+__device__ __forceinline__ f32x4 mfma_bf16(const uint4 a, const uint4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b),
+                                                 c, 0, 0, 0);
+}
+
+// 16x16x128 OCP-e4m3 product with unit block scales (scale operands of zero
+// select the unscaled instruction).
+__device__ __forceinline__ f32x4 mfma_e4m3(const i32x8 a, const i32x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4 mfma_f32(const float a, const float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// ---------------------------------------------------------------- reductions
+
+__device__ __forceinline__ float wave_max_16(float v) {  // over lanes sharing l >> 4
+  v = fmaxf(v, __shfl_xor(v, 1));
+  v = fmaxf(v, __shfl_xor(v, 2));
+  v = fmaxf(v, __shfl_xor(v, 4));
+  v = fmaxf(v, __shfl_xor(v, 8));
+  return v;
+}
+
+__device__ __forceinline__ float silu_f32(float g) { return g / (1.0f + expf(-g)); }
+
+__device__ __forceinline__ float sigmoid_f32(float z) { return 1.0f / (1.0f + expf(-z)); }
+
+__host__ __device__ constexpr int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+}  // namespace moe

@@ -1,0 +1,93 @@
+"""Helpers for comparing the GPU library with the CPU oracle.
+
+Routing comparison (selection is discrete, so it must match exactly except
+where the biased scores are within 1e-6 of a tie):
+  * tokens whose oracle gap v_(K) - v_(K+1) exceeds 1e-6: the GPU's set of
+    experts equals the oracle's;
+  * near-tie tokens: the GPU's set holds every expert with v > v_(K) + 1e-6
+    and only experts with v >= v_(K) - 1e-6; they are counted and reported.
+The oracle then adopts the GPU's selection, so grouping (counts, offsets,
+perm_token, pos) is compared bit-exactly and outputs element-wise.
+"""
+
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+from moe_workloads import to_numpy_f32
+from oracle import moe_oracle as O
+
+BAND = 1e-6
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def check_selection(v: np.ndarray, gap: np.ndarray, oracle_idx: np.ndarray, gpu_idx: np.ndarray, k: int) -> int:
+    """Assert the selection rule; return the number of near-tie tokens."""
+    T = v.shape[0]
+    near = gap <= BAND
+    n = v.shape[1]
+    for t in range(T):
+        g = gpu_idx[t]
+        assert len(set(g.tolist())) == k, f"token {t}: repeated experts {g}"
+        assert ((g >= 0) & (g < n)).all(), f"token {t}: out of range {g}"
+        if not near[t]:
+            assert set(g.tolist()) == set(oracle_idx[t].tolist()), \
+                f"token {t}: gpu {sorted(g.tolist())} oracle {sorted(oracle_idx[t].tolist())} gap {gap[t]}"
+        else:
+            vk = v[t, oracle_idx[t, k - 1]]
+            must = set(np.nonzero(v[t] > vk + BAND)[0].tolist())
+            may = set(np.nonzero(v[t] >= vk - BAND)[0].tolist())
+            gs = set(g.tolist())
+            assert must <= gs <= may, f"near-tie token {t}: {gs} not within [{must}, {may}]"
+    return int(near.sum())
+
+
+def check_routing(out: dict, u: np.ndarray, E: np.ndarray, b: np.ndarray, k: int, n_routed: int) -> dict:
+    """Full routing parity.  Returns the oracle route (with the GPU's selection adopted)."""
+    gpu_idx = out["topk_idx"].cpu().numpy()
+    r = O.route(u, E, b, k)
+    near = check_selection(r["v"], r["gap"], r["idx"], gpu_idx, k)
+    r = O.route(u, E, b, k, selection=gpu_idx)
+    gates = out["topk_gate"].cpu().numpy().astype(np.float64)
+    np.testing.assert_allclose(gates, r["gate"], rtol=2e-6, atol=2e-7)
+    np.testing.assert_allclose(gates.sum(axis=1), 1.0, atol=2e-6)
+    # informational: the GPU lists a token's experts in descending v
+    vsel = np.take_along_axis(r["v"], gpu_idx.astype(np.int64), 1)
+    order_ok = (np.diff(vsel, axis=1) <= BAND).all()
+    grp = O.group_by_expert(gpu_idx, n_routed)
+    for key in ("expert_counts", "expert_offsets", "perm_token", "pos"):
+        ref = grp[{"expert_counts": "counts", "expert_offsets": "offsets"}.get(key, key)]
+        got = out[key].cpu().numpy()
+        assert got.shape == ref.shape and (got == ref).all(), f"{key} differs"
+    r["near_ties"] = near
+    r["order_ok"] = bool(order_ok)
+    return r
+
+
+def output_errors(y_gpu: np.ndarray, y_orc: np.ndarray, u: np.ndarray) -> dict:
+    err = np.abs(y_gpu.astype(np.float64) - y_orc)
+    rms = float(np.sqrt(np.mean(y_orc ** 2)))
+    branch = y_orc - u.astype(np.float64)
+    brms = float(np.sqrt(np.mean(branch ** 2))) or 1.0
+    return {"max_abs": float(err.max()) if err.size else 0.0, "rms": rms,
+            "rel_to_rms": float(err.max() / rms) if err.size else 0.0,
+            "branch_rel": float(err.max() / brms) if err.size else 0.0}
+
+
+def expert_fns(inp, device_weights: bool):
+    """Oracle-side accessors of the expert weights (downloaded on demand)."""
+    def routed(e):
+        return to_numpy_f32(inp.w_gate_up[e]), to_numpy_f32(inp.w_down[e])
+    shared = [(to_numpy_f32(inp.ws_gate_up[s]), to_numpy_f32(inp.ws_down[s])) for s in range(inp.cfg.n_shared)]
+    return routed, shared
+
+
+def rows_of(t: torch.Tensor) -> np.ndarray:
+    return t.detach().float().cpu().numpy()

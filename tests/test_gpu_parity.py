@@ -1,0 +1,224 @@
+"""GPU parity: the HIP library (called through its C ABI) against the CPU oracle.
+
+Bar: expert indices, counts, offsets, perm_token and pos bit-exact (near ties
+within 1e-6 of the K-th biased score allowed and counted); gates to fp32
+rounding; FP8 codes and scales of the quantisers bit-exact; outputs within
+max|y_gpu - y_oracle| <= 1e-2 * rms(y_oracle) (bf16 and fp32 configs) or
+4e-2 * rms(y_oracle) (FP8).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import mixture_experts_layer_deepseekmoe_amd as moe
+from moe_workloads import CONFIGS, PARITY_CONFIGS, make_inputs, to_numpy_f32
+from oracle import moe_oracle as O
+from tests.parity import check_routing, expert_fns, output_errors, rows_of, say
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"bf16": 1e-2, "f32": 1e-2, "e4m3": 4e-2}
+DEV = "cuda"
+
+
+def _dev(inp):
+    return (inp.u.to(DEV).contiguous(), inp.centroids.to(DEV).contiguous(), inp.bias.to(DEV).contiguous())
+
+
+def _run_forward(cfg, inp, weights=None):
+    shape = moe.LayerShape.from_config(cfg)
+    u, E, b = _dev(inp)
+    w = moe.prepare_weights(cfg, inp) if weights is None else weights
+    routing = moe.alloc_routing(shape)
+    y = moe.moe_forward(shape, u, E, b, w, routing=routing)
+    torch.cuda.synchronize()
+    return y, routing, w
+
+
+# ------------------------------------------------------------------ quantisers
+
+def test_quantize_weight_e4m3_bitexact():
+    say("case: quantize_weight_e4m3 [3,256,384] bf16")
+    g = torch.Generator().manual_seed(1)
+    w = (torch.randn((3, 256, 384), generator=g) * 0.02).to(torch.bfloat16)
+    w[1, :128, 128:256] = 0
+    w[2, 128:, :128] *= 1000
+    codes, scales = moe.moe_quantize_weight_e4m3(w.to(DEV))
+    torch.cuda.synchronize()
+    for m in range(3):
+        q, s = O.quantize_weight_128x128(to_numpy_f32(w[m]))
+        assert (codes[m].cpu().numpy() == q).all()
+        assert (scales[m].cpu().numpy() == s).all()
+
+
+def test_quantize_weight_e4m3_f32_source():
+    say("case: quantize_weight_e4m3 [128,256] f32")
+    g = torch.Generator().manual_seed(2)
+    w = torch.randn((128, 256), generator=g) * 3
+    codes, scales = moe.moe_quantize_weight_e4m3(w.to(DEV))
+    torch.cuda.synchronize()
+    q, s = O.quantize_weight_128x128(w.numpy())
+    assert (codes.cpu().numpy() == q).all() and (scales.cpu().numpy() == s).all()
+
+
+def test_quantize_act_e4m3_bitexact():
+    say("case: quantize_act_e4m3 [37,640] bf16")
+    g = torch.Generator().manual_seed(3)
+    x = (torch.randn((37, 640), generator=g) * 2).to(torch.bfloat16)
+    x[5, 128:256] = 0
+    x[9, :] *= 1e-3
+    codes, scales = moe.moe_quantize_act_e4m3(x.to(DEV))
+    torch.cuda.synchronize()
+    q, s = O.quantize_act_1x128(to_numpy_f32(x))
+    assert (codes.cpu().numpy() == q).all()
+    assert (scales.cpu().numpy() == s).all()
+
+
+# ------------------------------------------------------------------ routing
+
+ROUTE_CASES = ["tiny_fp32"] + list(PARITY_CONFIGS)
+
+
+@pytest.mark.parametrize("name", ROUTE_CASES)
+def test_route_parity(name):
+    cfg = CONFIGS.get(name) or PARITY_CONFIGS[name]
+    say(f"case: moe_route {name}")
+    inp = make_inputs(cfg, 0, with_weights=False)
+    shape = moe.LayerShape.from_config(cfg)
+    u, E, b = _dev(inp)
+    out = moe.moe_route(shape, u, E, b)
+    torch.cuda.synchronize()
+    r = check_routing(out, to_numpy_f32(inp.u), to_numpy_f32(inp.centroids), inp.bias.numpy(), cfg.top_k, cfg.n_routed)
+    say(f"  near ties {r['near_ties']}, descending order {r['order_ok']}")
+
+
+# ------------------------------------------------------------------ forward, small
+
+FWD_CASES = ["tiny_fp32"] + list(PARITY_CONFIGS)
+
+
+@pytest.mark.parametrize("name", FWD_CASES)
+def test_forward_parity(name):
+    cfg = CONFIGS.get(name) or PARITY_CONFIGS[name]
+    say(f"case: moe_forward {name}")
+    inp = make_inputs(cfg, 0)
+    y, routing, _ = _run_forward(cfg, inp)
+    u, E, b = to_numpy_f32(inp.u), to_numpy_f32(inp.centroids), inp.bias.numpy()
+    r = check_routing(routing, u, E, b, cfg.top_k, cfg.n_routed)
+    routed, shared = expert_fns(inp, False)
+    ref = O.layer_forward(u, E, b, cfg.top_k, routed, cfg.n_routed, shared,
+                          selection=routing["topk_idx"].cpu().numpy(), fp8=cfg.fp8)
+    err = output_errors(rows_of(y), ref["y"], u)
+    say(f"  {err} near ties {r['near_ties']}")
+    assert err["rel_to_rms"] <= TOL[cfg.w_dtype], err
+
+
+def test_forward_empty_batch():
+    cfg = PARITY_CONFIGS["small_bf16"].replace(T=0)
+    say("case: moe_forward T=0")
+    inp = make_inputs(cfg, 0)
+    y, routing, _ = _run_forward(cfg, inp)
+    assert y.shape == (0, cfg.d)
+    assert (routing["expert_counts"].cpu() == 0).all()
+    assert (routing["expert_offsets"].cpu() == 0).all()
+
+
+def test_forward_deterministic_and_batch_invariant():
+    cfg = PARITY_CONFIGS["small_bf16"]
+    say("case: determinism / batch invariance small_bf16")
+    inp = make_inputs(cfg, 0)
+    y1, _, w = _run_forward(cfg, inp)
+    y2, _, _ = _run_forward(cfg, inp, w)
+    assert torch.equal(y1, y2)
+    sub = torch.tensor([0, 5, 77, 299])
+    inp_s = make_inputs(cfg, 0, with_weights=False)
+    inp_s.u = inp.u[sub].contiguous()
+    y3, _, _ = _run_forward(cfg.replace(T=len(sub)), inp_s, w)
+    assert torch.equal(y3, y1[sub.to(DEV)])
+
+
+# ------------------------------------------------------------------ bias update
+
+def test_update_bias_bitexact():
+    say("case: moe_update_bias")
+    g = torch.Generator().manual_seed(4)
+    n, TK = 256, 2048
+    counts = torch.randint(0, 17, (n,), generator=g, dtype=torch.int32)
+    counts[:5] = 8     # exactly the mean: unchanged
+    bias = (torch.randn(n, generator=g) * 0.01).float()
+    bd = bias.to(DEV)
+    moe.moe_update_bias(bd, counts.to(DEV), TK, 0.001)
+    torch.cuda.synchronize()
+    ref = O.update_bias(bias.numpy(), counts.numpy(), TK)
+    assert (bd.cpu().numpy() == ref).all()
+
+
+def test_skewed_bias_loop_stepwise():
+    """100 route + update steps on the decode-like skewed batch; every step
+    is checked against the oracle from the GPU's own bias (step-wise parity)."""
+    cfg = CONFIGS["skew_decode_d7168"]
+    say("case: skew_decode_d7168 bias loop, 100 steps")
+    inp = make_inputs(cfg, 0, with_weights=False)
+    shape = moe.LayerShape.from_config(cfg)
+    u, E, b = _dev(inp)
+    un, En = to_numpy_f32(inp.u), to_numpy_f32(inp.centroids)
+    s = O.affinities(un, En)
+    TK = cfg.T * cfg.top_k
+    ratios = []
+    near_total = 0
+    for step in range(100):
+        b_before = b.cpu().numpy().copy()
+        out = moe.moe_route(shape, u, E, b)
+        moe.moe_update_bias(b, out["expert_counts"], TK, 0.001)
+        torch.cuda.synchronize()
+        gi = out["topk_idx"].cpu().numpy()
+        sel = O.select_topk(s, b_before, cfg.top_k)
+        from tests.parity import check_selection
+        near_total += check_selection(sel["v"], sel["gap"], sel["idx"], gi, cfg.top_k)
+        counts = O.group_by_expert(gi, cfg.n_routed)["counts"]
+        assert (out["expert_counts"].cpu().numpy() == counts).all()
+        assert (b.cpu().numpy() == O.update_bias(b_before, counts, TK)).all(), f"step {step}"
+        ratios.append(counts.max() / counts.mean())
+    say(f"  max/mean load: step0 {ratios[0]:.2f} step10 {ratios[10]:.2f} step50 {ratios[50]:.2f} "
+        f"step99 {ratios[-1]:.2f}; near ties {near_total}")
+    assert ratios[0] >= 9.0
+    assert ratios[-1] < ratios[0] / 2
+
+
+# ------------------------------------------------------------------ full-size workloads
+
+def _sampled_forward(name, sample):
+    cfg = CONFIGS[name]
+    say(f"case: moe_forward {name} full size, oracle on tokens {sample}")
+    inp = make_inputs(cfg, 0, weights_device=DEV)
+    y, routing, w = _run_forward(cfg, inp)
+    u, E, b = to_numpy_f32(inp.u), to_numpy_f32(inp.centroids), inp.bias.numpy()
+    r = check_routing(routing, u, E, b, cfg.top_k, cfg.n_routed)
+    routed, shared = expert_fns(inp, True)
+    gi = routing["topk_idx"].cpu().numpy()
+    ref = O.layer_forward(u[sample], E, b, cfg.top_k, routed, cfg.n_routed, shared, selection=gi[sample],
+                          fp8=cfg.fp8)
+    yg = rows_of(y[torch.tensor(sample, device=DEV)])
+    err = output_errors(yg, ref["y"], u[sample])
+    say(f"  near ties {r['near_ties']}; sampled output error {err}")
+    assert err["rel_to_rms"] <= TOL[cfg.w_dtype], err
+    assert torch.isfinite(y).all()
+    del w, inp
+    torch.cuda.empty_cache()
+
+
+def test_full_bf16_d2048():
+    _sampled_forward("bf16_d2048", [0, 1, 2047, 4095, 1234, 3000])
+
+
+def test_full_bf16_d7168():
+    _sampled_forward("bf16_d7168", [0, 4097, 8191, 2500])
+
+
+def test_full_fp8_d2048():
+    _sampled_forward("fp8_d2048", [0, 4095, 777])
+
+
+def test_full_skew_decode_d7168():
+    _sampled_forward("skew_decode_d7168", [0, 100, 255])
