@@ -13,7 +13,6 @@ before timing starts.  Prints ONE JSON line on stdout.
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -32,14 +31,6 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kernel_source_hash() -> str:
-    csrc = os.path.join(ROOT, "mixture_experts_layer_deepseekmoe_amd", "csrc")
-    h = hashlib.sha256()
-    for f in ("gemm_core.hpp", "ggemm.hip", "moe_common.hpp", "kernels.hpp"):
-        h.update(open(os.path.join(csrc, f), "rb").read())
-    return h.hexdigest()[:16]
-
-
 def measured_traffic(workload: str):
     """HBM bytes per gate/up launch from the committed rocprofv3 counter runs, if
     they were taken on the current grouped-GEMM source; else None."""
@@ -47,7 +38,8 @@ def measured_traffic(workload: str):
         return None
     table = json.load(open(TRAFFIC_FILE))
     rec = table.get(workload)
-    if not rec or rec.get("kernel_source_hash") != kernel_source_hash():
+    from mixture_experts_layer_deepseekmoe_amd.profiling import source_hash
+    if not rec or rec.get("kernel_source_hash") != source_hash():
         return None
     return rec.get("gate_up_bytes_per_launch")
 

@@ -33,7 +33,7 @@ def hipcc() -> str:
 
 
 def common_flags(debug: bool = False):
-    flags = [f"--offload-arch={ARCH}", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
+    flags = [f"--offload-arch={ARCH}", "-std=c++20", "-fPIC", "-Wall", "-Wno-unused-function",
              "-I", os.path.join(ROOT, "include"),
              # keep every packed-fp32 VALU form out of the generated code
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]

@@ -15,11 +15,12 @@
 //           per 128 columns, quantised in the epilogue.
 // down:     Y[r, c] = H_r . Wd[c], stored bf16 (fp32 on the fp32 path).
 //
-// Block tiles: 256 rows x 256 B rows (gate/up: 128 gate + 128 up rows =
-// 128 h columns; down: 256 output columns).  Blocks are mapped to XCDs so
-// that each XCD walks a contiguous run of the tile list (expert-major): the
-// tiles of one expert run together on one XCD and share its L2 for the
-// expert's weights and gathered rows.
+// Tiles: BM rows (256; 128 on the FP8 path, whose 128-byte K-steps need the
+// LDS) x 256 W rows (gate/up: 128 gate + 128 up rows = 128 h columns; down:
+// 256 output columns).  Blocks are mapped to XCDs so that each XCD walks a
+// contiguous run of the tile list (expert-major): the tiles of one expert run
+// together on one XCD and share its L2 for the expert's weights and gathered
+// rows.
 #include "gemm_core.hpp"
 #include "kernels.hpp"
 
@@ -27,8 +28,15 @@ namespace moe {
 
 namespace {
 
-constexpr int BM = GG_BM, BNW = GG_BNW;
+constexpr int BNW = GG_BNW;
 constexpr int NXCD = 8;
+
+template <int FMT>
+struct GG {
+  static constexpr int BM = FMT == FMT_E4M3 ? 128 : 256;
+  static constexpr int NST = FMT == FMT_E4M3 ? 3 : 5;
+  using P = Pipe<FMT, BM, BNW, NST>;
+};
 
 // Logical tile index of this block, or -1 if the block has no work.
 __device__ __forceinline__ int xcd_tile(int n_tiles) {
@@ -40,127 +48,219 @@ __device__ __forceinline__ int xcd_tile(int n_tiles) {
   return q < n_tiles ? q : -1;
 }
 
-template <int FMT>
-__global__ __launch_bounds__(256, 1) void gateup_kernel(GateUpArgs a) {
-  using Core = GemmCore<FMT, BM, BNW>;
-  __shared__ __attribute__((aligned(16))) TileSmem<BM, BNW> smem;
-  __shared__ float red[4][BM];
+// Tile q -> (m-tile, n-block): within a unit of up to MT_UNIT m-tiles of one
+// group, the m-tile index runs fastest, so the tiles that read the same weight
+// block are dispatched back to back (onto the same XCD) and share its L2.
+__device__ __forceinline__ void tile_coords(const int4* mtiles, int q, int nb_n, int& mt, int& nb) {
+  const int t = q / nb_n;
+  const int w = mtiles[t].w;
+  const int s = t - (w >> 8), k = w & 0xff;
+  const int local = q - s * nb_n;
+  nb = local / k;
+  mt = s + local % k;
+}
 
-  const int nb_n = ceil_div(a.inter, GG_HCOLS);
-  const int q = xcd_tile(*a.mt_count * nb_n);
-  if (q < 0) return;
-  const int mt = q / nb_n, nb = q % nb_n;
-  const int4 tl = a.mtiles[mt];
-  const int g = tl.x, row0 = tl.y, rows = tl.z;
-  const int n0 = nb * GG_HCOLS;
+constexpr int MAX_KB = 256;   // FP8: at most 256 scale blocks along K (d, I <= 32768)
 
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+// The stage ring: NST separate LDS objects (so the compiler can tell the
+// asynchronous writes of one stage from the reads of another).
+#define MOE_STAGE_RING(P, NST)                                                         \
+  __shared__ __attribute__((aligned(1024))) uint8_t st0[P::STAGE_BYTES];              \
+  __shared__ __attribute__((aligned(1024))) uint8_t st1[P::STAGE_BYTES];              \
+  __shared__ __attribute__((aligned(1024))) uint8_t st2[NST > 2 ? P::STAGE_BYTES : 16]; \
+  __shared__ __attribute__((aligned(1024))) uint8_t st3[NST > 3 ? P::STAGE_BYTES : 16]; \
+  __shared__ __attribute__((aligned(1024))) uint8_t st4[NST > 4 ? P::STAGE_BYTES : 16];
+
+template <int NST>
+struct Ring {
+  uint8_t* s[NST];
+};
+
+template <int NST>
+__device__ __forceinline__ Ring<NST> make_ring(uint8_t* a, uint8_t* b, uint8_t* c, uint8_t* d, uint8_t* e) {
+  uint8_t* all[5] = {a, b, c, d, e};
+  Ring<NST> r;
+#pragma unroll
+  for (int i = 0; i < NST; ++i) r.s[i] = all[i];
+  return r;
+}
+
+// Calls f.template operator()<NSUB>() with NSUB = rows rounded up to a
+// multiple of 32, as 16-row subtiles (2 .. MI).
+template <int MI, int N = 2, class F>
+__device__ __forceinline__ void dispatch_rows(int rows, F&& f) {
+  if constexpr (N >= MI) {
+    f.template operator()<MI>();
+  } else {
+    if (rows <= 16 * N)
+      f.template operator()<N>();
+    else
+      dispatch_rows<MI, N + 2>(rows, f);
+  }
+}
+
+// ------------------------------------------------------------------ gate/up
+
+template <int FMT, int NSUB>
+__device__ __forceinline__ void gateup_tile(const GateUpArgs& a, typename GG<FMT>::P& p, uint8_t* const (&st)[GG<FMT>::NST],
+                                            const float* swl, int kb, int nk, int row0, int rows, int n0, int nb,
+                                            float (*red)[GG<FMT>::BM]) {
+  using P = typename GG<FMT>::P;
+  const int w = wave_id(), lane = threadIdx.x & 63;
   const int lr = lane & 15, lg = lane >> 4;
-  const int es = FMT == FMT_F32 ? 4 : (FMT == FMT_BF16 ? 2 : 1);
-  const size_t xrow = static_cast<size_t>(a.d) * es;
-  const int nk = static_cast<int>(xrow / KSTEP_BYTES);
-  const bool shared = g >= a.n_routed;
-  const int gs = shared ? g - a.n_routed : g;
-  const uint8_t* wbase = static_cast<const uint8_t*>(shared ? a.w_shared : a.w_routed) +
-                         static_cast<size_t>(gs) * 2 * a.inter * xrow;
-  auto token_of = [&](int r) -> int {
-    const int gr = row0 + r;
-    return shared ? gr - a.TK - gs * a.T : a.perm_token[gr];
-  };
-
-  Core core;
-#pragma unroll
-  for (int i = 0; i < Core::NA; ++i) {
-    int r = Core::slot_row(i);
-    if (r >= rows) r = 0;
-    core.pa[i] = static_cast<const uint8_t*>(a.x) + static_cast<size_t>(token_of(r)) * xrow + Core::slot_col();
-  }
-#pragma unroll
-  for (int i = 0; i < Core::NB; ++i) {
-    const int rb = Core::slot_row(i);
-    int n = n0 + (rb & 127);
-    if (n >= a.inter) n = 0;
-    const int wr = rb < 128 ? n : a.inter + n;
-    core.pb[i] = wbase + static_cast<size_t>(wr) * xrow + Core::slot_col();
-  }
-  core.psa = nullptr;
-  const float* sw_ptr[4] = {nullptr, nullptr, nullptr, nullptr};
-  if constexpr (FMT == FMT_E4M3) {
-    const int kb = a.d / 128;
-    if (tid < BM) core.psa = a.x_scale + static_cast<size_t>(token_of(tid < rows ? tid : 0)) * kb;
-    const float* sbase = (shared ? a.sw_shared : a.sw_routed) + static_cast<size_t>(gs) * (2 * a.inter / 128) * kb;
-    sw_ptr[0] = sw_ptr[1] = sbase + static_cast<size_t>(n0 / 128) * kb;
-    sw_ptr[2] = sw_ptr[3] = sbase + static_cast<size_t>((a.inter + n0) / 128) * kb;
-  }
-
-  // wave w: gate columns 32w..32w+31 (subtiles 0,1) and the same up columns (2,3)
   const int brow[4] = {32 * w, 32 * w + 16, 128 + 32 * w, 128 + 32 * w + 16};
-  const int nvalid = ceil_div(rows, 16);
-  f32x4 acc[BM / 16][4];
-#pragma unroll
-  for (int i = 0; i < BM / 16; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  f32x4 acc[P::MI][4];
+  zero_acc(acc);
+  pipe_mainloop<P, GG<FMT>::NST, NSUB>(p, st, nk, brow, acc, swl, kb);
 
-  gemm_mainloop<FMT, BM, BNW>(core, smem, nk, brow, nvalid, acc, sw_ptr);
-
-  // ---- epilogue: h = SiLU(gate) * up
   if constexpr (FMT != FMT_E4M3) {
 #pragma unroll
-    for (int i = 0; i < BM / 16; ++i) {
+    for (int i = 0; i < NSUB; ++i) {
+      const int row = 16 * i + lr;
 #pragma unroll
       for (int jj = 0; jj < 2; ++jj) {
-        const int col = n0 + 32 * w + 16 * jj + lr;
+        const int col = n0 + 32 * w + 16 * jj + 4 * lg;
+        if (row < rows && col < a.inter) {
+          float h[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int row = 16 * i + 4 * lg + r;
-          if (i < nvalid && col < a.inter && row < rows) {
-            const float hv = silu_f32(acc[i][jj][r]) * acc[i][jj + 2][r];
-            const size_t o = static_cast<size_t>(row0 + row) * a.inter + col;
-            if constexpr (FMT == FMT_F32)
-              static_cast<float*>(a.h)[o] = hv;
-            else
-              static_cast<uint16_t*>(a.h)[o] = f32_to_bf16(hv);
+          for (int r = 0; r < 4; ++r) h[r] = silu_f32(acc[i][jj][r]) * acc[i][jj + 2][r];
+          const size_t o = static_cast<size_t>(row0 + row) * a.inter + col;
+          if constexpr (FMT == FMT_F32) {
+            *reinterpret_cast<float4*>(static_cast<float*>(a.h) + o) = make_float4(h[0], h[1], h[2], h[3]);
+          } else {
+            const uint32_t lo = f32_to_bf16(h[0]) | (static_cast<uint32_t>(f32_to_bf16(h[1])) << 16);
+            const uint32_t hi = f32_to_bf16(h[2]) | (static_cast<uint32_t>(f32_to_bf16(h[3])) << 16);
+            *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.h) + o) = make_uint2(lo, hi);
           }
         }
       }
     }
   } else {
     // 1x128 quantisation of h along I: the 128 columns of this tile are one
-    // scale group; a row's amax is reduced across lanes and then waves.
-    float hv[BM / 16][2][4];
+    // scale group.  A row's amax is reduced over its lane's 8 values, the 4
+    // lane groups, then the 4 waves.
+    float hv[NSUB][2][4];
 #pragma unroll
-    for (int i = 0; i < BM / 16; ++i)
+    for (int i = 0; i < NSUB; ++i) {
+      float m = 0.f;
 #pragma unroll
       for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) hv[i][jj][r] = i < nvalid ? silu_f32(acc[i][jj][r]) * acc[i][jj + 2][r] : 0.f;
-#pragma unroll
-    for (int i = 0; i < BM / 16; ++i) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        float m = fmaxf(fabsf(hv[i][0][r]), fabsf(hv[i][1][r]));
-        m = wave_max_16(m);
-        if (lr == 0) red[w][16 * i + 4 * lg + r] = m;
-      }
+        for (int r = 0; r < 4; ++r) {
+          hv[i][jj][r] = silu_f32(acc[i][jj][r]) * acc[i][jj + 2][r];
+          m = fmaxf(m, fabsf(hv[i][jj][r]));
+        }
+      m = fmaxf(m, __shfl_xor(m, 16));
+      m = fmaxf(m, __shfl_xor(m, 32));
+      if (lg == 0) red[w][16 * i + lr] = m;
     }
     __syncthreads();
     const int ncb = a.inter / 128;
 #pragma unroll
-    for (int i = 0; i < BM / 16; ++i) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = 16 * i + 4 * lg + r;
-        if (i >= nvalid || row >= rows) continue;
+    for (int i = 0; i < NSUB; ++i) {
+      const int row = 16 * i + lr;
+      if (row < rows) {
         const float m = fmaxf(fmaxf(red[0][row], red[1][row]), fmaxf(red[2][row], red[3][row]));
         const float inv = m == 0.f ? 0.f : 448.f / m;
         const size_t grow = static_cast<size_t>(row0 + row);
 #pragma unroll
         for (int jj = 0; jj < 2; ++jj) {
-          const int col = n0 + 32 * w + 16 * jj + lr;
-          static_cast<uint8_t*>(a.h)[grow * a.inter + col] = static_cast<uint8_t>(f32_to_e4m3(hv[i][jj][r] * inv));
+          const int col = n0 + 32 * w + 16 * jj + 4 * lg;
+          uint32_t q = 0;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) q |= f32_to_e4m3(hv[i][jj][r] * inv) << (8 * r);
+          *reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(a.h) + grow * a.inter + col) = q;
         }
-        if (w == 0 && lr == 0) a.h_scale[grow * ncb + nb] = m == 0.f ? 1.f : m / 448.f;
+        if (w == 0 && lg == 0) a.h_scale[grow * ncb + nb] = m == 0.f ? 1.f : m / 448.f;
+      }
+    }
+  }
+}
+
+template <int FMT>
+__global__ __launch_bounds__(256, 1) void gateup_kernel(GateUpArgs a) {
+  using P = typename GG<FMT>::P;
+  constexpr int NST = GG<FMT>::NST, BM = GG<FMT>::BM;
+  MOE_STAGE_RING(P, NST)
+  __shared__ float red[FMT == FMT_E4M3 ? 4 : 1][BM];
+  __shared__ float swl[FMT == FMT_E4M3 ? 2 * MAX_KB : 1];
+
+  const int nb_n = ceil_div(a.inter, GG_HCOLS);
+  const int q = xcd_tile(*a.mt_count * nb_n);
+  if (q < 0) return;
+  int mt, nb;
+  tile_coords(a.mtiles, q, nb_n, mt, nb);
+  const int4 tl = a.mtiles[mt];
+  const int g = tl.x, row0 = tl.y, rows = tl.z;
+  const int n0 = nb * GG_HCOLS;
+
+  const int es = FMT == FMT_F32 ? 4 : (FMT == FMT_BF16 ? 2 : 1);
+  const size_t xrow = static_cast<size_t>(a.d) * es;
+  const int nk = static_cast<int>(xrow / P::SB);
+  const bool shared = g >= a.n_routed;
+  const int gs = shared ? g - a.n_routed : g;
+  const uint8_t* wbase = static_cast<const uint8_t*>(shared ? a.w_shared : a.w_routed) +
+                         static_cast<size_t>(gs) * 2 * a.inter * xrow;
+  auto token_of = [&](int r) -> int {
+    if (r >= rows) r = 0;
+    const int gr = row0 + r;
+    return shared ? gr - a.TK - gs * a.T : a.perm_token[gr];
+  };
+  const int kb = a.d / 128;
+
+  P p;
+  p.init([&](int r) { return static_cast<const uint8_t*>(a.x) + static_cast<size_t>(token_of(r)) * xrow; },
+         [&](int r) {
+           int n = n0 + (r & 127);
+           if (n >= a.inter) n = 0;
+           return wbase + static_cast<size_t>(r < 128 ? n : a.inter + n) * xrow;
+         },
+         [&](int r) { return a.x_scale + static_cast<size_t>(token_of(r)) * kb; });
+
+  if constexpr (FMT == FMT_E4M3) {
+    // this tile's weight-block scales: gate block n0/128 and up block (I+n0)/128, all K blocks
+    const float* sb = (shared ? a.sw_shared : a.sw_routed) + static_cast<size_t>(gs) * (2 * a.inter / 128) * kb;
+    for (int i = threadIdx.x; i < 2 * kb; i += 256)
+      swl[i] = i < kb ? sb[static_cast<size_t>(n0 / 128) * kb + i] : sb[static_cast<size_t>((a.inter + n0) / 128) * kb + i - kb];
+    __syncthreads();
+  }
+
+  const Ring<NST> ring = make_ring<NST>(st0, st1, st2, st3, st4);
+  const float* sw = FMT == FMT_E4M3 ? swl : nullptr;
+  // the K loop instantiated for the tile's valid rows, in 32-row steps
+  dispatch_rows<P::MI>(rows, [&]<int NSUB>() {
+    gateup_tile<FMT, NSUB>(a, p, ring.s, sw, kb, nk, row0, rows, n0, nb, red);
+  });
+}
+
+// ------------------------------------------------------------------ down
+
+template <int FMT, int NSUB>
+__device__ __forceinline__ void down_tile(const DownArgs& a, typename GG<FMT>::P& p, uint8_t* const (&st)[GG<FMT>::NST],
+                                          const float* swl, int kb, int nk, int row0, int rows, int n0) {
+  using P = typename GG<FMT>::P;
+  const int w = wave_id(), lane = threadIdx.x & 63;
+  const int lr = lane & 15, lg = lane >> 4;
+  const int brow[4] = {64 * w, 64 * w + 16, 64 * w + 32, 64 * w + 48};
+  f32x4 acc[P::MI][4];
+  zero_acc(acc);
+  pipe_mainloop<P, GG<FMT>::NST, NSUB>(p, st, nk, brow, acc, FMT == FMT_E4M3 ? swl + (w >> 1) * kb : nullptr, 0);
+#pragma unroll
+  for (int i = 0; i < NSUB; ++i) {
+    const int row = 16 * i + lr;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int col = n0 + 64 * w + 16 * j + 4 * lg;
+      if (row < rows && col < a.d) {
+        const size_t o = static_cast<size_t>(row0 + row) * a.d + col;
+        if constexpr (FMT == FMT_F32) {
+          *reinterpret_cast<float4*>(static_cast<float*>(a.y) + o) =
+              make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
+        } else {
+          const uint32_t lo = f32_to_bf16(acc[i][j][0]) | (static_cast<uint32_t>(f32_to_bf16(acc[i][j][1])) << 16);
+          const uint32_t hi = f32_to_bf16(acc[i][j][2]) | (static_cast<uint32_t>(f32_to_bf16(acc[i][j][3])) << 16);
+          *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.y) + o) = make_uint2(lo, hi);
+        }
       }
     }
   }
@@ -168,78 +268,51 @@ __global__ __launch_bounds__(256, 1) void gateup_kernel(GateUpArgs a) {
 
 template <int FMT>
 __global__ __launch_bounds__(256, 1) void down_kernel(DownArgs a) {
-  using Core = GemmCore<FMT, BM, BNW>;
-  __shared__ __attribute__((aligned(16))) TileSmem<BM, BNW> smem;
+  using P = typename GG<FMT>::P;
+  constexpr int NST = GG<FMT>::NST;
+  MOE_STAGE_RING(P, NST)
+  __shared__ float swl[FMT == FMT_E4M3 ? 2 * MAX_KB : 1];
 
   const int nb_n = ceil_div(a.d, BNW);
   const int q = xcd_tile(*a.mt_count * nb_n);
   if (q < 0) return;
-  const int mt = q / nb_n, nb = q % nb_n;
+  int mt, nb;
+  tile_coords(a.mtiles, q, nb_n, mt, nb);
   const int4 tl = a.mtiles[mt];
   const int g = tl.x, row0 = tl.y, rows = tl.z;
   const int n0 = nb * BNW;
 
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
-  const int lr = lane & 15, lg = lane >> 4;
   const int es = FMT == FMT_F32 ? 4 : (FMT == FMT_BF16 ? 2 : 1);
   const size_t hrow = static_cast<size_t>(a.inter) * es;
-  const int nk = static_cast<int>(hrow / KSTEP_BYTES);
+  const int nk = static_cast<int>(hrow / P::SB);
   const bool shared = g >= a.n_routed;
   const int gs = shared ? g - a.n_routed : g;
   const uint8_t* wbase = static_cast<const uint8_t*>(shared ? a.w_shared : a.w_routed) +
                          static_cast<size_t>(gs) * a.d * hrow;
+  const int kb = a.inter / 128;
 
-  Core core;
-#pragma unroll
-  for (int i = 0; i < Core::NA; ++i) {
-    int r = Core::slot_row(i);
-    if (r >= rows) r = 0;
-    core.pa[i] = static_cast<const uint8_t*>(a.h) + static_cast<size_t>(row0 + r) * hrow + Core::slot_col();
-  }
-#pragma unroll
-  for (int i = 0; i < Core::NB; ++i) {
-    int c = n0 + Core::slot_row(i);
-    if (c >= a.d) c = 0;
-    core.pb[i] = wbase + static_cast<size_t>(c) * hrow + Core::slot_col();
-  }
-  core.psa = nullptr;
-  const float* sw_ptr[4] = {nullptr, nullptr, nullptr, nullptr};
+  P p;
+  p.init([&](int r) { return static_cast<const uint8_t*>(a.h) + static_cast<size_t>(row0 + (r < rows ? r : 0)) * hrow; },
+         [&](int r) {
+           int c = n0 + r;
+           if (c >= a.d) c = 0;
+           return wbase + static_cast<size_t>(c) * hrow;
+         },
+         [&](int r) { return a.h_scale + static_cast<size_t>(row0 + (r < rows ? r : 0)) * kb; });
+
   if constexpr (FMT == FMT_E4M3) {
-    const int kb = a.inter / 128;
-    if (tid < BM) core.psa = a.h_scale + static_cast<size_t>(row0 + (tid < rows ? tid : 0)) * kb;
-    const float* sbase = (shared ? a.sw_shared : a.sw_routed) + static_cast<size_t>(gs) * (a.d / 128) * kb;
-    const int cb = min(n0 + 64 * w, a.d - 1) / 128;
-    sw_ptr[0] = sw_ptr[1] = sw_ptr[2] = sw_ptr[3] = sbase + static_cast<size_t>(cb) * kb;
+    // weight-block scales of this tile's two 128-column blocks (the second
+    // clamped at the matrix edge), all K blocks
+    const float* sb = (shared ? a.sw_shared : a.sw_routed) + static_cast<size_t>(gs) * (a.d / 128) * kb;
+    const int b0 = n0 / 128, b1 = min(n0 / 128 + 1, a.d / 128 - 1);
+    for (int i = threadIdx.x; i < 2 * kb; i += 256)
+      swl[i] = i < kb ? sb[static_cast<size_t>(b0) * kb + i] : sb[static_cast<size_t>(b1) * kb + i - kb];
+    __syncthreads();
   }
 
-  const int brow[4] = {64 * w, 64 * w + 16, 64 * w + 32, 64 * w + 48};
-  const int nvalid = ceil_div(rows, 16);
-  f32x4 acc[BM / 16][4];
-#pragma unroll
-  for (int i = 0; i < BM / 16; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  gemm_mainloop<FMT, BM, BNW>(core, smem, nk, brow, nvalid, acc, sw_ptr);
-
-#pragma unroll
-  for (int i = 0; i < BM / 16; ++i) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int col = n0 + 64 * w + 16 * j + lr;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = 16 * i + 4 * lg + r;
-        if (i < nvalid && col < a.d && row < rows) {
-          const size_t o = static_cast<size_t>(row0 + row) * a.d + col;
-          if constexpr (FMT == FMT_F32)
-            static_cast<float*>(a.y)[o] = acc[i][j][r];
-          else
-            static_cast<uint16_t*>(a.y)[o] = f32_to_bf16(acc[i][j][r]);
-        }
-      }
-    }
-  }
+  const Ring<NST> ring = make_ring<NST>(st0, st1, st2, st3, st4);
+  const float* sw = FMT == FMT_E4M3 ? swl : nullptr;
+  dispatch_rows<P::MI>(rows, [&]<int NSUB>() { down_tile<FMT, NSUB>(a, p, ring.s, sw, kb, nk, row0, rows, n0); });
 }
 
 int grid_for(int max_mtiles, int nb_n) {
@@ -248,6 +321,8 @@ int grid_for(int max_mtiles, int nb_n) {
 }
 
 }  // namespace
+
+int gg_bm(int fmt) { return fmt == FMT_E4M3 ? GG<FMT_E4M3>::BM : GG<FMT_BF16>::BM; }
 
 hipError_t launch_gateup(int fmt, const GateUpArgs& a, hipStream_t s) {
   const int grid = grid_for(a.max_mtiles, ceil_div(a.inter, GG_HCOLS));

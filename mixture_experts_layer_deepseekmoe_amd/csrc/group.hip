@@ -67,7 +67,7 @@ __global__ __launch_bounds__(SCAN_THREADS) void scan_kernel(GroupArgs a, int nbl
   const long long TK = static_cast<long long>(a.T) * a.top_k;
   for (int g = tid; g < ng; g += SCAN_THREADS) {
     const int M = g < nr ? (sc[g] - (g ? sc[g - 1] : 0)) : a.T;
-    tmp[g] = ceil_div(M, GG_BM);
+    tmp[g] = ceil_div(M, a.bm);
   }
   __syncthreads();
   if (tid == 0) {   // at most 520 groups: a short serial scan
@@ -77,13 +77,19 @@ __global__ __launch_bounds__(SCAN_THREADS) void scan_kernel(GroupArgs a, int nbl
     *a.mt_count = run;
   }
   __syncthreads();
+  // .w = (index within its unit << 8) | unit size: consecutive m-tiles of a
+  // group form units of at most MT_UNIT, whose tiles the GEMMs visit with the
+  // m-tile index fastest, so the tiles sharing one weight block run together.
   for (int g = tid; g < ng; g += SCAN_THREADS) {
     const long long M = g < nr ? (sc[g] - (g ? sc[g - 1] : 0)) : a.T;
     const long long first = g < nr ? (g ? sc[g - 1] : 0) : TK + static_cast<long long>(g - nr) * a.T;
     const int n = tmp[g + 1] - tmp[g];
     for (int k = 0; k < n; ++k) {
       const long long r0 = k * M / n, r1 = (k + 1) * M / n;
-      a.mtiles[tmp[g] + k] = make_int4(g, static_cast<int>(first + r0), static_cast<int>(r1 - r0), 0);
+      const int ustart = k - k % MT_UNIT;
+      const int usize = min(MT_UNIT, n - ustart);
+      a.mtiles[tmp[g] + k] = make_int4(g, static_cast<int>(first + r0), static_cast<int>(r1 - r0),
+                                       ((k - ustart) << 8) | usize);
     }
   }
 }

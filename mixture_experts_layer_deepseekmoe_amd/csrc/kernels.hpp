@@ -10,8 +10,6 @@
 
 namespace moe {
 
-// Tile rows of the grouped GEMMs (m-tiles hold at most this many rows).
-constexpr int GG_BM = 256;
 // B rows per grouped-GEMM tile: 128 gate + 128 up rows (128 h columns), or
 // 256 output columns for the down projection.
 constexpr int GG_BNW = 256;
@@ -21,6 +19,7 @@ constexpr int GROUP_TB = 256;     // tokens per histogram / permute block
 constexpr int MAX_ROUTED = 512;
 constexpr int MAX_SHARED = 8;
 constexpr int MAX_TOPK = 16;
+constexpr int MT_UNIT = 4;        // m-tiles of one group visited together by the grouped GEMMs
 
 struct RouteArgs {
   const void* u;          // [T][d] fmt
@@ -39,8 +38,9 @@ struct GroupArgs {
   int32_t* offsets;       // [N_r + 1]
   int32_t* perm_token;    // [T*K]
   int32_t* pos;           // [T][K]
-  int4* mtiles;           // [max_mtiles] (group, first grouped row, rows, 0); null: routing only
+  int4* mtiles;           // [max_mtiles] (group, first grouped row, rows, unit info); null: routing only
   int32_t* mt_count;      // [1]
+  int bm;                 // grouped-GEMM tile rows (m-tiles hold at most bm rows)
 };
 
 struct GateUpArgs {
@@ -94,9 +94,12 @@ hipError_t launch_gateup(int fmt, const GateUpArgs& a, hipStream_t s);
 hipError_t launch_down(int fmt, const DownArgs& a, hipStream_t s);
 hipError_t launch_combine(int xfmt, int yfmt, int ofmt, const CombineArgs& a, hipStream_t s);
 
-inline int max_mtiles(long long T, int K, int n_routed, int n_shared) {
-  // sum over groups of ceil(M_g / BM) <= (T*K)/BM + N_r + N_s * ceil(T/BM)
-  return static_cast<int>((T * K) / GG_BM + n_routed + n_shared * ((T + GG_BM - 1) / GG_BM));
+// Tile rows of the grouped GEMMs for a weight format (m-tiles hold at most this many rows).
+int gg_bm(int fmt);
+
+inline int max_mtiles(long long T, int K, int n_routed, int n_shared, int bm) {
+  // sum over groups of ceil(M_g / bm) <= (T*K)/bm + N_r + N_s * ceil(T/bm)
+  return static_cast<int>((T * K) / bm + n_routed + n_shared * ((T + bm - 1) / bm));
 }
 
 }  // namespace moe

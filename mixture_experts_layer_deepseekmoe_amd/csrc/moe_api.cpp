@@ -1,7 +1,7 @@
 // Host side of the C ABI declared in include/moe.h: argument validation,
 // workspace carving and the launch sequence.  Never allocates, frees or
 // synchronises; every kernel goes on the caller's stream.
-#include "../../include/moe.h"
+#include "moe.h"
 
 #include <hip/hip_runtime.h>
 
@@ -21,6 +21,8 @@ inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 
 
 inline int elem_bytes(int dt) { return dt == MOE_DTYPE_F32 ? 4 : (dt == MOE_DTYPE_BF16 ? 2 : 1); }
 
+int fmt_of(int dt) { return dt == MOE_DTYPE_F32 ? FMT_F32 : (dt == MOE_DTYPE_BF16 ? FMT_BF16 : FMT_E4M3); }
+
 // Workspace map (byte offsets, each 256-byte aligned).
 struct Layout {
   size_t hist, idx, gate, counts, offsets, perm, pos, mtiles, mtcount, uq, us, h, hs, y, total;
@@ -32,7 +34,7 @@ Layout make_layout(const moe_shape& s) {
   Layout L{};
   const long long T = s.T, TK = T * s.top_k;
   L.nblk = moe::ceil_div(s.T, moe::GROUP_TB);
-  L.max_mt = moe::max_mtiles(T, s.top_k, s.n_routed, s.n_shared);
+  L.max_mt = moe::max_mtiles(T, s.top_k, s.n_routed, s.n_shared, moe::gg_bm(fmt_of(s.w_dtype)));
   L.rows = TK + static_cast<long long>(s.n_shared) * T;
   size_t o = 0;
   auto take = [&](size_t bytes) { const size_t at = o; o += align_up(bytes); return at; };
@@ -72,8 +74,10 @@ int validate_shape(const moe_shape* s) {
   if (s->d % kmult != 0 || s->inter % kmult != 0) return MOE_ERR_UNSUPPORTED;
   const long long T = s->T;
   if (T * (s->top_k + s->n_shared) >= (1LL << 31)) return MOE_ERR_UNSUPPORTED;
-  const long long gu_tiles = static_cast<long long>(moe::max_mtiles(T, s->top_k, s->n_routed, s->n_shared)) *
-                             moe::ceil_div(s->d > s->inter ? s->d : s->inter, 128);
+  if (s->w_dtype == MOE_DTYPE_E4M3 && (s->d > 32768 || s->inter > 32768)) return MOE_ERR_UNSUPPORTED;
+  const long long gu_tiles =
+      static_cast<long long>(moe::max_mtiles(T, s->top_k, s->n_routed, s->n_shared, moe::gg_bm(fmt_of(s->w_dtype)))) *
+      moe::ceil_div(s->d > s->inter ? s->d : s->inter, 128);
   if (gu_tiles >= (1LL << 31) - 64) return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
@@ -97,8 +101,6 @@ struct Stages {
   }
 };
 
-int fmt_of(int dt) { return dt == MOE_DTYPE_F32 ? FMT_F32 : (dt == MOE_DTYPE_BF16 ? FMT_BF16 : FMT_E4M3); }
-
 // Route + group.  `mtiles` null: routing only (no GEMM tile list).
 int run_route(const moe_shape& s, const void* u, const void* cen, const float* bias, int32_t* idx, float* gate,
               int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* pos, int32_t* hist, int4* mtiles,
@@ -106,7 +108,8 @@ int run_route(const moe_shape& s, const void* u, const void* cen, const float* b
   moe::RouteArgs ra{u, cen, bias, s.T, s.d, s.n_routed, s.top_k, idx, gate};
   int rc = check_launch(moe::launch_route(fmt_of(s.x_dtype), ra, st));
   if (rc != MOE_OK) return rc;
-  moe::GroupArgs ga{idx, s.T, s.top_k, s.n_routed, s.n_shared, hist, counts, offsets, perm, pos, mtiles, mtcount};
+  moe::GroupArgs ga{idx,     s.T,  s.top_k, s.n_routed, s.n_shared, hist,   counts,
+                    offsets, perm, pos,     mtiles,     mtcount,    moe::gg_bm(fmt_of(s.w_dtype))};
   return check_launch(moe::launch_group(ga, st));
 }
 
@@ -189,8 +192,8 @@ int moe_forward(const moe_shape* shape, const void* u, const void* centroids, co
   if (rc != MOE_OK) return rc;
   stg.end(MOE_STAGE_ROUTE);
   stg.begin(MOE_STAGE_GROUP);
-  moe::GroupArgs gra{idx, s.T, s.top_k, s.n_routed, s.n_shared, at<int32_t>(workspace, L.hist), counts, offsets,
-                     perm, pos, mtiles, mtcount};
+  moe::GroupArgs gra{idx,     s.T,  s.top_k, s.n_routed, s.n_shared, at<int32_t>(workspace, L.hist), counts,
+                     offsets, perm, pos,     mtiles,     mtcount,    moe::gg_bm(fmt_of(s.w_dtype))};
   rc = check_launch(moe::launch_group(gra, stream));
   if (rc != MOE_OK) return rc;
   stg.end(MOE_STAGE_GROUP);

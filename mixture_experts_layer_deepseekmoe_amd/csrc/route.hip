@@ -4,9 +4,10 @@
 // the K_r largest of {s_{j,t} + b_j}, else 0; g_{i,t} = g' normalised).
 //
 // One block routes 32 tokens against every expert: the logits of one chunk
-// of 256 experts come from the MFMA tile core (fp32 accumulation); their
-// sigmoids go to LDS (the logits never reach HBM); then each wave selects
-// the top-K of 8 tokens, with the N_r scores of a token spread 1..8 per lane.
+// of 256 experts come from the pipelined MFMA tile core (fp32 accumulation);
+// their sigmoids go to LDS (the logits never reach HBM); then each wave
+// selects the top-K of 8 tokens, with the N_r scores of a token spread 1..8
+// per lane.
 // Ordering is by v = s + b descending, exact ties to the lower expert index;
 // a NaN score ranks below every number, so K distinct in-range experts are
 // always produced.  Gates are s_k / sum of the K selected s, summed in
@@ -20,69 +21,65 @@ namespace {
 
 constexpr int RBT = ROUTE_BT;
 constexpr int RCHUNK = 256;   // experts per MFMA pass
-
-template <int FMT, int NRMAX>
-struct RouteSmem {
-  static constexpr int SSTRIDE = NRMAX + 4;
-  static constexpr size_t kTile = sizeof(TileSmem<RBT, RCHUNK>);
-  static constexpr size_t kScores = sizeof(float) * RBT * SSTRIDE;
-  // With a single expert chunk the score buffer reuses the staging buffers.
-  static constexpr size_t kBytes = NRMAX <= RCHUNK ? (kTile > kScores ? kTile : kScores) : kTile + kScores;
-  static constexpr size_t kScoreOff = NRMAX <= RCHUNK ? 0 : kTile;
-};
+constexpr int RNST = 4;
 
 template <int FMT, int NRMAX>
 __global__ __launch_bounds__(256) void route_kernel(RouteArgs a) {
-  using Core = GemmCore<FMT, RBT, RCHUNK>;
-  using SM = RouteSmem<FMT, NRMAX>;
-  __shared__ __attribute__((aligned(16))) uint8_t lds[SM::kBytes];
-  auto& tile = *reinterpret_cast<TileSmem<RBT, RCHUNK>*>(lds);
-  float* sbuf = reinterpret_cast<float*>(lds + SM::kScoreOff);
+  using P = Pipe<FMT, RBT, RCHUNK, RNST>;
+  constexpr int SSTRIDE = NRMAX + 4;
+  __shared__ __attribute__((aligned(1024))) uint8_t st0[P::STAGE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t st1[P::STAGE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t st2[P::STAGE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t st3[P::STAGE_BYTES];
+  __shared__ __attribute__((aligned(16))) float sbuf[RBT * SSTRIDE];
+  uint8_t* const st[RNST] = {st0, st1, st2, st3};   // a ring of separate LDS objects
 
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int w = wave_id(), lane = threadIdx.x & 63;
   const int lr = lane & 15, lg = lane >> 4;
   const int t0 = blockIdx.x * RBT;
   const int es = FMT == FMT_F32 ? 4 : 2;
   const size_t row_bytes = static_cast<size_t>(a.d) * es;
-  const int nk = static_cast<int>(row_bytes / KSTEP_BYTES);
+  const int nk = static_cast<int>(row_bytes / P::SB);
   const int brow[4] = {64 * w, 64 * w + 16, 64 * w + 32, 64 * w + 48};
-  const float* no_scale[4] = {nullptr, nullptr, nullptr, nullptr};
-  const int nvalid = ceil_div(min(RBT, a.T - t0), 16);
+  const int valid = min(RBT, a.T - t0);
 
   for (int ec = 0; ec < a.n_routed; ec += RCHUNK) {
-    Core core;
-    core.psa = nullptr;
-    {
-      int r = Core::slot_row(0);
-      int t = t0 + r < a.T ? t0 + r : t0;
-      core.pa[0] = static_cast<const uint8_t*>(a.u) + t * row_bytes + Core::slot_col();
-#pragma unroll
-      for (int i = 0; i < Core::NB; ++i) {
-        int e = ec + Core::slot_row(i);
-        if (e >= a.n_routed) e = 0;
-        core.pb[i] = static_cast<const uint8_t*>(a.centroids) + e * row_bytes + Core::slot_col();
-      }
-    }
-    f32x4 acc[RBT / 16][4];
-#pragma unroll
-    for (int i = 0; i < RBT / 16; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    P p;
+    p.init(
+        [&](int r) {
+          const int t = (r < valid) ? t0 + r : t0;
+          return static_cast<const uint8_t*>(a.u) + static_cast<size_t>(t) * row_bytes;
+        },
+        [&](int r) {
+          const int e = ec + r < a.n_routed ? ec + r : 0;
+          return static_cast<const uint8_t*>(a.centroids) + static_cast<size_t>(e) * row_bytes;
+        },
+        [&](int) { return static_cast<const float*>(nullptr); });
+    f32x4 acc[P::MI][4];
+    zero_acc(acc);
+    if (valid > 16)
+      pipe_mainloop<P, RNST, 2>(p, st, nk, brow, acc);
+    else
+      pipe_mainloop<P, RNST, 1>(p, st, nk, brow, acc);
 
-    gemm_mainloop<FMT, RBT, RCHUNK>(core, tile, nk, brow, nvalid, acc, no_scale);
-
+    // lane: token 16i + lr, experts ec + brow[j] + 4lg .. +3
 #pragma unroll
-    for (int i = 0; i < RBT / 16; ++i)
+    for (int i = 0; i < P::MI; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int e = ec + brow[j] + lr;
-        if (e < a.n_routed) {
+        const int e = ec + brow[j] + 4 * lg;
+        float* dst = sbuf + (16 * i + lr) * SSTRIDE + e;
+        if (e + 3 < a.n_routed) {
+          *reinterpret_cast<float4*>(dst) = make_float4(sigmoid_f32(acc[i][j][0]), sigmoid_f32(acc[i][j][1]),
+                                                        sigmoid_f32(acc[i][j][2]), sigmoid_f32(acc[i][j][3]));
+        } else {
 #pragma unroll
-          for (int r = 0; r < 4; ++r) sbuf[(16 * i + 4 * lg + r) * SM::SSTRIDE + e] = sigmoid_f32(acc[i][j][r]);
+          for (int r = 0; r < 4; ++r)
+            if (e + r < a.n_routed) dst[r] = sigmoid_f32(acc[i][j][r]);
         }
       }
-    __syncthreads();
   }
+  __syncthreads();
 
   // ---- top-K: wave w takes tokens 8w .. 8w+7 of the block
   constexpr int NQ = NRMAX / 64;
@@ -96,7 +93,7 @@ __global__ __launch_bounds__(256) void route_kernel(RouteArgs a) {
     const int tl = w * (RBT / 4) + tt;
     const int t = t0 + tl;
     if (t >= a.T) break;
-    const float* srow = sbuf + tl * SM::SSTRIDE;
+    const float* srow = sbuf + tl * SSTRIDE;
     float key[NQ];
 #pragma unroll
     for (int q = 0; q < NQ; ++q) {

@@ -1,0 +1,192 @@
+"""Profiling helpers for rocprofv3 runs of the MoE layer.
+
+    # the workload to profile (run it under rocprofv3):
+    python -m mixture_experts_layer_deepseekmoe_amd.profiling run --workload bf16_d7168 --steps 3
+    # turn rocprofv3's CSV output into the summaries kept under profiles/:
+    python -m mixture_experts_layer_deepseekmoe_amd.profiling summarize --trace DIR --pmc DIR [DIR...] \
+        --workload bf16_d7168 --out profiles
+
+``run`` first launches one plain streaming kernel of known size (an fp32
+elementwise multiply of a 1 GiB tensor into another: 1 GiB read, 1 GiB
+written), which calibrates the HBM byte counters (FETCH_SIZE / WRITE_SIZE),
+then a few layer forwards.  ``summarize`` averages every counter per kernel
+and per dispatch, scales FETCH_SIZE / WRITE_SIZE by the calibration, and
+writes a markdown summary plus profiles/traffic_counters.json.
+"""
+
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import os
+import sys
+from collections import defaultdict
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CALIB_BYTES = 1 << 30
+
+
+def _run(args):
+    sys.path.insert(0, ROOT)
+    import torch
+
+    import mixture_experts_layer_deepseekmoe_amd as moe
+    from moe_workloads import get_config, make_inputs
+
+    torch.cuda.set_device(0)
+    src = torch.ones(CALIB_BYTES // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.mul(src, 2.0, out=dst)
+    torch.cuda.synchronize()
+    del src, dst
+
+    cfg = get_config(args.workload)
+    inp = make_inputs(cfg, 0, weights_device="cuda")
+    shape = moe.LayerShape.from_config(cfg)
+    u, cen, bias = (t.cuda().contiguous() for t in (inp.u, inp.centroids, inp.bias))
+    w = moe.prepare_weights(cfg, inp)
+    ws = moe.alloc_workspace(shape)
+    routing = moe.alloc_routing(shape)
+    y = torch.empty((cfg.T, cfg.d), dtype=torch.float32 if cfg.out_dtype == "f32" else torch.bfloat16, device="cuda")
+    for i in range(args.steps):
+        moe.moe_forward(shape, u, cen, bias, w, y=y, routing=routing, workspace=ws)
+        moe.moe_update_bias(bias, routing["expert_counts"], cfg.T * cfg.top_k)
+        torch.cuda.synchronize()
+        print(f"[profile] step {i} done", flush=True)
+
+
+def _short(name: str) -> str:
+    for key in ("gateup_kernel", "down_kernel", "route_kernel", "combine_kernel", "hist_kernel", "scan_kernel",
+                "permute_kernel", "quant_act_kernel", "quant_weight_kernel", "bias_update_kernel"):
+        if key in name:
+            fmt = ""
+            if "ILi1E" in name:
+                fmt = "<bf16>"
+            elif "ILi2E" in name:
+                fmt = "<e4m3>"
+            elif "ILi0E" in name:
+                fmt = "<f32>"
+            return key + fmt
+    if name.startswith("void at::native::"):
+        return "torch:" + name[len("void at::native::"):].split("<")[0].split("(")[0]
+    return name[:60]
+
+
+CALIB = "calibration_stream(1GiB read + 1GiB write)"
+
+
+def _is_calibration(row) -> bool:
+    # the fp32 multiply of the 1 GiB calibration tensor (4 elements per work-item)
+    return "MulFunctor<float>" in row["Kernel_Name"] and int(row["Grid_Size"]) == CALIB_BYTES // 16
+
+
+def _csvs(d, pattern):
+    return sorted(glob.glob(os.path.join(d, "**", pattern), recursive=True))
+
+
+def kernel_stats(trace_dir):
+    rows = []
+    for f in _csvs(trace_dir, "*kernel_stats.csv"):
+        rows += list(csv.DictReader(open(f)))
+    return rows
+
+
+def counters(pmc_dirs):
+    """{kernel: {counter: mean value per dispatch}}"""
+    acc = defaultdict(lambda: defaultdict(list))
+    for d in pmc_dirs:
+        for f in _csvs(d, "*counter_collection.csv"):
+            per = defaultdict(float)
+            for r in csv.DictReader(open(f)):
+                name = CALIB if _is_calibration(r) else _short(r["Kernel_Name"])
+                key = (r["Dispatch_Id"], name, r["Counter_Name"])
+                per[key] += float(r["Counter_Value"])
+            for (disp, k, c), v in per.items():
+                acc[k][c].append(v)
+    return {k: {c: sum(v) / len(v) for c, v in cs.items()} for k, cs in acc.items()}
+
+
+def source_hash():
+    """Hash of the grouped-GEMM sources, stamped on stored counter readings."""
+    csrc = os.path.join(ROOT, "mixture_experts_layer_deepseekmoe_amd", "csrc")
+    h = hashlib.sha256()
+    for f in ("gemm_core.hpp", "ggemm.hip", "moe_common.hpp", "kernels.hpp"):
+        h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def _summarize(args):
+    os.makedirs(args.out, exist_ok=True)
+    lines = [f"# rocprofv3 summary: {args.workload}", ""]
+    if args.command:
+        lines += ["Commands:", ""] + [f"    {c}" for c in args.command] + [""]
+    ks = kernel_stats(args.trace) if args.trace else []
+    if ks:
+        lines += ["## Kernel trace (--kernel-trace --stats)", "",
+                  "| kernel | calls | total ms | avg us | min us | max us | % |", "|---|---|---|---|---|---|---|"]
+        for r in ks:
+            name = _short(r.get("Name", r.get("KernelName", "")))
+            calls = int(r.get("Calls", 0))
+            tot = float(r.get("TotalDurationNs", 0)) / 1e6
+            avg = float(r.get("AverageNs", 0)) / 1e3
+            mn = float(r.get("MinNs", 0)) / 1e3
+            mx = float(r.get("MaxNs", 0)) / 1e3
+            pct = float(r.get("Percentage", 0))
+            lines.append(f"| {name} | {calls} | {tot:.3f} | {avg:.1f} | {mn:.1f} | {mx:.1f} | {pct:.2f} |")
+        lines.append("")
+    traffic = None
+    if args.pmc:
+        cs = counters(args.pmc)
+        cal = cs.get(CALIB, {})
+        fetch_f = CALIB_BYTES / (cal["FETCH_SIZE"] * 1024) if cal.get("FETCH_SIZE") else None
+        write_f = CALIB_BYTES / (cal["WRITE_SIZE"] * 1024) if cal.get("WRITE_SIZE") else None
+        lines += ["## Counters (mean per dispatch)", "",
+                  f"Calibration: a streaming kernel that reads and writes {CALIB_BYTES} bytes each reads "
+                  f"FETCH_SIZE = {cal.get('FETCH_SIZE', float('nan')):.0f} KiB and WRITE_SIZE = "
+                  f"{cal.get('WRITE_SIZE', float('nan')):.0f} KiB; scale factors fetch {fetch_f}, write {write_f}.", ""]
+        names = sorted({c for v in cs.values() for c in v})
+        lines += ["| kernel | " + " | ".join(names) + " |", "|---" * (len(names) + 1) + "|"]
+        for k, v in sorted(cs.items()):
+            if k.startswith("torch:") or k.startswith("__amd"):
+                continue   # input generation, not part of the layer
+            lines.append(f"| {k} | " + " | ".join(f"{v[c]:.4g}" if c in v else "" for c in names) + " |")
+        lines.append("")
+        gu = next((v for k, v in cs.items() if k.startswith("gateup_kernel")), None)
+        if gu and fetch_f and write_f and "FETCH_SIZE" in gu and "WRITE_SIZE" in gu:
+            traffic = gu["FETCH_SIZE"] * 1024 * fetch_f + gu["WRITE_SIZE"] * 1024 * write_f
+            lines += [f"gate/up HBM traffic per launch (scaled): fetch "
+                      f"{gu['FETCH_SIZE'] * 1024 * fetch_f / 1e9:.3f} GB + write "
+                      f"{gu['WRITE_SIZE'] * 1024 * write_f / 1e9:.3f} GB = {traffic / 1e9:.3f} GB", ""]
+            tf = os.path.join(args.out, "traffic_counters.json")
+            table = json.load(open(tf)) if os.path.exists(tf) else {}
+            table[args.workload] = {"gate_up_bytes_per_launch": traffic, "kernel_source_hash": source_hash(),
+                                    "fetch_scale": fetch_f, "write_scale": write_f,
+                                    "gate_up_fetch_kib": gu["FETCH_SIZE"], "gate_up_write_kib": gu["WRITE_SIZE"]}
+            json.dump(table, open(tf, "w"), indent=1, sort_keys=True)
+    out = os.path.join(args.out, args.name or f"rocprof_{args.workload}.md")
+    open(out, "w").write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    r = sub.add_parser("run")
+    r.add_argument("--workload", default="bf16_d7168")
+    r.add_argument("--steps", type=int, default=3)
+    s = sub.add_parser("summarize")
+    s.add_argument("--trace")
+    s.add_argument("--pmc", nargs="*")
+    s.add_argument("--workload", default="bf16_d7168")
+    s.add_argument("--out", default=os.path.join(ROOT, "profiles"))
+    s.add_argument("--name")
+    s.add_argument("--command", nargs="*")
+    args = ap.parse_args()
+    _run(args) if args.cmd == "run" else _summarize(args)
+
+
+if __name__ == "__main__":
+    main()
