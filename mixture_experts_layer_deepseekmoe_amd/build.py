@@ -36,7 +36,10 @@ def common_flags(debug: bool = False):
     flags = [f"--offload-arch={ARCH}", "-std=c++20", "-fPIC", "-Wall", "-Wno-unused-function",
              "-I", os.path.join(ROOT, "include"),
              # keep every packed-fp32 VALU form out of the generated code
-             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+             # MFMA accumulators in VGPRs: with 256 live accumulator registers
+             # the AGPR form makes the allocator rotate them through copies
+             "-mllvm", "-amdgpu-mfma-vgpr-form"]
     flags += ["-O1", "-g", "-DMOE_DEBUG=1"] if debug else ["-O3"]
     return flags
 

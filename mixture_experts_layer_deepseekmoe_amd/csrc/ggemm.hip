@@ -33,9 +33,12 @@ constexpr int NXCD = 8;
 
 template <int FMT>
 struct GG {
-  static constexpr int BM = FMT == FMT_E4M3 ? 128 : 256;
+  // bf16: 192 rows (a wave holds 6 x 8 accumulator subtiles = 192 VGPRs,
+  // leaving the rest of the register file to the pipeline), a 5-stage ring.
+  // FP8 (128-byte K-steps) and fp32 (only small layers): 128 rows.
+  static constexpr int BM = FMT == FMT_BF16 ? 192 : 128;
   static constexpr int NST = FMT == FMT_E4M3 ? 3 : 5;
-  using P = Pipe<FMT, BM, BNW, NST>;
+  using P = Pipe<FMT, BM, BNW, NST, 2>;   // 2 x 2 waves
 };
 
 // Logical tile index of this block, or -1 if the block has no work.
@@ -85,17 +88,17 @@ __device__ __forceinline__ Ring<NST> make_ring(uint8_t* a, uint8_t* b, uint8_t* 
   return r;
 }
 
-// Calls f.template operator()<NSUB>() with NSUB = rows rounded up to a
-// multiple of 32, as 16-row subtiles (2 .. MI).
-template <int MI, int N = 2, class F>
+// Calls f.template operator()<NSUB>() with NSUB = the number of row subtiles
+// each of the two wave rows computes: ceil(rows / 32), 1 .. MI.
+template <int MI, int N = 1, class F>
 __device__ __forceinline__ void dispatch_rows(int rows, F&& f) {
   if constexpr (N >= MI) {
     f.template operator()<MI>();
   } else {
-    if (rows <= 16 * N)
+    if (rows <= 32 * N)
       f.template operator()<N>();
     else
-      dispatch_rows<MI, N + 2>(rows, f);
+      dispatch_rows<MI, N + 1>(rows, f);
   }
 }
 
@@ -108,22 +111,30 @@ __device__ __forceinline__ void gateup_tile(const GateUpArgs& a, typename GG<FMT
   using P = typename GG<FMT>::P;
   const int w = wave_id(), lane = threadIdx.x & 63;
   const int lr = lane & 15, lg = lane >> 4;
-  const int brow[4] = {32 * w, 32 * w + 16, 128 + 32 * w, 128 + 32 * w + 16};
-  f32x4 acc[P::MI][4];
+  const int wm = w & 1, wn = w >> 1;
+  // wave (wm, wn): h columns 64 wn .. 64 wn + 63 of the tile -- gate subtiles
+  // 0-3 and the matching up subtiles 4-7 -- on row subtiles wm, wm+2, ...
+  int brow[8];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    brow[j] = 64 * wn + 16 * j;
+    brow[4 + j] = 128 + 64 * wn + 16 * j;
+  }
+  f32x4 acc[P::MI][P::NJ];
   zero_acc(acc);
   pipe_mainloop<P, GG<FMT>::NST, NSUB>(p, st, nk, brow, acc, swl, kb);
 
   if constexpr (FMT != FMT_E4M3) {
 #pragma unroll
     for (int i = 0; i < NSUB; ++i) {
-      const int row = 16 * i + lr;
+      const int row = 16 * (2 * i + wm) + lr;
 #pragma unroll
-      for (int jj = 0; jj < 2; ++jj) {
-        const int col = n0 + 32 * w + 16 * jj + 4 * lg;
+      for (int jj = 0; jj < 4; ++jj) {
+        const int col = n0 + 64 * wn + 16 * jj + 4 * lg;
         if (row < rows && col < a.inter) {
           float h[4];
 #pragma unroll
-          for (int r = 0; r < 4; ++r) h[r] = silu_f32(acc[i][jj][r]) * acc[i][jj + 2][r];
+          for (int r = 0; r < 4; ++r) h[r] = silu_f32(acc[i][jj][r]) * acc[i][jj + 4][r];
           const size_t o = static_cast<size_t>(row0 + row) * a.inter + col;
           if constexpr (FMT == FMT_F32) {
             *reinterpret_cast<float4*>(static_cast<float*>(a.h) + o) = make_float4(h[0], h[1], h[2], h[3]);
@@ -137,41 +148,41 @@ __device__ __forceinline__ void gateup_tile(const GateUpArgs& a, typename GG<FMT
     }
   } else {
     // 1x128 quantisation of h along I: the 128 columns of this tile are one
-    // scale group.  A row's amax is reduced over its lane's 8 values, the 4
-    // lane groups, then the 4 waves.
-    float hv[NSUB][2][4];
+    // scale group.  A row's amax is reduced over its lane's 16 values, the 4
+    // lane groups, then the two waves (wn = 0, 1) that share the row.
+    float hv[NSUB][4][4];
 #pragma unroll
     for (int i = 0; i < NSUB; ++i) {
       float m = 0.f;
 #pragma unroll
-      for (int jj = 0; jj < 2; ++jj)
+      for (int jj = 0; jj < 4; ++jj)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          hv[i][jj][r] = silu_f32(acc[i][jj][r]) * acc[i][jj + 2][r];
+          hv[i][jj][r] = silu_f32(acc[i][jj][r]) * acc[i][jj + 4][r];
           m = fmaxf(m, fabsf(hv[i][jj][r]));
         }
       m = fmaxf(m, __shfl_xor(m, 16));
       m = fmaxf(m, __shfl_xor(m, 32));
-      if (lg == 0) red[w][16 * i + lr] = m;
+      if (lg == 0) red[wn][16 * (2 * i + wm) + lr] = m;
     }
     __syncthreads();
     const int ncb = a.inter / 128;
 #pragma unroll
     for (int i = 0; i < NSUB; ++i) {
-      const int row = 16 * i + lr;
+      const int row = 16 * (2 * i + wm) + lr;
       if (row < rows) {
-        const float m = fmaxf(fmaxf(red[0][row], red[1][row]), fmaxf(red[2][row], red[3][row]));
+        const float m = fmaxf(red[0][row], red[1][row]);
         const float inv = m == 0.f ? 0.f : 448.f / m;
         const size_t grow = static_cast<size_t>(row0 + row);
 #pragma unroll
-        for (int jj = 0; jj < 2; ++jj) {
-          const int col = n0 + 32 * w + 16 * jj + 4 * lg;
+        for (int jj = 0; jj < 4; ++jj) {
+          const int col = n0 + 64 * wn + 16 * jj + 4 * lg;
           uint32_t q = 0;
 #pragma unroll
           for (int r = 0; r < 4; ++r) q |= f32_to_e4m3(hv[i][jj][r] * inv) << (8 * r);
           *reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(a.h) + grow * a.inter + col) = q;
         }
-        if (w == 0 && lg == 0) a.h_scale[grow * ncb + nb] = m == 0.f ? 1.f : m / 448.f;
+        if (wn == 0 && lg == 0) a.h_scale[grow * ncb + nb] = m == 0.f ? 1.f : m / 448.f;
       }
     }
   }
@@ -182,7 +193,7 @@ __global__ __launch_bounds__(256, 1) void gateup_kernel(GateUpArgs a) {
   using P = typename GG<FMT>::P;
   constexpr int NST = GG<FMT>::NST, BM = GG<FMT>::BM;
   MOE_STAGE_RING(P, NST)
-  __shared__ float red[FMT == FMT_E4M3 ? 4 : 1][BM];
+  __shared__ float red[FMT == FMT_E4M3 ? 2 : 1][BM];
   __shared__ float swl[FMT == FMT_E4M3 ? 2 * MAX_KB : 1];
 
   const int nb_n = ceil_div(a.inter, GG_HCOLS);
@@ -241,16 +252,21 @@ __device__ __forceinline__ void down_tile(const DownArgs& a, typename GG<FMT>::P
   using P = typename GG<FMT>::P;
   const int w = wave_id(), lane = threadIdx.x & 63;
   const int lr = lane & 15, lg = lane >> 4;
-  const int brow[4] = {64 * w, 64 * w + 16, 64 * w + 32, 64 * w + 48};
-  f32x4 acc[P::MI][4];
+  const int wm = w & 1, wn = w >> 1;
+  // wave (wm, wn): output columns 128 wn .. 128 wn + 127 of the tile (one
+  // 128-wide weight scale block), row subtiles wm, wm+2, ...
+  int brow[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) brow[j] = 128 * wn + 16 * j;
+  f32x4 acc[P::MI][P::NJ];
   zero_acc(acc);
-  pipe_mainloop<P, GG<FMT>::NST, NSUB>(p, st, nk, brow, acc, FMT == FMT_E4M3 ? swl + (w >> 1) * kb : nullptr, 0);
+  pipe_mainloop<P, GG<FMT>::NST, NSUB>(p, st, nk, brow, acc, FMT == FMT_E4M3 ? swl + wn * kb : nullptr, 0);
 #pragma unroll
   for (int i = 0; i < NSUB; ++i) {
-    const int row = 16 * i + lr;
+    const int row = 16 * (2 * i + wm) + lr;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int col = n0 + 64 * w + 16 * j + 4 * lg;
+    for (int j = 0; j < 8; ++j) {
+      const int col = n0 + 128 * wn + 16 * j + 4 * lg;
       if (row < rows && col < a.d) {
         const size_t o = static_cast<size_t>(row0 + row) * a.d + col;
         if constexpr (FMT == FMT_F32) {
@@ -322,7 +338,9 @@ int grid_for(int max_mtiles, int nb_n) {
 
 }  // namespace
 
-int gg_bm(int fmt) { return fmt == FMT_E4M3 ? GG<FMT_E4M3>::BM : GG<FMT_BF16>::BM; }
+int gg_bm(int fmt) {
+  return fmt == FMT_E4M3 ? GG<FMT_E4M3>::BM : (fmt == FMT_F32 ? GG<FMT_F32>::BM : GG<FMT_BF16>::BM);
+}
 
 hipError_t launch_gateup(int fmt, const GateUpArgs& a, hipStream_t s) {
   const int grid = grid_for(a.max_mtiles, ceil_div(a.inter, GG_HCOLS));

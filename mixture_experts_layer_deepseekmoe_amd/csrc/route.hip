@@ -55,7 +55,7 @@ __global__ __launch_bounds__(256) void route_kernel(RouteArgs a) {
           return static_cast<const uint8_t*>(a.centroids) + static_cast<size_t>(e) * row_bytes;
         },
         [&](int) { return static_cast<const float*>(nullptr); });
-    f32x4 acc[P::MI][4];
+    f32x4 acc[P::MI][P::NJ];
     zero_acc(acc);
     if (valid > 16)
       pipe_mainloop<P, RNST, 2>(p, st, nk, brow, acc);

@@ -6,10 +6,10 @@
     python -m mixture_experts_layer_deepseekmoe_amd.profiling summarize --trace DIR --pmc DIR [DIR...] \
         --workload bf16_d7168 --out profiles
 
-``run`` first launches one plain streaming kernel of known size (an fp32
+``run`` first launches one plain streaming kernel of known size (an fp64
 elementwise multiply of a 1 GiB tensor into another: 1 GiB read, 1 GiB
-written), which calibrates the HBM byte counters (FETCH_SIZE / WRITE_SIZE),
-then a few layer forwards.  ``summarize`` averages every counter per kernel
+written; nothing else in the run is fp64), which calibrates the HBM byte
+counters (FETCH_SIZE / WRITE_SIZE), then a few layer forwards.  ``summarize`` averages every counter per kernel
 and per dispatch, scales FETCH_SIZE / WRITE_SIZE by the calibration, and
 writes a markdown summary plus profiles/traffic_counters.json.
 """
@@ -37,7 +37,7 @@ def _run(args):
     from moe_workloads import get_config, make_inputs
 
     torch.cuda.set_device(0)
-    src = torch.ones(CALIB_BYTES // 4, dtype=torch.float32, device="cuda")
+    src = torch.ones(CALIB_BYTES // 8, dtype=torch.float64, device="cuda")
     dst = torch.empty_like(src)
     torch.mul(src, 2.0, out=dst)
     torch.cuda.synchronize()
@@ -79,8 +79,13 @@ CALIB = "calibration_stream(1GiB read + 1GiB write)"
 
 
 def _is_calibration(row) -> bool:
-    # the fp32 multiply of the 1 GiB calibration tensor (4 elements per work-item)
-    return "MulFunctor<float>" in row["Kernel_Name"] and int(row["Grid_Size"]) == CALIB_BYTES // 16
+    # the fp64 multiply of the 1 GiB calibration tensor
+    return "MulFunctor<double>" in row["Kernel_Name"]
+
+
+# rocprofv3 --kernel-include-regex for counter runs: the layer's kernels and
+# the calibration stream (keeps the input generators' kernels out of the CSV)
+KERNEL_REGEX = "gateup_kernel|down_kernel|route_kernel|combine_kernel|hist_kernel|scan_kernel|permute_kernel|quant_act_kernel|bias_update_kernel|MulFunctor<double>"
 
 
 def _csvs(d, pattern):

@@ -365,3 +365,41 @@ def test_fp8_layer_close_to_bf16_layer():
     err = np.abs(r8["y"] - r16["y"]).max()
     assert err < 0.1 * np.sqrt(np.mean(branch ** 2)) * 10
     assert err > 0                                      # quantisation did happen
+
+
+def test_fp8_ffn_against_torch_float8_composition():
+    """The FP8 expert, rebuilt independently: torch's float8_e4m3fn cast for
+    every quantisation (values are scaled below 464 first, where its
+    round-to-nearest-even agrees with a saturating encoder), float64 matmuls
+    and torch's SiLU."""
+    rng = np.random.default_rng(12)
+    x = rng.normal(0, 1, (5, 256)).astype(np.float32)
+    wgu = rng.normal(0, 0.05, (2 * 128, 256)).astype(np.float32)
+    wd = rng.normal(0, 0.05, (256, 128)).astype(np.float32)
+
+    def tq_act(a):          # 1x128 tiles
+        a = torch.from_numpy(a)
+        t = a.view(a.shape[0], -1, 128)
+        amax = t.abs().amax(-1, keepdim=True)
+        scale = amax / 448.0
+        q = (t * (448.0 / amax)).to(torch.float8_e4m3fn).to(torch.float64)
+        return (q * scale.to(torch.float64)).view_as(a).to(torch.float64)
+
+    def tq_w(w):            # 128x128 blocks
+        w = torch.from_numpy(w)
+        R, C = w.shape
+        t = w.view(R // 128, 128, C // 128, 128)
+        amax = t.abs().amax(dim=(1, 3), keepdim=True)
+        q = (t * (448.0 / amax)).to(torch.float8_e4m3fn).to(torch.float64)
+        return (q * (amax / 448.0).to(torch.float64)).view(R, C)
+
+    xd, gd, dd = tq_act(x), tq_w(wgu), tq_w(wd)
+    g, u = xd @ gd[:128].T, xd @ gd[128:].T
+    h = (torch.nn.functional.silu(g) * u).to(torch.float32).numpy()
+    ref = (tq_act(h) @ dd.T).numpy()
+
+    xq, xs = O.quantize_act_1x128(x)
+    gq, gs = O.quantize_weight_128x128(wgu)
+    dq, ds = O.quantize_weight_128x128(wd)
+    out = O.swiglu_ffn_fp8(O.dequantize_act(xq, xs), gq, gs, dq, ds)
+    np.testing.assert_allclose(out, ref, rtol=1e-12, atol=1e-12)
