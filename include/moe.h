@@ -73,8 +73,11 @@ typedef enum {
  *                    come pre-quantised per 128x128 block (moe_quantize_weight_e4m3).
  *                    The router and the residual use the unquantised bf16 u.
  *   out_dtype dtype of y: F32 or BF16
- * Limits: d and inter multiples of 64 (F32: 32 is enough; E4M3: 128);
- * T * top_k and (top_k + n_shared) * T below 2^31.
+ * Limits: d and inter multiples of 64 (F32: 32 is enough; E4M3: 128, and
+ * at most 32768); T * top_k and (top_k + n_shared) * T below 2^31; the
+ * bytes of u (T * d * size of x_dtype) and of one expert's gate/up matrix
+ * (2 * inter * d * size of w_dtype) below 2^32.  Outside them the calls
+ * return MOE_ERR_UNSUPPORTED.
  */
 typedef struct {
   int32_t T, d, n_routed, n_shared, inter, top_k;

@@ -3,7 +3,7 @@
 //
 // Data movement: every K-step ("stage") moves SB bytes of K per row (64 bytes
 // = 32 bf16 / 16 fp32, or 128 bytes = 128 e4m3) straight from global memory
-// into LDS with global_load_lds_dwordx4 (no register staging).  NST stage
+// into LDS with buffer_load_dwordx4 ... lds (no register staging).  NST stage
 // buffers form a ring; loads run NST-2 stages ahead of the MFMAs.  Each stage
 // buffer is its own __shared__ object, so the compiler's wait insertion can
 // tell the asynchronous LDS writes of one stage from the reads of another; the
@@ -37,13 +37,24 @@
 namespace moe {
 
 typedef __attribute__((address_space(3))) void* lds_void_ptr;
-typedef __attribute__((address_space(1))) void* global_void_ptr;
 
-__device__ __forceinline__ void dma16(const void* g, void* l) {
-  __builtin_amdgcn_global_load_lds((global_void_ptr)g, (lds_void_ptr)l, 16, 0, 0);
+// Raw buffer resource over [base, base + bytes): loads at offsets past the
+// range return zeros instead of touching memory.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes), 0x00020000);
 }
-__device__ __forceinline__ void dma4(const void* g, void* l) {
-  __builtin_amdgcn_global_load_lds((global_void_ptr)g, (lds_void_ptr)l, 4, 0, 0);
+
+// buffer_load ... lds: each lane's 16 (4) bytes at voff + soff go to LDS at
+// l + 16 * lane (4 * lane).  The buffer form (not global_load_lds) matters:
+// the compiler treats a global LDS DMA as a FLAT access that may touch LDS
+// and then waits for every outstanding LDS read (lgkmcnt(0)) before the next
+// use of any of them, which would serialise the fragment prefetch.
+__device__ __forceinline__ void dma16(rsrc_t r, uint32_t voff, uint32_t soff, void* l) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_ptr)l, 16, voff, soff, 0, 0);
+}
+__device__ __forceinline__ void dma4(rsrc_t r, uint32_t voff, uint32_t soff, void* l) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_ptr)l, 4, voff, soff, 0, 0);
 }
 
 // s_waitcnt vmcnt(N) expcnt(any) lgkmcnt(0)  (gfx9 encoding)
@@ -75,6 +86,17 @@ __device__ __forceinline__ int swz(int r) {
     return (r ^ (r >> 3)) & 7;
 }
 
+// W rows read by one wave: subtile j covers rows base + 16 j, plus SPLIT
+// for the second half of the subtiles (j >= NJ / 2).  base is wave-uniform
+// and a multiple of 64, so a row's swizzle is fixed at compile time by j and
+// the lane, and every fragment address is one register plus an immediate
+// (given as a runtime array of rows, the compiler kept one address register
+// per subtile and spilled them).
+template <int SPLIT>
+struct WRows {
+  int base;
+};
+
 template <int FMT, int BM, int BNW, int NST, int WM = 1>
 struct Pipe {
   static constexpr int SB = FMT == FMT_E4M3 ? 128 : 64;
@@ -92,38 +114,84 @@ struct Pipe {
   static constexpr int MI = (BM / 16 + WM - 1) / WM;     // row subtiles per wave
   static_assert(BNW % (4 * RPI) == 0, "W rows must fill whole DMA instructions");
 
-  const uint8_t* pa[NIA];
-  const uint8_t* pb[NIB];
-  const float* psa;
+  rsrc_t ra, rb, rs;
+  uint32_t oa[NIA];   // per-lane byte offsets of the lane's 16-byte piece, K-step 0
+  uint32_t ob[NIB];
+  uint32_t os;
 
-  // a_row(r): first byte of X row r of the tile (r < AROWS; the caller clamps
-  // rows past the valid ones to a valid row).  b_row(r): W row r (r < BNW).
-  // sa_row(r): FP8 scale row of X row r (r < 256).
+  // X rows come from resource a (a_off(r): byte offset of X row r of the
+  // tile, r < AROWS; the caller maps rows past the valid ones to a valid
+  // row), W rows from resource b (b_off(r), r < BNW), FP8 X scales from
+  // resource s (s_off(r): byte offset of the scale row of X row r, r < 256).
+  // The loads are spread over 4 waves: wave w (or w - 4, in the
+  // wave-specialised pipeline) issues row groups w, w + 4, w + 8, ...
   template <class FA, class FB, class FS>
-  __device__ __forceinline__ void init(FA a_row, FB b_row, FS sa_row) {
-    const int w = wave_id(), lane = threadIdx.x & 63;
+  __device__ __forceinline__ void init(rsrc_t a, FA a_off, rsrc_t b, FB b_off, rsrc_t sc, FS s_off) {
+    const int w = wave_id() & 3, lane = threadIdx.x & 63;
+    ra = a;
+    rb = b;
+    rs = sc;
 #pragma unroll
     for (int i = 0; i < NIA; ++i) {
       const int r = RPI * (w + 4 * i) + lane / CPR;
-      pa[i] = a_row(r) + ((lane % CPR) ^ swz<SB>(r)) * 16;
+      oa[i] = a_off(r) + ((lane % CPR) ^ swz<SB>(r)) * 16;
     }
 #pragma unroll
     for (int i = 0; i < NIB; ++i) {
       const int r = RPI * (w + 4 * i) + lane / CPR;
-      pb[i] = b_row(r) + ((lane % CPR) ^ swz<SB>(r)) * 16;
+      ob[i] = b_off(r) + ((lane % CPR) ^ swz<SB>(r)) * 16;
     }
-    psa = nullptr;
-    if constexpr (FMT == FMT_E4M3) psa = sa_row(64 * w + lane);
+    os = 0;
+    if constexpr (FMT == FMT_E4M3) os = s_off(64 * w + lane);
   }
 
-  __device__ __forceinline__ void issue(uint8_t* st, int ks) const {
-    const int w = wave_id();
-    const size_t kofs = static_cast<size_t>(ks) * SB;
-#pragma unroll
-    for (int i = 0; i < NIA; ++i) dma16(pa[i] + kofs, st + A_OFF + RPI * (w + 4 * i) * SB);
-#pragma unroll
-    for (int i = 0; i < NIB; ++i) dma16(pb[i] + kofs, st + B_OFF + RPI * (w + 4 * i) * SB);
-    if constexpr (FMT == FMT_E4M3) dma4(psa + ks, st + S_OFF + 256 * w);
+  // X row-group DMA instructions a stage needs when each wave computes only
+  // its first NSUB row subtiles (tile rows < 16 * WM * NSUB): the row groups
+  // wholly past them are not loaded at all.
+  template <int NSUB>
+  static constexpr int nia_for() {
+    constexpr int need = (16 * WM * NSUB + 4 * RPI - 1) / (4 * RPI);
+    return need < NIA ? need : NIA;
+  }
+  template <int NSUB>
+  static constexpr int nl_for() {
+    return nia_for<NSUB>() + NIB + (FMT == FMT_E4M3 ? 1 : 0);
+  }
+
+  // DMA instruction Q of a stage: NA X row groups, then the W row groups,
+  // then (FP8) the X scales.
+  template <int Q, int NA>
+  __device__ __forceinline__ void issue_one(uint8_t* st, int ks) const {
+    const int w = wave_id() & 3;
+    const uint32_t kofs = static_cast<uint32_t>(ks) * SB;
+    if constexpr (Q < NA)
+      dma16(ra, oa[Q], kofs, st + A_OFF + RPI * (w + 4 * Q) * SB);
+    else if constexpr (Q < NA + NIB)
+      dma16(rb, ob[Q - NA], kofs, st + B_OFF + RPI * (w + 4 * (Q - NA)) * SB);
+    else
+      dma4(rs, os, static_cast<uint32_t>(ks) * 4, st + S_OFF + 256 * w);
+  }
+  template <int LO, int HI, int NA>
+  __device__ __forceinline__ void issue_range(uint8_t* st, int ks) const {
+    if constexpr (LO < HI) {
+      issue_one<LO, NA>(st, ks);
+      issue_range<LO + 1, HI, NA>(st, ks);
+    }
+  }
+  // Instructions LO..HI-1 of K-steps ks (into st0) and ks+1 (into st1),
+  // interleaved so that the two 64-byte halves of every 128-byte line are
+  // requested back to back: the L1 then merges them into one L2 request.
+  // With 64-byte pieces requested a K-step apart, each half costs a request
+  // of its own, and the number of L2 requests a CU keeps in flight is what
+  // limits the loads (measured: 25 vs 32 TB/s of L2 hits, 5.7 vs 6.2 TB/s
+  // from HBM).
+  template <int LO, int HI, int NA>
+  __device__ __forceinline__ void issue_pair_range(uint8_t* st0, uint8_t* st1, int ks) const {
+    if constexpr (LO < HI) {
+      issue_one<LO, NA>(st0, ks);
+      issue_one<LO, NA>(st1, ks + 1);
+      issue_pair_range<LO + 1, HI, NA>(st0, st1, ks);
+    }
   }
 
   __device__ __forceinline__ static uint4 frag16(const uint8_t* base, int r, int chunk) {
@@ -157,16 +225,18 @@ struct Pipe {
 
   // Reads of a stage's first fragments (issued at the end of the previous
   // stage, so each stage starts on MFMAs).
-  template <int NSUB>
-  __device__ __forceinline__ static void prefetch(const uint8_t* st, const int (&brow)[NJ], Frags& f) {
+  template <int NSUB, int SPLIT>
+  __device__ __forceinline__ static void prefetch(const uint8_t* st, WRows<SPLIT> wr, Frags& f) {
     const int lane = threadIdx.x & 63, lr = lane & 15, lg = lane >> 4;
+    const uint8_t* wst = st + B_OFF + wr.base * SB;
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
+      const int r = 16 * j + (j >= NJ / 2 ? SPLIT : 0) + lr;
       if constexpr (FMT == FMT_E4M3) {
-        f.w[2 * j] = frag16(st + B_OFF, brow[j] + lr, 2 * lg);
-        f.w[2 * j + 1] = frag16(st + B_OFF, brow[j] + lr, 2 * lg + 1);
+        f.w[2 * j] = frag16(wst, r, 2 * lg);
+        f.w[2 * j + 1] = frag16(wst, r, 2 * lg + 1);
       } else {
-        f.w[j] = frag16(st + B_OFF, brow[j] + lr, lg);
+        f.w[j] = frag16(wst, r, lg);
       }
     }
     load_x(st, 0, &f.x[0], f.sx[0]);
@@ -178,18 +248,23 @@ struct Pipe {
   // SIMD the MFMA issue blocks for the length of the previous MFMAs, so a read
   // issued after a group of MFMAs would expose its whole LDS latency.
   // sched_barrier pins that order.  sw[j]: FP8 weight scale of subtile j.
-  template <int NSUB>
-  __device__ __forceinline__ static void compute(const uint8_t* st, Frags& f, f32x4 (&acc)[MI][NJ], const float (&sw)[NJ]) {
-    uint4 xc[XW], xnx[XW], xn[XW];
-    float sc = f.sx[0], snx = f.sx[1], sn = 0.f;
-#pragma unroll
-    for (int q = 0; q < XW; ++q) { xc[q] = f.x[q]; xnx[q] = f.x[XW + q]; }
-#pragma unroll
-    for (int i = 0; i < NSUB; ++i) {
+  //
+  // hook<i>() runs after the MFMAs of subtile i: the pipelines below use it
+  // to spread the loads of a refilled stage over the subtiles, a few after
+  // each group of MFMAs -- issued back to back they fill the vector memory
+  // queue and hold up the wave's MFMA issue.
+  template <int NSUB, int I, class H>
+  __device__ __forceinline__ static void compute_from(const uint8_t* st, Frags& f, f32x4 (&acc)[MI][NJ],
+                                                      const float (&sw)[NJ], H& hook, uint4 (&xc)[XW],
+                                                      uint4 (&xnx)[XW], float& sc, float& snx) {
+    if constexpr (I < NSUB) {
+      constexpr int i = I;
+      uint4 xn[XW];
+      float sn = 0.f;
 #pragma unroll
       for (int q = 0; q < XW; ++q) xn[q] = xnx[q];
       sn = snx;
-      if (i + 2 < NSUB) load_x(st, i + 2, xn, sn);
+      if constexpr (i + 2 < NSUB) load_x(st, i + 2, xn, sn);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int j = 0; j < NJ; ++j) {
@@ -210,21 +285,41 @@ struct Pipe {
         }
       }
       __builtin_amdgcn_sched_barrier(0);
+      hook.template operator()<i>();
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int q = 0; q < XW; ++q) { xc[q] = xnx[q]; xnx[q] = xn[q]; }
       sc = snx;
       snx = sn;
+      compute_from<NSUB, I + 1>(st, f, acc, sw, hook, xc, xnx, sc, snx);
     }
+  }
+
+  // hook.template operator()<i>() runs after the MFMAs of row subtile i.
+  template <int NSUB, class H>
+  __device__ __forceinline__ static void compute(const uint8_t* st, Frags& f, f32x4 (&acc)[MI][NJ],
+                                                 const float (&sw)[NJ], H&& hook) {
+    uint4 xc[XW], xnx[XW];
+    float sc = f.sx[0], snx = f.sx[1];
+#pragma unroll
+    for (int q = 0; q < XW; ++q) { xc[q] = f.x[q]; xnx[q] = f.x[XW + q]; }
+    compute_from<NSUB, 0>(st, f, acc, sw, hook, xc, xnx, sc, snx);
   }
 };
 
-template <class P, int NST, int S, int NSUB, bool GUARD>
+// ---------------------------------------------------------------------------
+// Single-stage pipeline (NST >= 3 stage buffers; used with 128-byte K-steps,
+// whose loads are whole lines already, and by the router).
+
+template <class P, int NST, int S, int NSUB, bool GUARD, bool SPREAD, class WR>
 __device__ __forceinline__ void pipe_step(const P& p, uint8_t* const (&st)[NST], int ks, int nk,
-                                          const int (&brow)[P::NJ], typename P::Frags& f,
+                                          const WR& wr, typename P::Frags& f,
                                           f32x4 (&acc)[P::MI][P::NJ], const float* sw_lds, int sw_stride) {
   if constexpr (GUARD) {
     if (ks >= nk) return;
   }
+  constexpr int NA = P::template nia_for<NSUB>();
+  constexpr int NL = P::template nl_for<NSUB>();
   // Every step issues exactly one stage of loads (clamped to the last K-step
   // past the end: it lands in a buffer nobody reads), so NST-3 stages newer
   // than ks+1 are always in flight here.  The wait makes stage ks+1 complete
@@ -233,9 +328,11 @@ __device__ __forceinline__ void pipe_step(const P& p, uint8_t* const (&st)[NST],
   // of NST steps carry no branch: at a control-flow join the compiler loses
   // track of which stage buffer an LDS DMA targets and would wait for every
   // outstanding load before the next LDS read, serialising the pipeline.
-  wait_vm_lgkm0<(NST - 3) * P::NL>();
+  wait_vm_lgkm0<(NST - 3) * NL>();
   block_barrier();
-  p.issue(st[(S + NST - 1) % NST], min(ks + NST - 1, nk - 1));
+  uint8_t* const dst = st[(S + NST - 1) % NST];
+  const int kn = min(ks + NST - 1, nk - 1);
+  if constexpr (!SPREAD) p.template issue_range<0, NL, NA>(dst, kn);
   float sw[P::NJ];
 #pragma unroll
   for (int j = 0; j < P::NJ; ++j) sw[j] = 1.f;
@@ -244,40 +341,120 @@ __device__ __forceinline__ void pipe_step(const P& p, uint8_t* const (&st)[NST],
 #pragma unroll
     for (int j = 0; j < P::NJ; ++j) sw[j] = sw_lds[(j >= P::NJ / 2 ? sw_stride : 0) + ks];
   }
-  P::template compute<NSUB>(st[S], f, acc, sw);
+  P::template compute<NSUB>(st[S], f, acc, sw, [&]<int I>() {
+    if constexpr (SPREAD) p.template issue_range<I * NL / NSUB, (I + 1) * NL / NSUB, NA>(dst, kn);
+  });
   // stage ks+1 (if any: past the end this reads a clamped, unused buffer)
-  P::template prefetch<NSUB>(st[(S + 1) % NST], brow, f);
+  P::template prefetch<NSUB>(st[(S + 1) % NST], wr, f);
 }
 
-template <class P, int NST, int S, int NSUB, bool GUARD>
+template <class P, int NST, int S, int NSUB, bool GUARD, bool SPREAD, class WR>
 __device__ __forceinline__ void pipe_round(const P& p, uint8_t* const (&st)[NST], int base, int nk,
-                                           const int (&brow)[P::NJ], typename P::Frags& f,
+                                           const WR& wr, typename P::Frags& f,
                                            f32x4 (&acc)[P::MI][P::NJ], const float* sw_lds, int sw_stride) {
-  pipe_step<P, NST, S, NSUB, GUARD>(p, st, base + S, nk, brow, f, acc, sw_lds, sw_stride);
-  if constexpr (S + 1 < NST) pipe_round<P, NST, S + 1, NSUB, GUARD>(p, st, base, nk, brow, f, acc, sw_lds, sw_stride);
+  pipe_step<P, NST, S, NSUB, GUARD, SPREAD>(p, st, base + S, nk, wr, f, acc, sw_lds, sw_stride);
+  if constexpr (S + 1 < NST)
+    pipe_round<P, NST, S + 1, NSUB, GUARD, SPREAD>(p, st, base, nk, wr, f, acc, sw_lds, sw_stride);
 }
 
 // The whole K loop (unrolled by the ring size so every stage buffer is a
 // compile-time object).  FP8: sw_lds holds the tile's weight-block scales,
 // two rows (column subtiles 0-1 and 2-3) of sw_stride entries, one per stage.
-template <class P, int NST, int NSUB>
+template <class P, int NST, int NSUB, bool SPREAD = false, class WR>
 __device__ __forceinline__ void pipe_mainloop(const P& p, uint8_t* const (&st)[NST], int nk,
-                                              const int (&brow)[P::NJ], f32x4 (&acc)[P::MI][P::NJ],
+                                              const WR& wr, f32x4 (&acc)[P::MI][P::NJ],
                                               const float* sw_lds = nullptr, int sw_stride = 0) {
-  static_assert(NST >= 3 && P::NL * (NST - 2) < 64, "stage ring");
+  constexpr int NA = P::template nia_for<NSUB>();
+  constexpr int NL = P::template nl_for<NSUB>();
+  static_assert(NST >= 3 && NL * (NST - 2) < 64, "stage ring");
 #pragma unroll
-  for (int s = 0; s < NST - 1; ++s) p.issue(st[s], min(s, nk - 1));
-  wait_vm_lgkm0<(NST - 2) * P::NL>();   // stage 0
+  for (int s = 0; s < NST - 1; ++s) p.template issue_range<0, NL, NA>(st[s], min(s, nk - 1));
+  wait_vm_lgkm0<(NST - 2) * NL>();   // stage 0
   block_barrier();
   typename P::Frags f;
-  P::template prefetch<NSUB>(st[0], brow, f);
+  P::template prefetch<NSUB>(st[0], wr, f);
   int base = 0;
   for (; base + NST <= nk; base += NST)
-    pipe_round<P, NST, 0, NSUB, false>(p, st, base, nk, brow, f, acc, sw_lds, sw_stride);
-  if (base < nk) pipe_round<P, NST, 0, NSUB, true>(p, st, base, nk, brow, f, acc, sw_lds, sw_stride);
+    pipe_round<P, NST, 0, NSUB, false, SPREAD>(p, st, base, nk, wr, f, acc, sw_lds, sw_stride);
+  if (base < nk) pipe_round<P, NST, 0, NSUB, true, SPREAD>(p, st, base, nk, wr, f, acc, sw_lds, sw_stride);
   // drain the clamped tail loads; every wave is done with every buffer
   wait_vm_lgkm0<0>();
   block_barrier();
+}
+
+// ---------------------------------------------------------------------------
+// Wave-specialised paired pipeline (8 waves, 64-byte K-steps, a ring of 5
+// stage buffers, stage s in buffer s % 5).  Waves 4-7 only issue loads; waves
+// 0-3 only read fragments and run the MFMAs.  A wave that issues a load while
+// the memory pipeline is backed up stalls until the load is accepted; in a
+// wave that also issues the MFMAs, that stall idles the matrix core for as
+// long as the memory system is the bottleneck, serialising memory and math.
+//
+// Per pair q (K-steps 2q, 2q+1), both roles pass two barriers:
+//   A_q  the MFMA waves are done with stage 2q: the loader refills the
+//        buffers of stages 2q-1 and 2q with pair q+2;
+//   B_q  the loader's wait completed pair q+1: the MFMA waves read it.
+// So pair q+2 has the MFMA time of K-steps 2q+1 .. 2q+3 to arrive.
+
+template <class P, int Q, int NSUB, bool GUARD>
+__device__ __forceinline__ void ws_load_pairs(const P& p, uint8_t* const (&st)[5], int q0, int np) {
+  constexpr int NA = P::template nia_for<NSUB>();
+  constexpr int NL = P::template nl_for<NSUB>();
+  const int q = q0 + Q;
+  if constexpr (GUARD) {
+    if (q >= np) return;
+  }
+  block_barrier();   // A_q
+  // past the last pair the loads repeat it into buffers nobody reads
+  p.template issue_pair_range<0, NL, NA>(st[(2 * Q + 4) % 5], st[(2 * Q + 5) % 5], 2 * min(q + 2, np - 1));
+  wait_vm_lgkm0<2 * NL>();   // pair q+1
+  block_barrier();   // B_q
+  if constexpr (Q + 1 < 5) ws_load_pairs<P, Q + 1, NSUB, GUARD>(p, st, q0, np);
+}
+
+template <class P, int Q, int NSUB, bool GUARD, class WR>
+__device__ __forceinline__ void ws_mfma_pairs(uint8_t* const (&st)[5], int q0, int np, const WR& wr,
+                                              typename P::Frags& f, f32x4 (&acc)[P::MI][P::NJ]) {
+  const int q = q0 + Q;
+  if constexpr (GUARD) {
+    if (q >= np) return;
+  }
+  const float sw[P::NJ] = {};
+  P::template compute<NSUB>(st[(2 * Q) % 5], f, acc, sw, []<int I>() {});
+  P::template prefetch<NSUB>(st[(2 * Q + 1) % 5], wr, f);
+  block_barrier();   // A_q
+  P::template compute<NSUB>(st[(2 * Q + 1) % 5], f, acc, sw, []<int I>() {});
+  block_barrier();   // B_q
+  P::template prefetch<NSUB>(st[(2 * Q + 2) % 5], wr, f);
+  if constexpr (Q + 1 < 5) ws_mfma_pairs<P, Q + 1, NSUB, GUARD>(st, q0, np, wr, f, acc);
+}
+
+// Returns on every wave; only waves 0-3 hold results in acc.
+template <class P, int NSUB, class WR>
+__device__ __forceinline__ void pipe_mainloop_ws(const P& p, uint8_t* const (&st)[5], int nk,
+                                                 const WR& wr, f32x4 (&acc)[P::MI][P::NJ]) {
+  static_assert(P::SB == 64, "pairs of 64-byte K-steps");
+  constexpr int NA = P::template nia_for<NSUB>();
+  constexpr int NL = P::template nl_for<NSUB>();
+  static_assert(4 * NL < 64, "vmcnt range");
+  const int np = nk / 2;
+  if (wave_id() >= 4) {
+    p.template issue_pair_range<0, NL, NA>(st[0], st[1], 0);
+    p.template issue_pair_range<0, NL, NA>(st[2], st[3], 2 * min(1, np - 1));
+    wait_vm_lgkm0<2 * NL>();   // pair 0
+    block_barrier();
+    int q = 0;
+    for (; q + 5 <= np; q += 5) ws_load_pairs<P, 0, NSUB, false>(p, st, q, np);
+    if (q < np) ws_load_pairs<P, 0, NSUB, true>(p, st, q, np);
+    wait_vm_lgkm0<0>();   // the clamped tail loads land before the block ends
+  } else {
+    block_barrier();
+    typename P::Frags f;
+    P::template prefetch<NSUB>(st[0], wr, f);
+    int q = 0;
+    for (; q + 5 <= np; q += 5) ws_mfma_pairs<P, 0, NSUB, false>(st, q, np, wr, f, acc);
+    if (q < np) ws_mfma_pairs<P, 0, NSUB, true>(st, q, np, wr, f, acc);
+  }
 }
 
 template <int MI, int NJ>

@@ -15,8 +15,7 @@
 //           per 128 columns, quantised in the epilogue.
 // down:     Y[r, c] = H_r . Wd[c], stored bf16 (fp32 on the fp32 path).
 //
-// Tiles: BM rows (256; 128 on the FP8 path, whose 128-byte K-steps need the
-// LDS) x 256 W rows (gate/up: 128 gate + 128 up rows = 128 h columns; down:
+// Tiles: BM rows (192; 128 on the FP8 and fp32 paths) x 256 W rows (gate/up: 128 gate + 128 up rows = 128 h columns; down:
 // 256 output columns).  Blocks are mapped to XCDs so that each XCD walks a
 // contiguous run of the tile list (expert-major): the tiles of one expert run
 // together on one XCD and share its L2 for the expert's weights and gathered
@@ -33,13 +32,29 @@ constexpr int NXCD = 8;
 
 template <int FMT>
 struct GG {
-  // bf16: 192 rows (a wave holds 6 x 8 accumulator subtiles = 192 VGPRs,
-  // leaving the rest of the register file to the pipeline), a 5-stage ring.
-  // FP8 (128-byte K-steps) and fp32 (only small layers): 128 rows.
+  // bf16: 192 rows (an MFMA wave holds 6 x 8 accumulator subtiles = 192
+  // VGPRs), the wave-specialised pipeline on a ring of 5 stage buffers.  FP8
+  // (128-byte K-steps, 3 stages) and fp32 (only small layers, 5 stages):
+  // 128 rows, the single-stage pipeline.
   static constexpr int BM = FMT == FMT_BF16 ? 192 : 128;
   static constexpr int NST = FMT == FMT_E4M3 ? 3 : 5;
-  using P = Pipe<FMT, BM, BNW, NST, 2>;   // 2 x 2 waves
+  // bf16: 4 MFMA waves + 4 load waves; FP8 and fp32: 4 waves doing both
+  static constexpr int THREADS = FMT == FMT_BF16 ? 512 : 256;
+  using P = Pipe<FMT, BM, BNW, NST, 2>;   // 2 x 2 MFMA waves
 };
+
+// make_pipe() returns the tile's initialised Pipe (the loads' per-lane
+// state).  wr: the W rows of this wave's column subtiles.
+template <int FMT, int NSUB, class MK, class WR>
+__device__ __forceinline__ void gg_mainloop(const MK& make_pipe, uint8_t* const (&st)[GG<FMT>::NST], int nk,
+                                            const WR& wr, f32x4 (&acc)[GG<FMT>::P::MI][GG<FMT>::P::NJ],
+                                            const float* sw_lds, int sw_stride) {
+  using P = typename GG<FMT>::P;
+  if constexpr (FMT == FMT_BF16)
+    pipe_mainloop_ws<P, NSUB>(make_pipe(), st, nk, wr, acc);
+  else
+    pipe_mainloop<P, GG<FMT>::NST, NSUB>(make_pipe(), st, nk, wr, acc, sw_lds, sw_stride);
+}
 
 // Logical tile index of this block, or -1 if the block has no work.
 __device__ __forceinline__ int xcd_tile(int n_tiles) {
@@ -104,8 +119,8 @@ __device__ __forceinline__ void dispatch_rows(int rows, F&& f) {
 
 // ------------------------------------------------------------------ gate/up
 
-template <int FMT, int NSUB>
-__device__ __forceinline__ void gateup_tile(const GateUpArgs& a, typename GG<FMT>::P& p, uint8_t* const (&st)[GG<FMT>::NST],
+template <int FMT, int NSUB, class MK>
+__device__ __forceinline__ void gateup_tile(const GateUpArgs& a, const MK& make_pipe, uint8_t* const (&st)[GG<FMT>::NST],
                                             const float* swl, int kb, int nk, int row0, int rows, int n0, int nb,
                                             float (*red)[GG<FMT>::BM]) {
   using P = typename GG<FMT>::P;
@@ -114,15 +129,11 @@ __device__ __forceinline__ void gateup_tile(const GateUpArgs& a, typename GG<FMT
   const int wm = w & 1, wn = w >> 1;
   // wave (wm, wn): h columns 64 wn .. 64 wn + 63 of the tile -- gate subtiles
   // 0-3 and the matching up subtiles 4-7 -- on row subtiles wm, wm+2, ...
-  int brow[8];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    brow[j] = 64 * wn + 16 * j;
-    brow[4 + j] = 128 + 64 * wn + 16 * j;
-  }
+  const WRows<64> wr{64 * wn};
   f32x4 acc[P::MI][P::NJ];
   zero_acc(acc);
-  pipe_mainloop<P, GG<FMT>::NST, NSUB>(p, st, nk, brow, acc, swl, kb);
+  gg_mainloop<FMT, NSUB>(make_pipe, st, nk, wr, acc, swl, kb);
+  if (GG<FMT>::THREADS > 256 && w >= 4) return;   // load waves
 
   if constexpr (FMT != FMT_E4M3) {
 #pragma unroll
@@ -189,7 +200,7 @@ __device__ __forceinline__ void gateup_tile(const GateUpArgs& a, typename GG<FMT
 }
 
 template <int FMT>
-__global__ __launch_bounds__(256, 1) void gateup_kernel(GateUpArgs a) {
+__global__ __launch_bounds__(GG<FMT>::THREADS, 1) void gateup_kernel(GateUpArgs a) {
   using P = typename GG<FMT>::P;
   constexpr int NST = GG<FMT>::NST, BM = GG<FMT>::BM;
   MOE_STAGE_RING(P, NST)
@@ -219,14 +230,21 @@ __global__ __launch_bounds__(256, 1) void gateup_kernel(GateUpArgs a) {
   };
   const int kb = a.d / 128;
 
-  P p;
-  p.init([&](int r) { return static_cast<const uint8_t*>(a.x) + static_cast<size_t>(token_of(r)) * xrow; },
-         [&](int r) {
-           int n = n0 + (r & 127);
-           if (n >= a.inter) n = 0;
-           return wbase + static_cast<size_t>(r < 128 ? n : a.inter + n) * xrow;
-         },
-         [&](int r) { return a.x_scale + static_cast<size_t>(token_of(r)) * kb; });
+  // byte offsets fit 32 bits: T * d * element size < 2^32 is checked on the host
+  auto make_pipe = [&]() {
+    P p;
+    p.init(make_rsrc(a.x, static_cast<uint32_t>(a.T * xrow)),
+           [&](int r) { return static_cast<uint32_t>(token_of(r) * xrow); },
+           make_rsrc(wbase, static_cast<uint32_t>(2 * a.inter * xrow)),
+           [&](int r) {
+             int n = n0 + (r & 127);
+             if (n >= a.inter) n = 0;
+             return static_cast<uint32_t>((r < 128 ? n : a.inter + n) * xrow);
+           },
+           FMT == FMT_E4M3 ? make_rsrc(a.x_scale, static_cast<uint32_t>(a.T * kb * 4)) : make_rsrc(a.x, 0),
+           [&](int r) { return static_cast<uint32_t>(token_of(r) * kb * 4); });
+    return p;
+  };
 
   if constexpr (FMT == FMT_E4M3) {
     // this tile's weight-block scales: gate block n0/128 and up block (I+n0)/128, all K blocks
@@ -240,14 +258,14 @@ __global__ __launch_bounds__(256, 1) void gateup_kernel(GateUpArgs a) {
   const float* sw = FMT == FMT_E4M3 ? swl : nullptr;
   // the K loop instantiated for the tile's valid rows, in 32-row steps
   dispatch_rows<P::MI>(rows, [&]<int NSUB>() {
-    gateup_tile<FMT, NSUB>(a, p, ring.s, sw, kb, nk, row0, rows, n0, nb, red);
+    gateup_tile<FMT, NSUB>(a, make_pipe, ring.s, sw, kb, nk, row0, rows, n0, nb, red);
   });
 }
 
 // ------------------------------------------------------------------ down
 
-template <int FMT, int NSUB>
-__device__ __forceinline__ void down_tile(const DownArgs& a, typename GG<FMT>::P& p, uint8_t* const (&st)[GG<FMT>::NST],
+template <int FMT, int NSUB, class MK>
+__device__ __forceinline__ void down_tile(const DownArgs& a, const MK& make_pipe, uint8_t* const (&st)[GG<FMT>::NST],
                                           const float* swl, int kb, int nk, int row0, int rows, int n0) {
   using P = typename GG<FMT>::P;
   const int w = wave_id(), lane = threadIdx.x & 63;
@@ -255,12 +273,11 @@ __device__ __forceinline__ void down_tile(const DownArgs& a, typename GG<FMT>::P
   const int wm = w & 1, wn = w >> 1;
   // wave (wm, wn): output columns 128 wn .. 128 wn + 127 of the tile (one
   // 128-wide weight scale block), row subtiles wm, wm+2, ...
-  int brow[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) brow[j] = 128 * wn + 16 * j;
+  const WRows<0> wr{128 * wn};
   f32x4 acc[P::MI][P::NJ];
   zero_acc(acc);
-  pipe_mainloop<P, GG<FMT>::NST, NSUB>(p, st, nk, brow, acc, FMT == FMT_E4M3 ? swl + wn * kb : nullptr, 0);
+  gg_mainloop<FMT, NSUB>(make_pipe, st, nk, wr, acc, FMT == FMT_E4M3 ? swl + wn * kb : nullptr, 0);
+  if (GG<FMT>::THREADS > 256 && w >= 4) return;   // load waves
 #pragma unroll
   for (int i = 0; i < NSUB; ++i) {
     const int row = 16 * (2 * i + wm) + lr;
@@ -283,7 +300,7 @@ __device__ __forceinline__ void down_tile(const DownArgs& a, typename GG<FMT>::P
 }
 
 template <int FMT>
-__global__ __launch_bounds__(256, 1) void down_kernel(DownArgs a) {
+__global__ __launch_bounds__(GG<FMT>::THREADS, 1) void down_kernel(DownArgs a) {
   using P = typename GG<FMT>::P;
   constexpr int NST = GG<FMT>::NST;
   MOE_STAGE_RING(P, NST)
@@ -307,14 +324,22 @@ __global__ __launch_bounds__(256, 1) void down_kernel(DownArgs a) {
                          static_cast<size_t>(gs) * a.d * hrow;
   const int kb = a.inter / 128;
 
-  P p;
-  p.init([&](int r) { return static_cast<const uint8_t*>(a.h) + static_cast<size_t>(row0 + (r < rows ? r : 0)) * hrow; },
-         [&](int r) {
-           int c = n0 + r;
-           if (c >= a.d) c = 0;
-           return wbase + static_cast<size_t>(c) * hrow;
-         },
-         [&](int r) { return a.h_scale + static_cast<size_t>(row0 + (r < rows ? r : 0)) * kb; });
+  // the tile's rows of H (and of its FP8 scales) as resources of their own
+  auto make_pipe = [&]() {
+    P p;
+    p.init(make_rsrc(static_cast<const uint8_t*>(a.h) + static_cast<size_t>(row0) * hrow, static_cast<uint32_t>(rows * hrow)),
+           [&](int r) { return static_cast<uint32_t>((r < rows ? r : 0) * hrow); },
+           make_rsrc(wbase, static_cast<uint32_t>(a.d * hrow)),
+           [&](int r) {
+             int c = n0 + r;
+             if (c >= a.d) c = 0;
+             return static_cast<uint32_t>(c * hrow);
+           },
+           FMT == FMT_E4M3 ? make_rsrc(a.h_scale + static_cast<size_t>(row0) * kb, static_cast<uint32_t>(rows * kb * 4))
+                           : make_rsrc(a.h, 0),
+           [&](int r) { return static_cast<uint32_t>((r < rows ? r : 0) * kb * 4); });
+    return p;
+  };
 
   if constexpr (FMT == FMT_E4M3) {
     // weight-block scales of this tile's two 128-column blocks (the second
@@ -328,7 +353,7 @@ __global__ __launch_bounds__(256, 1) void down_kernel(DownArgs a) {
 
   const Ring<NST> ring = make_ring<NST>(st0, st1, st2, st3, st4);
   const float* sw = FMT == FMT_E4M3 ? swl : nullptr;
-  dispatch_rows<P::MI>(rows, [&]<int NSUB>() { down_tile<FMT, NSUB>(a, p, ring.s, sw, kb, nk, row0, rows, n0); });
+  dispatch_rows<P::MI>(rows, [&]<int NSUB>() { down_tile<FMT, NSUB>(a, make_pipe, ring.s, sw, kb, nk, row0, rows, n0); });
 }
 
 int grid_for(int max_mtiles, int nb_n) {
@@ -346,11 +371,11 @@ hipError_t launch_gateup(int fmt, const GateUpArgs& a, hipStream_t s) {
   const int grid = grid_for(a.max_mtiles, ceil_div(a.inter, GG_HCOLS));
   if (grid == 0) return hipSuccess;
   if (fmt == FMT_BF16)
-    hipLaunchKernelGGL(gateup_kernel<FMT_BF16>, dim3(grid), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(gateup_kernel<FMT_BF16>, dim3(grid), dim3(GG<FMT_BF16>::THREADS), 0, s, a);
   else if (fmt == FMT_E4M3)
-    hipLaunchKernelGGL(gateup_kernel<FMT_E4M3>, dim3(grid), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(gateup_kernel<FMT_E4M3>, dim3(grid), dim3(GG<FMT_E4M3>::THREADS), 0, s, a);
   else
-    hipLaunchKernelGGL(gateup_kernel<FMT_F32>, dim3(grid), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(gateup_kernel<FMT_F32>, dim3(grid), dim3(GG<FMT_F32>::THREADS), 0, s, a);
   return hipGetLastError();
 }
 
@@ -358,11 +383,11 @@ hipError_t launch_down(int fmt, const DownArgs& a, hipStream_t s) {
   const int grid = grid_for(a.max_mtiles, ceil_div(a.d, BNW));
   if (grid == 0) return hipSuccess;
   if (fmt == FMT_BF16)
-    hipLaunchKernelGGL(down_kernel<FMT_BF16>, dim3(grid), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(down_kernel<FMT_BF16>, dim3(grid), dim3(GG<FMT_BF16>::THREADS), 0, s, a);
   else if (fmt == FMT_E4M3)
-    hipLaunchKernelGGL(down_kernel<FMT_E4M3>, dim3(grid), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(down_kernel<FMT_E4M3>, dim3(grid), dim3(GG<FMT_E4M3>::THREADS), 0, s, a);
   else
-    hipLaunchKernelGGL(down_kernel<FMT_F32>, dim3(grid), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(down_kernel<FMT_F32>, dim3(grid), dim3(GG<FMT_F32>::THREADS), 0, s, a);
   return hipGetLastError();
 }
 

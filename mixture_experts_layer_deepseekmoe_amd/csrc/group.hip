@@ -62,7 +62,11 @@ __global__ __launch_bounds__(SCAN_THREADS) void scan_kernel(GroupArgs a, int nbl
   if (a.mtiles == nullptr) return;
   __syncthreads();
   // 3. m-tiles: group g (routed experts, then shared experts over all T
-  //    tokens) is cut into ceil(M_g / BM) tiles of balanced size.
+  //    tokens) is cut into ceil(M_g / BM) tiles of balanced size.  The tiles
+  //    of a group read the same weight blocks at the same time and share
+  //    them in L2 only while they run at the same speed; a short remainder
+  //    tile would drift away from its partners (measured: 1.5x the HBM
+  //    traffic of the grouped GEMM).
   const int ng = nr + a.n_shared;
   const long long TK = static_cast<long long>(a.T) * a.top_k;
   for (int g = tid; g < ng; g += SCAN_THREADS) {

@@ -75,6 +75,11 @@ int validate_shape(const moe_shape* s) {
   const long long T = s->T;
   if (T * (s->top_k + s->n_shared) >= (1LL << 31)) return MOE_ERR_UNSUPPORTED;
   if (s->w_dtype == MOE_DTYPE_E4M3 && (s->d > 32768 || s->inter > 32768)) return MOE_ERR_UNSUPPORTED;
+  // the kernels address the activations and one expert's weight matrix with
+  // 32-bit byte offsets
+  const long long xes = s->x_dtype == MOE_DTYPE_F32 ? 4 : 2;
+  const long long wes = s->w_dtype == MOE_DTYPE_F32 ? 4 : (s->w_dtype == MOE_DTYPE_BF16 ? 2 : 1);
+  if (T * s->d * xes >= (1LL << 32) || 2LL * s->inter * s->d * wes >= (1LL << 32)) return MOE_ERR_UNSUPPORTED;
   const long long gu_tiles =
       static_cast<long long>(moe::max_mtiles(T, s->top_k, s->n_routed, s->n_shared, moe::gg_bm(fmt_of(s->w_dtype)))) *
       moe::ceil_div(s->d > s->inter ? s->d : s->inter, 128);

@@ -40,34 +40,30 @@ __global__ __launch_bounds__(256) void route_kernel(RouteArgs a) {
   const int es = FMT == FMT_F32 ? 4 : 2;
   const size_t row_bytes = static_cast<size_t>(a.d) * es;
   const int nk = static_cast<int>(row_bytes / P::SB);
-  const int brow[4] = {64 * w, 64 * w + 16, 64 * w + 32, 64 * w + 48};
+  const WRows<0> wr{64 * w};   // expert subtile j: rows 64 w + 16 j of the chunk
   const int valid = min(RBT, a.T - t0);
 
   for (int ec = 0; ec < a.n_routed; ec += RCHUNK) {
     P p;
-    p.init(
-        [&](int r) {
-          const int t = (r < valid) ? t0 + r : t0;
-          return static_cast<const uint8_t*>(a.u) + static_cast<size_t>(t) * row_bytes;
-        },
-        [&](int r) {
-          const int e = ec + r < a.n_routed ? ec + r : 0;
-          return static_cast<const uint8_t*>(a.centroids) + static_cast<size_t>(e) * row_bytes;
-        },
-        [&](int) { return static_cast<const float*>(nullptr); });
+    const rsrc_t ru = make_rsrc(static_cast<const uint8_t*>(a.u) + static_cast<size_t>(t0) * row_bytes,
+                                static_cast<uint32_t>(valid * row_bytes));
+    p.init(ru, [&](int r) { return static_cast<uint32_t>((r < valid ? r : 0) * row_bytes); },
+           make_rsrc(a.centroids, static_cast<uint32_t>(a.n_routed * row_bytes)),
+           [&](int r) { return static_cast<uint32_t>((ec + r < a.n_routed ? ec + r : 0) * row_bytes); },
+           ru, [](int) { return 0u; });
     f32x4 acc[P::MI][P::NJ];
     zero_acc(acc);
     if (valid > 16)
-      pipe_mainloop<P, RNST, 2>(p, st, nk, brow, acc);
+      pipe_mainloop<P, RNST, 2>(p, st, nk, wr, acc);
     else
-      pipe_mainloop<P, RNST, 1>(p, st, nk, brow, acc);
+      pipe_mainloop<P, RNST, 1>(p, st, nk, wr, acc);
 
-    // lane: token 16i + lr, experts ec + brow[j] + 4lg .. +3
+    // lane: token 16i + lr, experts ec + 64 w + 16 j + 4lg .. +3
 #pragma unroll
     for (int i = 0; i < P::MI; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int e = ec + brow[j] + 4 * lg;
+        const int e = ec + 64 * w + 16 * j + 4 * lg;
         float* dst = sbuf + (16 * i + lr) * SSTRIDE + e;
         if (e + 3 < a.n_routed) {
           *reinterpret_cast<float4*>(dst) = make_float4(sigmoid_f32(acc[i][j][0]), sigmoid_f32(acc[i][j][1]),
