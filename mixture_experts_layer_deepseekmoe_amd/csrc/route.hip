@@ -21,18 +21,34 @@ namespace {
 
 constexpr int RBT = ROUTE_BT;
 constexpr int RCHUNK = 256;   // experts per MFMA pass
-constexpr int RNST = 4;
+
+// Every block streams all centroids (from L2) beside its own token rows, so
+// the router is bound by the loads a CU keeps in flight.  Up to 256 experts
+// it runs the wave-specialised paired pipeline (8 waves: whole-line L2
+// requests, loads issued by their own waves); beyond, the score buffer
+// leaves room only for the 4-wave single-stage pipeline on a 4-stage ring.
+template <int NRMAX>
+struct RouteCfg {
+  static constexpr bool WS = NRMAX <= 256;
+  static constexpr int NW = WS ? 8 : 4;     // waves per block
+  static constexpr int NST = WS ? 5 : 4;    // stage buffers
+};
 
 template <int FMT, int NRMAX>
-__global__ __launch_bounds__(256) void route_kernel(RouteArgs a) {
-  using P = Pipe<FMT, RBT, RCHUNK, RNST>;
+__global__ __launch_bounds__(64 * RouteCfg<NRMAX>::NW) void route_kernel(RouteArgs a) {
+  using C = RouteCfg<NRMAX>;
+  using P = Pipe<FMT, RBT, RCHUNK, C::NST>;
   constexpr int SSTRIDE = NRMAX + 4;
   __shared__ __attribute__((aligned(1024))) uint8_t st0[P::STAGE_BYTES];
   __shared__ __attribute__((aligned(1024))) uint8_t st1[P::STAGE_BYTES];
   __shared__ __attribute__((aligned(1024))) uint8_t st2[P::STAGE_BYTES];
   __shared__ __attribute__((aligned(1024))) uint8_t st3[P::STAGE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t st4[C::NST > 4 ? P::STAGE_BYTES : 16];
   __shared__ __attribute__((aligned(16))) float sbuf[RBT * SSTRIDE];
-  uint8_t* const st[RNST] = {st0, st1, st2, st3};   // a ring of separate LDS objects
+  uint8_t* const all[5] = {st0, st1, st2, st3, st4};
+  uint8_t* st[C::NST];   // a ring of separate LDS objects
+#pragma unroll
+  for (int i = 0; i < C::NST; ++i) st[i] = all[i];
 
   const int w = wave_id(), lane = threadIdx.x & 63;
   const int lr = lane & 15, lg = lane >> 4;
@@ -40,7 +56,7 @@ __global__ __launch_bounds__(256) void route_kernel(RouteArgs a) {
   const int es = FMT == FMT_F32 ? 4 : 2;
   const size_t row_bytes = static_cast<size_t>(a.d) * es;
   const int nk = static_cast<int>(row_bytes / P::SB);
-  const WRows<0> wr{64 * w};   // expert subtile j: rows 64 w + 16 j of the chunk
+  const WRows<0> wr{64 * (w & 3)};   // expert subtile j: rows 64 w + 16 j of the chunk
   const int valid = min(RBT, a.T - t0);
 
   for (int ec = 0; ec < a.n_routed; ec += RCHUNK) {
@@ -53,10 +69,18 @@ __global__ __launch_bounds__(256) void route_kernel(RouteArgs a) {
            ru, [](int) { return 0u; });
     f32x4 acc[P::MI][P::NJ];
     zero_acc(acc);
-    if (valid > 16)
-      pipe_mainloop<P, RNST, 2>(p, st, nk, wr, acc);
-    else
-      pipe_mainloop<P, RNST, 1>(p, st, nk, wr, acc);
+    if constexpr (C::WS) {
+      if (valid > 16)
+        pipe_mainloop_ws<P, 2>(p, st, nk, wr, acc);
+      else
+        pipe_mainloop_ws<P, 1>(p, st, nk, wr, acc);
+      if (w >= 4) continue;   // load waves hold no scores
+    } else {
+      if (valid > 16)
+        pipe_mainloop<P, C::NST, 2>(p, st, nk, wr, acc);
+      else
+        pipe_mainloop<P, C::NST, 1>(p, st, nk, wr, acc);
+    }
 
     // lane: token 16i + lr, experts ec + 64 w + 16 j + 4lg .. +3
 #pragma unroll
@@ -77,16 +101,17 @@ __global__ __launch_bounds__(256) void route_kernel(RouteArgs a) {
   }
   __syncthreads();
 
-  // ---- top-K: wave w takes tokens 8w .. 8w+7 of the block
+  // ---- top-K: wave w takes tokens w * RBT / NW .. of the block
   constexpr int NQ = NRMAX / 64;
+  constexpr int TPW = RBT / C::NW;
   float bq[NQ];
 #pragma unroll
   for (int q = 0; q < NQ; ++q) {
     const int e = lane + 64 * q;
     bq[q] = e < a.n_routed ? a.bias[e] : 0.f;
   }
-  for (int tt = 0; tt < RBT / 4; ++tt) {
-    const int tl = w * (RBT / 4) + tt;
+  for (int tt = 0; tt < TPW; ++tt) {
+    const int tl = w * TPW + tt;
     const int t = t0 + tl;
     if (t >= a.T) break;
     const float* srow = sbuf + tl * SSTRIDE;
@@ -135,7 +160,7 @@ __global__ __launch_bounds__(256) void route_kernel(RouteArgs a) {
 template <int FMT, int NRMAX>
 hipError_t launch_route_t(const RouteArgs& a, hipStream_t s) {
   const int grid = ceil_div(a.T, RBT);
-  hipLaunchKernelGGL((route_kernel<FMT, NRMAX>), dim3(grid), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((route_kernel<FMT, NRMAX>), dim3(grid), dim3(64 * RouteCfg<NRMAX>::NW), 0, s, a);
   return hipGetLastError();
 }
 
