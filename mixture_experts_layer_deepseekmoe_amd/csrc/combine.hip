@@ -4,7 +4,7 @@
 // at row T*K + s*T + t, routed choice k at row pos[t,k]) and summed in fp32 in
 // a fixed order: u, then the shared experts in order, then the routed choices
 // in selection order.  No atomics: the result is bit-reproducible.
-// One wave per token, 8 columns per lane per step (16-byte bf16 loads).
+// One wave per token, 8 columns per lane per chunk (16-byte bf16 loads).
 #include "kernels.hpp"
 #include "moe_common.hpp"
 
@@ -48,33 +48,55 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
     gs[k] = __shfl(gk, k);
     ps[k] = __shfl(pk, k);
   }
+  // CC column chunks of 8 per lane at a time: the loads of one row are
+  // independent of each other, so a wave keeps CC of them in flight (the
+  // loop over the K choices has a runtime bound and runs in order).
+  constexpr int CC = 4;
   const size_t d = a.d;
-  for (int c = lane * 8; c < a.d; c += 64 * 8) {
-    float acc[8], v[8];
-    load8<XF>(a.u, static_cast<size_t>(t) * d + c, acc);
-    for (int s = 0; s < a.n_shared; ++s) {
-      load8<YF>(a.yrows, static_cast<size_t>(a.TK + static_cast<long long>(s) * a.T + t) * d + c, v);
+  for (int c0 = lane * 8; c0 < a.d; c0 += 64 * 8 * CC) {
+    float acc[CC][8], v[CC][8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] += v[i];
+    for (int u = 0; u < CC; ++u)
+      if (c0 + 512 * u < a.d) load8<XF>(a.u, static_cast<size_t>(t) * d + c0 + 512 * u, acc[u]);
+    for (int s = 0; s < a.n_shared; ++s) {
+      const size_t row = static_cast<size_t>(a.TK + static_cast<long long>(s) * a.T + t) * d;
+#pragma unroll
+      for (int u = 0; u < CC; ++u)
+        if (c0 + 512 * u < a.d) load8<YF>(a.yrows, row + c0 + 512 * u, v[u]);
+#pragma unroll
+      for (int u = 0; u < CC; ++u)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[u][i] += v[u][i];
     }
 #pragma unroll
     for (int k = 0; k < MAX_TOPK; ++k) {
       if (k >= a.top_k) break;
-      load8<YF>(a.yrows, static_cast<size_t>(ps[k]) * d + c, v);
+      const size_t row = static_cast<size_t>(ps[k]) * d;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] = fmaf(gs[k], v[i], acc[i]);
+      for (int u = 0; u < CC; ++u)
+        if (c0 + 512 * u < a.d) load8<YF>(a.yrows, row + c0 + 512 * u, v[u]);
+#pragma unroll
+      for (int u = 0; u < CC; ++u)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[u][i] = fmaf(gs[k], v[u][i], acc[u][i]);
     }
-    if constexpr (OF == FMT_F32) {
-      float* o = static_cast<float*>(a.out) + static_cast<size_t>(t) * d + c;
-      *reinterpret_cast<float4*>(o) = make_float4(acc[0], acc[1], acc[2], acc[3]);
-      *reinterpret_cast<float4*>(o + 4) = make_float4(acc[4], acc[5], acc[6], acc[7]);
-    } else {
-      uint32_t w[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        w[i] = static_cast<uint32_t>(f32_to_bf16(acc[2 * i])) | (static_cast<uint32_t>(f32_to_bf16(acc[2 * i + 1])) << 16);
-      *reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.out) + static_cast<size_t>(t) * d + c) =
-          make_uint4(w[0], w[1], w[2], w[3]);
+    for (int u = 0; u < CC; ++u) {
+      const int c = c0 + 512 * u;
+      if (c >= a.d) continue;
+      if constexpr (OF == FMT_F32) {
+        float* o = static_cast<float*>(a.out) + static_cast<size_t>(t) * d + c;
+        *reinterpret_cast<float4*>(o) = make_float4(acc[u][0], acc[u][1], acc[u][2], acc[u][3]);
+        *reinterpret_cast<float4*>(o + 4) = make_float4(acc[u][4], acc[u][5], acc[u][6], acc[u][7]);
+      } else {
+        uint32_t w[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          w[i] = static_cast<uint32_t>(f32_to_bf16(acc[u][2 * i])) |
+                 (static_cast<uint32_t>(f32_to_bf16(acc[u][2 * i + 1])) << 16);
+        *reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.out) + static_cast<size_t>(t) * d + c) =
+            make_uint4(w[0], w[1], w[2], w[3]);
+      }
     }
   }
 }
