@@ -66,10 +66,18 @@ def _ws_rc(shape):
     (dict(w_dtype="e4m3", d=192), B.MOE_ERR_UNSUPPORTED),   # e4m3 needs d % 128 == 0
     (dict(w_dtype="e4m3", inter=64), B.MOE_ERR_UNSUPPORTED),
     (dict(T=2 ** 28, top_k=8), B.MOE_ERR_UNSUPPORTED),       # T*K beyond int32
+    (dict(T=299_594, d=7168, top_k=1), B.MOE_ERR_UNSUPPORTED),   # bytes of u reach 2^32 (32-bit offsets)
+    (dict(inter=65_536, d=16_384, top_k=1), B.MOE_ERR_UNSUPPORTED),   # one expert's gate/up matrix reaches 2^32 bytes
 ])
 def test_shape_validation(kw, code):
     rc, _ = _ws_rc(_shape(**kw))
     assert rc == code
+
+
+def test_largest_activation_within_32_bit_offsets_is_accepted():
+    # T * d * 2 bytes just below 2^32
+    rc, _ = _ws_rc(_shape(T=299_593, d=7168, top_k=1))
+    assert rc == B.MOE_OK
 
 
 def test_valid_shapes_and_workspace_monotone():
