@@ -122,10 +122,22 @@ def main():
     gu_tflops = gu_flops / gu_s / 1e12
     touched = int((counts > 0).sum())
     gu_bytes = (touched + cfg.n_shared) * 2 * cfg.inter * cfg.d * es + cfg.T * cfg.d * es + rows * cfg.inter * es
-    roofline = {"bound": "mfma", "kernel": "gateup_kernel (grouped gate/up GEMM + SwiGLU)",
-                "achieved": round(gu_tflops, 2), "peak": peak, "unit": "TFLOP/s",
-                "frac": round(gu_tflops / peak, 4), "traffic": measured_traffic(cfg.name),
+    # The binding roof follows the kernel's arithmetic intensity: below the
+    # ridge (peak flops / HBM bandwidth) the weight stream bounds it.
+    intensity = gu_flops / gu_bytes
+    ridge = peak * 1e12 / (PEAK_HBM_GBS * 1e9)
+    gu_gbs = gu_bytes / gu_s / 1e9
+    if intensity < ridge:
+        bound, achieved, peak_r, unit = "hbm", gu_gbs, PEAK_HBM_GBS, "GB/s"
+    else:
+        bound, achieved, peak_r, unit = "mfma", gu_tflops, peak, "TFLOP/s"
+    roofline = {"bound": bound, "kernel": "gateup_kernel (grouped gate/up GEMM + SwiGLU)",
+                "achieved": round(achieved, 2), "peak": peak_r, "unit": unit,
+                "frac": round(achieved / peak_r, 4), "traffic": measured_traffic(cfg.name),
                 "flops_per_launch": gu_flops, "algorithmic_bytes_per_launch": gu_bytes,
+                "flop_per_byte": round(intensity, 1), "ridge_flop_per_byte": round(ridge, 1),
+                "mfma_tflops": round(gu_tflops, 2), "mfma_frac": round(gu_tflops / peak, 4),
+                "hbm_gbs": round(gu_gbs, 1), "hbm_frac": round(gu_gbs / PEAK_HBM_GBS, 4),
                 "avg_launch_ms": round(stages["gate_up"], 4)}
     grouped_frac = (gu_flops + dn_flops) / (gu_s + dn_s) / 1e12 / peak
 
