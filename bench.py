@@ -44,6 +44,13 @@ def measured_traffic(workload: str):
     return rec.get("gate_up_bytes_per_launch")
 
 
+def measured_peaks():
+    """Ceilings measured on this chip by profiling.py peaks (MFMA with random
+    operands, HBM read stream), if stored; else None."""
+    f = os.path.join(os.path.dirname(TRAFFIC_FILE), "measured_peaks.json")
+    return json.load(open(f)) if os.path.exists(f) else None
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -139,6 +146,15 @@ def main():
                 "mfma_tflops": round(gu_tflops, 2), "mfma_frac": round(gu_tflops / peak, 4),
                 "hbm_gbs": round(gu_gbs, 1), "hbm_frac": round(gu_gbs / PEAK_HBM_GBS, 4),
                 "avg_launch_ms": round(stages["gate_up"], 4)}
+    mp = measured_peaks()
+    if mp:
+        key = "mfma_e4m3_16x16x128_random_operands" if cfg.w_dtype == "e4m3" else "mfma_bf16_16x16x32_random_operands"
+        m_tf = mp.get(key, {}).get("tflops_sustained")
+        m_bw = mp.get("hbm_read_lds_dma_paired_64B", {}).get("gbs_best")
+        if m_tf and m_bw and cfg.w_dtype != "f32":
+            roofline["measured_ceilings"] = {
+                "mfma_tflops_random_operands": m_tf, "mfma_frac": round(gu_tflops / m_tf, 4),
+                "hbm_read_gbs": m_bw, "hbm_frac": round(gu_gbs / m_bw, 4)}
     grouped_frac = (gu_flops + dn_flops) / (gu_s + dn_s) / 1e12 / peak
 
     xs = 4 if cfg.x_dtype == "f32" else 2

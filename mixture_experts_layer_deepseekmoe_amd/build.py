@@ -23,6 +23,10 @@ LIB_PATH = os.path.join(PKG, LIB_NAME)
 
 SOURCES = ["route.hip", "group.hip", "ggemm.hip", "combine.hip", "moe_api.cpp"]
 ARCH = "gfx950"
+# measured-ceiling probes (MFMA with random / zero operands, HBM stream), a
+# standalone program run by `profiling.py peaks`
+PROBES_SRC = os.path.join(PKG, "peaks", "peak_probes.hip")
+PROBES_BIN = os.path.join(PKG, "peak_probes.bin")
 
 
 def hipcc() -> str:
@@ -63,6 +67,11 @@ def build(verbose: bool = True, debug: bool = False) -> str:
     if res.returncode != 0:
         raise RuntimeError(f"link failed:\n{res.stderr}")
     os.replace(tmp, LIB_PATH)
+    cmd = [hipcc()] + common_flags(debug) + ["-o", PROBES_BIN + ".tmp", PROBES_SRC]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"hipcc failed for peak_probes.hip:\n{res.stderr}")
+    os.replace(PROBES_BIN + ".tmp", PROBES_BIN)
     if verbose:
         print(f"built {LIB_PATH}")
     return LIB_PATH

@@ -2,6 +2,8 @@
 
     # the workload to profile (run it under rocprofv3):
     python -m mixture_experts_layer_deepseekmoe_amd.profiling run --workload bf16_d7168 --steps 3
+    # measured ceilings (MFMA with random / zero operands, HBM stream) -> profiles/measured_peaks.json:
+    python -m mixture_experts_layer_deepseekmoe_amd.profiling peaks
     # turn rocprofv3's CSV output into the summaries kept under profiles/:
     python -m mixture_experts_layer_deepseekmoe_amd.profiling summarize --trace DIR --pmc DIR [DIR...] \
         --workload bf16_d7168 --out profiles
@@ -176,6 +178,21 @@ def _summarize(args):
     print("\n".join(lines))
 
 
+def _peaks(args):
+    """Run the measured-ceiling probes and store their results."""
+    import subprocess
+
+    binary = os.path.join(ROOT, "mixture_experts_layer_deepseekmoe_amd", "peak_probes.bin")
+    if not os.path.exists(binary):
+        raise SystemExit(f"{binary} is missing: build first (python -m mixture_experts_layer_deepseekmoe_amd.build)")
+    res = subprocess.run([binary], capture_output=True, text=True, check=True)
+    probes = [json.loads(line) for line in res.stdout.splitlines() if line.startswith("{")]
+    table = {p.pop("probe"): p for p in probes}
+    os.makedirs(args.out, exist_ok=True)
+    json.dump(table, open(os.path.join(args.out, "measured_peaks.json"), "w"), indent=1, sort_keys=True)
+    print(json.dumps(table, indent=1, sort_keys=True))
+
+
 def main():
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -189,8 +206,10 @@ def main():
     s.add_argument("--out", default=os.path.join(ROOT, "profiles"))
     s.add_argument("--name")
     s.add_argument("--command", nargs="*")
+    pk = sub.add_parser("peaks")
+    pk.add_argument("--out", default=os.path.join(ROOT, "profiles"))
     args = ap.parse_args()
-    _run(args) if args.cmd == "run" else _summarize(args)
+    {"run": _run, "summarize": _summarize, "peaks": _peaks}[args.cmd](args)
 
 
 if __name__ == "__main__":
