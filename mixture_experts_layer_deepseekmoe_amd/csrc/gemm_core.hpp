@@ -466,9 +466,14 @@ __device__ __forceinline__ void ws_load_pairs(const P& p, uint8_t* const (&st)[5
     if (q >= np) return;
   }
   block_barrier();   // A_q
-  // past the last pair the loads repeat it into buffers nobody reads
-  p.template issue_pair_range<0, NL, NA>(st[(2 * Q + 4) % 5], st[(2 * Q + 5) % 5], 2 * min(q + 2, np - 1));
-  wait_vm_lgkm0<2 * NL>();   // pair q+1
+  // Only the load waves issue loads and they read no LDS, so a branch costs
+  // nothing here: the last two pairs issue none.
+  if (q + 2 < np) {
+    p.template issue_pair_range<0, NL, NA>(st[(2 * Q + 4) % 5], st[(2 * Q + 5) % 5], 2 * (q + 2));
+    wait_vm_lgkm0<2 * NL>();   // pair q+1
+  } else {
+    wait_vm_lgkm0<0>();        // pair q+1 (if any) is the newest
+  }
   block_barrier();   // B_q
   if constexpr (Q + 1 < 5) ws_load_pairs<P, Q + 1, NSUB, GUARD>(p, st, q0, np);
 }
@@ -501,13 +506,16 @@ __device__ __forceinline__ void pipe_mainloop_ws(const P& p, uint8_t* const (&st
   const int np = nk / 2;
   if (wave_id() >= 4) {
     p.template issue_pair_range<0, NL, NA>(st[0], st[1], 0);
-    p.template issue_pair_range<0, NL, NA>(st[2], st[3], 2 * min(1, np - 1));
-    wait_vm_lgkm0<2 * NL>();   // pair 0
+    if (np > 1) {
+      p.template issue_pair_range<0, NL, NA>(st[2], st[3], 2);
+      wait_vm_lgkm0<2 * NL>();   // pair 0
+    } else {
+      wait_vm_lgkm0<0>();
+    }
     block_barrier();
     int q = 0;
     for (; q + 5 <= np; q += 5) ws_load_pairs<P, 0, NSUB, false>(p, st, q, np);
     if (q < np) ws_load_pairs<P, 0, NSUB, true>(p, st, q, np);
-    wait_vm_lgkm0<0>();   // the clamped tail loads land before the block ends
   } else {
     block_barrier();
     typename P::Frags f;
