@@ -74,16 +74,19 @@ __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane
 
 // Chunk swizzle per row.  Chosen by measurement on gfx950 (SQ_LDS_BANK_CONFLICT
 // over a sweep of lane->chunk permutations): a ds_read_b128 in which lane l
-// reads row (l & 15) of a 16-row block at logical chunk (l >> 4) is free of
-// bank conflicts with these two maps (64- and 128-byte rows), at every block
-// base; plain row-major, 144-byte padded rows and several XOR maps that are
-// conflict-free under a plain address-modulo bank model all conflict there.
+// reads row (l & 15) of a 16-row block at logical chunk (l >> 4) (64-byte
+// rows; 2 (l >> 4) and 2 (l >> 4) + 1 for 128-byte rows) is free of bank
+// conflicts with these two maps, at every block base; plain row-major,
+// 144-byte padded rows and several maps that are conflict-free under a plain
+// address-modulo bank model (e.g. (r >> 1) & 7 for 128-byte rows) conflict
+// there.  Both depend on the row modulo 16 only, so every fragment of a
+// 16-row subtile shares one lane address pattern.
 template <int SB>
 __device__ __forceinline__ int swz(int r) {
   if constexpr (SB == 64)
     return (r >> 1) & 3;
   else
-    return (r ^ (r >> 3)) & 7;
+    return (r & 7) ^ ((r >> 3) & 1);
 }
 
 // W rows read by one wave: subtile j covers rows base + 16 j, plus SPLIT
@@ -350,6 +353,91 @@ struct Pipe {
     }
   }
 
+  // ---- FP8, W-subtile-outer order (the wave-specialised FP8 pipeline).
+  // The stage's X fragments and scales for all NSUB row subtiles are held in
+  // registers; the W fragments stream two column subtiles ahead of their
+  // MFMAs; the products of column subtile j are promoted while the MFMAs of
+  // subtile j+1 run, and the last subtile's products (pp, with their scales
+  // psc) are carried into the next stage.  About 250 registers, so that two
+  // waves can share a SIMD.
+  struct FragsJ {
+    uint4 x[MI][2];
+    float sx[MI];
+    uint4 w[2][2];   // the stage's first two W subtiles
+  };
+
+  template <int SPLIT>
+  __device__ __forceinline__ static void wfrag(const uint8_t* st, WRows<SPLIT> wr, int j, uint4 (&w)[2]) {
+    const int lane = threadIdx.x & 63, lr = lane & 15, lg = lane >> 4;
+    const uint8_t* wst = st + B_OFF + wr.base * SB;
+    const int r = 16 * j + (j >= NJ / 2 ? SPLIT : 0) + lr;
+    w[0] = frag16(wst, r, 2 * lg);
+    w[1] = frag16(wst, r, 2 * lg + 1);
+  }
+
+  template <int NSUB, int SPLIT>
+  __device__ __forceinline__ static void prefetch_jo(const uint8_t* st, WRows<SPLIT> wr, FragsJ& f) {
+#pragma unroll
+    for (int i = 0; i < NSUB; ++i) load_x(st, i, f.x[i], f.sx[i]);
+    wfrag(st, wr, 0, f.w[0]);
+    if constexpr (NJ > 1) wfrag(st, wr, 1, f.w[1]);
+  }
+
+  template <int NSUB, int J, int SPLIT, class H>
+  __device__ __forceinline__ static void compute_jo_from(const uint8_t* st, WRows<SPLIT> wr, FragsJ& f,
+                                                         f32x4 (&acc)[MI][NJ], const float (&sw)[NJ], H& hook,
+                                                         uint4 (&wc)[2], uint4 (&wn1)[2], f32x4 (&pp)[MI],
+                                                         float (&psc)[MI]) {
+    if constexpr (J < NJ) {
+      uint4 wn2[2];
+      if constexpr (J + 2 < NJ) wfrag(st, wr, J + 2, wn2);
+      __builtin_amdgcn_sched_barrier(0);
+      f32x4 pn[MI];
+      const i32x8 wv = {(int)wc[0].x, (int)wc[0].y, (int)wc[0].z, (int)wc[0].w,
+                        (int)wc[1].x, (int)wc[1].y, (int)wc[1].z, (int)wc[1].w};
+#pragma unroll
+      for (int i = 0; i < NSUB; ++i) {
+        const i32x8 xv = {(int)f.x[i][0].x, (int)f.x[i][0].y, (int)f.x[i][0].z, (int)f.x[i][0].w,
+                          (int)f.x[i][1].x, (int)f.x[i][1].y, (int)f.x[i][1].z, (int)f.x[i][1].w};
+        pn[i] = mfma_e4m3(wv, xv, f32x4{0.f, 0.f, 0.f, 0.f});
+        // the previous column subtile's product (the previous stage's last, for J == 0)
+        if constexpr (J == 0)
+          acc[i][NJ - 1] += pp[i] * psc[i];
+        else
+          acc[i][J - 1] += pp[i] * (f.sx[i] * sw[J - 1]);
+      }
+#pragma unroll
+      for (int i = 0; i < NSUB; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);   // then one promotion
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      hook.template operator()<J>();
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < NSUB; ++i) pp[i] = pn[i];
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        wc[q] = wn1[q];
+        if constexpr (J + 2 < NJ) wn1[q] = wn2[q];
+      }
+      compute_jo_from<NSUB, J + 1>(st, wr, f, acc, sw, hook, wc, wn1, pp, psc);
+    } else {
+#pragma unroll
+      for (int i = 0; i < NSUB; ++i) psc[i] = f.sx[i] * sw[NJ - 1];
+    }
+  }
+
+  // hook.template operator()<j>() runs after the MFMAs of column subtile j.
+  template <int NSUB, int SPLIT, class H>
+  __device__ __forceinline__ static void compute_jo(const uint8_t* st, WRows<SPLIT> wr, FragsJ& f,
+                                                    f32x4 (&acc)[MI][NJ], const float (&sw)[NJ], H&& hook,
+                                                    f32x4 (&pp)[MI], float (&psc)[MI]) {
+    uint4 wc[2] = {f.w[0][0], f.w[0][1]};
+    uint4 wn1[2] = {f.w[1][0], f.w[1][1]};
+    compute_jo_from<NSUB, 0>(st, wr, f, acc, sw, hook, wc, wn1, pp, psc);
+  }
+
   // hook.template operator()<i>() runs after the MFMAs of row subtile i.
   template <int NSUB, class H>
   __device__ __forceinline__ static void compute(const uint8_t* st, Frags& f, f32x4 (&acc)[MI][NJ],
@@ -523,6 +611,97 @@ __device__ __forceinline__ void pipe_mainloop_ws(const P& p, uint8_t* const (&st
     int q = 0;
     for (; q + 5 <= np; q += 5) ws_mfma_pairs<P, 0, NSUB, false>(st, q, np, wr, f, acc);
     if (q < np) ws_mfma_pairs<P, 0, NSUB, true>(st, q, np, wr, f, acc);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Wave-specialised FP8 pipeline (8 waves, 128-byte K-steps = one scale block,
+// a ring of 3 stage buffers, stage s in buffer s % 3).  Waves 4-7 issue the
+// loads of stage k+2 as soon as stage k-1's buffer is free; waves 0-3 run the
+// MFMAs in W-subtile-outer order.  Two barriers per stage, in this order:
+//   B_k  (halfway through the MFMAs of stage k) stage k+1 has landed;
+//   A_k  (after the MFMA waves read stage k+1's first fragments) nobody
+//        reads stage k any more, and its buffer takes stage k+3.
+// Stages k+1 and k+2 are in flight while stage k is computed (the 4-wave
+// single-stage ring of 3 keeps one).
+
+template <class P, int S, int NSUB, bool GUARD>
+__device__ __forceinline__ void ws8_load_steps(const P& p, uint8_t* const (&st)[3], int k0, int nk) {
+  constexpr int NA = P::template nia_for<NSUB>();
+  constexpr int NL = P::template nl_for<NSUB>();
+  const int ks = k0 + S;
+  if constexpr (GUARD) {
+    if (ks >= nk) return;
+  }
+  if (ks + 2 < nk) {
+    p.template issue_range<0, NL, NA>(st[(S + 2) % 3], ks + 2);
+    wait_vm_lgkm0<NL>();   // stage ks+1
+  } else {
+    wait_vm_lgkm0<0>();    // stage ks+1 (if any) is the newest
+  }
+  block_barrier();   // B_ks
+  block_barrier();   // A_ks
+  if constexpr (S + 1 < 3) ws8_load_steps<P, S + 1, NSUB, GUARD>(p, st, k0, nk);
+}
+
+template <class P, int S, int NSUB, bool GUARD, class WR>
+__device__ __forceinline__ void ws8_mfma_steps(uint8_t* const (&st)[3], int k0, int nk, const WR& wr,
+                                               typename P::FragsJ& f, f32x4 (&acc)[P::MI][P::NJ],
+                                               f32x4 (&pp)[P::MI], float (&psc)[P::MI], const float* sw_lds,
+                                               int sw_stride) {
+  const int ks = k0 + S;
+  if constexpr (GUARD) {
+    if (ks >= nk) return;
+  }
+  float sw[P::NJ];
+#pragma unroll
+  for (int j = 0; j < P::NJ; ++j) sw[j] = sw_lds[(j >= P::NJ / 2 ? sw_stride : 0) + ks];
+  P::template compute_jo<NSUB>(st[S], wr, f, acc, sw, []<int J>() {
+    if constexpr (J == P::NJ / 2 - 1) block_barrier();   // B_ks
+  }, pp, psc);
+  // stage ks+1 (past the end: a stale buffer, read and unused)
+  P::template prefetch_jo<NSUB>(st[(S + 1) % 3], wr, f);
+  block_barrier();   // A_ks
+  if constexpr (S + 1 < 3)
+    ws8_mfma_steps<P, S + 1, NSUB, GUARD>(st, k0, nk, wr, f, acc, pp, psc, sw_lds, sw_stride);
+}
+
+// Returns on every wave; only waves 0-3 hold results in acc.
+template <class P, int NSUB, class WR>
+__device__ __forceinline__ void pipe_mainloop_ws8(const P& p, uint8_t* const (&st)[3], int nk, const WR& wr,
+                                                  f32x4 (&acc)[P::MI][P::NJ], const float* sw_lds,
+                                                  int sw_stride) {
+  static_assert(P::SB == 128 && P::NJ >= 2, "FP8 stages");
+  constexpr int NA = P::template nia_for<NSUB>();
+  constexpr int NL = P::template nl_for<NSUB>();
+  if (wave_id() >= 4) {
+    p.template issue_range<0, NL, NA>(st[0], 0);
+    if (nk > 1) {
+      p.template issue_range<0, NL, NA>(st[1], 1);
+      wait_vm_lgkm0<NL>();   // stage 0
+    } else {
+      wait_vm_lgkm0<0>();
+    }
+    block_barrier();
+    int k = 0;
+    for (; k + 3 <= nk; k += 3) ws8_load_steps<P, 0, NSUB, false>(p, st, k, nk);
+    if (k < nk) ws8_load_steps<P, 0, NSUB, true>(p, st, k, nk);
+  } else {
+    block_barrier();
+    typename P::FragsJ f;
+    P::template prefetch_jo<NSUB>(st[0], wr, f);
+    f32x4 pp[P::MI];
+    float psc[P::MI];
+#pragma unroll
+    for (int i = 0; i < P::MI; ++i) {
+      pp[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+      psc[i] = 0.f;
+    }
+    int k = 0;
+    for (; k + 3 <= nk; k += 3) ws8_mfma_steps<P, 0, NSUB, false>(st, k, nk, wr, f, acc, pp, psc, sw_lds, sw_stride);
+    if (k < nk) ws8_mfma_steps<P, 0, NSUB, true>(st, k, nk, wr, f, acc, pp, psc, sw_lds, sw_stride);
+#pragma unroll
+    for (int i = 0; i < NSUB; ++i) acc[i][P::NJ - 1] += pp[i] * psc[i];
   }
 }
 

@@ -33,13 +33,14 @@ constexpr int NXCD = 8;
 template <int FMT>
 struct GG {
   // bf16: 192 rows (an MFMA wave holds 6 x 8 accumulator subtiles = 192
-  // VGPRs), the wave-specialised pipeline on a ring of 5 stage buffers.  FP8
-  // (128-byte K-steps, 3 stages) and fp32 (only small layers, 5 stages):
-  // 128 rows, the single-stage pipeline.
+  // VGPRs), the wave-specialised paired pipeline on a ring of 5 stage
+  // buffers.  FP8: 128 rows, the wave-specialised FP8 pipeline on a ring of 3
+  // (128-byte K-steps).  fp32 (only small layers): 128 rows, the single-stage
+  // pipeline on 5.
   static constexpr int BM = FMT == FMT_BF16 ? 192 : 128;
   static constexpr int NST = FMT == FMT_E4M3 ? 3 : 5;
-  // bf16: 4 MFMA waves + 4 load waves; FP8 and fp32: 4 waves doing both
-  static constexpr int THREADS = FMT == FMT_BF16 ? 512 : 256;
+  // bf16 and FP8: 4 MFMA waves + 4 load waves; fp32: 4 waves doing both
+  static constexpr int THREADS = FMT == FMT_F32 ? 256 : 512;
   using P = Pipe<FMT, BM, BNW, NST, 2>;   // 2 x 2 MFMA waves
 };
 
@@ -52,6 +53,8 @@ __device__ __forceinline__ void gg_mainloop(const MK& make_pipe, uint8_t* const 
   using P = typename GG<FMT>::P;
   if constexpr (FMT == FMT_BF16)
     pipe_mainloop_ws<P, NSUB>(make_pipe(), st, nk, wr, acc);
+  else if constexpr (FMT == FMT_E4M3)
+    pipe_mainloop_ws8<P, NSUB>(make_pipe(), st, nk, wr, acc, sw_lds, sw_stride);
   else
     pipe_mainloop<P, GG<FMT>::NST, NSUB>(make_pipe(), st, nk, wr, acc, sw_lds, sw_stride);
 }
@@ -133,7 +136,8 @@ __device__ __forceinline__ void gateup_tile(const GateUpArgs& a, const MK& make_
   f32x4 acc[P::MI][P::NJ];
   zero_acc(acc);
   gg_mainloop<FMT, NSUB>(make_pipe, st, nk, wr, acc, swl, kb);
-  if (GG<FMT>::THREADS > 256 && w >= 4) return;   // load waves
+  // the load waves hold no results (the FP8 epilogue keeps them for its barrier)
+  if (FMT != FMT_E4M3 && GG<FMT>::THREADS > 256 && w >= 4) return;
 
   if constexpr (FMT != FMT_E4M3) {
 #pragma unroll
@@ -162,21 +166,25 @@ __device__ __forceinline__ void gateup_tile(const GateUpArgs& a, const MK& make_
     // scale group.  A row's amax is reduced over its lane's 16 values, the 4
     // lane groups, then the two waves (wn = 0, 1) that share the row.
     float hv[NSUB][4][4];
+    const bool mw = w < 4;   // an MFMA wave
+    if (mw) {
 #pragma unroll
-    for (int i = 0; i < NSUB; ++i) {
-      float m = 0.f;
+      for (int i = 0; i < NSUB; ++i) {
+        float m = 0.f;
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj)
+        for (int jj = 0; jj < 4; ++jj)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          hv[i][jj][r] = silu_f32(acc[i][jj][r]) * acc[i][jj + 4][r];
-          m = fmaxf(m, fabsf(hv[i][jj][r]));
-        }
-      m = fmaxf(m, __shfl_xor(m, 16));
-      m = fmaxf(m, __shfl_xor(m, 32));
-      if (lg == 0) red[wn][16 * (2 * i + wm) + lr] = m;
+          for (int r = 0; r < 4; ++r) {
+            hv[i][jj][r] = silu_f32(acc[i][jj][r]) * acc[i][jj + 4][r];
+            m = fmaxf(m, fabsf(hv[i][jj][r]));
+          }
+        m = fmaxf(m, __shfl_xor(m, 16));
+        m = fmaxf(m, __shfl_xor(m, 32));
+        if (lg == 0) red[wn][16 * (2 * i + wm) + lr] = m;
+      }
     }
     __syncthreads();
+    if (!mw) return;
     const int ncb = a.inter / 128;
 #pragma unroll
     for (int i = 0; i < NSUB; ++i) {
@@ -249,7 +257,7 @@ __global__ __launch_bounds__(GG<FMT>::THREADS, 1) void gateup_kernel(GateUpArgs 
   if constexpr (FMT == FMT_E4M3) {
     // this tile's weight-block scales: gate block n0/128 and up block (I+n0)/128, all K blocks
     const float* sb = (shared ? a.sw_shared : a.sw_routed) + static_cast<size_t>(gs) * (2 * a.inter / 128) * kb;
-    for (int i = threadIdx.x; i < 2 * kb; i += 256)
+    for (int i = threadIdx.x; i < 2 * kb; i += GG<FMT>::THREADS)
       swl[i] = i < kb ? sb[static_cast<size_t>(n0 / 128) * kb + i] : sb[static_cast<size_t>((a.inter + n0) / 128) * kb + i - kb];
     __syncthreads();
   }
@@ -346,7 +354,7 @@ __global__ __launch_bounds__(GG<FMT>::THREADS, 1) void down_kernel(DownArgs a) {
     // clamped at the matrix edge), all K blocks
     const float* sb = (shared ? a.sw_shared : a.sw_routed) + static_cast<size_t>(gs) * (a.d / 128) * kb;
     const int b0 = n0 / 128, b1 = min(n0 / 128 + 1, a.d / 128 - 1);
-    for (int i = threadIdx.x; i < 2 * kb; i += 256)
+    for (int i = threadIdx.x; i < 2 * kb; i += GG<FMT>::THREADS)
       swl[i] = i < kb ? sb[static_cast<size_t>(b0) * kb + i] : sb[static_cast<size_t>(b1) * kb + i - kb];
     __syncthreads();
   }
