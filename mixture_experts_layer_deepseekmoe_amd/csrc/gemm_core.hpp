@@ -15,7 +15,7 @@
 // (see swz below).  The loader picks, for each lane, the global chunk that
 // belongs at the LDS position the DMA writes it to.
 //
-// Compute: block = 4 waves laid out WM x (4/WM).  A wave owns NJ = 4*WM
+// Compute: block = 4 waves laid out WM x (4/WM).  A wave owns NJ = BNW*WM/64
 // column subtiles of W (16 W rows each, offsets chosen by the caller) and
 // every WM-th 16-row subtile of X starting at subtile wm = w % WM, so short
 // tiles stay balanced across the wave rows.  The MFMA's first operand is the
@@ -91,8 +91,9 @@ __device__ __forceinline__ int swz(int r) {
 
 // W rows read by one wave: subtile j covers rows base + 16 j, plus SPLIT
 // for the second half of the subtiles (j >= NJ / 2).  base is wave-uniform
-// and a multiple of 64, so a row's swizzle is fixed at compile time by j and
-// the lane, and every fragment address is one register plus an immediate
+// and a multiple of 16, so a row's swizzle (a function of the row modulo 16)
+// is fixed by the lane, and every fragment address is one register plus an
+// immediate
 // (given as a runtime array of rows, the compiler kept one address register
 // per subtile and spilled them).
 template <int SPLIT>
@@ -113,9 +114,10 @@ struct Pipe {
   static constexpr int S_OFF = B_OFF + BNW * SB;
   static constexpr int STAGE_BYTES = S_OFF + (FMT == FMT_E4M3 ? 1024 : 0);
   static constexpr int NL = NIA + NIB + (FMT == FMT_E4M3 ? 1 : 0);   // DMA ops per lane per stage
-  static constexpr int NJ = 4 * WM;                     // column subtiles per wave
+  static constexpr int NJ = BNW * WM / 64;              // column subtiles per wave
   static constexpr int MI = (BM / 16 + WM - 1) / WM;     // row subtiles per wave
   static_assert(BNW % (4 * RPI) == 0, "W rows must fill whole DMA instructions");
+  static_assert(NJ >= 1 && BNW * WM % 64 == 0, "whole column subtiles per wave");
 
   rsrc_t ra, rb, rs;
   uint32_t oa[NIA];   // per-lane byte offsets of the lane's 16-byte piece, K-step 0

@@ -28,7 +28,13 @@ struct RouteArgs {
   int T, d, n_routed, top_k;
   int32_t* idx;           // [T][K]
   float* gate;            // [T][K]
+  float* scores;          // [T][N_r] scratch, used when route_split(T)
 };
+
+// Batches under 128 router blocks (T < 4096) spread the experts over blocks
+// too: a score kernel writes the sigmoids to scratch, a second kernel selects.
+constexpr int ROUTE_SPLIT_T = 4096;
+inline bool route_split(long long T) { return T < ROUTE_SPLIT_T; }
 
 struct GroupArgs {
   const int32_t* idx;     // [T][K]

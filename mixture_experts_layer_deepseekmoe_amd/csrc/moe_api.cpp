@@ -25,7 +25,7 @@ int fmt_of(int dt) { return dt == MOE_DTYPE_F32 ? FMT_F32 : (dt == MOE_DTYPE_BF1
 
 // Workspace map (byte offsets, each 256-byte aligned).
 struct Layout {
-  size_t hist, idx, gate, counts, offsets, perm, pos, mtiles, mtcount, uq, us, h, hs, y, total;
+  size_t hist, idx, gate, counts, offsets, perm, pos, mtiles, mtcount, uq, us, h, hs, y, scores, total;
   int nblk, max_mt;
   long long rows;   // grouped rows: T*K routed + N_s*T shared
 };
@@ -53,6 +53,7 @@ Layout make_layout(const moe_shape& s) {
   L.h = take(static_cast<size_t>(L.rows) * s.inter * elem_bytes(s.w_dtype));
   L.hs = take(fp8 ? static_cast<size_t>(L.rows) * (s.inter / 128) * 4 : 0);
   L.y = take(static_cast<size_t>(L.rows) * s.d * (s.w_dtype == MOE_DTYPE_F32 ? 4 : 2));
+  L.scores = take(moe::route_split(T) ? static_cast<size_t>(T) * s.n_routed * 4 : 0);
   L.total = o;
   return L;
 }
@@ -108,9 +109,9 @@ struct Stages {
 
 // Route + group.  `mtiles` null: routing only (no GEMM tile list).
 int run_route(const moe_shape& s, const void* u, const void* cen, const float* bias, int32_t* idx, float* gate,
-              int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* pos, int32_t* hist, int4* mtiles,
-              int32_t* mtcount, hipStream_t st) {
-  moe::RouteArgs ra{u, cen, bias, s.T, s.d, s.n_routed, s.top_k, idx, gate};
+              int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* pos, int32_t* hist, float* scores,
+              int4* mtiles, int32_t* mtcount, hipStream_t st) {
+  moe::RouteArgs ra{u, cen, bias, s.T, s.d, s.n_routed, s.top_k, idx, gate, scores};
   int rc = check_launch(moe::launch_route(fmt_of(s.x_dtype), ra, st));
   if (rc != MOE_OK) return rc;
   moe::GroupArgs ga{idx,     s.T,  s.top_k, s.n_routed, s.n_shared, hist,   counts,
@@ -156,7 +157,8 @@ int moe_route(const moe_shape* shape, const void* u, const void* centroids, cons
   const Layout L = make_layout(s);
   if (workspace == nullptr || workspace_bytes < L.total) return MOE_ERR_WORKSPACE;
   return run_route(s, u, centroids, bias, out->topk_idx, out->topk_gate, out->expert_counts, out->expert_offsets,
-                   out->perm_token, out->pos, at<int32_t>(workspace, L.hist), nullptr, nullptr, stream);
+                   out->perm_token, out->pos, at<int32_t>(workspace, L.hist), at<float>(workspace, L.scores),
+                   nullptr, nullptr, stream);
 }
 
 int moe_forward(const moe_shape* shape, const void* u, const void* centroids, const float* bias,
@@ -192,7 +194,7 @@ int moe_forward(const moe_shape* shape, const void* u, const void* centroids, co
 
   Stages stg{trace, stream};
   stg.begin(MOE_STAGE_ROUTE);
-  moe::RouteArgs ra{u, centroids, bias, s.T, s.d, s.n_routed, s.top_k, idx, gate};
+  moe::RouteArgs ra{u, centroids, bias, s.T, s.d, s.n_routed, s.top_k, idx, gate, at<float>(workspace, L.scores)};
   rc = check_launch(moe::launch_route(fmt_of(s.x_dtype), ra, stream));
   if (rc != MOE_OK) return rc;
   stg.end(MOE_STAGE_ROUTE);

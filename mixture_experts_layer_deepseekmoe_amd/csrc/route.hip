@@ -6,8 +6,9 @@
 // One block routes 32 tokens against every expert: the logits of one chunk
 // of 256 experts come from the pipelined MFMA tile core (fp32 accumulation);
 // their sigmoids go to LDS (the logits never reach HBM); then each wave
-// selects the top-K of 8 tokens, with the N_r scores of a token spread 1..8
-// per lane.
+// selects the top-K of its tokens, with the N_r scores of a token spread
+// 1..8 per lane.  Small batches (too few such blocks to fill the chip) split
+// the experts over blocks as well and pass the sigmoids through scratch.
 // Ordering is by v = s + b descending, exact ties to the lower expert index;
 // a NaN score ranks below every number, so K distinct in-range experts are
 // always produced.  Gates are s_k / sum of the K selected s, summed in
@@ -21,6 +22,64 @@ namespace {
 
 constexpr int RBT = ROUTE_BT;
 constexpr int RCHUNK = 256;   // experts per MFMA pass
+
+// Top-K of one token by one wave: srow holds the token's N_r sigmoid scores
+// (LDS or global), bq[q] the bias of expert lane + 64 q.  Lane k < K writes
+// the k-th selected expert and its gate.
+template <int NQ>
+__device__ __forceinline__ void select_topk(const float* srow, const float (&bq)[NQ], int n_routed, int top_k,
+                                            int32_t* idx_out, float* gate_out) {
+  const int lane = threadIdx.x & 63;
+  float key[NQ];
+#pragma unroll
+  for (int q = 0; q < NQ; ++q) {
+    const int e = lane + 64 * q;
+    float v = -INFINITY;
+    if (e < n_routed) {
+      v = srow[e] + bq[q];
+      if (v != v) v = -INFINITY;
+    }
+    key[q] = v;
+  }
+  uint32_t taken = 0;
+  int chosen = 0;     // lane k keeps the k-th selected expert
+  float chosen_s = 0.f;
+  float sum = 0.f;
+  for (int k = 0; k < top_k; ++k) {
+    float bv = -INFINITY;
+    int be = 0x7fffffff;
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+      const int e = lane + 64 * q;
+      const bool cand = e < n_routed && !((taken >> q) & 1u);
+      if (cand && (key[q] > bv || (key[q] == bv && e < be))) { bv = key[q]; be = e; }
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      const float ov = __shfl_xor(bv, off);
+      const int oe = __shfl_xor(be, off);
+      if (ov > bv || (ov == bv && oe < be)) { bv = ov; be = oe; }
+    }
+    if ((be & 63) == lane) taken |= 1u << (be >> 6);
+    const float s_sel = srow[be];
+    sum += s_sel;
+    if (lane == k) { chosen = be; chosen_s = s_sel; }
+  }
+  if (lane < top_k) {
+    idx_out[lane] = chosen;
+    gate_out[lane] = chosen_s / sum;
+  }
+}
+
+template <int NQ>
+__device__ __forceinline__ void load_bias(const float* bias, int n_routed, float (&bq)[NQ]) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int q = 0; q < NQ; ++q) {
+    const int e = lane + 64 * q;
+    bq[q] = e < n_routed ? bias[e] : 0.f;
+  }
+}
 
 // Every block streams all centroids (from L2) beside its own token rows, so
 // the router is bound by the loads a CU keeps in flight.  Up to 256 experts
@@ -105,62 +164,87 @@ __global__ __launch_bounds__(64 * RouteCfg<NRMAX>::NW) void route_kernel(RouteAr
   constexpr int NQ = NRMAX / 64;
   constexpr int TPW = RBT / C::NW;
   float bq[NQ];
-#pragma unroll
-  for (int q = 0; q < NQ; ++q) {
-    const int e = lane + 64 * q;
-    bq[q] = e < a.n_routed ? a.bias[e] : 0.f;
-  }
+  load_bias(a.bias, a.n_routed, bq);
   for (int tt = 0; tt < TPW; ++tt) {
     const int tl = w * TPW + tt;
     const int t = t0 + tl;
     if (t >= a.T) break;
-    const float* srow = sbuf + tl * SSTRIDE;
-    float key[NQ];
-#pragma unroll
-    for (int q = 0; q < NQ; ++q) {
-      const int e = lane + 64 * q;
-      float v = -INFINITY;
-      if (e < a.n_routed) {
-        v = srow[e] + bq[q];
-        if (v != v) v = -INFINITY;
-      }
-      key[q] = v;
-    }
-    uint32_t taken = 0;
-    int chosen = 0;     // lane k keeps the k-th selected expert
-    float chosen_s = 0.f;
-    float sum = 0.f;
-    for (int k = 0; k < a.top_k; ++k) {
-      float bv = -INFINITY;
-      int be = 0x7fffffff;
-#pragma unroll
-      for (int q = 0; q < NQ; ++q) {
-        const int e = lane + 64 * q;
-        const bool cand = e < a.n_routed && !((taken >> q) & 1u);
-        if (cand && (key[q] > bv || (key[q] == bv && e < be))) { bv = key[q]; be = e; }
-      }
-#pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) {
-        const float ov = __shfl_xor(bv, off);
-        const int oe = __shfl_xor(be, off);
-        if (ov > bv || (ov == bv && oe < be)) { bv = ov; be = oe; }
-      }
-      if ((be & 63) == lane) taken |= 1u << (be >> 6);
-      const float s_sel = srow[be];
-      sum += s_sel;
-      if (lane == k) { chosen = be; chosen_s = s_sel; }
-    }
-    if (lane < a.top_k) {
-      a.idx[static_cast<size_t>(t) * a.top_k + lane] = chosen;
-      a.gate[static_cast<size_t>(t) * a.top_k + lane] = chosen_s / sum;
-    }
+    select_topk(sbuf + tl * SSTRIDE, bq, a.n_routed, a.top_k, a.idx + static_cast<size_t>(t) * a.top_k,
+                a.gate + static_cast<size_t>(t) * a.top_k);
   }
+}
+
+// ---- small batches: expert chunks of 64 over blocks too
+constexpr int SCHUNK = 64;
+
+// Scores of 32 tokens against 64 experts on the wave-specialised paired
+// pipeline (each MFMA wave owns 16 experts), written to scratch.
+template <int FMT>
+__global__ __launch_bounds__(512) void route_scores_kernel(RouteArgs a) {
+  using P = Pipe<FMT, RBT, SCHUNK, 5>;
+  __shared__ __attribute__((aligned(1024))) uint8_t st0[P::STAGE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t st1[P::STAGE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t st2[P::STAGE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t st3[P::STAGE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t st4[P::STAGE_BYTES];
+  uint8_t* const st[5] = {st0, st1, st2, st3, st4};
+
+  const int w = wave_id(), lane = threadIdx.x & 63;
+  const int lr = lane & 15, lg = lane >> 4;
+  const int t0 = blockIdx.x * RBT, ec = blockIdx.y * SCHUNK;
+  const int es = FMT == FMT_F32 ? 4 : 2;
+  const size_t row_bytes = static_cast<size_t>(a.d) * es;
+  const int nk = static_cast<int>(row_bytes / P::SB);
+  const int valid = min(RBT, a.T - t0);
+  P p;
+  const rsrc_t ru = make_rsrc(static_cast<const uint8_t*>(a.u) + static_cast<size_t>(t0) * row_bytes,
+                              static_cast<uint32_t>(valid * row_bytes));
+  p.init(ru, [&](int r) { return static_cast<uint32_t>((r < valid ? r : 0) * row_bytes); },
+         make_rsrc(a.centroids, static_cast<uint32_t>(a.n_routed * row_bytes)),
+         [&](int r) { return static_cast<uint32_t>((ec + r < a.n_routed ? ec + r : 0) * row_bytes); },
+         ru, [](int) { return 0u; });
+  const WRows<0> wr{16 * (w & 3)};   // this wave's 16 experts of the chunk
+  f32x4 acc[P::MI][P::NJ];
+  zero_acc(acc);
+  if (valid > 16)
+    pipe_mainloop_ws<P, 2>(p, st, nk, wr, acc);
+  else
+    pipe_mainloop_ws<P, 1>(p, st, nk, wr, acc);
+  if (w >= 4) return;
+  // lane: token 16 i + lr, experts ec + 16 w + 4 lg .. +3
+  const int e = ec + 16 * w + 4 * lg;
+#pragma unroll
+  for (int i = 0; i < P::MI; ++i) {
+    const int t = t0 + 16 * i + lr;
+    if (t >= a.T) continue;
+    float* dst = a.scores + static_cast<size_t>(t) * a.n_routed + e;
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      if (e + r < a.n_routed) dst[r] = sigmoid_f32(acc[i][0][r]);
+  }
+}
+
+// One wave per token: top-K over its scores in scratch.
+template <int NRMAX>
+__global__ __launch_bounds__(256) void route_topk_kernel(RouteArgs a) {
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  constexpr int NQ = NRMAX / 64;
+  float bq[NQ];
+  load_bias(a.bias, a.n_routed, bq);
+  if (t >= a.T) return;
+  select_topk(a.scores + static_cast<size_t>(t) * a.n_routed, bq, a.n_routed, a.top_k,
+              a.idx + static_cast<size_t>(t) * a.top_k, a.gate + static_cast<size_t>(t) * a.top_k);
 }
 
 template <int FMT, int NRMAX>
 hipError_t launch_route_t(const RouteArgs& a, hipStream_t s) {
-  const int grid = ceil_div(a.T, RBT);
-  hipLaunchKernelGGL((route_kernel<FMT, NRMAX>), dim3(grid), dim3(64 * RouteCfg<NRMAX>::NW), 0, s, a);
+  if (route_split(a.T) && a.scores != nullptr) {
+    hipLaunchKernelGGL((route_scores_kernel<FMT>), dim3(ceil_div(a.T, RBT), ceil_div(a.n_routed, SCHUNK)), dim3(512),
+                       0, s, a);
+    hipLaunchKernelGGL((route_topk_kernel<NRMAX>), dim3(ceil_div(a.T, 4)), dim3(256), 0, s, a);
+  } else {
+    hipLaunchKernelGGL((route_kernel<FMT, NRMAX>), dim3(ceil_div(a.T, RBT)), dim3(64 * RouteCfg<NRMAX>::NW), 0, s, a);
+  }
   return hipGetLastError();
 }
 
