@@ -585,8 +585,11 @@ __device__ __forceinline__ void ws_mfma_pairs(uint8_t* const (&st)[5], int q0, i
   if constexpr (Q + 1 < 5) ws_mfma_pairs<P, Q + 1, NSUB, GUARD>(st, q0, np, wr, f, acc);
 }
 
-// Returns on every wave; only waves 0-3 hold results in acc.
-template <class P, int NSUB, class WR>
+// Returns on every wave; only waves 0-3 hold results in acc.  NSUB: the row
+// subtiles loaded (the most any wave row computes); NSUBC: those this wave
+// computes (one fewer for the second wave row when the tile's 16-row
+// subtiles are odd in number).
+template <class P, int NSUB, int NSUBC = NSUB, class WR>
 __device__ __forceinline__ void pipe_mainloop_ws(const P& p, uint8_t* const (&st)[5], int nk,
                                                  const WR& wr, f32x4 (&acc)[P::MI][P::NJ]) {
   static_assert(P::SB == 64, "pairs of 64-byte K-steps");
@@ -609,10 +612,10 @@ __device__ __forceinline__ void pipe_mainloop_ws(const P& p, uint8_t* const (&st
   } else {
     block_barrier();
     typename P::Frags f;
-    P::template prefetch<NSUB>(st[0], wr, f);
+    P::template prefetch<NSUBC>(st[0], wr, f);
     int q = 0;
-    for (; q + 5 <= np; q += 5) ws_mfma_pairs<P, 0, NSUB, false>(st, q, np, wr, f, acc);
-    if (q < np) ws_mfma_pairs<P, 0, NSUB, true>(st, q, np, wr, f, acc);
+    for (; q + 5 <= np; q += 5) ws_mfma_pairs<P, 0, NSUBC, false>(st, q, np, wr, f, acc);
+    if (q < np) ws_mfma_pairs<P, 0, NSUBC, true>(st, q, np, wr, f, acc);
   }
 }
 

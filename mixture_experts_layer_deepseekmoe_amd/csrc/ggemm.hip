@@ -46,13 +46,13 @@ struct GG {
 
 // make_pipe() returns the tile's initialised Pipe (the loads' per-lane
 // state).  wr: the W rows of this wave's column subtiles.
-template <int FMT, int NSUB, class MK, class WR>
+template <int FMT, int NSUB, int NSUBC, class MK, class WR>
 __device__ __forceinline__ void gg_mainloop(const MK& make_pipe, uint8_t* const (&st)[GG<FMT>::NST], int nk,
                                             const WR& wr, f32x4 (&acc)[GG<FMT>::P::MI][GG<FMT>::P::NJ],
                                             const float* sw_lds, int sw_stride) {
   using P = typename GG<FMT>::P;
   if constexpr (FMT == FMT_BF16)
-    pipe_mainloop_ws<P, NSUB>(make_pipe(), st, nk, wr, acc);
+    pipe_mainloop_ws<P, NSUB, NSUBC>(make_pipe(), st, nk, wr, acc);
   else if constexpr (FMT == FMT_E4M3)
     pipe_mainloop_ws8<P, NSUB>(make_pipe(), st, nk, wr, acc, sw_lds, sw_stride);
   else
@@ -120,9 +120,17 @@ __device__ __forceinline__ void dispatch_rows(int rows, F&& f) {
   }
 }
 
+// bf16: a tile with an odd number of 16-row subtiles leaves the second wave
+// row (wm = 1) one subtile short; its waves compute one fewer instead of a
+// subtile of padding (the loads still cover the first wave row's rows).
+template <int FMT>
+__device__ __forceinline__ bool odd_second_row(int rows) {
+  return FMT == FMT_BF16 && (wave_id() & 1) && (((rows + 15) / 16) & 1);
+}
+
 // ------------------------------------------------------------------ gate/up
 
-template <int FMT, int NSUB, class MK>
+template <int FMT, int NSUB, int NSUBC, class MK>
 __device__ __forceinline__ void gateup_tile(const GateUpArgs& a, const MK& make_pipe, uint8_t* const (&st)[GG<FMT>::NST],
                                             const float* swl, int kb, int nk, int row0, int rows, int n0, int nb,
                                             float (*red)[GG<FMT>::BM]) {
@@ -135,13 +143,13 @@ __device__ __forceinline__ void gateup_tile(const GateUpArgs& a, const MK& make_
   const WRows<64> wr{64 * wn};
   f32x4 acc[P::MI][P::NJ];
   zero_acc(acc);
-  gg_mainloop<FMT, NSUB>(make_pipe, st, nk, wr, acc, swl, kb);
+  gg_mainloop<FMT, NSUB, NSUBC>(make_pipe, st, nk, wr, acc, swl, kb);
   // the load waves hold no results (the FP8 epilogue keeps them for its barrier)
   if (FMT != FMT_E4M3 && GG<FMT>::THREADS > 256 && w >= 4) return;
 
   if constexpr (FMT != FMT_E4M3) {
 #pragma unroll
-    for (int i = 0; i < NSUB; ++i) {
+    for (int i = 0; i < NSUBC; ++i) {
       const int row = 16 * (2 * i + wm) + lr;
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
@@ -165,11 +173,11 @@ __device__ __forceinline__ void gateup_tile(const GateUpArgs& a, const MK& make_
     // 1x128 quantisation of h along I: the 128 columns of this tile are one
     // scale group.  A row's amax is reduced over its lane's 16 values, the 4
     // lane groups, then the two waves (wn = 0, 1) that share the row.
-    float hv[NSUB][4][4];
+    float hv[NSUBC][4][4];
     const bool mw = w < 4;   // an MFMA wave
     if (mw) {
 #pragma unroll
-      for (int i = 0; i < NSUB; ++i) {
+      for (int i = 0; i < NSUBC; ++i) {
         float m = 0.f;
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj)
@@ -187,7 +195,7 @@ __device__ __forceinline__ void gateup_tile(const GateUpArgs& a, const MK& make_
     if (!mw) return;
     const int ncb = a.inter / 128;
 #pragma unroll
-    for (int i = 0; i < NSUB; ++i) {
+    for (int i = 0; i < NSUBC; ++i) {
       const int row = 16 * (2 * i + wm) + lr;
       if (row < rows) {
         const float m = fmaxf(red[0][row], red[1][row]);
@@ -265,14 +273,19 @@ __global__ __launch_bounds__(GG<FMT>::THREADS, 1) void gateup_kernel(GateUpArgs 
   const Ring<NST> ring = make_ring<NST>(st0, st1, st2, st3, st4);
   const float* sw = FMT == FMT_E4M3 ? swl : nullptr;
   // the K loop instantiated for the tile's valid rows, in 32-row steps
+  const bool short_row = odd_second_row<FMT>(rows);
   dispatch_rows<P::MI>(rows, [&]<int NSUB>() {
-    gateup_tile<FMT, NSUB>(a, make_pipe, ring.s, sw, kb, nk, row0, rows, n0, nb, red);
+    if (short_row)
+      gateup_tile<FMT, NSUB, (FMT == FMT_BF16 ? NSUB - 1 : NSUB)>(a, make_pipe, ring.s, sw, kb, nk, row0, rows, n0, nb,
+                                                                  red);
+    else
+      gateup_tile<FMT, NSUB, NSUB>(a, make_pipe, ring.s, sw, kb, nk, row0, rows, n0, nb, red);
   });
 }
 
 // ------------------------------------------------------------------ down
 
-template <int FMT, int NSUB, class MK>
+template <int FMT, int NSUB, int NSUBC, class MK>
 __device__ __forceinline__ void down_tile(const DownArgs& a, const MK& make_pipe, uint8_t* const (&st)[GG<FMT>::NST],
                                           const float* swl, int kb, int nk, int row0, int rows, int n0) {
   using P = typename GG<FMT>::P;
@@ -284,10 +297,10 @@ __device__ __forceinline__ void down_tile(const DownArgs& a, const MK& make_pipe
   const WRows<0> wr{128 * wn};
   f32x4 acc[P::MI][P::NJ];
   zero_acc(acc);
-  gg_mainloop<FMT, NSUB>(make_pipe, st, nk, wr, acc, FMT == FMT_E4M3 ? swl + wn * kb : nullptr, 0);
+  gg_mainloop<FMT, NSUB, NSUBC>(make_pipe, st, nk, wr, acc, FMT == FMT_E4M3 ? swl + wn * kb : nullptr, 0);
   if (GG<FMT>::THREADS > 256 && w >= 4) return;   // load waves
 #pragma unroll
-  for (int i = 0; i < NSUB; ++i) {
+  for (int i = 0; i < NSUBC; ++i) {
     const int row = 16 * (2 * i + wm) + lr;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
@@ -361,7 +374,13 @@ __global__ __launch_bounds__(GG<FMT>::THREADS, 1) void down_kernel(DownArgs a) {
 
   const Ring<NST> ring = make_ring<NST>(st0, st1, st2, st3, st4);
   const float* sw = FMT == FMT_E4M3 ? swl : nullptr;
-  dispatch_rows<P::MI>(rows, [&]<int NSUB>() { down_tile<FMT, NSUB>(a, make_pipe, ring.s, sw, kb, nk, row0, rows, n0); });
+  const bool short_row = odd_second_row<FMT>(rows);
+  dispatch_rows<P::MI>(rows, [&]<int NSUB>() {
+    if (short_row)
+      down_tile<FMT, NSUB, (FMT == FMT_BF16 ? NSUB - 1 : NSUB)>(a, make_pipe, ring.s, sw, kb, nk, row0, rows, n0);
+    else
+      down_tile<FMT, NSUB, NSUB>(a, make_pipe, ring.s, sw, kb, nk, row0, rows, n0);
+  });
 }
 
 int grid_for(int max_mtiles, int nb_n) {
