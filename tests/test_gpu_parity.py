@@ -220,5 +220,9 @@ def test_full_fp8_d2048():
     _sampled_forward("fp8_d2048", [0, 4095, 777])
 
 
+def test_full_fp8_d7168():
+    _sampled_forward("fp8_d7168", [0, 8191, 3333])
+
+
 def test_full_skew_decode_d7168():
     _sampled_forward("skew_decode_d7168", [0, 100, 255])
