@@ -46,15 +46,25 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
 }
 
 // buffer_load ... lds: each lane's 16 (4) bytes at voff + soff go to LDS at
-// l + 16 * lane (4 * lane).  The buffer form (not global_load_lds) matters:
-// the compiler treats a global LDS DMA as a FLAT access that may touch LDS
-// and then waits for every outstanding LDS read (lgkmcnt(0)) before the next
-// use of any of them, which would serialise the fragment prefetch.
+// l + 16 * lane (4 * lane); soff and l (in M0) are wave-uniform.  Written as asm so that
+// the compiler does not track these LDS writes: it cannot tell most fragment
+// reads from the stage buffers being refilled, and before such a read it
+// would wait for every load in flight (vmcnt(0)), loads just issued for
+// stages two ahead included.  The pipelines order the DMA and the reads
+// themselves (explicit vmcnt waits, then a barrier).  No register outputs:
+// the instruction reads voff, r and soff at issue and writes only LDS.
+__device__ __forceinline__ uint32_t lds_addr(const void* l) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void_ptr)const_cast<void*>(l)));
+}
 __device__ __forceinline__ void dma16(rsrc_t r, uint32_t voff, uint32_t soff, void* l) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_ptr)l, 16, voff, soff, 0, 0);
+  asm volatile("s_mov_b32 m0, %3\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
+               :: "v"(voff), "s"(r), "s"(__builtin_amdgcn_readfirstlane(soff)),
+                  "s"(__builtin_amdgcn_readfirstlane(lds_addr(l))) : "m0");
 }
 __device__ __forceinline__ void dma4(rsrc_t r, uint32_t voff, uint32_t soff, void* l) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_ptr)l, 4, voff, soff, 0, 0);
+  asm volatile("s_mov_b32 m0, %3\n\ts_nop 0\n\tbuffer_load_dword %0, %1, %2 offen lds"
+               :: "v"(voff), "s"(r), "s"(__builtin_amdgcn_readfirstlane(soff)),
+                  "s"(__builtin_amdgcn_readfirstlane(lds_addr(l))) : "m0");
 }
 
 // s_waitcnt vmcnt(N) expcnt(any) lgkmcnt(0)  (gfx9 encoding)
@@ -101,23 +111,33 @@ struct WRows {
   int base;
 };
 
-template <int FMT, int BM, int BNW, int NST, int WM = 1>
+// NW waves compute, laid out WM x (NW / WM); LW waves issue the loads (the
+// same waves, or as many load-only waves).
+// ACC: how the bf16 MFMAs accumulate -- ACC_BUILTIN, or in place through asm
+// in VGPRs (ACC_TIED) or AGPRs (ACC_AGPR).
+enum : int { ACC_BUILTIN = 0, ACC_TIED = 1, ACC_AGPR = 2 };
+template <int FMT, int BM, int BNW, int NST, int WM = 1, int ACC = ACC_BUILTIN, int NW = 4, int LW = NW>
 struct Pipe {
   static constexpr int SB = FMT == FMT_E4M3 ? 128 : 64;
   static constexpr int CPR = SB / 16;            // 16-byte chunks per row
   static constexpr int RPI = 64 / CPR;           // rows per wave DMA instruction
-  static constexpr int NIA = (BM + 4 * RPI - 1) / (4 * RPI);
-  static constexpr int NIB = BNW / (4 * RPI);
-  static constexpr int AROWS = NIA * 4 * RPI;
+  static constexpr int NIA = (BM + LW * RPI - 1) / (LW * RPI);
+  static constexpr int NIB = BNW / (LW * RPI);
+  static constexpr int AROWS = NIA * LW * RPI;
   static constexpr int A_OFF = 0;
   static constexpr int B_OFF = AROWS * SB;
   static constexpr int S_OFF = B_OFF + BNW * SB;
   static constexpr int STAGE_BYTES = S_OFF + (FMT == FMT_E4M3 ? 1024 : 0);
   static constexpr int NL = NIA + NIB + (FMT == FMT_E4M3 ? 1 : 0);   // DMA ops per lane per stage
-  static constexpr int NJ = BNW * WM / 64;              // column subtiles per wave
+  static constexpr int NJ = BNW * WM / (16 * NW);       // column subtiles per wave
   static constexpr int MI = (BM / 16 + WM - 1) / WM;     // row subtiles per wave
-  static_assert(BNW % (4 * RPI) == 0, "W rows must fill whole DMA instructions");
-  static_assert(NJ >= 1 && BNW * WM % 64 == 0, "whole column subtiles per wave");
+  static_assert(BNW % (LW * RPI) == 0, "W rows must fill whole DMA instructions");
+  static_assert(NJ >= 1 && BNW * WM % (16 * NW) == 0, "whole column subtiles per wave");
+  static_assert((NW == 4 || NW == 8) && NW % WM == 0 && (LW == 4 || LW == 8), "wave layout");
+  static_assert(FMT != FMT_E4M3 || LW == 4, "FP8 scale loads: 4 loading waves");
+  static constexpr int N_COMPUTE = NW;
+  static_assert(ACC == ACC_BUILTIN || FMT == FMT_BF16, "asm accumulation: bf16 only");
+  static constexpr int ACCM = ACC;
 
   rsrc_t ra, rb, rs;
   uint32_t oa[NIA];   // per-lane byte offsets of the lane's 16-byte piece, K-step 0
@@ -128,22 +148,22 @@ struct Pipe {
   // tile, r < AROWS; the caller maps rows past the valid ones to a valid
   // row), W rows from resource b (b_off(r), r < BNW), FP8 X scales from
   // resource s (s_off(r): byte offset of the scale row of X row r, r < 256).
-  // The loads are spread over 4 waves: wave w (or w - 4, in the
-  // wave-specialised pipeline) issues row groups w, w + 4, w + 8, ...
+  // The loads are spread over LW waves: loading wave w (its wave index
+  // modulo LW) issues row groups w, w + LW, w + 2 LW, ...
   template <class FA, class FB, class FS>
   __device__ __forceinline__ void init(rsrc_t a, FA a_off, rsrc_t b, FB b_off, rsrc_t sc, FS s_off) {
-    const int w = wave_id() & 3, lane = threadIdx.x & 63;
+    const int w = wave_id() % LW, lane = threadIdx.x & 63;
     ra = a;
     rb = b;
     rs = sc;
 #pragma unroll
     for (int i = 0; i < NIA; ++i) {
-      const int r = RPI * (w + 4 * i) + lane / CPR;
+      const int r = RPI * (w + LW * i) + lane / CPR;
       oa[i] = a_off(r) + ((lane % CPR) ^ swz<SB>(r)) * 16;
     }
 #pragma unroll
     for (int i = 0; i < NIB; ++i) {
-      const int r = RPI * (w + 4 * i) + lane / CPR;
+      const int r = RPI * (w + LW * i) + lane / CPR;
       ob[i] = b_off(r) + ((lane % CPR) ^ swz<SB>(r)) * 16;
     }
     os = 0;
@@ -155,7 +175,7 @@ struct Pipe {
   // wholly past them are not loaded at all.
   template <int NSUB>
   static constexpr int nia_for() {
-    constexpr int need = (16 * WM * NSUB + 4 * RPI - 1) / (4 * RPI);
+    constexpr int need = (16 * WM * NSUB + LW * RPI - 1) / (LW * RPI);
     return need < NIA ? need : NIA;
   }
   template <int NSUB>
@@ -167,12 +187,12 @@ struct Pipe {
   // then (FP8) the X scales.
   template <int Q, int NA>
   __device__ __forceinline__ void issue_one(uint8_t* st, int ks) const {
-    const int w = wave_id() & 3;
+    const int w = wave_id() % LW;
     const uint32_t kofs = static_cast<uint32_t>(ks) * SB;
     if constexpr (Q < NA)
-      dma16(ra, oa[Q], kofs, st + A_OFF + RPI * (w + 4 * Q) * SB);
+      dma16(ra, oa[Q], kofs, st + A_OFF + RPI * (w + LW * Q) * SB);
     else if constexpr (Q < NA + NIB)
-      dma16(rb, ob[Q - NA], kofs, st + B_OFF + RPI * (w + 4 * (Q - NA)) * SB);
+      dma16(rb, ob[Q - NA], kofs, st + B_OFF + RPI * (w + LW * (Q - NA)) * SB);
     else
       dma4(rs, os, static_cast<uint32_t>(ks) * 4, st + S_OFF + 256 * w);
   }
@@ -199,16 +219,46 @@ struct Pipe {
     }
   }
 
-  __device__ __forceinline__ static uint4 frag16(const uint8_t* base, int r, int chunk) {
-    return *reinterpret_cast<const uint4*>(base + r * SB + ((chunk ^ swz<SB>(r)) << 4));
+  // The same with the loads of a pair past the end of K (live == false)
+  // issued against empty buffer resources: they fetch nothing and write zeros
+  // to stage buffers nobody reads, so a pipeline need not branch around them.
+  template <int Q, int NA>
+  __device__ __forceinline__ void issue_one_r(uint8_t* st, int ks, rsrc_t a, rsrc_t b) const {
+    const int w = wave_id() % LW;
+    const uint32_t kofs = static_cast<uint32_t>(ks) * SB;
+    if constexpr (Q < NA)
+      dma16(a, oa[Q], kofs, st + A_OFF + RPI * (w + LW * Q) * SB);
+    else
+      dma16(b, ob[Q - NA], kofs, st + B_OFF + RPI * (w + LW * (Q - NA)) * SB);
+  }
+  template <int LO, int HI, int NA>
+  __device__ __forceinline__ void issue_pair_range_r(uint8_t* st0, uint8_t* st1, int ks, rsrc_t a, rsrc_t b) const {
+    if constexpr (LO < HI) {
+      issue_one_r<LO, NA>(st0, ks, a, b);
+      issue_one_r<LO, NA>(st1, ks + 1, a, b);
+      issue_pair_range_r<LO + 1, HI, NA>(st0, st1, ks, a, b);
+    }
+  }
+
+  // One 128-bit LDS read.  Fragments are vector values (i32x4), not i32x4
+  // structs: a struct is split into four 32-bit loads that the backend merges
+  // again, and the merged read loses the LDS object's alias information; the
+  // wait insertion then cannot tell it from the stage buffers being refilled
+  // by DMA and waits for every load in flight before it.
+  __device__ __forceinline__ static i32x4 frag16(const uint8_t* base, int r, int chunk) {
+    return *reinterpret_cast<const i32x4*>(base + r * SB + ((chunk ^ swz<SB>(r)) << 4));
   }
 
   // Fragments carried from one stage to the next: the W fragments of the
   // wave's column subtiles and the first two X fragments.
   static constexpr int XW = FMT == FMT_E4M3 ? 2 : 1;   // 16-byte pieces per fragment
+  // X fragments are read XPD row subtiles ahead of their MFMAs: two with one
+  // MFMA wave per SIMD, one with two (the other wave's MFMAs cover the read,
+  // and the MFMA wave keeps 4 registers more in a 168-register budget).
+  static constexpr int XPD = NW > 4 ? 1 : 2;
   struct Frags {
-    uint4 w[NJ * XW];
-    uint4 x[2 * XW];
+    i32x4 w[NJ * XW];
+    i32x4 x[2 * XW];
     float sx[2];
   };
 
@@ -216,7 +266,7 @@ struct Pipe {
     return 16 * (WM * i + (WM > 1 ? wave_id() % WM : 0));
   }
 
-  __device__ __forceinline__ static void load_x(const uint8_t* st, int i, uint4* x, float& sx) {
+  __device__ __forceinline__ static void load_x(const uint8_t* st, int i, i32x4* x, float& sx) {
     const int lane = threadIdx.x & 63, lr = lane & 15, lg = lane >> 4;
     const int r = xrow(i) + lr;
     if constexpr (FMT == FMT_E4M3) {
@@ -245,7 +295,7 @@ struct Pipe {
       }
     }
     load_x(st, 0, &f.x[0], f.sx[0]);
-    if constexpr (NSUB > 1) load_x(st, 1, &f.x[XW], f.sx[1]);
+    if constexpr (NSUB > 1 && XPD == 2) load_x(st, 1, &f.x[XW], f.sx[1]);
   }
 
   // MFMAs of one stage for the wave's first NSUB row subtiles.  X fragments
@@ -260,21 +310,32 @@ struct Pipe {
   // queue and hold up the wave's MFMA issue.
   template <int NSUB, int I, class H>
   __device__ __forceinline__ static void compute_from(const uint8_t* st, Frags& f, f32x4 (&acc)[MI][NJ],
-                                                      const float (&sw)[NJ], H& hook, uint4 (&xc)[XW],
-                                                      uint4 (&xnx)[XW], float& sc, float& snx) {
+                                                      const float (&sw)[NJ], H& hook, i32x4 (&xc)[XW],
+                                                      i32x4 (&xnx)[XW], float& sc, float& snx) {
     if constexpr (I < NSUB) {
       constexpr int i = I;
-      uint4 xn[XW];
+      i32x4 xn[XW];
       float sn = 0.f;
+      if constexpr (XPD == 2) {
 #pragma unroll
-      for (int q = 0; q < XW; ++q) xn[q] = xnx[q];
-      sn = snx;
-      if constexpr (i + 2 < NSUB) load_x(st, i + 2, xn, sn);
+        for (int q = 0; q < XW; ++q) xn[q] = xnx[q];
+        sn = snx;
+        if constexpr (i + 2 < NSUB) load_x(st, i + 2, xn, sn);
+      } else {
+#pragma unroll
+        for (int q = 0; q < XW; ++q) xn[q] = xc[q];
+        if constexpr (i + 1 < NSUB) load_x(st, i + 1, xn, sn);
+      }
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int j = 0; j < NJ; ++j) {
         if constexpr (FMT == FMT_BF16) {
-          acc[i][j] = mfma_bf16(f.w[j], xc[0], acc[i][j]);
+          if constexpr (ACC == ACC_AGPR)
+            mfma_bf16_acc(acc[i][j], f.w[j], xc[0]);
+          else if constexpr (ACC == ACC_TIED)
+            mfma_bf16_tied(acc[i][j], f.w[j], xc[0]);
+          else
+            acc[i][j] = mfma_bf16(f.w[j], xc[0], acc[i][j]);
         } else if constexpr (FMT == FMT_F32) {
           acc[i][j] = mfma_f32(__uint_as_float(f.w[j].x), __uint_as_float(xc[0].x), acc[i][j]);
           acc[i][j] = mfma_f32(__uint_as_float(f.w[j].y), __uint_as_float(xc[0].y), acc[i][j]);
@@ -292,10 +353,16 @@ struct Pipe {
       __builtin_amdgcn_sched_barrier(0);
       hook.template operator()<i>();
       __builtin_amdgcn_sched_barrier(0);
+      if constexpr (XPD == 2) {
 #pragma unroll
-      for (int q = 0; q < XW; ++q) { xc[q] = xnx[q]; xnx[q] = xn[q]; }
-      sc = snx;
-      snx = sn;
+        for (int q = 0; q < XW; ++q) { xc[q] = xnx[q]; xnx[q] = xn[q]; }
+        sc = snx;
+        snx = sn;
+      } else {
+#pragma unroll
+        for (int q = 0; q < XW; ++q) xc[q] = xn[q];
+        sc = sn;
+      }
       compute_from<NSUB, I + 1>(st, f, acc, sw, hook, xc, xnx, sc, snx);
     }
   }
@@ -307,11 +374,11 @@ struct Pipe {
   // previous subtile's products and its activation scale.
   template <int NSUB, int I, class H>
   __device__ __forceinline__ static void compute_fp8_from(const uint8_t* st, Frags& f, f32x4 (&acc)[MI][NJ],
-                                                          const float (&sw)[NJ], H& hook, uint4 (&xc)[XW],
-                                                          uint4 (&xnx)[XW], float& sc, float& snx,
+                                                          const float (&sw)[NJ], H& hook, i32x4 (&xc)[XW],
+                                                          i32x4 (&xnx)[XW], float& sc, float& snx,
                                                           f32x4 (&pp)[NJ], float& sp) {
     if constexpr (I <= NSUB) {
-      uint4 xn[XW];
+      i32x4 xn[XW];
       float sn = 0.f;
       if constexpr (I < NSUB) {
 #pragma unroll
@@ -363,13 +430,13 @@ struct Pipe {
   // psc) are carried into the next stage.  About 250 registers, so that two
   // waves can share a SIMD.
   struct FragsJ {
-    uint4 x[MI][2];
+    i32x4 x[MI][2];
     float sx[MI];
-    uint4 w[2][2];   // the stage's first two W subtiles
+    i32x4 w[2][2];   // the stage's first two W subtiles
   };
 
   template <int SPLIT>
-  __device__ __forceinline__ static void wfrag(const uint8_t* st, WRows<SPLIT> wr, int j, uint4 (&w)[2]) {
+  __device__ __forceinline__ static void wfrag(const uint8_t* st, WRows<SPLIT> wr, int j, i32x4 (&w)[2]) {
     const int lane = threadIdx.x & 63, lr = lane & 15, lg = lane >> 4;
     const uint8_t* wst = st + B_OFF + wr.base * SB;
     const int r = 16 * j + (j >= NJ / 2 ? SPLIT : 0) + lr;
@@ -388,10 +455,10 @@ struct Pipe {
   template <int NSUB, int J, int SPLIT, class H>
   __device__ __forceinline__ static void compute_jo_from(const uint8_t* st, WRows<SPLIT> wr, FragsJ& f,
                                                          f32x4 (&acc)[MI][NJ], const float (&sw)[NJ], H& hook,
-                                                         uint4 (&wc)[2], uint4 (&wn1)[2], f32x4 (&pp)[MI],
+                                                         i32x4 (&wc)[2], i32x4 (&wn1)[2], f32x4 (&pp)[MI],
                                                          float (&psc)[MI]) {
     if constexpr (J < NJ) {
-      uint4 wn2[2];
+      i32x4 wn2[2];
       if constexpr (J + 2 < NJ) wfrag(st, wr, J + 2, wn2);
       __builtin_amdgcn_sched_barrier(0);
       f32x4 pn[MI];
@@ -435,8 +502,8 @@ struct Pipe {
   __device__ __forceinline__ static void compute_jo(const uint8_t* st, WRows<SPLIT> wr, FragsJ& f,
                                                     f32x4 (&acc)[MI][NJ], const float (&sw)[NJ], H&& hook,
                                                     f32x4 (&pp)[MI], float (&psc)[MI]) {
-    uint4 wc[2] = {f.w[0][0], f.w[0][1]};
-    uint4 wn1[2] = {f.w[1][0], f.w[1][1]};
+    i32x4 wc[2] = {f.w[0][0], f.w[0][1]};
+    i32x4 wn1[2] = {f.w[1][0], f.w[1][1]};
     compute_jo_from<NSUB, 0>(st, wr, f, acc, sw, hook, wc, wn1, pp, psc);
   }
 
@@ -444,7 +511,7 @@ struct Pipe {
   template <int NSUB, class H>
   __device__ __forceinline__ static void compute(const uint8_t* st, Frags& f, f32x4 (&acc)[MI][NJ],
                                                  const float (&sw)[NJ], H&& hook) {
-    uint4 xc[XW], xnx[XW];
+    i32x4 xc[XW], xnx[XW];
     float sc = f.sx[0], snx = f.sx[1];
 #pragma unroll
     for (int q = 0; q < XW; ++q) { xc[q] = f.x[q]; xnx[q] = f.x[XW + q]; }
@@ -534,12 +601,15 @@ __device__ __forceinline__ void pipe_mainloop(const P& p, uint8_t* const (&st)[N
 }
 
 // ---------------------------------------------------------------------------
-// Wave-specialised paired pipeline (8 waves, 64-byte K-steps, a ring of 5
-// stage buffers, stage s in buffer s % 5).  Waves 4-7 only issue loads; waves
-// 0-3 only read fragments and run the MFMAs.  A wave that issues a load while
-// the memory pipeline is backed up stalls until the load is accepted; in a
-// wave that also issues the MFMAs, that stall idles the matrix core for as
-// long as the memory system is the bottleneck, serialising memory and math.
+// Wave-specialised paired pipeline (64-byte K-steps, a ring of 5 stage
+// buffers, stage s in buffer s % 5).  Waves 0 .. N_COMPUTE-1 only read
+// fragments and run the MFMAs; the waves after them only issue loads.  A wave
+// that issues a load while the CU's memory requests are backed up (it keeps a
+// bounded number in flight) stalls until the load is accepted; in a wave that
+// also issues the MFMAs, that stall idles the matrix core for as long as the
+// memory system is the bottleneck, serialising memory and math (measured:
+// loads alone and MFMAs alone add up to the time of a tile whose MFMA waves
+// issue their own loads).
 //
 // Per pair q (K-steps 2q, 2q+1), both roles pass two barriers:
 //   A_q  the MFMA waves are done with stage 2q: the loader refills the
@@ -585,10 +655,10 @@ __device__ __forceinline__ void ws_mfma_pairs(uint8_t* const (&st)[5], int q0, i
   if constexpr (Q + 1 < 5) ws_mfma_pairs<P, Q + 1, NSUB, GUARD>(st, q0, np, wr, f, acc);
 }
 
-// Returns on every wave; only waves 0-3 hold results in acc.  NSUB: the row
-// subtiles loaded (the most any wave row computes); NSUBC: those this wave
-// computes (one fewer for the second wave row when the tile's 16-row
-// subtiles are odd in number).
+// Returns on every wave; only the computing waves hold results in acc.
+// NSUB: the row subtiles loaded (the most any wave row computes); NSUBC:
+// those this wave computes (one fewer for a wave row whose last subtile is
+// past the tile's rows).
 template <class P, int NSUB, int NSUBC = NSUB, class WR>
 __device__ __forceinline__ void pipe_mainloop_ws(const P& p, uint8_t* const (&st)[5], int nk,
                                                  const WR& wr, f32x4 (&acc)[P::MI][P::NJ]) {
@@ -597,7 +667,7 @@ __device__ __forceinline__ void pipe_mainloop_ws(const P& p, uint8_t* const (&st
   constexpr int NL = P::template nl_for<NSUB>();
   static_assert(4 * NL < 64, "vmcnt range");
   const int np = nk / 2;
-  if (wave_id() >= 4) {
+  if (wave_id() >= P::N_COMPUTE) {
     p.template issue_pair_range<0, NL, NA>(st[0], st[1], 0);
     if (np > 1) {
       p.template issue_pair_range<0, NL, NA>(st[2], st[3], 2);
@@ -613,10 +683,104 @@ __device__ __forceinline__ void pipe_mainloop_ws(const P& p, uint8_t* const (&st
     block_barrier();
     typename P::Frags f;
     P::template prefetch<NSUBC>(st[0], wr, f);
+    if constexpr (P::ACCM != ACC_BUILTIN) acc_fence<P::ACCM == ACC_AGPR>(acc);
     int q = 0;
     for (; q + 5 <= np; q += 5) ws_mfma_pairs<P, 0, NSUBC, false>(st, q, np, wr, f, acc);
     if (q < np) ws_mfma_pairs<P, 0, NSUBC, true>(st, q, np, wr, f, acc);
+    if constexpr (P::ACCM != ACC_BUILTIN) acc_fence<P::ACCM == ACC_AGPR>(acc);
   }
+}
+
+// ---------------------------------------------------------------------------
+// Paired pipeline for 4 waves that both load and compute, each wave alone on
+// its SIMD with its accumulators in AGPRs (bf16, 256-row tiles: 8 x 8
+// accumulator subtiles = 256 AGPRs per wave).  64-byte K-steps, a ring of 5
+// stage buffers, stage s in buffer s % 5.  Per pair q (K-steps 2q, 2q+1):
+//   compute stage 2q, read stage 2q+1's first fragments;
+//   A_q  nobody reads stages 2q-1 and 2q any more;
+//   compute stage 2q+1, issuing pair q+2 into the buffers of stages 2q-1 and
+//        2q, a few loads after each row subtile's MFMAs;
+//   B_q  this wave's loads of pair q+1 are complete (vmcnt), so after the
+//        barrier they are complete for all: read stage 2q+2's fragments.
+// Pair q+2 has the MFMA time of K-steps 2q+1 .. 2q+3 to arrive.  Pairs past
+// the end of K are issued against empty resources (issue_pair_range_r), so
+// the loop carries no branch besides the guard of the last round.
+
+template <class P, int Q, int NSUB, int NSUBC, bool GUARD, class WR>
+__device__ __forceinline__ void pairs_step(const P& p, uint8_t* const (&st)[5], int q0, int np, const WR& wr,
+                                           typename P::Frags& f, f32x4 (&acc)[P::MI][P::NJ], rsrc_t none) {
+  constexpr int NA = P::template nia_for<NSUB>();
+  constexpr int NL = P::template nl_for<NSUB>();
+  const int q = q0 + Q;
+  if constexpr (GUARD) {
+    if (q >= np) return;
+  }
+  const float sw[P::NJ] = {};
+  P::template compute<NSUBC>(st[(2 * Q) % 5], f, acc, sw, []<int I>() {});
+  P::template prefetch<NSUBC>(st[(2 * Q + 1) % 5], wr, f);
+  block_barrier();   // A_q
+  const bool live = q + 2 < np;
+  const rsrc_t ra = live ? p.ra : none, rb = live ? p.rb : none;
+  uint8_t* const d0 = st[(2 * Q + 4) % 5];
+  uint8_t* const d1 = st[(2 * Q + 5) % 5];
+  if constexpr (NSUBC >= 2) {
+    // B_q comes before the last row subtile: the reads of stage 2q+2's first
+    // fragments (into fn) then run under that subtile's MFMAs instead of
+    // stalling every wave right after the barrier.
+    typename P::Frags fn;
+    P::template compute<NSUBC>(st[(2 * Q + 1) % 5], f, acc, sw, [&]<int I>() {
+      if constexpr (I + 1 < NSUBC) {
+        p.template issue_pair_range_r<I * NL / (NSUBC - 1), (I + 1) * NL / (NSUBC - 1), NA>(d0, d1, 2 * (q + 2), ra,
+                                                                                           rb);
+      }
+      if constexpr (I + 2 == NSUBC) {
+        wait_vm_lgkm0<2 * NL>();   // pair q+1
+        block_barrier();           // B_q
+        P::template prefetch<NSUBC>(st[(2 * Q + 2) % 5], wr, fn);
+      }
+    });
+    f = fn;
+  } else {
+    if constexpr (NSUBC == 0) {
+      p.template issue_pair_range_r<0, NL, NA>(d0, d1, 2 * (q + 2), ra, rb);
+    } else {
+      P::template compute<NSUBC>(st[(2 * Q + 1) % 5], f, acc, sw, [&]<int I>() {
+        p.template issue_pair_range_r<I * NL / NSUBC, (I + 1) * NL / NSUBC, NA>(d0, d1, 2 * (q + 2), ra, rb);
+      });
+    }
+    wait_vm_lgkm0<2 * NL>();   // pair q+1
+    block_barrier();           // B_q
+    P::template prefetch<NSUBC>(st[(2 * Q + 2) % 5], wr, f);
+  }
+  if constexpr (Q + 1 < 5) pairs_step<P, Q + 1, NSUB, NSUBC, GUARD>(p, st, q0, np, wr, f, acc, none);
+}
+
+// NSUB: the row subtiles loaded (the most any wave row computes); NSUBC:
+// those this wave computes.  acc must be zero on entry.
+template <class P, int NSUB, int NSUBC = NSUB, class WR>
+__device__ __forceinline__ void pipe_mainloop_pairs(const P& p, uint8_t* const (&st)[5], int nk, const WR& wr,
+                                                    f32x4 (&acc)[P::MI][P::NJ]) {
+  static_assert(P::SB == 64, "pairs of 64-byte K-steps");
+  constexpr int NA = P::template nia_for<NSUB>();
+  constexpr int NL = P::template nl_for<NSUB>();
+  static_assert(4 * NL < 64, "vmcnt range");
+  const int np = nk / 2;
+  const rsrc_t none = make_rsrc(nullptr, 0);
+  p.template issue_pair_range_r<0, NL, NA>(st[0], st[1], 0, p.ra, p.rb);
+  p.template issue_pair_range_r<0, NL, NA>(st[2], st[3], 2, np > 1 ? p.ra : none, np > 1 ? p.rb : none);
+  wait_vm_lgkm0<2 * NL>();   // pair 0
+  block_barrier();
+  typename P::Frags f;
+  P::template prefetch<NSUBC>(st[0], wr, f);
+  if constexpr (P::ACCM != ACC_BUILTIN) acc_fence<P::ACCM == ACC_AGPR>(acc);
+  int q = 0;
+  for (; q + 5 <= np; q += 5) pairs_step<P, 0, NSUB, NSUBC, false>(p, st, q, np, wr, f, acc, none);
+  if (q < np) pairs_step<P, 0, NSUB, NSUBC, true>(p, st, q, np, wr, f, acc, none);
+  if constexpr (P::ACCM != ACC_BUILTIN) acc_fence<P::ACCM == ACC_AGPR>(acc);
+  // every load (the empty ones included) has landed before the block's LDS
+  // can be released
+  wait_vm_lgkm0<0>();
+  block_barrier();
 }
 
 // ---------------------------------------------------------------------------

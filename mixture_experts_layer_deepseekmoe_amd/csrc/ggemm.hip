@@ -15,7 +15,7 @@
 //           per 128 columns, quantised in the epilogue.
 // down:     Y[r, c] = H_r . Wd[c], stored bf16 (fp32 on the fp32 path).
 //
-// Tiles: BM rows (192; 128 on the FP8 and fp32 paths) x 256 W rows (gate/up: 128 gate + 128 up rows = 128 h columns; down:
+// Tiles: BM rows (256; 128 on the FP8 and fp32 paths) x 256 W rows (gate/up: 128 gate + 128 up rows = 128 h columns; down:
 // 256 output columns).  Blocks are mapped to XCDs so that each XCD walks a
 // contiguous run of the tile list (expert-major): the tiles of one expert run
 // together on one XCD and share its L2 for the expert's weights and gathered
@@ -32,16 +32,24 @@ constexpr int NXCD = 8;
 
 template <int FMT>
 struct GG {
-  // bf16: 192 rows (an MFMA wave holds 6 x 8 accumulator subtiles = 192
-  // VGPRs), the wave-specialised paired pipeline on a ring of 5 stage
-  // buffers.  FP8: 128 rows, the wave-specialised FP8 pipeline on a ring of 3
-  // (128-byte K-steps).  fp32 (only small layers): 128 rows, the single-stage
-  // pipeline on 5.
-  static constexpr int BM = FMT == FMT_BF16 ? 192 : 128;
+  // bf16: 256 rows, 8 MFMA waves (two per SIMD) laid out 2 x 4 (128 rows x
+  // 64 W rows each: 8 x 4 accumulator subtiles) + 4 load waves, the
+  // wave-specialised paired pipeline on a ring of 5 stage buffers (5 x 32
+  // KB: all of the LDS).  Three waves per SIMD leave an MFMA wave 168
+  // registers.  FP8: 128 rows, 4 MFMA waves (2 x 2) + 4 load waves, the
+  // wave-specialised FP8 pipeline on a ring of 3 (128-byte K-steps).  fp32
+  // (only small layers): 128 rows, 4 waves (2 x 2) that load and compute, the
+  // single-stage pipeline on 5.
+  static constexpr int BM = FMT == FMT_BF16 ? 256 : 128;
   static constexpr int NST = FMT == FMT_E4M3 ? 3 : 5;
-  // bf16 and FP8: 4 MFMA waves + 4 load waves; fp32: 4 waves doing both
-  static constexpr int THREADS = FMT == FMT_F32 ? 256 : 512;
-  using P = Pipe<FMT, BM, BNW, NST, 2>;   // 2 x 2 MFMA waves
+  static constexpr int THREADS = FMT == FMT_BF16 ? 768 : (FMT == FMT_E4M3 ? 512 : 256);
+  static constexpr int WM = 2;                          // wave rows
+  static constexpr int NW = FMT == FMT_BF16 ? 8 : 4;   // computing waves
+  static constexpr int LW = 4;                          // loading waves
+  // bf16 accumulates in place through asm: with 128 accumulators in a
+  // 168-register budget the builtin's accumulators get rotated and spilled
+  using P = Pipe<FMT, BM, BNW, NST, WM, FMT == FMT_BF16 ? ACC_TIED : ACC_BUILTIN, NW, LW>;
+  static constexpr int HW = 8 * P::NJ;                  // gate/up: h columns per wave
 };
 
 // make_pipe() returns the tile's initialised Pipe (the loads' per-lane
@@ -107,25 +115,32 @@ __device__ __forceinline__ Ring<NST> make_ring(uint8_t* a, uint8_t* b, uint8_t* 
 }
 
 // Calls f.template operator()<NSUB>() with NSUB = the number of row subtiles
-// each of the two wave rows computes: ceil(rows / 32), 1 .. MI.
-template <int MI, int N = 1, class F>
+// the first of the WM wave rows computes: ceil(rows / (16 WM)), 1 .. MI.
+template <int MI, int WM, int N = 1, class F>
 __device__ __forceinline__ void dispatch_rows(int rows, F&& f) {
   if constexpr (N >= MI) {
     f.template operator()<MI>();
   } else {
-    if (rows <= 32 * N)
+    if (rows <= 16 * WM * N)
       f.template operator()<N>();
     else
-      dispatch_rows<MI, N + 1>(rows, f);
+      dispatch_rows<MI, WM, N + 1>(rows, f);
   }
 }
 
-// bf16: a tile with an odd number of 16-row subtiles leaves the second wave
-// row (wm = 1) one subtile short; its waves compute one fewer instead of a
-// subtile of padding (the loads still cover the first wave row's rows).
+// bf16: wave row wm computes the tile's 16-row subtiles wm, wm + WM, ...; when
+// the last of them is past the tile's rows, its waves compute one fewer than
+// the first wave row instead of a subtile of padding (the loads still cover
+// the first wave row's rows).
 template <int FMT>
-__device__ __forceinline__ bool odd_second_row(int rows) {
-  return FMT == FMT_BF16 && (wave_id() & 1) && (((rows + 15) / 16) & 1);
+__device__ __forceinline__ bool short_wave_row(int rows) {
+  if constexpr (FMT != FMT_BF16) {
+    return false;
+  } else {
+    constexpr int WM = GG<FMT>::WM;
+    const int s = (rows + 15) / 16, nsub = (s + WM - 1) / WM;
+    return wave_id() % WM + WM * (nsub - 1) >= s;
+  }
 }
 
 // ------------------------------------------------------------------ gate/up
@@ -137,27 +152,30 @@ __device__ __forceinline__ void gateup_tile(const GateUpArgs& a, const MK& make_
   using P = typename GG<FMT>::P;
   const int w = wave_id(), lane = threadIdx.x & 63;
   const int lr = lane & 15, lg = lane >> 4;
-  const int wm = w & 1, wn = w >> 1;
-  // wave (wm, wn): h columns 64 wn .. 64 wn + 63 of the tile -- gate subtiles
-  // 0-3 and the matching up subtiles 4-7 -- on row subtiles wm, wm+2, ...
-  const WRows<64> wr{64 * wn};
+  constexpr int WM = GG<FMT>::WM, HW = GG<FMT>::HW, NJ2 = P::NJ / 2;
+  const int wm = w % WM, wn = w / WM;
+  // wave (wm, wn): h columns HW wn .. HW wn + HW - 1 of the tile -- gate
+  // subtiles 0 .. NJ/2-1 and the matching up subtiles NJ/2 .. NJ-1 (gate rows
+  // 0-127 of the stage, up rows 128-255) -- on row subtiles wm, wm + WM, ...
+  const WRows<128 - HW> wr{HW * wn};
   f32x4 acc[P::MI][P::NJ];
   zero_acc(acc);
   gg_mainloop<FMT, NSUB, NSUBC>(make_pipe, st, nk, wr, acc, swl, kb);
-  // the load waves hold no results (the FP8 epilogue keeps them for its barrier)
-  if (FMT != FMT_E4M3 && GG<FMT>::THREADS > 256 && w >= 4) return;
+  // the load-only waves hold no results (the FP8 epilogue keeps them for its
+  // barrier)
+  if (FMT != FMT_E4M3 && w >= GG<FMT>::NW) return;
 
   if constexpr (FMT != FMT_E4M3) {
 #pragma unroll
     for (int i = 0; i < NSUBC; ++i) {
-      const int row = 16 * (2 * i + wm) + lr;
+      const int row = 16 * (WM * i + wm) + lr;
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const int col = n0 + 64 * wn + 16 * jj + 4 * lg;
+      for (int jj = 0; jj < NJ2; ++jj) {
+        const int col = n0 + HW * wn + 16 * jj + 4 * lg;
         if (row < rows && col < a.inter) {
           float h[4];
 #pragma unroll
-          for (int r = 0; r < 4; ++r) h[r] = silu_f32(acc[i][jj][r]) * acc[i][jj + 4][r];
+          for (int r = 0; r < 4; ++r) h[r] = silu_f32(acc[i][jj][r]) * acc[i][jj + NJ2][r];
           const size_t o = static_cast<size_t>(row0 + row) * a.inter + col;
           if constexpr (FMT == FMT_F32) {
             *reinterpret_cast<float4*>(static_cast<float*>(a.h) + o) = make_float4(h[0], h[1], h[2], h[3]);
@@ -173,22 +191,22 @@ __device__ __forceinline__ void gateup_tile(const GateUpArgs& a, const MK& make_
     // 1x128 quantisation of h along I: the 128 columns of this tile are one
     // scale group.  A row's amax is reduced over its lane's 16 values, the 4
     // lane groups, then the two waves (wn = 0, 1) that share the row.
-    float hv[NSUBC][4][4];
+    float hv[NSUBC][NJ2][4];
     const bool mw = w < 4;   // an MFMA wave
     if (mw) {
 #pragma unroll
       for (int i = 0; i < NSUBC; ++i) {
         float m = 0.f;
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj)
+        for (int jj = 0; jj < NJ2; ++jj)
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            hv[i][jj][r] = silu_f32(acc[i][jj][r]) * acc[i][jj + 4][r];
+            hv[i][jj][r] = silu_f32(acc[i][jj][r]) * acc[i][jj + NJ2][r];
             m = fmaxf(m, fabsf(hv[i][jj][r]));
           }
         m = fmaxf(m, __shfl_xor(m, 16));
         m = fmaxf(m, __shfl_xor(m, 32));
-        if (lg == 0) red[wn][16 * (2 * i + wm) + lr] = m;
+        if (lg == 0) red[wn][16 * (WM * i + wm) + lr] = m;
       }
     }
     __syncthreads();
@@ -196,14 +214,14 @@ __device__ __forceinline__ void gateup_tile(const GateUpArgs& a, const MK& make_
     const int ncb = a.inter / 128;
 #pragma unroll
     for (int i = 0; i < NSUBC; ++i) {
-      const int row = 16 * (2 * i + wm) + lr;
+      const int row = 16 * (WM * i + wm) + lr;
       if (row < rows) {
         const float m = fmaxf(red[0][row], red[1][row]);
         const float inv = m == 0.f ? 0.f : 448.f / m;
         const size_t grow = static_cast<size_t>(row0 + row);
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          const int col = n0 + 64 * wn + 16 * jj + 4 * lg;
+        for (int jj = 0; jj < NJ2; ++jj) {
+          const int col = n0 + HW * wn + 16 * jj + 4 * lg;
           uint32_t q = 0;
 #pragma unroll
           for (int r = 0; r < 4; ++r) q |= f32_to_e4m3(hv[i][jj][r] * inv) << (8 * r);
@@ -220,8 +238,16 @@ __global__ __launch_bounds__(GG<FMT>::THREADS, 1) void gateup_kernel(GateUpArgs 
   using P = typename GG<FMT>::P;
   constexpr int NST = GG<FMT>::NST, BM = GG<FMT>::BM;
   MOE_STAGE_RING(P, NST)
-  __shared__ float red[FMT == FMT_E4M3 ? 2 : 1][BM];
-  __shared__ float swl[FMT == FMT_E4M3 ? 2 * MAX_KB : 1];
+  // FP8 only: the epilogue's row-amax exchange and the weight-block scales
+  // (the bf16 ring takes all of the LDS)
+  float (*red)[BM] = nullptr;
+  float* swl = nullptr;
+  if constexpr (FMT == FMT_E4M3) {
+    __shared__ float red_s[2][BM];
+    __shared__ float swl_s[2 * MAX_KB];
+    red = red_s;
+    swl = swl_s;
+  }
 
   const int nb_n = ceil_div(a.inter, GG_HCOLS);
   const int q = xcd_tile(*a.mt_count * nb_n);
@@ -273,8 +299,8 @@ __global__ __launch_bounds__(GG<FMT>::THREADS, 1) void gateup_kernel(GateUpArgs 
   const Ring<NST> ring = make_ring<NST>(st0, st1, st2, st3, st4);
   const float* sw = FMT == FMT_E4M3 ? swl : nullptr;
   // the K loop instantiated for the tile's valid rows, in 32-row steps
-  const bool short_row = odd_second_row<FMT>(rows);
-  dispatch_rows<P::MI>(rows, [&]<int NSUB>() {
+  const bool short_row = short_wave_row<FMT>(rows);
+  dispatch_rows<P::MI, GG<FMT>::WM>(rows, [&]<int NSUB>() {
     if (short_row)
       gateup_tile<FMT, NSUB, (FMT == FMT_BF16 ? NSUB - 1 : NSUB)>(a, make_pipe, ring.s, sw, kb, nk, row0, rows, n0, nb,
                                                                   red);
@@ -291,20 +317,21 @@ __device__ __forceinline__ void down_tile(const DownArgs& a, const MK& make_pipe
   using P = typename GG<FMT>::P;
   const int w = wave_id(), lane = threadIdx.x & 63;
   const int lr = lane & 15, lg = lane >> 4;
-  const int wm = w & 1, wn = w >> 1;
-  // wave (wm, wn): output columns 128 wn .. 128 wn + 127 of the tile (one
-  // 128-wide weight scale block), row subtiles wm, wm+2, ...
-  const WRows<0> wr{128 * wn};
+  constexpr int WM = GG<FMT>::WM;
+  const int wm = w % WM, wn = w / WM;
+  // wave (wm, wn): output columns 16 NJ wn .. 16 NJ (wn + 1) - 1 of the tile
+  // (FP8: 128 columns, one weight scale block), row subtiles wm, wm + WM, ...
+  const WRows<0> wr{16 * P::NJ * wn};
   f32x4 acc[P::MI][P::NJ];
   zero_acc(acc);
   gg_mainloop<FMT, NSUB, NSUBC>(make_pipe, st, nk, wr, acc, FMT == FMT_E4M3 ? swl + wn * kb : nullptr, 0);
-  if (GG<FMT>::THREADS > 256 && w >= 4) return;   // load waves
+  if (w >= GG<FMT>::NW) return;   // FP8: the load-only waves
 #pragma unroll
   for (int i = 0; i < NSUBC; ++i) {
-    const int row = 16 * (2 * i + wm) + lr;
+    const int row = 16 * (WM * i + wm) + lr;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int col = n0 + 128 * wn + 16 * j + 4 * lg;
+    for (int j = 0; j < P::NJ; ++j) {
+      const int col = n0 + 16 * P::NJ * wn + 16 * j + 4 * lg;
       if (row < rows && col < a.d) {
         const size_t o = static_cast<size_t>(row0 + row) * a.d + col;
         if constexpr (FMT == FMT_F32) {
@@ -325,7 +352,11 @@ __global__ __launch_bounds__(GG<FMT>::THREADS, 1) void down_kernel(DownArgs a) {
   using P = typename GG<FMT>::P;
   constexpr int NST = GG<FMT>::NST;
   MOE_STAGE_RING(P, NST)
-  __shared__ float swl[FMT == FMT_E4M3 ? 2 * MAX_KB : 1];
+  float* swl = nullptr;   // FP8 only: the weight-block scales
+  if constexpr (FMT == FMT_E4M3) {
+    __shared__ float swl_s[2 * MAX_KB];
+    swl = swl_s;
+  }
 
   const int nb_n = ceil_div(a.d, BNW);
   const int q = xcd_tile(*a.mt_count * nb_n);
@@ -374,8 +405,8 @@ __global__ __launch_bounds__(GG<FMT>::THREADS, 1) void down_kernel(DownArgs a) {
 
   const Ring<NST> ring = make_ring<NST>(st0, st1, st2, st3, st4);
   const float* sw = FMT == FMT_E4M3 ? swl : nullptr;
-  const bool short_row = odd_second_row<FMT>(rows);
-  dispatch_rows<P::MI>(rows, [&]<int NSUB>() {
+  const bool short_row = short_wave_row<FMT>(rows);
+  dispatch_rows<P::MI, GG<FMT>::WM>(rows, [&]<int NSUB>() {
     if (short_row)
       down_tile<FMT, NSUB, (FMT == FMT_BF16 ? NSUB - 1 : NSUB)>(a, make_pipe, ring.s, sw, kb, nk, row0, rows, n0);
     else

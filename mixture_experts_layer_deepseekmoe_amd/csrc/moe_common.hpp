@@ -9,6 +9,7 @@ namespace moe {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 // Element formats handled by the kernels.
@@ -63,9 +64,41 @@ __device__ __forceinline__ uint32_t f32_to_e4m3(float x) {
 // assignment gives the exact dot products.  Output: lane l holds rows
 // 4*(l >> 4) + r, r = 0..3, of column (l & 15).
 
-__device__ __forceinline__ f32x4 mfma_bf16(const uint4 a, const uint4 b, f32x4 c) {
+__device__ __forceinline__ f32x4 mfma_bf16(const i32x4 a, const i32x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b),
                                                  c, 0, 0, 0);
+}
+
+// The same product accumulated in place (acc tied to the MFMA's destination)
+// in AGPRs (mfma_bf16_acc) or VGPRs (mfma_bf16_tied).  Written through the
+// builtin, accumulators under register pressure are rotated through other
+// registers and copies, or spilled.  The compiler does not see these as
+// MFMAs, so the code around them keeps the hazard distances itself:
+// acc_fence() before the first and after the last such MFMA, and a VALU
+// write of an operand is kept two wait states away by the s_nop in front.
+__device__ __forceinline__ void mfma_bf16_acc(f32x4& acc, const i32x4 a, const i32x4 b) {
+  asm volatile("s_nop 1\n\tv_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_bf16_tied(f32x4& acc, const i32x4 a, const i32x4 b) {
+  asm volatile("s_nop 1\n\tv_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
+}
+
+// Pins the accumulators in AGPRs at this point and waits out the MFMA
+// dependency distances (at most 19 wait states on gfx950 for an 8-pass MFMA
+// result read by VALU, 2 for a VALU write read by an MFMA).
+template <bool AGPR, int MI, int NJ>
+__device__ __forceinline__ void acc_fence(f32x4 (&acc)[MI][NJ]) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+#pragma unroll
+  for (int i = 0; i < MI; ++i)
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      if constexpr (AGPR)
+        asm volatile("" : "+a"(acc[i][j]));
+      else
+        asm volatile("" : "+v"(acc[i][j]));
+    }
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
 }
 
 // 16x16x128 OCP-e4m3 product with unit block scales (scale operands of zero
