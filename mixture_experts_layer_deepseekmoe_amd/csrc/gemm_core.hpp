@@ -4,27 +4,25 @@
 // Data movement: every K-step ("stage") moves SB bytes of K per row (64 bytes
 // = 32 bf16 / 16 fp32, or 128 bytes = 128 e4m3) straight from global memory
 // into LDS with buffer_load_dwordx4 ... lds (no register staging).  NST stage
-// buffers form a ring; loads run NST-2 stages ahead of the MFMAs.  Each stage
-// buffer is its own __shared__ object, so the compiler's wait insertion can
-// tell the asynchronous LDS writes of one stage from the reads of another; the
-// waits on the asynchronous loads are explicit (vmcnt), and the per-stage
-// barrier is a bare s_barrier.
+// buffers form a ring and the loads run ahead of the MFMAs.  The DMA is
+// issued through asm and the pipelines order it against the fragment reads
+// themselves: explicit vmcnt waits by the loading waves, then a bare
+// s_barrier.
 //
 // LDS layout: rows of SB bytes, unpadded; the 16-byte chunk j of row r sits at
 // position j ^ swz(r), which makes the MFMA fragment reads bank-conflict free
 // (see swz below).  The loader picks, for each lane, the global chunk that
 // belongs at the LDS position the DMA writes it to.
 //
-// Compute: block = 4 waves laid out WM x (4/WM).  A wave owns NJ = BNW*WM/64
-// column subtiles of W (16 W rows each, offsets chosen by the caller) and
-// every WM-th 16-row subtile of X starting at subtile wm = w % WM, so short
-// tiles stay balanced across the wave rows.  The MFMA's first operand is the
-// W fragment, its second the X fragment, so a lane's four accumulators are
-// four consecutive output columns of one X row (row lane & 15 of a subtile).
-// The K loop is instantiated for NSUB = number of the wave's leading row
-// subtiles to compute, so a short expert group issues MFMAs only for its rows
-// and the loop carries no branches.  2 x 2 (128 x 128 per wave) reads 20%
-// fewer LDS bytes per MFMA than 1 x 4 and measured ~40% faster on gfx950.
+// Compute: NW computing waves laid out WM x (NW/WM).  A wave owns NJ =
+// BNW*WM/(16 NW) column subtiles of W (16 W rows each, offsets chosen by the
+// caller) and every WM-th 16-row subtile of X starting at subtile wm = w % WM,
+// so short tiles stay balanced across the wave rows.  The MFMA's first
+// operand is the W fragment, its second the X fragment, so a lane's four
+// accumulators are four consecutive output columns of one X row (row
+// lane & 15 of a subtile).  The K loop is instantiated for NSUB = number of
+// the wave's leading row subtiles to compute, so a short expert group issues
+// MFMAs only for its rows and the loop carries no branches.
 //
 // FP8 (OCP e4m3): a stage is exactly one 128-wide scale block along K; each
 // 16x16x128 product is formed from zero and promoted into the fp32
@@ -113,9 +111,9 @@ struct WRows {
 
 // NW waves compute, laid out WM x (NW / WM); LW waves issue the loads (the
 // same waves, or as many load-only waves).
-// ACC: how the bf16 MFMAs accumulate -- ACC_BUILTIN, or in place through asm
-// in VGPRs (ACC_TIED) or AGPRs (ACC_AGPR).
-enum : int { ACC_BUILTIN = 0, ACC_TIED = 1, ACC_AGPR = 2 };
+// ACC: how the bf16 MFMAs accumulate -- through the builtin (ACC_BUILTIN) or
+// in place through asm (ACC_TIED).
+enum : int { ACC_BUILTIN = 0, ACC_TIED = 1 };
 template <int FMT, int BM, int BNW, int NST, int WM = 1, int ACC = ACC_BUILTIN, int NW = 4, int LW = NW>
 struct Pipe {
   static constexpr int SB = FMT == FMT_E4M3 ? 128 : 64;
@@ -219,27 +217,6 @@ struct Pipe {
     }
   }
 
-  // The same with the loads of a pair past the end of K (live == false)
-  // issued against empty buffer resources: they fetch nothing and write zeros
-  // to stage buffers nobody reads, so a pipeline need not branch around them.
-  template <int Q, int NA>
-  __device__ __forceinline__ void issue_one_r(uint8_t* st, int ks, rsrc_t a, rsrc_t b) const {
-    const int w = wave_id() % LW;
-    const uint32_t kofs = static_cast<uint32_t>(ks) * SB;
-    if constexpr (Q < NA)
-      dma16(a, oa[Q], kofs, st + A_OFF + RPI * (w + LW * Q) * SB);
-    else
-      dma16(b, ob[Q - NA], kofs, st + B_OFF + RPI * (w + LW * (Q - NA)) * SB);
-  }
-  template <int LO, int HI, int NA>
-  __device__ __forceinline__ void issue_pair_range_r(uint8_t* st0, uint8_t* st1, int ks, rsrc_t a, rsrc_t b) const {
-    if constexpr (LO < HI) {
-      issue_one_r<LO, NA>(st0, ks, a, b);
-      issue_one_r<LO, NA>(st1, ks + 1, a, b);
-      issue_pair_range_r<LO + 1, HI, NA>(st0, st1, ks, a, b);
-    }
-  }
-
   // One 128-bit LDS read.  Fragments are vector values (i32x4), not i32x4
   // structs: a struct is split into four 32-bit loads that the backend merges
   // again, and the merged read loses the LDS object's alias information; the
@@ -330,9 +307,7 @@ struct Pipe {
 #pragma unroll
       for (int j = 0; j < NJ; ++j) {
         if constexpr (FMT == FMT_BF16) {
-          if constexpr (ACC == ACC_AGPR)
-            mfma_bf16_acc(acc[i][j], f.w[j], xc[0]);
-          else if constexpr (ACC == ACC_TIED)
+          if constexpr (ACC == ACC_TIED)
             mfma_bf16_tied(acc[i][j], f.w[j], xc[0]);
           else
             acc[i][j] = mfma_bf16(f.w[j], xc[0], acc[i][j]);
@@ -683,104 +658,12 @@ __device__ __forceinline__ void pipe_mainloop_ws(const P& p, uint8_t* const (&st
     block_barrier();
     typename P::Frags f;
     P::template prefetch<NSUBC>(st[0], wr, f);
-    if constexpr (P::ACCM != ACC_BUILTIN) acc_fence<P::ACCM == ACC_AGPR>(acc);
+    if constexpr (P::ACCM == ACC_TIED) acc_fence(acc);
     int q = 0;
     for (; q + 5 <= np; q += 5) ws_mfma_pairs<P, 0, NSUBC, false>(st, q, np, wr, f, acc);
     if (q < np) ws_mfma_pairs<P, 0, NSUBC, true>(st, q, np, wr, f, acc);
-    if constexpr (P::ACCM != ACC_BUILTIN) acc_fence<P::ACCM == ACC_AGPR>(acc);
+    if constexpr (P::ACCM == ACC_TIED) acc_fence(acc);
   }
-}
-
-// ---------------------------------------------------------------------------
-// Paired pipeline for 4 waves that both load and compute, each wave alone on
-// its SIMD with its accumulators in AGPRs (bf16, 256-row tiles: 8 x 8
-// accumulator subtiles = 256 AGPRs per wave).  64-byte K-steps, a ring of 5
-// stage buffers, stage s in buffer s % 5.  Per pair q (K-steps 2q, 2q+1):
-//   compute stage 2q, read stage 2q+1's first fragments;
-//   A_q  nobody reads stages 2q-1 and 2q any more;
-//   compute stage 2q+1, issuing pair q+2 into the buffers of stages 2q-1 and
-//        2q, a few loads after each row subtile's MFMAs;
-//   B_q  this wave's loads of pair q+1 are complete (vmcnt), so after the
-//        barrier they are complete for all: read stage 2q+2's fragments.
-// Pair q+2 has the MFMA time of K-steps 2q+1 .. 2q+3 to arrive.  Pairs past
-// the end of K are issued against empty resources (issue_pair_range_r), so
-// the loop carries no branch besides the guard of the last round.
-
-template <class P, int Q, int NSUB, int NSUBC, bool GUARD, class WR>
-__device__ __forceinline__ void pairs_step(const P& p, uint8_t* const (&st)[5], int q0, int np, const WR& wr,
-                                           typename P::Frags& f, f32x4 (&acc)[P::MI][P::NJ], rsrc_t none) {
-  constexpr int NA = P::template nia_for<NSUB>();
-  constexpr int NL = P::template nl_for<NSUB>();
-  const int q = q0 + Q;
-  if constexpr (GUARD) {
-    if (q >= np) return;
-  }
-  const float sw[P::NJ] = {};
-  P::template compute<NSUBC>(st[(2 * Q) % 5], f, acc, sw, []<int I>() {});
-  P::template prefetch<NSUBC>(st[(2 * Q + 1) % 5], wr, f);
-  block_barrier();   // A_q
-  const bool live = q + 2 < np;
-  const rsrc_t ra = live ? p.ra : none, rb = live ? p.rb : none;
-  uint8_t* const d0 = st[(2 * Q + 4) % 5];
-  uint8_t* const d1 = st[(2 * Q + 5) % 5];
-  if constexpr (NSUBC >= 2) {
-    // B_q comes before the last row subtile: the reads of stage 2q+2's first
-    // fragments (into fn) then run under that subtile's MFMAs instead of
-    // stalling every wave right after the barrier.
-    typename P::Frags fn;
-    P::template compute<NSUBC>(st[(2 * Q + 1) % 5], f, acc, sw, [&]<int I>() {
-      if constexpr (I + 1 < NSUBC) {
-        p.template issue_pair_range_r<I * NL / (NSUBC - 1), (I + 1) * NL / (NSUBC - 1), NA>(d0, d1, 2 * (q + 2), ra,
-                                                                                           rb);
-      }
-      if constexpr (I + 2 == NSUBC) {
-        wait_vm_lgkm0<2 * NL>();   // pair q+1
-        block_barrier();           // B_q
-        P::template prefetch<NSUBC>(st[(2 * Q + 2) % 5], wr, fn);
-      }
-    });
-    f = fn;
-  } else {
-    if constexpr (NSUBC == 0) {
-      p.template issue_pair_range_r<0, NL, NA>(d0, d1, 2 * (q + 2), ra, rb);
-    } else {
-      P::template compute<NSUBC>(st[(2 * Q + 1) % 5], f, acc, sw, [&]<int I>() {
-        p.template issue_pair_range_r<I * NL / NSUBC, (I + 1) * NL / NSUBC, NA>(d0, d1, 2 * (q + 2), ra, rb);
-      });
-    }
-    wait_vm_lgkm0<2 * NL>();   // pair q+1
-    block_barrier();           // B_q
-    P::template prefetch<NSUBC>(st[(2 * Q + 2) % 5], wr, f);
-  }
-  if constexpr (Q + 1 < 5) pairs_step<P, Q + 1, NSUB, NSUBC, GUARD>(p, st, q0, np, wr, f, acc, none);
-}
-
-// NSUB: the row subtiles loaded (the most any wave row computes); NSUBC:
-// those this wave computes.  acc must be zero on entry.
-template <class P, int NSUB, int NSUBC = NSUB, class WR>
-__device__ __forceinline__ void pipe_mainloop_pairs(const P& p, uint8_t* const (&st)[5], int nk, const WR& wr,
-                                                    f32x4 (&acc)[P::MI][P::NJ]) {
-  static_assert(P::SB == 64, "pairs of 64-byte K-steps");
-  constexpr int NA = P::template nia_for<NSUB>();
-  constexpr int NL = P::template nl_for<NSUB>();
-  static_assert(4 * NL < 64, "vmcnt range");
-  const int np = nk / 2;
-  const rsrc_t none = make_rsrc(nullptr, 0);
-  p.template issue_pair_range_r<0, NL, NA>(st[0], st[1], 0, p.ra, p.rb);
-  p.template issue_pair_range_r<0, NL, NA>(st[2], st[3], 2, np > 1 ? p.ra : none, np > 1 ? p.rb : none);
-  wait_vm_lgkm0<2 * NL>();   // pair 0
-  block_barrier();
-  typename P::Frags f;
-  P::template prefetch<NSUBC>(st[0], wr, f);
-  if constexpr (P::ACCM != ACC_BUILTIN) acc_fence<P::ACCM == ACC_AGPR>(acc);
-  int q = 0;
-  for (; q + 5 <= np; q += 5) pairs_step<P, 0, NSUB, NSUBC, false>(p, st, q, np, wr, f, acc, none);
-  if (q < np) pairs_step<P, 0, NSUB, NSUBC, true>(p, st, q, np, wr, f, acc, none);
-  if constexpr (P::ACCM != ACC_BUILTIN) acc_fence<P::ACCM == ACC_AGPR>(acc);
-  // every load (the empty ones included) has landed before the block's LDS
-  // can be released
-  wait_vm_lgkm0<0>();
-  block_barrier();
 }
 
 // ---------------------------------------------------------------------------

@@ -69,35 +69,27 @@ __device__ __forceinline__ f32x4 mfma_bf16(const i32x4 a, const i32x4 b, f32x4 c
                                                  c, 0, 0, 0);
 }
 
-// The same product accumulated in place (acc tied to the MFMA's destination)
-// in AGPRs (mfma_bf16_acc) or VGPRs (mfma_bf16_tied).  Written through the
-// builtin, accumulators under register pressure are rotated through other
-// registers and copies, or spilled.  The compiler does not see these as
-// MFMAs, so the code around them keeps the hazard distances itself:
-// acc_fence() before the first and after the last such MFMA, and a VALU
-// write of an operand is kept two wait states away by the s_nop in front.
-__device__ __forceinline__ void mfma_bf16_acc(f32x4& acc, const i32x4 a, const i32x4 b) {
-  asm volatile("s_nop 1\n\tv_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
-}
+// The same product accumulated in place (acc tied to the MFMA's destination).
+// Written through the builtin, accumulators under register pressure are
+// rotated through other registers and copies, or spilled.  The compiler does
+// not see this as an MFMA, so the code around it keeps the hazard distances
+// itself: acc_fence() before the first and after the last such MFMA, and a
+// VALU write of an operand is kept two wait states away by the s_nop in
+// front.
 __device__ __forceinline__ void mfma_bf16_tied(f32x4& acc, const i32x4 a, const i32x4 b) {
   asm volatile("s_nop 1\n\tv_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
 }
 
-// Pins the accumulators in AGPRs at this point and waits out the MFMA
+// Pins the accumulators in registers at this point and waits out the MFMA
 // dependency distances (at most 19 wait states on gfx950 for an 8-pass MFMA
 // result read by VALU, 2 for a VALU write read by an MFMA).
-template <bool AGPR, int MI, int NJ>
+template <int MI, int NJ>
 __device__ __forceinline__ void acc_fence(f32x4 (&acc)[MI][NJ]) {
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
 #pragma unroll
   for (int i = 0; i < MI; ++i)
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      if constexpr (AGPR)
-        asm volatile("" : "+a"(acc[i][j]));
-      else
-        asm volatile("" : "+v"(acc[i][j]));
-    }
+    for (int j = 0; j < NJ; ++j) asm volatile("" : "+v"(acc[i][j]));
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
 }
 
