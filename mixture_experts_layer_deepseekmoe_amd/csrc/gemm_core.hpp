@@ -141,6 +141,12 @@ struct Pipe {
   uint32_t oa[NIA];   // per-lane byte offsets of the lane's 16-byte piece, K-step 0
   uint32_t ob[NIB];
   uint32_t os;
+  // K-step ks of the loop loads K-step (ks + krot) mod nks: tiles that read
+  // the same rows start at different points of K, so one fetches a line and
+  // the others find it in L2 later instead of all waiting on the same miss.
+  // The sum over K is the same, in another order.  0 for FP8 (its scales
+  // follow the loop's K-step).
+  int krot = 0, nks = 1 << 30;
 
   // X rows come from resource a (a_off(r): byte offset of X row r of the
   // tile, r < AROWS; the caller maps rows past the valid ones to a valid
@@ -186,7 +192,9 @@ struct Pipe {
   template <int Q, int NA>
   __device__ __forceinline__ void issue_one(uint8_t* st, int ks) const {
     const int w = wave_id() % LW;
-    const uint32_t kofs = static_cast<uint32_t>(ks) * SB;
+    int kr = ks + krot;
+    if (kr >= nks) kr -= nks;
+    const uint32_t kofs = static_cast<uint32_t>(kr) * SB;
     if constexpr (Q < NA)
       dma16(ra, oa[Q], kofs, st + A_OFF + RPI * (w + LW * Q) * SB);
     else if constexpr (Q < NA + NIB)

@@ -80,13 +80,27 @@ __device__ __forceinline__ int xcd_tile(int n_tiles) {
 // Tile q -> (m-tile, n-block): within a unit of up to MT_UNIT m-tiles of one
 // group, the m-tile index runs fastest, so the tiles that read the same weight
 // block are dispatched back to back (onto the same XCD) and share its L2.
-__device__ __forceinline__ void tile_coords(const int4* mtiles, int q, int nb_n, int& mt, int& nb) {
+__device__ __forceinline__ void tile_coords(const int4* mtiles, int q, int nb_n, int& mt, int& nb, int& in_unit) {
   const int t = q / nb_n;
   const int w = mtiles[t].w;
   const int s = t - (w >> 8), k = w & 0xff;
   const int local = q - s * nb_n;
   nb = local / k;
-  mt = s + local % k;
+  in_unit = local % k;
+  mt = s + in_unit;
+}
+
+// bf16: where a tile starts along K, in 64-byte K-steps (whole pairs).  The
+// n-blocks of an m-tile (which share its X rows) start 2 pairs apart, the
+// m-tiles of a unit (which share the weight block) 1 pair apart.
+template <int FMT>
+__device__ __forceinline__ int k_rotation(int nb, int in_unit, int nk) {
+  if constexpr (FMT != FMT_BF16) {
+    return 0;
+  } else {
+    const int np = nk / 2;
+    return 2 * ((2 * nb + in_unit) % np);
+  }
 }
 
 constexpr int MAX_KB = 256;   // FP8: at most 256 scale blocks along K (d, I <= 32768)
@@ -252,8 +266,8 @@ __global__ __launch_bounds__(GG<FMT>::THREADS, 1) void gateup_kernel(GateUpArgs 
   const int nb_n = ceil_div(a.inter, GG_HCOLS);
   const int q = xcd_tile(*a.mt_count * nb_n);
   if (q < 0) return;
-  int mt, nb;
-  tile_coords(a.mtiles, q, nb_n, mt, nb);
+  int mt, nb, in_unit;
+  tile_coords(a.mtiles, q, nb_n, mt, nb, in_unit);
   const int4 tl = a.mtiles[mt];
   const int g = tl.x, row0 = tl.y, rows = tl.z;
   const int n0 = nb * GG_HCOLS;
@@ -285,6 +299,8 @@ __global__ __launch_bounds__(GG<FMT>::THREADS, 1) void gateup_kernel(GateUpArgs 
            },
            FMT == FMT_E4M3 ? make_rsrc(a.x_scale, static_cast<uint32_t>(a.T * kb * 4)) : make_rsrc(a.x, 0),
            [&](int r) { return static_cast<uint32_t>(token_of(r) * kb * 4); });
+    p.krot = k_rotation<FMT>(nb, in_unit, nk);
+    p.nks = nk;
     return p;
   };
 
@@ -361,8 +377,8 @@ __global__ __launch_bounds__(GG<FMT>::THREADS, 1) void down_kernel(DownArgs a) {
   const int nb_n = ceil_div(a.d, BNW);
   const int q = xcd_tile(*a.mt_count * nb_n);
   if (q < 0) return;
-  int mt, nb;
-  tile_coords(a.mtiles, q, nb_n, mt, nb);
+  int mt, nb, in_unit;
+  tile_coords(a.mtiles, q, nb_n, mt, nb, in_unit);
   const int4 tl = a.mtiles[mt];
   const int g = tl.x, row0 = tl.y, rows = tl.z;
   const int n0 = nb * BNW;
@@ -390,6 +406,8 @@ __global__ __launch_bounds__(GG<FMT>::THREADS, 1) void down_kernel(DownArgs a) {
            FMT == FMT_E4M3 ? make_rsrc(a.h_scale + static_cast<size_t>(row0) * kb, static_cast<uint32_t>(rows * kb * 4))
                            : make_rsrc(a.h, 0),
            [&](int r) { return static_cast<uint32_t>((r < rows ? r : 0) * kb * 4); });
+    p.krot = k_rotation<FMT>(nb, in_unit, nk);
+    p.nks = nk;
     return p;
   };
 
