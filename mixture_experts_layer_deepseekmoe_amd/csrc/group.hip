@@ -36,6 +36,7 @@ constexpr int SCAN_THREADS = 1024;
 __global__ __launch_bounds__(SCAN_THREADS) void scan_kernel(GroupArgs a, int nblk) {
   __shared__ int sc[MAX_ROUTED + MAX_SHARED + 1];
   __shared__ int tmp[MAX_ROUTED + MAX_SHARED + 1];
+  __shared__ int pc[MAX_ROUTED + MT_SEGMENTS * MAX_SHARED + 1];
   const int tid = threadIdx.x;
   const int nr = a.n_routed;
   // 1. per-expert totals and per-block bases
@@ -67,33 +68,67 @@ __global__ __launch_bounds__(SCAN_THREADS) void scan_kernel(GroupArgs a, int nbl
   //    them in L2 only while they run at the same speed; a short remainder
   //    tile would drift away from its partners (measured: 1.5x the HBM
   //    traffic of the grouped GEMM).
-  const int ng = nr + a.n_shared;
+  //    The list is laid out in MT_SEGMENTS segments -- the GEMMs give each
+  //    XCD an equal share of it, in order -- and each segment holds an equal
+  //    share of the routed experts and of every shared expert's tiles.  With
+  //    the shared experts' full tiles at the end of the list, the last XCD
+  //    carried ~8% more work than the others and the rest idled for it.
+  const int ns = a.n_shared;
+  const int n_sh = ceil_div(a.T, a.bm);   // m-tiles of one shared expert
+  const int np = nr + MT_SEGMENTS * ns;   // pieces: one per routed expert, one per (shared expert, segment)
   const long long TK = static_cast<long long>(a.T) * a.top_k;
-  for (int g = tid; g < ng; g += SCAN_THREADS) {
-    const int M = g < nr ? (sc[g] - (g ? sc[g - 1] : 0)) : a.T;
-    tmp[g] = ceil_div(M, a.bm);
+  // piece p -> group, its m-tiles k0 .. k1-1, the group's m-tile count and rows
+  auto piece = [&](int p, int& g, int& k0, int& k1, int& n, long long& M) {
+    int seg = 0, base = 0;
+    for (; seg < MT_SEGMENTS - 1; ++seg) {
+      const int len = (seg + 1) * nr / MT_SEGMENTS - seg * nr / MT_SEGMENTS + ns;
+      if (p < base + len) break;
+      base += len;
+    }
+    const int r0 = seg * nr / MT_SEGMENTS, rn = (seg + 1) * nr / MT_SEGMENTS - r0;
+    const int loc = p - base;
+    if (loc < rn) {
+      g = r0 + loc;
+      M = sc[g] - (g ? sc[g - 1] : 0);
+      n = ceil_div(static_cast<int>(M), a.bm);
+      k0 = 0;
+      k1 = n;
+    } else {
+      g = nr + (loc - rn);
+      M = a.T;
+      n = n_sh;
+      k0 = seg * n_sh / MT_SEGMENTS;
+      k1 = (seg + 1) * n_sh / MT_SEGMENTS;
+    }
+  };
+  for (int p = tid; p < np; p += SCAN_THREADS) {
+    int g, k0, k1, n;
+    long long M;
+    piece(p, g, k0, k1, n, M);
+    pc[p] = k1 - k0;
   }
   __syncthreads();
-  if (tid == 0) {   // at most 520 groups: a short serial scan
+  if (tid == 0) {   // at most 576 pieces: a short serial scan
     int run = 0;
-    for (int g = 0; g < ng; ++g) { const int n = tmp[g]; tmp[g] = run; run += n; }
-    tmp[ng] = run;
+    for (int p = 0; p < np; ++p) { const int c = pc[p]; pc[p] = run; run += c; }
+    pc[np] = run;
     *a.mt_count = run;
   }
   __syncthreads();
   // .w = (index within its unit << 8) | unit size: consecutive m-tiles of a
-  // group form units of at most MT_UNIT, whose tiles the GEMMs visit with the
+  // piece form units of at most MT_UNIT, whose tiles the GEMMs visit with the
   // m-tile index fastest, so the tiles sharing one weight block run together.
-  for (int g = tid; g < ng; g += SCAN_THREADS) {
-    const long long M = g < nr ? (sc[g] - (g ? sc[g - 1] : 0)) : a.T;
+  for (int p = tid; p < np; p += SCAN_THREADS) {
+    int g, k0, k1, n;
+    long long M;
+    piece(p, g, k0, k1, n, M);
     const long long first = g < nr ? (g ? sc[g - 1] : 0) : TK + static_cast<long long>(g - nr) * a.T;
-    const int n = tmp[g + 1] - tmp[g];
-    for (int k = 0; k < n; ++k) {
+    for (int k = k0; k < k1; ++k) {
       const long long r0 = k * M / n, r1 = (k + 1) * M / n;
-      const int ustart = k - k % MT_UNIT;
-      const int usize = min(MT_UNIT, n - ustart);
-      a.mtiles[tmp[g] + k] = make_int4(g, static_cast<int>(first + r0), static_cast<int>(r1 - r0),
-                                       ((k - ustart) << 8) | usize);
+      const int loc = k - k0, ustart = loc - loc % MT_UNIT;
+      const int usize = min(MT_UNIT, (k1 - k0) - ustart);
+      a.mtiles[pc[p] + loc] = make_int4(g, static_cast<int>(first + r0), static_cast<int>(r1 - r0),
+                                        ((loc - ustart) << 8) | usize);
     }
   }
 }

@@ -20,6 +20,7 @@ constexpr int MAX_ROUTED = 512;
 constexpr int MAX_SHARED = 8;
 constexpr int MAX_TOPK = 16;
 constexpr int MT_UNIT = 4;        // m-tiles of one group visited together by the grouped GEMMs
+constexpr int MT_SEGMENTS = 8;    // segments of the m-tile list (one per XCD), each with a share of every group
 
 struct RouteArgs {
   const void* u;          // [T][d] fmt
