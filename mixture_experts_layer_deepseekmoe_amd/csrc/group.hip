@@ -37,6 +37,7 @@ __global__ __launch_bounds__(SCAN_THREADS) void scan_kernel(GroupArgs a, int nbl
   __shared__ int sc[MAX_ROUTED + MAX_SHARED + 1];
   __shared__ int tmp[MAX_ROUTED + MAX_SHARED + 1];
   __shared__ int pc[MAX_ROUTED + MT_SEGMENTS * MAX_SHARED + 1];
+  __shared__ int rb[MT_SEGMENTS + 1];
   const int tid = threadIdx.x;
   const int nr = a.n_routed;
   // 1. per-expert totals and per-block bases
@@ -70,22 +71,52 @@ __global__ __launch_bounds__(SCAN_THREADS) void scan_kernel(GroupArgs a, int nbl
   //    traffic of the grouped GEMM).
   //    The list is laid out in MT_SEGMENTS segments -- the GEMMs give each
   //    XCD an equal share of it, in order -- and each segment holds an equal
-  //    share of the routed experts and of every shared expert's tiles.  With
-  //    the shared experts' full tiles at the end of the list, the last XCD
-  //    carried ~8% more work than the others and the rest idled for it.
+  //    share of the routed experts' m-tiles (whole experts) and of every
+  //    shared expert's tiles.  With the shared experts' full tiles at the end
+  //    of the list, the last XCD carried ~8% more work than the others and
+  //    the rest idled for it.
   const int ns = a.n_shared;
   const int n_sh = ceil_div(a.T, a.bm);   // m-tiles of one shared expert
   const int np = nr + MT_SEGMENTS * ns;   // pieces: one per routed expert, one per (shared expert, segment)
   const long long TK = static_cast<long long>(a.T) * a.top_k;
+  // segment s takes routed experts rb[s] .. rb[s+1]-1: expert g goes to the
+  // segment of its first m-tile, seg(g) = floor(MT_SEGMENTS * (m-tiles
+  // before g) / routed m-tiles), a monotone map (inclusive scan of the
+  // per-expert m-tile counts in tmp)
+  for (int g = tid; g < nr; g += SCAN_THREADS) tmp[g] = ceil_div(sc[g] - (g ? sc[g - 1] : 0), a.bm);
+  __syncthreads();
+  for (int off = 1; off < nr; off <<= 1) {
+    int v[(MAX_ROUTED + SCAN_THREADS - 1) / SCAN_THREADS];
+    int c = 0;
+    for (int g = tid; g < nr; g += SCAN_THREADS) v[c++] = tmp[g] + (g >= off ? tmp[g - off] : 0);
+    __syncthreads();
+    c = 0;
+    for (int g = tid; g < nr; g += SCAN_THREADS) tmp[g] = v[c++];
+    __syncthreads();
+  }
+  {
+    const long long total = nr ? tmp[nr - 1] : 0;
+    auto seg_of = [&](int g) {   // segment of expert g (g = nr: past the end)
+      if (g >= nr || total == 0) return g >= nr ? MT_SEGMENTS : 0;
+      const long long before = g ? tmp[g - 1] : 0;
+      return static_cast<int>(before * MT_SEGMENTS / total);
+    };
+    if (tid == 0) rb[0] = 0;
+    for (int g = tid; g <= nr; g += SCAN_THREADS) {
+      const int s1 = seg_of(g), s0 = g ? seg_of(g - 1) : 0;
+      for (int x = s0 + 1; x <= s1; ++x) rb[x] = g;
+    }
+  }
+  __syncthreads();
   // piece p -> group, its m-tiles k0 .. k1-1, the group's m-tile count and rows
   auto piece = [&](int p, int& g, int& k0, int& k1, int& n, long long& M) {
     int seg = 0, base = 0;
     for (; seg < MT_SEGMENTS - 1; ++seg) {
-      const int len = (seg + 1) * nr / MT_SEGMENTS - seg * nr / MT_SEGMENTS + ns;
+      const int len = rb[seg + 1] - rb[seg] + ns;
       if (p < base + len) break;
       base += len;
     }
-    const int r0 = seg * nr / MT_SEGMENTS, rn = (seg + 1) * nr / MT_SEGMENTS - r0;
+    const int r0 = rb[seg], rn = rb[seg + 1] - r0;
     const int loc = p - base;
     if (loc < rn) {
       g = r0 + loc;
