@@ -105,27 +105,42 @@ __device__ __forceinline__ int k_rotation(int nb, int in_unit, int nk) {
 
 constexpr int MAX_KB = 256;   // FP8: at most 256 scale blocks along K (d, I <= 32768)
 
-// The stage ring: NST separate LDS objects (so the compiler can tell the
-// asynchronous writes of one stage from the reads of another).
-#define MOE_STAGE_RING(P, NST)                                                         \
-  __shared__ __attribute__((aligned(1024))) uint8_t st0[P::STAGE_BYTES];              \
-  __shared__ __attribute__((aligned(1024))) uint8_t st1[P::STAGE_BYTES];              \
-  __shared__ __attribute__((aligned(1024))) uint8_t st2[NST > 2 ? P::STAGE_BYTES : 16]; \
-  __shared__ __attribute__((aligned(1024))) uint8_t st3[NST > 3 ? P::STAGE_BYTES : 16]; \
-  __shared__ __attribute__((aligned(1024))) uint8_t st4[NST > 4 ? P::STAGE_BYTES : 16];
-
+// The stage ring: NST stage buffers, one after the other in one LDS array
+// (the bf16 epilogue reuses it whole as its output tile).
 template <int NST>
 struct Ring {
   uint8_t* s[NST];
 };
 
-template <int NST>
-__device__ __forceinline__ Ring<NST> make_ring(uint8_t* a, uint8_t* b, uint8_t* c, uint8_t* d, uint8_t* e) {
-  uint8_t* all[5] = {a, b, c, d, e};
+template <int NST, int SBY>
+__device__ __forceinline__ Ring<NST> make_ring(uint8_t* base) {
   Ring<NST> r;
 #pragma unroll
-  for (int i = 0; i < NST; ++i) r.s[i] = all[i];
+  for (int i = 0; i < NST; ++i) r.s[i] = base + i * SBY;
   return r;
+}
+
+// bf16 epilogue, second half: the block's output tile sits in LDS as rows of
+// COLS bf16 (PITCH bytes apart); every wave of the block copies it out in
+// 16-byte pieces, consecutive lanes along a row, so each store instruction
+// writes whole 128-byte lines.  (Written straight from the accumulators,
+// a store put 32 contiguous bytes per row and took ~14% of a down tile.)
+template <int COLS, int PITCH, int THREADS>
+__device__ __forceinline__ void store_tile_from_lds(const uint8_t* lds, int rows, int ncols, uint16_t* dst,
+                                                    size_t stride) {
+  constexpr int CPR = COLS / 8;   // 16-byte pieces per row
+  const int npr = ncols / 8;
+  for (int idx = threadIdx.x; idx < rows * CPR; idx += THREADS) {
+    const int r = idx / CPR, c = idx - r * CPR;
+    if (c < npr)
+      *reinterpret_cast<uint4*>(dst + static_cast<size_t>(r) * stride + c * 8) =
+          *reinterpret_cast<const uint4*>(lds + r * PITCH + c * 16);
+  }
+}
+
+__device__ __forceinline__ uint2 pack_bf16x4(float a, float b, float c, float d) {
+  return make_uint2(f32_to_bf16(a) | (static_cast<uint32_t>(f32_to_bf16(b)) << 16),
+                    f32_to_bf16(c) | (static_cast<uint32_t>(f32_to_bf16(d)) << 16));
 }
 
 // Calls f.template operator()<NSUB>() with NSUB = the number of row subtiles
@@ -175,6 +190,35 @@ __device__ __forceinline__ void gateup_tile(const GateUpArgs& a, const MK& make_
   f32x4 acc[P::MI][P::NJ];
   zero_acc(acc);
   gg_mainloop<FMT, NSUB, NSUBC>(make_pipe, st, nk, wr, acc, swl, kb);
+  if constexpr (FMT == FMT_BF16) {
+    // H tile (rows x 128 columns, bf16) through LDS; every wave stores
+    constexpr int PITCH = GG_HCOLS * 2 + 16;   // padded rows: the 16 rows of a subtile hit different banks
+    static_assert(GG<FMT>::BM * PITCH <= GG<FMT>::NST * P::STAGE_BYTES, "output tile fits the stage ring");
+    uint8_t* const lds = st[0];
+    wait_vm_lgkm0<0>();
+    block_barrier();   // every wave is done with the stage ring
+    if (w < GG<FMT>::NW) {
+#pragma unroll
+      for (int i = 0; i < NSUBC; ++i) {
+        const int row = 16 * (WM * i + wm) + lr;
+#pragma unroll
+        for (int jj = 0; jj < NJ2; ++jj) {
+          const int col = HW * wn + 16 * jj + 4 * lg;
+          float h[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) h[r] = silu_f32(acc[i][jj][r]) * acc[i][jj + NJ2][r];
+          *reinterpret_cast<uint2*>(lds + row * PITCH + col * 2) = pack_bf16x4(h[0], h[1], h[2], h[3]);
+        }
+      }
+    }
+    wait_vm_lgkm0<0>();
+    block_barrier();
+    store_tile_from_lds<GG_HCOLS, PITCH, GG<FMT>::THREADS>(lds, rows, min(GG_HCOLS, a.inter - n0),
+                                                           static_cast<uint16_t*>(a.h) +
+                                                               static_cast<size_t>(row0) * a.inter + n0,
+                                                           a.inter);
+    return;
+  }
   // the load-only waves hold no results (the FP8 epilogue keeps them for its
   // barrier)
   if (FMT != FMT_E4M3 && w >= GG<FMT>::NW) return;
@@ -251,7 +295,7 @@ template <int FMT>
 __global__ __launch_bounds__(GG<FMT>::THREADS, 1) void gateup_kernel(GateUpArgs a) {
   using P = typename GG<FMT>::P;
   constexpr int NST = GG<FMT>::NST, BM = GG<FMT>::BM;
-  MOE_STAGE_RING(P, NST)
+  __shared__ __attribute__((aligned(1024))) uint8_t ring_lds[NST * P::STAGE_BYTES];
   // FP8 only: the epilogue's row-amax exchange and the weight-block scales
   // (the bf16 ring takes all of the LDS)
   float (*red)[BM] = nullptr;
@@ -312,7 +356,7 @@ __global__ __launch_bounds__(GG<FMT>::THREADS, 1) void gateup_kernel(GateUpArgs 
     __syncthreads();
   }
 
-  const Ring<NST> ring = make_ring<NST>(st0, st1, st2, st3, st4);
+  const Ring<NST> ring = make_ring<NST, P::STAGE_BYTES>(ring_lds);
   const float* sw = FMT == FMT_E4M3 ? swl : nullptr;
   // the K loop instantiated for the tile's valid rows, in 32-row steps
   const bool short_row = short_wave_row<FMT>(rows);
@@ -341,6 +385,32 @@ __device__ __forceinline__ void down_tile(const DownArgs& a, const MK& make_pipe
   f32x4 acc[P::MI][P::NJ];
   zero_acc(acc);
   gg_mainloop<FMT, NSUB, NSUBC>(make_pipe, st, nk, wr, acc, FMT == FMT_E4M3 ? swl + wn * kb : nullptr, 0);
+  if constexpr (FMT == FMT_BF16) {
+    // Y tile (rows x 256 columns, bf16) through LDS; every wave stores
+    constexpr int PITCH = BNW * 2 + 16;   // padded rows: the 16 rows of a subtile hit different banks
+    static_assert(GG<FMT>::BM * PITCH <= GG<FMT>::NST * P::STAGE_BYTES, "output tile fits the stage ring");
+    uint8_t* const lds = st[0];
+    wait_vm_lgkm0<0>();
+    block_barrier();   // every wave is done with the stage ring
+    if (w < GG<FMT>::NW) {
+#pragma unroll
+      for (int i = 0; i < NSUBC; ++i) {
+        const int row = 16 * (WM * i + wm) + lr;
+#pragma unroll
+        for (int j = 0; j < P::NJ; ++j) {
+          const int col = 16 * P::NJ * wn + 16 * j + 4 * lg;
+          *reinterpret_cast<uint2*>(lds + row * PITCH + col * 2) =
+              pack_bf16x4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
+        }
+      }
+    }
+    wait_vm_lgkm0<0>();
+    block_barrier();
+    store_tile_from_lds<BNW, PITCH, GG<FMT>::THREADS>(lds, rows, min(BNW, a.d - n0),
+                                                      static_cast<uint16_t*>(a.y) + static_cast<size_t>(row0) * a.d + n0,
+                                                      a.d);
+    return;
+  }
   if (w >= GG<FMT>::NW) return;   // FP8: the load-only waves
 #pragma unroll
   for (int i = 0; i < NSUBC; ++i) {
@@ -367,7 +437,7 @@ template <int FMT>
 __global__ __launch_bounds__(GG<FMT>::THREADS, 1) void down_kernel(DownArgs a) {
   using P = typename GG<FMT>::P;
   constexpr int NST = GG<FMT>::NST;
-  MOE_STAGE_RING(P, NST)
+  __shared__ __attribute__((aligned(1024))) uint8_t ring_lds[NST * P::STAGE_BYTES];
   float* swl = nullptr;   // FP8 only: the weight-block scales
   if constexpr (FMT == FMT_E4M3) {
     __shared__ float swl_s[2 * MAX_KB];
@@ -421,7 +491,7 @@ __global__ __launch_bounds__(GG<FMT>::THREADS, 1) void down_kernel(DownArgs a) {
     __syncthreads();
   }
 
-  const Ring<NST> ring = make_ring<NST>(st0, st1, st2, st3, st4);
+  const Ring<NST> ring = make_ring<NST, P::STAGE_BYTES>(ring_lds);
   const float* sw = FMT == FMT_E4M3 ? swl : nullptr;
   const bool short_row = short_wave_row<FMT>(rows);
   dispatch_rows<P::MI, GG<FMT>::WM>(rows, [&]<int NSUB>() {
