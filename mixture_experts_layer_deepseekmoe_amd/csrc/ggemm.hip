@@ -29,6 +29,7 @@ namespace {
 
 constexpr int BNW = GG_BNW;
 constexpr int NXCD = 8;
+static_assert(NXCD == MT_SEGMENTS, "one tile-list segment per XCD");
 
 template <int FMT>
 struct GG {
@@ -67,14 +68,22 @@ __device__ __forceinline__ void gg_mainloop(const MK& make_pipe, uint8_t* const 
     pipe_mainloop<P, GG<FMT>::NST, NSUB>(make_pipe(), st, nk, wr, acc, sw_lds, sw_stride);
 }
 
-// Logical tile index of this block, or -1 if the block has no work.
-__device__ __forceinline__ int xcd_tile(int n_tiles) {
+// Logical tile index of this block, or -1 if the block has no work.  XCD x
+// (blocks bid with bid % 8 == x) takes the tiles of list segment x (whose
+// first m-tiles the scan kernel stores in mtc[1..9]), or, when the segments
+// do not fit the grid (mtc[1] < 0), an equal share of the tile list.
+__device__ __forceinline__ int xcd_tile(const int32_t* mtc, int nb_n) {
   const int bid = blockIdx.x;
   const int xcd = bid % NXCD, j = bid / NXCD;
-  const int chunk = ceil_div(n_tiles, NXCD);
-  if (j >= chunk) return -1;
-  const int q = xcd * chunk + j;
-  return q < n_tiles ? q : -1;
+  if (mtc[1] < 0) {
+    const int n_tiles = mtc[0] * nb_n;
+    const int chunk = ceil_div(n_tiles, NXCD);
+    if (j >= chunk) return -1;
+    const int q = xcd * chunk + j;
+    return q < n_tiles ? q : -1;
+  }
+  const int q = mtc[1 + xcd] * nb_n + j;
+  return q < mtc[2 + xcd] * nb_n ? q : -1;
 }
 
 // Tile q -> (m-tile, n-block): within a unit of up to MT_UNIT m-tiles of one
@@ -308,7 +317,7 @@ __global__ __launch_bounds__(GG<FMT>::THREADS, 1) void gateup_kernel(GateUpArgs 
   }
 
   const int nb_n = ceil_div(a.inter, GG_HCOLS);
-  const int q = xcd_tile(*a.mt_count * nb_n);
+  const int q = xcd_tile(a.mt_count, nb_n);
   if (q < 0) return;
   int mt, nb, in_unit;
   tile_coords(a.mtiles, q, nb_n, mt, nb, in_unit);
@@ -445,7 +454,7 @@ __global__ __launch_bounds__(GG<FMT>::THREADS, 1) void down_kernel(DownArgs a) {
   }
 
   const int nb_n = ceil_div(a.d, BNW);
-  const int q = xcd_tile(*a.mt_count * nb_n);
+  const int q = xcd_tile(a.mt_count, nb_n);
   if (q < 0) return;
   int mt, nb, in_unit;
   tile_coords(a.mtiles, q, nb_n, mt, nb, in_unit);
@@ -502,9 +511,9 @@ __global__ __launch_bounds__(GG<FMT>::THREADS, 1) void down_kernel(DownArgs a) {
   });
 }
 
+// NXCD x (tiles of the largest list segment the scan may form)
 int grid_for(int max_mtiles, int nb_n) {
-  const long long tiles = static_cast<long long>(max_mtiles) * nb_n;
-  return static_cast<int>(NXCD * ((tiles + NXCD - 1) / NXCD));
+  return static_cast<int>(static_cast<long long>(NXCD) * seg_cap(max_mtiles) * nb_n);
 }
 
 }  // namespace

@@ -38,6 +38,9 @@ __global__ __launch_bounds__(SCAN_THREADS) void scan_kernel(GroupArgs a, int nbl
   __shared__ int tmp[MAX_ROUTED + MAX_SHARED + 1];
   __shared__ int pc[MAX_ROUTED + MT_SEGMENTS * MAX_SHARED + 1];
   __shared__ int rb[MT_SEGMENTS + 1];
+  __shared__ int rbs[2][MT_SEGMENTS + 1];
+  __shared__ int cst[MAX_ROUTED];
+  __shared__ int seg_mode;
   const int tid = threadIdx.x;
   const int nr = a.n_routed;
   // 1. per-expert totals and per-block bases
@@ -79,33 +82,71 @@ __global__ __launch_bounds__(SCAN_THREADS) void scan_kernel(GroupArgs a, int nbl
   const int n_sh = ceil_div(a.T, a.bm);   // m-tiles of one shared expert
   const int np = nr + MT_SEGMENTS * ns;   // pieces: one per routed expert, one per (shared expert, segment)
   const long long TK = static_cast<long long>(a.T) * a.top_k;
-  // segment s takes routed experts rb[s] .. rb[s+1]-1: expert g goes to the
-  // segment of its first m-tile, seg(g) = floor(MT_SEGMENTS * (m-tiles
-  // before g) / routed m-tiles), a monotone map (inclusive scan of the
-  // per-expert m-tile counts in tmp)
-  for (int g = tid; g < nr; g += SCAN_THREADS) tmp[g] = ceil_div(sc[g] - (g ? sc[g - 1] : 0), a.bm);
+  // Segment s takes routed experts rb[s] .. rb[s+1]-1, cut where the prefix
+  // of a per-expert cost crosses s/MT_SEGMENTS of the total: expert g goes to
+  // the segment of its first unit of cost, a monotone map.  The cost of an
+  // expert is its m-tiles times BM (each tile streams a whole weight block)
+  // plus its rows; each segment must fit the blocks the GEMMs give an XCD
+  // (seg_cap m-tiles).  The other cut is by m-tile counts.  With the cost cut
+  // the GEMMs give XCD x exactly segment x; with the count cut (or when the
+  // cost cut does not fit) equal tile counts per XCD (mt_count[1] = -1).
+  for (int g = tid; g < nr; g += SCAN_THREADS) {
+    const int M = sc[g] - (g ? sc[g - 1] : 0), n = ceil_div(M, a.bm);
+    tmp[g] = n;
+    cst[g] = n * (a.bm / 16) + ceil_div(M, 16);   // in 16-row units: the prefix stays far below 2^31
+  }
   __syncthreads();
   for (int off = 1; off < nr; off <<= 1) {
-    int v[(MAX_ROUTED + SCAN_THREADS - 1) / SCAN_THREADS];
+    int v[(MAX_ROUTED + SCAN_THREADS - 1) / SCAN_THREADS], u[(MAX_ROUTED + SCAN_THREADS - 1) / SCAN_THREADS];
     int c = 0;
-    for (int g = tid; g < nr; g += SCAN_THREADS) v[c++] = tmp[g] + (g >= off ? tmp[g - off] : 0);
+    for (int g = tid; g < nr; g += SCAN_THREADS, ++c) {
+      v[c] = tmp[g] + (g >= off ? tmp[g - off] : 0);
+      u[c] = cst[g] + (g >= off ? cst[g - off] : 0);
+    }
     __syncthreads();
     c = 0;
-    for (int g = tid; g < nr; g += SCAN_THREADS) tmp[g] = v[c++];
+    for (int g = tid; g < nr; g += SCAN_THREADS, ++c) {
+      tmp[g] = v[c];
+      cst[g] = u[c];
+    }
     __syncthreads();
   }
-  {
-    const long long total = nr ? tmp[nr - 1] : 0;
+  // rbs[0][.]: cut by cost, rbs[1][.]: cut by m-tile count
+  for (int which = 0; which < 2; ++which) {
+    const int* pre = which ? tmp : cst;
+    const long long total = nr ? pre[nr - 1] : 0;
     auto seg_of = [&](int g) {   // segment of expert g (g = nr: past the end)
       if (g >= nr || total == 0) return g >= nr ? MT_SEGMENTS : 0;
-      const long long before = g ? tmp[g - 1] : 0;
+      const long long before = g ? pre[g - 1] : 0;
       return static_cast<int>(before * MT_SEGMENTS / total);
     };
-    if (tid == 0) rb[0] = 0;
+    if (tid == 0) rbs[which][0] = 0;
     for (int g = tid; g <= nr; g += SCAN_THREADS) {
       const int s1 = seg_of(g), s0 = g ? seg_of(g - 1) : 0;
-      for (int x = s0 + 1; x <= s1; ++x) rb[x] = g;
+      for (int x = s0 + 1; x <= s1; ++x) rbs[which][x] = g;
     }
+  }
+  __syncthreads();
+  if (tid == 0) {
+    // With few m-tiles per segment the GEMM tiles of an XCD run in a few
+    // rounds over its CUs, and equal tile counts matter more than equal cost
+    // (bf16 d = 2048, 160 m-tiles: the cost cut was 5% slower, at d = 7168
+    // with ~400 m-tiles 1.5% faster).
+    const int first = nr && tmp[nr - 1] >= 32 * MT_SEGMENTS ? 0 : 1;
+    int pick = -1;
+    for (int k = 0; k < 2 && pick < 0; ++k) {
+      const int which = k ? 1 - first : first;
+      bool fits = true;
+      for (int x = 0; x < MT_SEGMENTS; ++x) {
+        const int g0 = rbs[which][x], g1 = rbs[which][x + 1];
+        const int routed = (g1 ? tmp[g1 - 1] : 0) - (g0 ? tmp[g0 - 1] : 0);
+        const int shared = ns * ((x + 1) * n_sh / MT_SEGMENTS - x * n_sh / MT_SEGMENTS);
+        fits = fits && routed + shared <= a.seg_cap;
+      }
+      if (fits) pick = which;
+    }
+    seg_mode = pick;
+    for (int x = 0; x <= MT_SEGMENTS; ++x) rb[x] = rbs[pick < 0 ? 1 : pick][x];
   }
   __syncthreads();
   // piece p -> group, its m-tiles k0 .. k1-1, the group's m-tile count and rows
@@ -143,7 +184,12 @@ __global__ __launch_bounds__(SCAN_THREADS) void scan_kernel(GroupArgs a, int nbl
     int run = 0;
     for (int p = 0; p < np; ++p) { const int c = pc[p]; pc[p] = run; run += c; }
     pc[np] = run;
-    *a.mt_count = run;
+    a.mt_count[0] = run;
+    // the m-tile where each segment starts, for the GEMMs' XCD ranges
+    // (cut by cost only: with the cut by m-tile counts, equal tile counts per
+    // XCD -- mt_count[1] = -1 -- match the segments as closely and split an
+    // expert's tiles between two XCDs where the counts do not divide evenly)
+    for (int x = 0; x <= MT_SEGMENTS; ++x) a.mt_count[1 + x] = seg_mode != 0 ? -1 : pc[rb[x] + x * ns];
   }
   __syncthreads();
   // .w = (index within its unit << 8) | unit size: consecutive m-tiles of a

@@ -46,8 +46,9 @@ struct GroupArgs {
   int32_t* perm_token;    // [T*K]
   int32_t* pos;           // [T][K]
   int4* mtiles;           // [max_mtiles] (group, first grouped row, rows, unit info); null: routing only
-  int32_t* mt_count;      // [1]
+  int32_t* mt_count;      // [2 + MT_SEGMENTS]: m-tile count, then each list segment's first m-tile (-1: none)
   int bm;                 // grouped-GEMM tile rows (m-tiles hold at most bm rows)
+  int seg_cap;            // m-tiles one list segment may hold (the GEMM blocks of one XCD)
 };
 
 struct GateUpArgs {
@@ -103,6 +104,9 @@ hipError_t launch_combine(int xfmt, int yfmt, int ofmt, const CombineArgs& a, hi
 
 // Tile rows of the grouped GEMMs for a weight format (m-tiles hold at most this many rows).
 int gg_bm(int fmt);
+
+// m-tiles per XCD segment the GEMM grids cover
+inline int seg_cap(int max_mt) { return (max_mt + MT_SEGMENTS - 1) / MT_SEGMENTS; }
 
 inline int max_mtiles(long long T, int K, int n_routed, int n_shared, int bm) {
   // sum over groups of ceil(M_g / bm) <= (T*K)/bm + N_r + N_s * ceil(T/bm)

@@ -46,7 +46,7 @@ Layout make_layout(const moe_shape& s) {
   L.perm = take(TK * 4);
   L.pos = take(TK * 4);
   L.mtiles = take(static_cast<size_t>(L.max_mt) * 16);
-  L.mtcount = take(4);
+  L.mtcount = take(4 * (2 + moe::MT_SEGMENTS));
   const bool fp8 = s.w_dtype == MOE_DTYPE_E4M3;
   L.uq = take(fp8 ? static_cast<size_t>(T) * s.d : 0);
   L.us = take(fp8 ? static_cast<size_t>(T) * (s.d / 128) * 4 : 0);
@@ -114,8 +114,9 @@ int run_route(const moe_shape& s, const void* u, const void* cen, const float* b
   moe::RouteArgs ra{u, cen, bias, s.T, s.d, s.n_routed, s.top_k, idx, gate, scores};
   int rc = check_launch(moe::launch_route(fmt_of(s.x_dtype), ra, st));
   if (rc != MOE_OK) return rc;
-  moe::GroupArgs ga{idx,     s.T,  s.top_k, s.n_routed, s.n_shared, hist,   counts,
-                    offsets, perm, pos,     mtiles,     mtcount,    moe::gg_bm(fmt_of(s.w_dtype))};
+  const int bm = moe::gg_bm(fmt_of(s.w_dtype));
+  moe::GroupArgs ga{idx,     s.T,  s.top_k, s.n_routed, s.n_shared, hist, counts, offsets, perm, pos, mtiles, mtcount, bm,
+                    moe::seg_cap(moe::max_mtiles(s.T, s.top_k, s.n_routed, s.n_shared, bm))};
   return check_launch(moe::launch_group(ga, st));
 }
 
@@ -199,8 +200,8 @@ int moe_forward(const moe_shape* shape, const void* u, const void* centroids, co
   if (rc != MOE_OK) return rc;
   stg.end(MOE_STAGE_ROUTE);
   stg.begin(MOE_STAGE_GROUP);
-  moe::GroupArgs gra{idx,     s.T,  s.top_k, s.n_routed, s.n_shared, at<int32_t>(workspace, L.hist), counts,
-                     offsets, perm, pos,     mtiles,     mtcount,    moe::gg_bm(fmt_of(s.w_dtype))};
+  moe::GroupArgs gra{idx,    s.T,    s.top_k, s.n_routed, s.n_shared, at<int32_t>(workspace, L.hist), counts,
+                     offsets, perm, pos,      mtiles,     mtcount,    moe::gg_bm(fmt_of(s.w_dtype)), moe::seg_cap(L.max_mt)};
   rc = check_launch(moe::launch_group(gra, stream));
   if (rc != MOE_OK) return rc;
   stg.end(MOE_STAGE_GROUP);
