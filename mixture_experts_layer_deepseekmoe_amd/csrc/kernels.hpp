@@ -29,13 +29,36 @@ struct RouteArgs {
   int T, d, n_routed, top_k;
   int32_t* idx;           // [T][K]
   float* gate;            // [T][K]
-  float* scores;          // [T][N_r] scratch, used when route_split(T)
+  float* scores;          // scratch: [T][N_r] sigmoids (route_split), [ksplit][T][N_r] partial logits (ksplit > 0)
+  int ksplit;             // route_ksplit(...) of this shape: 0, or the number of K slices
 };
 
 // Batches under 128 router blocks (T < 4096) spread the experts over blocks
 // too: a score kernel writes the sigmoids to scratch, a second kernel selects.
 constexpr int ROUTE_SPLIT_T = 4096;
 inline bool route_split(long long T) { return T < ROUTE_SPLIT_T; }
+
+// bf16 batches of 256-token tiles that, with d cut into K slices of at least
+// 4 whole 128-byte pairs, give at least 128 blocks: 256-token x 256-expert
+// tiles on the grouped GEMM's pipeline, fp32 partial logits per slice to
+// scratch, then a kernel that sums the slices in order and selects.  Returns
+// the number of slices (every slice non-empty), or 0 where it does not apply.
+inline int route_ksplit(int fmt, long long T, long long d, int n_routed) {
+  if (fmt != FMT_BF16 || T <= 0 || n_routed < 128 || n_routed > 256 || n_routed % 4 != 0 || d % 64 != 0) return 0;
+  const long long tiles = (T + 255) / 256, np = d / 64;
+  long long s = (256 + tiles - 1) / tiles;
+  if (s > np / 4) s = np / 4;
+  if (s < 1 || tiles * s < 128) return 0;
+  const long long pps = (np + s - 1) / s;
+  return static_cast<int>((np + pps - 1) / pps);
+}
+
+// Floats of router scratch a shape needs.
+inline long long route_scratch_floats(int fmt, long long T, long long d, int n_routed) {
+  const int ks = route_ksplit(fmt, T, d, n_routed);
+  if (ks > 0) return ks * T * n_routed;
+  return route_split(T) ? T * n_routed : 0;
+}
 
 struct GroupArgs {
   const int32_t* idx;     // [T][K]

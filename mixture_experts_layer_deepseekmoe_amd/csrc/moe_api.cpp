@@ -53,7 +53,7 @@ Layout make_layout(const moe_shape& s) {
   L.h = take(static_cast<size_t>(L.rows) * s.inter * elem_bytes(s.w_dtype));
   L.hs = take(fp8 ? static_cast<size_t>(L.rows) * (s.inter / 128) * 4 : 0);
   L.y = take(static_cast<size_t>(L.rows) * s.d * (s.w_dtype == MOE_DTYPE_F32 ? 4 : 2));
-  L.scores = take(moe::route_split(T) ? static_cast<size_t>(T) * s.n_routed * 4 : 0);
+  L.scores = take(static_cast<size_t>(moe::route_scratch_floats(fmt_of(s.x_dtype), T, s.d, s.n_routed)) * 4);
   L.total = o;
   return L;
 }
@@ -111,7 +111,8 @@ struct Stages {
 int run_route(const moe_shape& s, const void* u, const void* cen, const float* bias, int32_t* idx, float* gate,
               int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* pos, int32_t* hist, float* scores,
               int4* mtiles, int32_t* mtcount, hipStream_t st) {
-  moe::RouteArgs ra{u, cen, bias, s.T, s.d, s.n_routed, s.top_k, idx, gate, scores};
+  moe::RouteArgs ra{u,   cen,  bias,  s.T, s.d, s.n_routed, s.top_k, idx, gate, scores,
+                    moe::route_ksplit(fmt_of(s.x_dtype), s.T, s.d, s.n_routed)};
   int rc = check_launch(moe::launch_route(fmt_of(s.x_dtype), ra, st));
   if (rc != MOE_OK) return rc;
   const int bm = moe::gg_bm(fmt_of(s.w_dtype));
@@ -195,7 +196,8 @@ int moe_forward(const moe_shape* shape, const void* u, const void* centroids, co
 
   Stages stg{trace, stream};
   stg.begin(MOE_STAGE_ROUTE);
-  moe::RouteArgs ra{u, centroids, bias, s.T, s.d, s.n_routed, s.top_k, idx, gate, at<float>(workspace, L.scores)};
+  moe::RouteArgs ra{u,    centroids, bias, s.T, s.d, s.n_routed, s.top_k, idx, gate, at<float>(workspace, L.scores),
+                    moe::route_ksplit(fmt_of(s.x_dtype), s.T, s.d, s.n_routed)};
   rc = check_launch(moe::launch_route(fmt_of(s.x_dtype), ra, stream));
   if (rc != MOE_OK) return rc;
   stg.end(MOE_STAGE_ROUTE);

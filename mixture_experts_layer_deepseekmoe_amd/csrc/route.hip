@@ -8,7 +8,9 @@
 // their sigmoids go to LDS (the logits never reach HBM); then each wave
 // selects the top-K of its tokens, with the N_r scores of a token spread
 // 1..8 per lane.  Small batches (too few such blocks to fill the chip) split
-// the experts over blocks as well and pass the sigmoids through scratch.
+// the experts over blocks as well and pass the sigmoids through scratch;
+// large bf16 batches take 256 x 256 tiles over slices of K instead and pass
+// fp32 partial logits through scratch.
 // Ordering is by v = s + b descending, exact ties to the lower expert index;
 // a NaN score ranks below every number, so K distinct in-range experts are
 // always produced.  Gates are s_k / sum of the K selected s, summed in
@@ -236,8 +238,100 @@ __global__ __launch_bounds__(256) void route_topk_kernel(RouteArgs a) {
               a.idx + static_cast<size_t>(t) * a.top_k, a.gate + static_cast<size_t>(t) * a.top_k);
 }
 
+// ---- large bf16 batches: K split over blocks
+//
+// A 32-token block streams every centroid beside its tokens, ~9x the bytes
+// of its token rows at 256 experts; the CU's loads, not the matrix cores,
+// bound it.  Here a block takes 256 tokens x 256 experts (the grouped
+// GEMM's tile and pipeline: 8 MFMA waves, 4 load waves, 5-stage ring) over
+// one slice of K, ~4x fewer bytes per logit, and the slices make up the
+// block count.  The fp32 logits of slice s go to scores[s][T][N_r].
+using KsPipe = Pipe<FMT_BF16, 256, 256, 5, 2, ACC_TIED, 8, 4>;
+constexpr int KS_THREADS = 768;
+
+__global__ __launch_bounds__(KS_THREADS, 1) void route_part_kernel(RouteArgs a) {
+  using P = KsPipe;
+  constexpr int WM = 2;
+  __shared__ __attribute__((aligned(1024))) uint8_t ring_lds[5 * P::STAGE_BYTES];
+  uint8_t* const st[5] = {ring_lds, ring_lds + P::STAGE_BYTES, ring_lds + 2 * P::STAGE_BYTES,
+                          ring_lds + 3 * P::STAGE_BYTES, ring_lds + 4 * P::STAGE_BYTES};
+  const int w = wave_id(), lane = threadIdx.x & 63;
+  const int lr = lane & 15, lg = lane >> 4;
+  const int wm = w % WM, wn = w / WM;
+  const int t0 = blockIdx.x * 256, slice = blockIdx.y;
+  const int valid = min(256, a.T - t0);
+  const size_t row_bytes = static_cast<size_t>(a.d) * 2;
+  const int np = a.d / 64;                        // 128-byte pairs along K
+  const int pps = ceil_div(np, a.ksplit);
+  const int p0 = slice * pps, p1 = min(np, p0 + pps);   // non-empty: the host sizes ksplit so
+
+  P p;
+  const rsrc_t ru = make_rsrc(static_cast<const uint8_t*>(a.u) + static_cast<size_t>(t0) * row_bytes,
+                              static_cast<uint32_t>(valid * row_bytes));
+  p.init(ru, [&](int r) { return static_cast<uint32_t>((r < valid ? r : 0) * row_bytes); },
+         make_rsrc(a.centroids, static_cast<uint32_t>(a.n_routed * row_bytes)),
+         [&](int r) { return static_cast<uint32_t>((r < a.n_routed ? r : 0) * row_bytes); },
+         ru, [](int) { return 0u; });
+  p.krot = 2 * p0;   // K-step offset of the slice (no wrap: nks stays past every K-step)
+  const WRows<0> wr{16 * P::NJ * wn};
+  f32x4 acc[P::MI][P::NJ];
+  zero_acc(acc);
+  pipe_mainloop_ws<P, P::MI, P::MI>(p, st, 2 * (p1 - p0), wr, acc);
+  if (w >= 8) return;   // load waves hold no logits
+
+  // lane: token 16 (WM i + wm) + lr, experts 16 NJ wn + 16 j + 4 lg .. +3
+  float* const part = a.scores + static_cast<size_t>(slice) * a.T * a.n_routed;
+#pragma unroll
+  for (int i = 0; i < P::MI; ++i) {
+    const int row = 16 * (WM * i + wm) + lr;
+    if (row >= valid) continue;
+    float* const dst = part + static_cast<size_t>(t0 + row) * a.n_routed;
+#pragma unroll
+    for (int j = 0; j < P::NJ; ++j) {
+      const int e = 16 * P::NJ * wn + 16 * j + 4 * lg;
+      if (e < a.n_routed)   // n_routed % 4 == 0: all four or none
+        *reinterpret_cast<float4*>(dst + e) = make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
+    }
+  }
+}
+
+// One wave per token: the slices' logits summed in slice order, sigmoid,
+// top-K.
+template <int NRMAX>
+__global__ __launch_bounds__(256) void route_finish_kernel(RouteArgs a) {
+  constexpr int NQ = NRMAX / 64;
+  __shared__ float srow_s[4][NRMAX];
+  const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + wv;
+  float bq[NQ];
+  load_bias(a.bias, a.n_routed, bq);
+  if (t >= a.T) return;
+  float* const srow = srow_s[wv];
+  const size_t slice_stride = static_cast<size_t>(a.T) * a.n_routed;
+  const float* const src = a.scores + static_cast<size_t>(t) * a.n_routed;
+#pragma unroll
+  for (int q = 0; q < NQ; ++q) {
+    const int e = lane + 64 * q;
+    if (e < a.n_routed) {
+      float z = 0.f;
+      for (int sl = 0; sl < a.ksplit; ++sl) z += src[sl * slice_stride + e];
+      srow[e] = sigmoid_f32(z);
+    }
+  }
+  __builtin_amdgcn_wave_barrier();
+  select_topk(srow, bq, a.n_routed, a.top_k, a.idx + static_cast<size_t>(t) * a.top_k,
+              a.gate + static_cast<size_t>(t) * a.top_k);
+}
+
 template <int FMT, int NRMAX>
 hipError_t launch_route_t(const RouteArgs& a, hipStream_t s) {
+  if constexpr (FMT == FMT_BF16 && NRMAX == 256) {
+    if (a.ksplit > 0 && a.scores != nullptr) {
+      hipLaunchKernelGGL(route_part_kernel, dim3(ceil_div(a.T, 256), a.ksplit), dim3(KS_THREADS), 0, s, a);
+      hipLaunchKernelGGL((route_finish_kernel<NRMAX>), dim3(ceil_div(a.T, 4)), dim3(256), 0, s, a);
+      return hipGetLastError();
+    }
+  }
   if (route_split(a.T) && a.scores != nullptr) {
     hipLaunchKernelGGL((route_scores_kernel<FMT>), dim3(ceil_div(a.T, RBT), ceil_div(a.n_routed, SCHUNK)), dim3(512),
                        0, s, a);

@@ -12,7 +12,7 @@ import pytest
 import torch
 
 import mixture_experts_layer_deepseekmoe_amd as moe
-from moe_workloads import CONFIGS, PARITY_CONFIGS, make_inputs, to_numpy_f32
+from moe_workloads import CONFIGS, PARITY_CONFIGS, MoEConfig, make_inputs, to_numpy_f32
 from oracle import moe_oracle as O
 from tests.parity import check_routing, expert_fns, output_errors, rows_of, say
 
@@ -84,6 +84,30 @@ ROUTE_CASES = ["tiny_fp32"] + list(PARITY_CONFIGS)
 def test_route_parity(name):
     cfg = CONFIGS.get(name) or PARITY_CONFIGS[name]
     say(f"case: moe_route {name}")
+    inp = make_inputs(cfg, 0, with_weights=False)
+    shape = moe.LayerShape.from_config(cfg)
+    u, E, b = _dev(inp)
+    out = moe.moe_route(shape, u, E, b)
+    torch.cuda.synchronize()
+    r = check_routing(out, to_numpy_f32(inp.u), to_numpy_f32(inp.centroids), inp.bias.numpy(), cfg.top_k, cfg.n_routed)
+    say(f"  near ties {r['near_ties']}, descending order {r['order_ok']}")
+
+
+# Shapes on the router's K-split path (256-token tiles over slices of d):
+# a ragged last token tile with 160 experts, and 67 pairs of K cut into 14
+# slices whose last one holds 2 pairs.
+ROUTE_KSPLIT_CASES = {
+    "ksplit_ragged": MoEConfig("ksplit_ragged", T=5000, d=2048, n_routed=160, n_shared=1, inter=128, top_k=6,
+                               x_dtype="bf16", w_dtype="bf16", out_dtype="f32", e_std=0.05, b_std=0.02, cfg_id=21),
+    "ksplit_uneven": MoEConfig("ksplit_uneven", T=2100, d=4288, n_routed=256, n_shared=1, inter=128, top_k=8,
+                               x_dtype="bf16", w_dtype="bf16", out_dtype="f32", e_std=0.02, b_std=0.01, cfg_id=22),
+}
+
+
+@pytest.mark.parametrize("name", list(ROUTE_KSPLIT_CASES))
+def test_route_ksplit_parity(name):
+    cfg = ROUTE_KSPLIT_CASES[name]
+    say(f"case: moe_route {name} T={cfg.T} d={cfg.d} N_r={cfg.n_routed}")
     inp = make_inputs(cfg, 0, with_weights=False)
     shape = moe.LayerShape.from_config(cfg)
     u, E, b = _dev(inp)
