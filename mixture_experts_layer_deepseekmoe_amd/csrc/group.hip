@@ -115,10 +115,13 @@ __global__ __launch_bounds__(SCAN_THREADS) void scan_kernel(GroupArgs a, int nbl
   for (int which = 0; which < 2; ++which) {
     const int* pre = which ? tmp : cst;
     const long long total = nr ? pre[nr - 1] : 0;
-    auto seg_of = [&](int g) {   // segment of expert g (g = nr: past the end)
+    // segment of expert g (g = nr: past the end).  Experts after the last
+    // unit of cost (trailing experts without rows) stay in the last segment:
+    // every expert 0 .. nr-1 lies in some segment, and rb[MT_SEGMENTS] = nr.
+    auto seg_of = [&](int g) {
       if (g >= nr || total == 0) return g >= nr ? MT_SEGMENTS : 0;
       const long long before = g ? pre[g - 1] : 0;
-      return static_cast<int>(before * MT_SEGMENTS / total);
+      return static_cast<int>(min(before * MT_SEGMENTS / total, static_cast<long long>(MT_SEGMENTS - 1)));
     };
     if (tid == 0) rbs[which][0] = 0;
     for (int g = tid; g <= nr; g += SCAN_THREADS) {

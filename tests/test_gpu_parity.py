@@ -138,6 +138,27 @@ def test_forward_parity(name):
     assert err["rel_to_rms"] <= TOL[cfg.w_dtype], err
 
 
+@pytest.mark.parametrize("name", ["small_bf16", "wide_router"])
+def test_forward_trailing_experts_empty(name):
+    """All tokens on experts 0..K-1: the experts after them hold no rows and
+    must still fall inside the tile list's segments."""
+    cfg = PARITY_CONFIGS[name]
+    say(f"case: moe_forward {name}, all tokens on experts 0..K-1")
+    inp = make_inputs(cfg, 0)
+    _force_first_k(cfg, inp)
+    y, routing, _ = _run_forward(cfg, inp)
+    u, E, b = to_numpy_f32(inp.u), to_numpy_f32(inp.centroids), inp.bias.numpy()
+    check_routing(routing, u, E, b, cfg.top_k, cfg.n_routed)
+    counts = routing["expert_counts"].cpu().numpy()
+    assert (counts[: cfg.top_k] == cfg.T).all() and (counts[cfg.top_k:] == 0).all()
+    routed, shared = expert_fns(inp, False)
+    ref = O.layer_forward(u, E, b, cfg.top_k, routed, cfg.n_routed, shared,
+                          selection=routing["topk_idx"].cpu().numpy(), fp8=cfg.fp8)
+    err = output_errors(rows_of(y), ref["y"], u)
+    say(f"  {err}")
+    assert err["rel_to_rms"] <= TOL[cfg.w_dtype], err
+
+
 def test_forward_empty_batch():
     cfg = PARITY_CONFIGS["small_bf16"].replace(T=0)
     say("case: moe_forward T=0")
@@ -212,10 +233,20 @@ def test_skewed_bias_loop_stepwise():
 
 # ------------------------------------------------------------------ full-size workloads
 
-def _sampled_forward(name, sample):
+def _force_first_k(cfg, inp):
+    """Every token selects experts 0..K-1 (a bias of +4 on them; sigmoid
+    scores lie in (0, 1)), so all later experts get no rows."""
+    inp.bias = inp.bias.clone()
+    inp.bias[: cfg.top_k] += 4.0
+
+
+def _sampled_forward(name, sample, first_k=False):
     cfg = CONFIGS[name]
-    say(f"case: moe_forward {name} full size, oracle on tokens {sample}")
+    say(f"case: moe_forward {name} full size{' (all tokens on experts 0..K-1)' if first_k else ''}, "
+        f"oracle on tokens {sample}")
     inp = make_inputs(cfg, 0, weights_device=DEV)
+    if first_k:
+        _force_first_k(cfg, inp)
     y, routing, w = _run_forward(cfg, inp)
     u, E, b = to_numpy_f32(inp.u), to_numpy_f32(inp.centroids), inp.bias.numpy()
     r = check_routing(routing, u, E, b, cfg.top_k, cfg.n_routed)
@@ -228,6 +259,9 @@ def _sampled_forward(name, sample):
     say(f"  near ties {r['near_ties']}; sampled output error {err}")
     assert err["rel_to_rms"] <= TOL[cfg.w_dtype], err
     assert torch.isfinite(y).all()
+    if first_k:
+        counts = routing["expert_counts"].cpu().numpy()
+        assert (counts[: cfg.top_k] == cfg.T).all() and (counts[cfg.top_k:] == 0).all()
     del w, inp
     torch.cuda.empty_cache()
 
@@ -238,6 +272,11 @@ def test_full_bf16_d2048():
 
 def test_full_bf16_d7168():
     _sampled_forward("bf16_d7168", [0, 4097, 8191, 2500])
+
+
+def test_full_bf16_d7168_trailing_experts_empty():
+    # 8 experts with 8192 rows each: 256 routed m-tiles, the cost-cut segments
+    _sampled_forward("bf16_d7168", [0, 8191, 1000], first_k=True)
 
 
 def test_full_fp8_d2048():
