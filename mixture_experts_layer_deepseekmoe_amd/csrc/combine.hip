@@ -12,14 +12,20 @@ namespace moe {
 
 namespace {
 
+// Every row is read once and y is written once: non-temporal loads and
+// stores keep the streams from displacing each other in the caches
+// (measured at d = 7168, 8 + 1 rows per token: 0.280 -> 0.240 ms, 5.9 TB/s).
+typedef float f32x4v __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+
 template <int F>
 __device__ __forceinline__ void load8(const void* base, size_t off, float v[8]) {
   if constexpr (F == FMT_F32) {
-    const float4 a = *reinterpret_cast<const float4*>(static_cast<const float*>(base) + off);
-    const float4 b = *reinterpret_cast<const float4*>(static_cast<const float*>(base) + off + 4);
+    const f32x4v* p = reinterpret_cast<const f32x4v*>(static_cast<const float*>(base) + off);
+    const f32x4v a = __builtin_nontemporal_load(p), b = __builtin_nontemporal_load(p + 1);
     v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
   } else {
-    const uint4 r = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + off);
+    const u32x4v r = __builtin_nontemporal_load(reinterpret_cast<const u32x4v*>(static_cast<const uint16_t*>(base) + off));
     const uint32_t w[4] = {r.x, r.y, r.z, r.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -85,17 +91,17 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
       const int c = c0 + 512 * u;
       if (c >= a.d) continue;
       if constexpr (OF == FMT_F32) {
-        float* o = static_cast<float*>(a.out) + static_cast<size_t>(t) * d + c;
-        *reinterpret_cast<float4*>(o) = make_float4(acc[u][0], acc[u][1], acc[u][2], acc[u][3]);
-        *reinterpret_cast<float4*>(o + 4) = make_float4(acc[u][4], acc[u][5], acc[u][6], acc[u][7]);
+        f32x4v* o = reinterpret_cast<f32x4v*>(static_cast<float*>(a.out) + static_cast<size_t>(t) * d + c);
+        __builtin_nontemporal_store(f32x4v{acc[u][0], acc[u][1], acc[u][2], acc[u][3]}, o);
+        __builtin_nontemporal_store(f32x4v{acc[u][4], acc[u][5], acc[u][6], acc[u][7]}, o + 1);
       } else {
         uint32_t w[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i)
           w[i] = static_cast<uint32_t>(f32_to_bf16(acc[u][2 * i])) |
                  (static_cast<uint32_t>(f32_to_bf16(acc[u][2 * i + 1])) << 16);
-        *reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.out) + static_cast<size_t>(t) * d + c) =
-            make_uint4(w[0], w[1], w[2], w[3]);
+        __builtin_nontemporal_store(u32x4v{w[0], w[1], w[2], w[3]},
+                                    reinterpret_cast<u32x4v*>(static_cast<uint16_t*>(a.out) + static_cast<size_t>(t) * d + c));
       }
     }
   }
