@@ -32,6 +32,7 @@ __global__ __launch_bounds__(GROUP_TB) void hist_kernel(GroupArgs a) {
 }
 
 constexpr int SCAN_THREADS = 1024;
+static_assert(MAX_ROUTED + MT_SEGMENTS * MAX_SHARED < SCAN_THREADS, "one tile-list piece per scan thread");
 
 __global__ __launch_bounds__(SCAN_THREADS) void scan_kernel(GroupArgs a, int nblk) {
   __shared__ int sc[MAX_ROUTED + MAX_SHARED + 1];
@@ -43,14 +44,20 @@ __global__ __launch_bounds__(SCAN_THREADS) void scan_kernel(GroupArgs a, int nbl
   __shared__ int seg_mode;
   const int tid = threadIdx.x;
   const int nr = a.n_routed;
-  // 1. per-expert totals and per-block bases
+  // 1. per-expert totals and per-block bases, 16 blocks' counts loaded at a
+  //    time (one after the other, each load waited behind the previous store)
+  constexpr int HB = 16;
   for (int e = tid; e < nr; e += SCAN_THREADS) {
     int run = 0;
-    for (int b = 0; b < nblk; ++b) {
-      int* p = a.block_hist + static_cast<size_t>(b) * nr + e;
-      const int h = *p;
-      *p = run;
-      run += h;
+    for (int b0 = 0; b0 < nblk; b0 += HB) {
+      int h[HB];
+#pragma unroll
+      for (int j = 0; j < HB; ++j) h[j] = b0 + j < nblk ? a.block_hist[static_cast<size_t>(b0 + j) * nr + e] : 0;
+#pragma unroll
+      for (int j = 0; j < HB; ++j) {
+        if (b0 + j < nblk) a.block_hist[static_cast<size_t>(b0 + j) * nr + e] = run;
+        run += h[j];
+      }
     }
     a.counts[e] = run;
     sc[e] = run;
@@ -183,10 +190,25 @@ __global__ __launch_bounds__(SCAN_THREADS) void scan_kernel(GroupArgs a, int nbl
     pc[p] = k1 - k0;
   }
   __syncthreads();
-  if (tid == 0) {   // at most 576 pieces: a short serial scan
-    int run = 0;
-    for (int p = 0; p < np; ++p) { const int c = pc[p]; pc[p] = run; run += c; }
-    pc[np] = run;
+  // exclusive prefix of the pieces' m-tile counts (np <= 576 < SCAN_THREADS:
+  // one piece per thread), pc[np] = the total
+  {
+    const int own = tid < np ? pc[tid] : 0;
+    for (int off = 1; off < np; off <<= 1) {
+      const int add = tid < np && tid >= off ? pc[tid - off] : 0;
+      __syncthreads();
+      if (tid < np) pc[tid] += add;
+      __syncthreads();
+    }
+    const int incl = tid < np ? pc[tid] : 0;
+    __syncthreads();
+    if (tid < np) pc[tid] = incl - own;
+    if (tid == np - 1) pc[np] = incl;
+    if (np == 0 && tid == 0) pc[0] = 0;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    const int run = pc[np];
     a.mt_count[0] = run;
     // the m-tile where each segment starts, for the GEMMs' XCD ranges
     // (cut by cost only: with the cut by m-tile counts, equal tile counts per
