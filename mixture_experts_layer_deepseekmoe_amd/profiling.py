@@ -61,7 +61,8 @@ def _run(args):
 
 
 def _short(name: str) -> str:
-    for key in ("gateup_kernel", "down_kernel", "route_kernel", "combine_kernel", "hist_kernel", "scan_kernel",
+    for key in ("gateup_kernel", "down_kernel", "route_part_kernel", "route_finish_kernel", "route_scores_kernel",
+                "route_topk_kernel", "route_kernel", "combine_kernel", "hist_kernel", "scan_kernel",
                 "permute_kernel", "quant_act_kernel", "quant_weight_kernel", "bias_update_kernel"):
         if key in name:
             fmt = ""
