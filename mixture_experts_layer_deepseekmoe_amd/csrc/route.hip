@@ -88,17 +88,22 @@ __device__ __forceinline__ void load_bias(const float* bias, int n_routed, float
 // it runs the wave-specialised paired pipeline (8 waves: whole-line L2
 // requests, loads issued by their own waves); beyond, the score buffer
 // leaves room only for the 4-wave single-stage pipeline on a 4-stage ring.
+// NRMAX: the expert count rounded up to 64, 128, 256 or 512.  Experts go
+// through the MFMAs in chunks of up to 256 (one chunk of NRMAX below), so
+// no chunk loads centroid rows past the last expert.
 template <int NRMAX>
 struct RouteCfg {
   static constexpr bool WS = NRMAX <= 256;
   static constexpr int NW = WS ? 8 : 4;     // waves per block
   static constexpr int NST = WS ? 5 : 4;    // stage buffers
+  static constexpr int CHUNK = NRMAX < RCHUNK ? NRMAX : RCHUNK;   // experts per MFMA pass
+  static constexpr int EW = CHUNK / 4;      // experts per MFMA wave
 };
 
 template <int FMT, int NRMAX>
 __global__ __launch_bounds__(64 * RouteCfg<NRMAX>::NW) void route_kernel(RouteArgs a) {
   using C = RouteCfg<NRMAX>;
-  using P = Pipe<FMT, RBT, RCHUNK, C::NST>;
+  using P = Pipe<FMT, RBT, C::CHUNK, C::NST>;
   constexpr int SSTRIDE = NRMAX + 4;
   __shared__ __attribute__((aligned(1024))) uint8_t st0[P::STAGE_BYTES];
   __shared__ __attribute__((aligned(1024))) uint8_t st1[P::STAGE_BYTES];
@@ -117,10 +122,10 @@ __global__ __launch_bounds__(64 * RouteCfg<NRMAX>::NW) void route_kernel(RouteAr
   const int es = FMT == FMT_F32 ? 4 : 2;
   const size_t row_bytes = static_cast<size_t>(a.d) * es;
   const int nk = static_cast<int>(row_bytes / P::SB);
-  const WRows<0> wr{64 * (w & 3)};   // expert subtile j: rows 64 w + 16 j of the chunk
+  const WRows<0> wr{C::EW * (w & 3)};   // expert subtile j: rows EW w + 16 j of the chunk
   const int valid = min(RBT, a.T - t0);
 
-  for (int ec = 0; ec < a.n_routed; ec += RCHUNK) {
+  for (int ec = 0; ec < a.n_routed; ec += C::CHUNK) {
     P p;
     const rsrc_t ru = make_rsrc(static_cast<const uint8_t*>(a.u) + static_cast<size_t>(t0) * row_bytes,
                                 static_cast<uint32_t>(valid * row_bytes));
@@ -143,12 +148,12 @@ __global__ __launch_bounds__(64 * RouteCfg<NRMAX>::NW) void route_kernel(RouteAr
         pipe_mainloop<P, C::NST, 1>(p, st, nk, wr, acc);
     }
 
-    // lane: token 16i + lr, experts ec + 64 w + 16 j + 4lg .. +3
+    // lane: token 16i + lr, experts ec + EW w + 16 j + 4lg .. +3
 #pragma unroll
     for (int i = 0; i < P::MI; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int e = ec + 64 * w + 16 * j + 4 * lg;
+      for (int j = 0; j < P::NJ; ++j) {
+        const int e = ec + C::EW * w + 16 * j + 4 * lg;
         float* dst = sbuf + (16 * i + lr) * SSTRIDE + e;
         if (e + 3 < a.n_routed) {
           *reinterpret_cast<float4*>(dst) = make_float4(sigmoid_f32(acc[i][j][0]), sigmoid_f32(acc[i][j][1]),
@@ -346,9 +351,15 @@ hipError_t launch_route_t(const RouteArgs& a, hipStream_t s) {
 
 hipError_t launch_route(int fmt, const RouteArgs& a, hipStream_t s) {
   if (a.T == 0) return hipSuccess;
-  const bool wide = a.n_routed > 256;
-  if (fmt == FMT_BF16) return wide ? launch_route_t<FMT_BF16, 512>(a, s) : launch_route_t<FMT_BF16, 256>(a, s);
-  return wide ? launch_route_t<FMT_F32, 512>(a, s) : launch_route_t<FMT_F32, 256>(a, s);
+  const int nr = a.n_routed;
+  if (fmt == FMT_BF16) {
+    if (nr <= 64) return launch_route_t<FMT_BF16, 64>(a, s);
+    if (nr <= 128) return launch_route_t<FMT_BF16, 128>(a, s);
+    return nr <= 256 ? launch_route_t<FMT_BF16, 256>(a, s) : launch_route_t<FMT_BF16, 512>(a, s);
+  }
+  if (nr <= 64) return launch_route_t<FMT_F32, 64>(a, s);
+  if (nr <= 128) return launch_route_t<FMT_F32, 128>(a, s);
+  return nr <= 256 ? launch_route_t<FMT_F32, 256>(a, s) : launch_route_t<FMT_F32, 512>(a, s);
 }
 
 }  // namespace moe
