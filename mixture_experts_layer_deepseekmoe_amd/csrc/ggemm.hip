@@ -289,9 +289,8 @@ __device__ __forceinline__ void gateup_tile(const GateUpArgs& a, const MK& make_
 #pragma unroll
         for (int jj = 0; jj < NJ2; ++jj) {
           const int col = n0 + HW * wn + 16 * jj + 4 * lg;
-          uint32_t q = 0;
-#pragma unroll
-          for (int r = 0; r < 4; ++r) q |= f32_to_e4m3(hv[i][jj][r] * inv) << (8 * r);
+          const uint32_t q =
+              e4m3x4(hv[i][jj][0] * inv, hv[i][jj][1] * inv, hv[i][jj][2] * inv, hv[i][jj][3] * inv);
           *reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(a.h) + grow * a.inter + col) = q;
         }
         if (wn == 0 && lg == 0) a.h_scale[grow * ncb + nb] = m == 0.f ? 1.f : m / 448.f;

@@ -289,11 +289,8 @@ __global__ __launch_bounds__(256) void quant_act_kernel(const uint16_t* __restri
     m = wave_max_16(m);
     const float sc = m == 0.f ? 1.f : m / 448.f;
     const float inv = m == 0.f ? 0.f : 448.f / m;
-    uint32_t lo = 0, hi = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) lo |= f32_to_e4m3(v[i] * inv) << (8 * i);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) hi |= f32_to_e4m3(v[4 + i] * inv) << (8 * i);
+    const uint32_t lo = e4m3x4(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv);
+    const uint32_t hi = e4m3x4(v[4] * inv, v[5] * inv, v[6] * inv, v[7] * inv);
     if (live) {
       *reinterpret_cast<uint2*>(q + off) = make_uint2(lo, hi);
       if (gl == 0) scale[static_cast<size_t>(row) * ntile + tile] = sc;
@@ -345,11 +342,8 @@ __global__ __launch_bounds__(256) void quant_weight_kernel(const void* __restric
   for (int i = 0; i < 8; ++i) {
     const int c = threadIdx.x + 256 * i;
     const size_t off = base + static_cast<size_t>(c >> 4) * cols + (c & 15) * 8;
-    uint32_t lo = 0, hi = 0;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) lo |= f32_to_e4m3(v[i][j] * inv) << (8 * j);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) hi |= f32_to_e4m3(v[i][4 + j] * inv) << (8 * j);
+    const uint32_t lo = e4m3x4(v[i][0] * inv, v[i][1] * inv, v[i][2] * inv, v[i][3] * inv);
+    const uint32_t hi = e4m3x4(v[i][4] * inv, v[i][5] * inv, v[i][6] * inv, v[i][7] * inv);
     *reinterpret_cast<uint2*>(q + off) = make_uint2(lo, hi);
   }
   if (threadIdx.x == 0) scale[blk] = sc;

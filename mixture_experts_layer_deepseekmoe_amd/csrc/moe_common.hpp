@@ -36,24 +36,16 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
 // E4M3: 1 sign, 4 exponent (bias 7), 3 mantissa bits; largest finite 448,
 // no infinities, S.1111.111 is NaN, subnormals m/8 * 2^-6.  Encoding rounds
 // to nearest with ties to the even code and saturates at +-448 (values at
-// or above the 464 midpoint clamp to 448; non-finite input is outside the
-// contract and also clamps).  The sign is kept, so -0 encodes as 0x80.
-__device__ __forceinline__ uint32_t f32_to_e4m3(float x) {
-  const uint32_t sign = (__float_as_uint(x) >> 24) & 0x80u;
-  const float a = fabsf(x);
-  if (!(a < 464.0f)) return sign | 0x7Eu;
-  if (a < 0.015625f) {                       // below 2^-6: the subnormal grid, step 2^-9
-    const float q = __builtin_rintf(a * 512.0f);   // exact scaling, round half to even
-    return sign | static_cast<uint32_t>(q);        // q == 8 is the smallest normal, code 0x08
-  }
-  const uint32_t ua = __float_as_uint(a);
-  uint32_t e = (ua >> 23) - 127u + 7u;       // 1..15
-  uint32_t m = (ua >> 20) & 7u;
-  const uint32_t rest = ua & 0xFFFFFu;
-  if (rest > 0x80000u || (rest == 0x80000u && (m & 1u))) {
-    if (++m == 8u) { m = 0; ++e; }
-  }
-  return sign | (e << 3) | m;
+// or above the 464 midpoint go to 448; non-finite input is outside the
+// contract).  The sign is kept, so -0 encodes as 0x80.
+// Four values to four codes (byte r of the result = value r) through the
+// hardware conversion, which rounds to nearest even and keeps subnormals.
+// Inputs are clamped to +-448 first, so values past the largest finite code
+// saturate instead of becoming NaN (fmin/fmax keep -0, which encodes as 0x80).
+__device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
+  auto cl = [](float x) { return fminf(fmaxf(x, -448.0f), 448.0f); };
+  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(cl(a), cl(b), 0, false);
+  return static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(cl(c), cl(d), lo, true));
 }
 
 // ---------------------------------------------------------------- MFMA

@@ -75,6 +75,37 @@ def test_quantize_act_e4m3_bitexact():
     assert (scales.cpu().numpy() == s).all()
 
 
+def test_quantize_act_e4m3_rounding_grid():
+    """Tiles whose largest magnitude is 448 quantise with scale 1, so the
+    codes are the conversion itself: every finite E4M3 value of both signs,
+    every midpoint between neighbours (ties to the even code), each midpoint
+    one bf16 step above and below, subnormal ties, and -0."""
+    say("case: quantize_act_e4m3 rounding grid (scale 1)")
+    mags = O.e4m3_decode(np.arange(0, 127)).astype(np.float64)
+    mids = (mags[:-1] + mags[1:]) / 2
+    ulp = np.exp2(np.floor(np.log2(np.maximum(mids, 2.0 ** -9))) - 7)   # bf16 step at the midpoint
+    vals = np.concatenate([mags, mids, mids + ulp, mids - ulp, [2.0 ** -11, 2.0 ** -10, 3 * 2.0 ** -11]])
+    vals = np.concatenate([vals, -vals, [-0.0]])
+    xb = torch.tensor(vals, dtype=torch.float32).to(torch.bfloat16)
+    assert (xb.float().double().numpy() == vals).all()   # every value is a bf16 value
+    per = 127
+    ntiles = (len(vals) + per - 1) // per
+    x = torch.zeros((ntiles, 128), dtype=torch.bfloat16)
+    x[:, 0] = 448.0
+    flat = torch.zeros(ntiles * per, dtype=torch.bfloat16)
+    flat[: len(vals)] = xb
+    x[:, 1:] = flat.view(ntiles, per)
+    x = x.reshape(1, ntiles * 128).repeat(2, 1).contiguous()
+    codes, scales = moe.moe_quantize_act_e4m3(x.to(DEV))
+    torch.cuda.synchronize()
+    q, sc = O.quantize_act_1x128(to_numpy_f32(x))
+    assert (sc == 1.0).all()
+    assert (scales.cpu().numpy() == sc).all()
+    got = codes.cpu().numpy()
+    bad = np.nonzero(got != q)
+    assert bad[0].size == 0, [(float(to_numpy_f32(x)[r, c]), int(got[r, c]), int(q[r, c])) for r, c in zip(*bad)][:10]
+
+
 # ------------------------------------------------------------------ routing
 
 ROUTE_CASES = ["tiny_fp32"] + list(PARITY_CONFIGS)
