@@ -98,8 +98,7 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
         uint32_t w[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          w[i] = static_cast<uint32_t>(f32_to_bf16(acc[u][2 * i])) |
-                 (static_cast<uint32_t>(f32_to_bf16(acc[u][2 * i + 1])) << 16);
+          w[i] = bf16x2(acc[u][2 * i], acc[u][2 * i + 1]);
         __builtin_nontemporal_store(u32x4v{w[0], w[1], w[2], w[3]},
                                     reinterpret_cast<u32x4v*>(static_cast<uint16_t*>(a.out) + static_cast<size_t>(t) * d + c));
       }

@@ -148,8 +148,7 @@ __device__ __forceinline__ void store_tile_from_lds(const uint8_t* lds, int rows
 }
 
 __device__ __forceinline__ uint2 pack_bf16x4(float a, float b, float c, float d) {
-  return make_uint2(f32_to_bf16(a) | (static_cast<uint32_t>(f32_to_bf16(b)) << 16),
-                    f32_to_bf16(c) | (static_cast<uint32_t>(f32_to_bf16(d)) << 16));
+  return make_uint2(bf16x2(a, b), bf16x2(c, d));
 }
 
 // Calls f.template operator()<NSUB>() with NSUB = the number of row subtiles
@@ -247,8 +246,8 @@ __device__ __forceinline__ void gateup_tile(const GateUpArgs& a, const MK& make_
           if constexpr (FMT == FMT_F32) {
             *reinterpret_cast<float4*>(static_cast<float*>(a.h) + o) = make_float4(h[0], h[1], h[2], h[3]);
           } else {
-            const uint32_t lo = f32_to_bf16(h[0]) | (static_cast<uint32_t>(f32_to_bf16(h[1])) << 16);
-            const uint32_t hi = f32_to_bf16(h[2]) | (static_cast<uint32_t>(f32_to_bf16(h[3])) << 16);
+            const uint32_t lo = bf16x2(h[0], h[1]);
+            const uint32_t hi = bf16x2(h[2], h[3]);
             *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.h) + o) = make_uint2(lo, hi);
           }
         }
@@ -432,8 +431,8 @@ __device__ __forceinline__ void down_tile(const DownArgs& a, const MK& make_pipe
           *reinterpret_cast<float4*>(static_cast<float*>(a.y) + o) =
               make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
         } else {
-          const uint32_t lo = f32_to_bf16(acc[i][j][0]) | (static_cast<uint32_t>(f32_to_bf16(acc[i][j][1])) << 16);
-          const uint32_t hi = f32_to_bf16(acc[i][j][2]) | (static_cast<uint32_t>(f32_to_bf16(acc[i][j][3])) << 16);
+          const uint32_t lo = bf16x2(acc[i][j][0], acc[i][j][1]);
+          const uint32_t hi = bf16x2(acc[i][j][2], acc[i][j][3]);
           *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.y) + o) = make_uint2(lo, hi);
         }
       }

@@ -23,12 +23,13 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t h) {
   return __uint_as_float(static_cast<uint32_t>(h) << 16);
 }
 
-// Round to nearest, ties to even; NaN stays NaN.
-__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return static_cast<uint16_t>(u >> 16);
+typedef __bf16 bf16pair_t __attribute__((ext_vector_type(2)));
+typedef float f32pair_t __attribute__((ext_vector_type(2)));
+
+// Two values to two bf16 (the low half holds a) through the hardware
+// conversion: round to nearest, ties to even; NaN stays NaN.
+__device__ __forceinline__ uint32_t bf16x2(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32pair_t{a, b}, bf16pair_t));
 }
 
 // ---------------------------------------------------------------- OCP FP8 E4M3
