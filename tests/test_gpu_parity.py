@@ -164,7 +164,7 @@ def test_forward_parity(name):
     routed, shared = expert_fns(inp, False)
     ref = O.layer_forward(u, E, b, cfg.top_k, routed, cfg.n_routed, shared,
                           selection=routing["topk_idx"].cpu().numpy(), fp8=cfg.fp8)
-    err = output_errors(rows_of(y), ref["y"], u)
+    err = output_errors(rows_of(y), ref["y"], u, cfg.out_dtype)
     say(f"  {err} near ties {r['near_ties']}")
     assert err["rel_to_rms"] <= TOL[cfg.w_dtype], err
 
@@ -185,8 +185,62 @@ def test_forward_trailing_experts_empty(name):
     routed, shared = expert_fns(inp, False)
     ref = O.layer_forward(u, E, b, cfg.top_k, routed, cfg.n_routed, shared,
                           selection=routing["topk_idx"].cpu().numpy(), fp8=cfg.fp8)
-    err = output_errors(rows_of(y), ref["y"], u)
+    err = output_errors(rows_of(y), ref["y"], u, cfg.out_dtype)
     say(f"  {err}")
+    assert err["rel_to_rms"] <= TOL[cfg.w_dtype], err
+
+
+def _random_shapes(n=16, seed=2024):
+    """Seeded small layer shapes across the library's envelope: ragged T,
+    N_r on both sides of 256, K up to 16, 0-3 shared experts, every dtype
+    path; sizes bounded so the fp64 oracle stays quick."""
+    rs = np.random.RandomState(seed)
+    out = []
+    for i in range(n):
+        w = ["bf16", "bf16", "e4m3", "e4m3", "f32"][rs.randint(5)]
+        x = "f32" if w == "f32" else "bf16"
+        kmult = {"f32": 32, "bf16": 64, "e4m3": 128}[w]
+        n_routed = int(rs.choice([int(rs.randint(1, 40)), int(rs.randint(40, 300))]))
+        top_k = int(rs.randint(1, min(16, n_routed) + 1))
+        d = kmult * int(rs.randint(1, 1024 // kmult + 1))
+        inter = kmult * int(rs.randint(1, 768 // kmult + 1))
+        while n_routed * d * inter > (1 << 24):   # keep the oracle's weights small
+            if d >= inter and d > kmult:
+                d -= kmult
+            elif inter > kmult:
+                inter -= kmult
+            else:
+                n_routed = max(top_k, n_routed // 2)
+        T = int(rs.randint(1, 700))
+        out.append(MoEConfig(f"rand{i}_{w}_T{T}_d{d}_I{inter}_Nr{n_routed}_K{top_k}", T=T, d=d,
+                             n_routed=n_routed, n_shared=int(rs.randint(0, 4)), inter=inter, top_k=top_k,
+                             x_dtype=x, w_dtype=w, out_dtype=["f32", "bf16"][rs.randint(2)],
+                             w_std=0.03, e_std=0.05, b_std=0.02, cfg_id=100 + i))
+    # the edges the draw may miss: more than 256 experts (two router chunks), a single expert
+    out.append(MoEConfig("edge_bf16_T333_Nr300_K16", T=333, d=128, n_routed=300, n_shared=1, inter=128, top_k=16,
+                         x_dtype="bf16", w_dtype="bf16", out_dtype="f32", w_std=0.03, e_std=0.05, b_std=0.02,
+                         cfg_id=100 + n))
+    out.append(MoEConfig("edge_bf16_T50_Nr1_K1", T=50, d=64, n_routed=1, n_shared=0, inter=64, top_k=1,
+                         x_dtype="bf16", w_dtype="bf16", out_dtype="bf16", w_std=0.03, e_std=0.05, b_std=0.02,
+                         cfg_id=101 + n))
+    return out
+
+
+RANDOM_SHAPES = _random_shapes()
+
+
+@pytest.mark.parametrize("cfg", RANDOM_SHAPES, ids=[c.name for c in RANDOM_SHAPES])
+def test_forward_random_shapes(cfg):
+    say(f"case: moe_forward {cfg}")
+    inp = make_inputs(cfg, 0)
+    y, routing, _ = _run_forward(cfg, inp)
+    u, E, b = to_numpy_f32(inp.u), to_numpy_f32(inp.centroids), inp.bias.numpy()
+    r = check_routing(routing, u, E, b, cfg.top_k, cfg.n_routed)
+    routed, shared = expert_fns(inp, False)
+    ref = O.layer_forward(u, E, b, cfg.top_k, routed, cfg.n_routed, shared,
+                          selection=routing["topk_idx"].cpu().numpy(), fp8=cfg.fp8)
+    err = output_errors(rows_of(y), ref["y"], u, cfg.out_dtype)
+    say(f"  T={cfg.T} N_s={cfg.n_shared} out={cfg.out_dtype}: {err} near ties {r['near_ties']}")
     assert err["rel_to_rms"] <= TOL[cfg.w_dtype], err
 
 
@@ -286,7 +340,7 @@ def _sampled_forward(name, sample, first_k=False):
     ref = O.layer_forward(u[sample], E, b, cfg.top_k, routed, cfg.n_routed, shared, selection=gi[sample],
                           fp8=cfg.fp8)
     yg = rows_of(y[torch.tensor(sample, device=DEV)])
-    err = output_errors(yg, ref["y"], u[sample])
+    err = output_errors(yg, ref["y"], u[sample], cfg.out_dtype)
     say(f"  near ties {r['near_ties']}; sampled output error {err}")
     assert err["rel_to_rms"] <= TOL[cfg.w_dtype], err
     assert torch.isfinite(y).all()
