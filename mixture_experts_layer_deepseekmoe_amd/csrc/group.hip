@@ -44,8 +44,9 @@ __global__ __launch_bounds__(SCAN_THREADS) void scan_kernel(GroupArgs a, int nbl
   __shared__ int seg_mode;
   const int tid = threadIdx.x;
   const int nr = a.n_routed;
-  // 1. per-expert totals and per-block bases, 16 blocks' counts loaded at a
-  //    time (one after the other, each load waited behind the previous store)
+  // 1. per-expert totals and per-block bases.  The counts of 16 blocks are
+  //    loaded together before their bases are written back: a load, store,
+  //    load chain per block kept a single load in flight.
   constexpr int HB = 16;
   for (int e = tid; e < nr; e += SCAN_THREADS) {
     int run = 0;
