@@ -93,6 +93,19 @@ def test_valid_shapes_and_workspace_monotone():
     assert rc == 0
 
 
+def test_workspace_holds_the_router_scratch():
+    # d = 7168, 256 experts: 8192 tokens take the K-split router (8 slices of fp32 logits), 4096 tokens 16
+    # slices, 256 tokens the expert-split router (one [T][N_r] block of sigmoids)
+    def ws(T):
+        return _ws_rc(_shape(T=T, d=7168, n_routed=256, top_k=8, inter=2048))[1]
+    assert ws(8192) >= 8 * 8192 * 256 * 4
+    assert ws(4096) >= 16 * 4096 * 256 * 4
+    assert ws(256) >= 256 * 256 * 4
+    # 254 experts (not a multiple of 4) stay on the fused router: no slice logits, the rest of the layout nearly equal
+    n254 = _ws_rc(_shape(T=8192, d=7168, n_routed=254, top_k=8, inter=2048))[1]
+    assert ws(8192) - n254 >= 8 * 8192 * 256 * 4 - (1 << 20)
+
+
 FAKE = 1 << 20          # 16-byte aligned, never dereferenced: every call below fails validation
 
 
