@@ -278,14 +278,17 @@ class HipEvents:
     through the HIP runtime (the same events the library records on its
     stream), with elapsed-time readout."""
 
-    def __init__(self):
+    def __init__(self, stages=STAGES):
+        """stages: the stage names to time (the library records no event
+        for the others)."""
         self.hip = ctypes.CDLL("libamdhip64.so")
         self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
         self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
         self.hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
         self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
         self.trace = Trace()
-        for i in range(NUM_STAGES):
+        self.idx = [STAGES.index(n) for n in stages]
+        for i in self.idx:
             for arr in (self.trace.start, self.trace.stop):
                 ev = ctypes.c_void_p()
                 if self.hip.hipEventCreate(ctypes.byref(ev)) != 0:
@@ -294,7 +297,8 @@ class HipEvents:
 
     def elapsed_ms(self) -> Dict[str, float]:
         out = {}
-        for i, name in enumerate(STAGES):
+        for i in self.idx:
+            name = STAGES[i]
             self.hip.hipEventSynchronize(self.trace.stop[i])
             ms = ctypes.c_float(0)
             if self.hip.hipEventElapsedTime(ctypes.byref(ms), self.trace.start[i], self.trace.stop[i]) != 0:
@@ -303,6 +307,6 @@ class HipEvents:
         return out
 
     def close(self):
-        for i in range(NUM_STAGES):
+        for i in self.idx:
             self.hip.hipEventDestroy(self.trace.start[i])
             self.hip.hipEventDestroy(self.trace.stop[i])
