@@ -34,6 +34,34 @@ __global__ __launch_bounds__(GROUP_TB) void hist_kernel(GroupArgs a) {
 constexpr int SCAN_THREADS = 1024;
 static_assert(MAX_ROUTED + MT_SEGMENTS * MAX_SHARED < SCAN_THREADS, "one tile-list piece per scan thread");
 
+// Inclusive prefix sum of one value per thread over the whole block: within
+// each wave by shuffles, then over the 16 wave totals in the first wave.
+// Three barriers, where a block-wide Hillis-Steele scan takes two per step.
+// wsum: 16 ints of shared memory, free again when this returns.
+__device__ __forceinline__ int block_incl_scan(int v, int* wsum) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int t = __shfl_up(v, off);
+    if (lane >= off) v += t;
+  }
+  if (lane == 63) wsum[w] = v;
+  __syncthreads();
+  if (w == 0) {
+    int s = lane < SCAN_THREADS / 64 ? wsum[lane] : 0;
+#pragma unroll
+    for (int off = 1; off < SCAN_THREADS / 64; off <<= 1) {
+      const int t = __shfl_up(s, off);
+      if (lane >= off) s += t;
+    }
+    if (lane < SCAN_THREADS / 64) wsum[lane] = s;
+  }
+  __syncthreads();
+  if (w > 0) v += wsum[w - 1];
+  __syncthreads();
+  return v;
+}
+
 __global__ __launch_bounds__(SCAN_THREADS) void scan_kernel(GroupArgs a, int nblk) {
   __shared__ int sc[MAX_ROUTED + MAX_SHARED + 1];
   __shared__ int tmp[MAX_ROUTED + MAX_SHARED + 1];
@@ -42,6 +70,7 @@ __global__ __launch_bounds__(SCAN_THREADS) void scan_kernel(GroupArgs a, int nbl
   __shared__ int rbs[2][MT_SEGMENTS + 1];
   __shared__ int cst[MAX_ROUTED];
   __shared__ int seg_mode;
+  __shared__ int wsum[SCAN_THREADS / 64];
   const int tid = threadIdx.x;
   const int nr = a.n_routed;
   // 1. per-expert totals and per-block bases.  The counts of 16 blocks are
@@ -64,13 +93,12 @@ __global__ __launch_bounds__(SCAN_THREADS) void scan_kernel(GroupArgs a, int nbl
     sc[e] = run;
   }
   __syncthreads();
-  // 2. inclusive scan (Hillis-Steele) over experts, then offsets
-  for (int off = 1; off < nr; off <<= 1) {
-    for (int e = tid; e < nr; e += SCAN_THREADS) tmp[e] = sc[e] + (e >= off ? sc[e - off] : 0);
-    __syncthreads();
-    for (int e = tid; e < nr; e += SCAN_THREADS) sc[e] = tmp[e];
-    __syncthreads();
+  // 2. inclusive scan over experts (nr <= MAX_ROUTED < SCAN_THREADS: one per thread), then offsets
+  {
+    const int incl = block_incl_scan(tid < nr ? sc[tid] : 0, wsum);
+    if (tid < nr) sc[tid] = incl;
   }
+  __syncthreads();
   for (int e = tid; e <= nr; e += SCAN_THREADS) a.offsets[e] = e == 0 ? 0 : sc[e - 1];
   if (a.mtiles == nullptr) return;
   __syncthreads();
@@ -104,21 +132,15 @@ __global__ __launch_bounds__(SCAN_THREADS) void scan_kernel(GroupArgs a, int nbl
     cst[g] = n * (a.bm / 16) + ceil_div(M, 16);   // in 16-row units: the prefix stays far below 2^31
   }
   __syncthreads();
-  for (int off = 1; off < nr; off <<= 1) {
-    int v[(MAX_ROUTED + SCAN_THREADS - 1) / SCAN_THREADS], u[(MAX_ROUTED + SCAN_THREADS - 1) / SCAN_THREADS];
-    int c = 0;
-    for (int g = tid; g < nr; g += SCAN_THREADS, ++c) {
-      v[c] = tmp[g] + (g >= off ? tmp[g - off] : 0);
-      u[c] = cst[g] + (g >= off ? cst[g - off] : 0);
+  {   // inclusive prefixes of the m-tile counts and of the costs
+    const int pt = block_incl_scan(tid < nr ? tmp[tid] : 0, wsum);
+    const int pcst = block_incl_scan(tid < nr ? cst[tid] : 0, wsum);
+    if (tid < nr) {
+      tmp[tid] = pt;
+      cst[tid] = pcst;
     }
-    __syncthreads();
-    c = 0;
-    for (int g = tid; g < nr; g += SCAN_THREADS, ++c) {
-      tmp[g] = v[c];
-      cst[g] = u[c];
-    }
-    __syncthreads();
   }
+  __syncthreads();
   // rbs[0][.]: cut by cost, rbs[1][.]: cut by m-tile count
   for (int which = 0; which < 2; ++which) {
     const int* pre = which ? tmp : cst;
@@ -195,14 +217,7 @@ __global__ __launch_bounds__(SCAN_THREADS) void scan_kernel(GroupArgs a, int nbl
   // one piece per thread), pc[np] = the total
   {
     const int own = tid < np ? pc[tid] : 0;
-    for (int off = 1; off < np; off <<= 1) {
-      const int add = tid < np && tid >= off ? pc[tid - off] : 0;
-      __syncthreads();
-      if (tid < np) pc[tid] += add;
-      __syncthreads();
-    }
-    const int incl = tid < np ? pc[tid] : 0;
-    __syncthreads();
+    const int incl = block_incl_scan(own, wsum);
     if (tid < np) pc[tid] = incl - own;
     if (tid == np - 1) pc[np] = incl;
     if (np == 0 && tid == 0) pc[0] = 0;
