@@ -253,24 +253,36 @@ __global__ __launch_bounds__(SCAN_THREADS) void scan_kernel(GroupArgs a, int nbl
 
 __global__ __launch_bounds__(GROUP_TB) void permute_kernel(GroupArgs a) {
   __shared__ uint32_t mask[MAX_ROUTED][GROUP_TB / 32];
-  for (int i = threadIdx.x; i < a.n_routed * (GROUP_TB / 32); i += GROUP_TB) (&mask[0][0])[i] = 0;
-  __syncthreads();
+  __shared__ int base_s[MAX_ROUTED];   // offsets[e] + this block's base for expert e
+  const int nr = a.n_routed;
+  for (int i = threadIdx.x; i < nr * (GROUP_TB / 32); i += GROUP_TB) (&mask[0][0])[i] = 0;
+  for (int e = threadIdx.x; e < nr; e += GROUP_TB)
+    base_s[e] = a.offsets[e] + a.block_hist[static_cast<size_t>(blockIdx.x) * nr + e];
   const int tl = threadIdx.x;
   const int t = blockIdx.x * GROUP_TB + tl;
+  const bool live = t < a.T;
   const int word = tl >> 5;
   const uint32_t bit = 1u << (tl & 31);
-  if (t < a.T) {
-    for (int k = 0; k < a.top_k; ++k) atomicOr(&mask[a.idx[static_cast<size_t>(t) * a.top_k + k]][word], bit);
+  // the token's K choices, loaded together
+  int ev[MAX_TOPK];
+#pragma unroll
+  for (int k = 0; k < MAX_TOPK; ++k) ev[k] = live && k < a.top_k ? a.idx[static_cast<size_t>(t) * a.top_k + k] : 0;
+  __syncthreads();
+  if (live) {
+#pragma unroll
+    for (int k = 0; k < MAX_TOPK; ++k)
+      if (k < a.top_k) atomicOr(&mask[ev[k]][word], bit);
   }
   __syncthreads();
-  if (t < a.T) {
-    for (int k = 0; k < a.top_k; ++k) {
-      const size_t ik = static_cast<size_t>(t) * a.top_k + k;
-      const int e = a.idx[ik];
+  if (live) {
+#pragma unroll
+    for (int k = 0; k < MAX_TOPK; ++k) {
+      if (k >= a.top_k) break;
+      const int e = ev[k];
       int rank = __popc(mask[e][word] & (bit - 1u));
       for (int wd = 0; wd < word; ++wd) rank += __popc(mask[e][wd]);
-      const int p = a.offsets[e] + a.block_hist[static_cast<size_t>(blockIdx.x) * a.n_routed + e] + rank;
-      a.pos[ik] = p;
+      const int p = base_s[e] + rank;
+      a.pos[static_cast<size_t>(t) * a.top_k + k] = p;
       a.perm_token[p] = t;
     }
   }
