@@ -63,8 +63,8 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
-              "(sharding is described in DESIGN.md, not implemented); run with --gpus 1", file=sys.stderr)
+        print("bench.py measures one GPU: the library has no multi-GPU path (expert and data sharding are "
+              "designed, not implemented); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np

@@ -21,7 +21,7 @@ computes.  Sources (pages about the DeepSeek-V3 Technical Report):
   expert FFN is a SwiGLU operator; scaling is per group along the GEMM's
   inner dimension; partial sums are promoted to FP32.
 
-Readings taken where the pages are silent (each also listed in the design doc):
+Readings taken where the pages are silent:
 * Expert FFN: W_down (SiLU(W_gate x) * (W_up x)), no biases; the gate/up
   weights are stored as one [2I, d] matrix, gate rows first.
 * Gate normalisation: divide the K selected (unbiased) s by their sum.
