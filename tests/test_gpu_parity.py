@@ -245,6 +245,46 @@ def test_forward_random_shapes(cfg):
     assert err["rel_to_rms"] <= TOL[cfg.w_dtype], err
 
 
+def test_forward_replays_from_a_hip_graph():
+    """The forward allocates, clears and synchronises nothing, so it can be
+    captured into a HIP graph: each replay, with eager launches and host
+    synchronisation between replays, matches the eager result bit for bit."""
+    cfg = PARITY_CONFIGS["small_bf16_ns2"]
+    say("case: moe_forward captured in a HIP graph, small_bf16_ns2")
+    inp = make_inputs(cfg, 0)
+    shape = moe.LayerShape.from_config(cfg)
+    u, E, b = _dev(inp)
+    w = moe.prepare_weights(cfg, inp)
+    ws = moe.alloc_workspace(shape)
+    routing = moe.alloc_routing(shape)
+    y = torch.empty((cfg.T, cfg.d), dtype=torch.float32, device=DEV)
+    moe.moe_forward(shape, u, E, b, w, y=y, routing=routing, workspace=ws)
+    torch.cuda.synchronize()
+    y_ref = y.clone()
+    idx_ref = routing["topk_idx"].clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):   # warm up on the capture stream
+        moe.moe_forward(shape, u, E, b, w, y=y, routing=routing, workspace=ws)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        moe.moe_forward(shape, u, E, b, w, y=y, routing=routing, workspace=ws)
+    for rep in range(3):
+        y.zero_()
+        routing["topk_idx"].zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y, y_ref), rep
+        assert torch.equal(routing["topk_idx"], idx_ref), rep
+        # eager work between replays
+        y2 = moe.moe_forward(shape, u, E, b, w)
+        torch.cuda.synchronize()
+        assert torch.equal(y2, y_ref), rep
+
+
 def test_forward_empty_batch():
     cfg = PARITY_CONFIGS["small_bf16"].replace(T=0)
     say("case: moe_forward T=0")
