@@ -175,7 +175,7 @@ def update_bias(bias: np.ndarray, counts: np.ndarray, total_assignments: int,
 # OCP FP8 E4M3 codec and fine-grained quantisation
 # --------------------------------------------------------------------------
 
-def e4m3_decode(code: np.ndarray) -> np.ndarray:
+def _e4m3_value(code: np.ndarray) -> np.ndarray:
     """Value of OCP E4M3 codes: bias 7, 3 mantissa bits, no infinities,
     S.1111.111 = NaN, subnormals m/8 * 2^-6."""
     code = np.asarray(code, dtype=np.int64)
@@ -187,71 +187,81 @@ def e4m3_decode(code: np.ndarray) -> np.ndarray:
     return sign * mag
 
 
-_POS_VALUES = e4m3_decode(np.arange(0, 127))   # the finite non-negative values, ascending
+_E4M3_TABLE = _e4m3_value(np.arange(256))      # the value of every code
+
+
+def e4m3_decode(code: np.ndarray) -> np.ndarray:
+    """Value of OCP E4M3 codes (a look-up in the table of all 256 values)."""
+    return _E4M3_TABLE[np.asarray(code).astype(np.uint8)]
 
 
 def e4m3_encode(x: np.ndarray) -> np.ndarray:
     """Round fp32 values to the nearest E4M3 value, ties to the even code,
-    saturating at +-448 (never producing NaN).  Returns uint8 codes."""
+    saturating at +-448 (never producing NaN for finite input).  Returns
+    uint8 codes.
+
+    In the binade [2^E, 2^(E+1)), E >= -6, the E4M3 values are the multiples
+    n * 2^(E-3), n = 8..15, with code 8 (E + 7) + (n - 8); below 2^-6 the
+    subnormals are the multiples n * 2^-9, n = 0..7, with code n, which is
+    the same formula at E = -6.  Rounding |x| to the nearest multiple of its
+    binade's spacing, ties to the even multiple (an even n is an even code),
+    is therefore round to nearest even on the E4M3 grid, and n = 16 (a value
+    rounded up past its binade's top) lands on the next binade's first code.
+    Codes past 126 (448) saturate.  Every step is exact in fp64."""
     x = np.asarray(x, dtype=F64)
     a = np.abs(x)
-    hi = np.clip(np.searchsorted(_POS_VALUES, a, side="left"), 1, 126)
-    lo = hi - 1
-    dlo = a - _POS_VALUES[lo]
-    dhi = _POS_VALUES[hi] - a
-    pick_hi = (dhi < dlo) | ((dhi == dlo) & (hi % 2 == 0))
-    code = np.where(pick_hi, hi, lo)
-    code = np.where(a >= E4M3_MAX, 126, code)                  # saturate
-    code = np.where(a <= _POS_VALUES[0], 0, code)
+    _, e = np.frexp(a)                                 # a = f * 2^e, 0.5 <= f < 1 (e = 0 for a = 0)
+    E = np.where(a < 2.0 ** -6, -6, e - 1)             # the binade of a; the subnormals share E = -6
+    n = np.rint(np.ldexp(a, 3 - E)).astype(np.int64)   # a / 2^(E-3), ties to even
+    code = np.minimum(8 * E + 48 + n, 126)
     return (code | np.where(np.signbit(x), 0x80, 0)).astype(np.uint8)   # sign kept, zero too
 
 
-def _tile_scale(amax: np.float32) -> Tuple[np.float32, np.float32]:
-    """(scale, inverse scale) of one tile, both fp32."""
-    if amax == 0:
-        return F32(1.0), F32(0.0)
-    return F32(F32(amax) / F32(E4M3_MAX)), F32(F32(E4M3_MAX) / F32(amax))
+def _tile_scales(amax: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+    """(scale, inverse scale) of each tile from its fp32 amax, both fp32:
+    scale = fl32(amax / 448), inverse = fl32(448 / amax); an all-zero tile
+    gets scale 1 and inverse 0 (zero codes)."""
+    amax = np.asarray(amax, F32)
+    zero = amax == 0
+    safe = np.where(zero, F32(1.0), amax).astype(F32)
+    scale = np.where(zero, F32(1.0), safe / F32(E4M3_MAX)).astype(F32)
+    inv = np.where(zero, F32(0.0), F32(E4M3_MAX) / safe).astype(F32)
+    return scale, inv
 
 
 def quantize_act_1x128(x: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
-    """Per row, per 128-column tile: codes [R, C] uint8 and scales [R, C/128] fp32."""
+    """Per row, per 128-column tile: codes [R, C] uint8 and scales [R, C/128] fp32.
+    Each tile's codes are E4M3(fl32(x * inverse scale))."""
     x = np.asarray(x, F32)
     R, C = x.shape
     assert C % QBLOCK == 0
-    q = np.empty((R, C), dtype=np.uint8)
-    sc = np.empty((R, C // QBLOCK), dtype=F32)
-    for r in range(R):
-        for j in range(C // QBLOCK):
-            tile = x[r, j * QBLOCK:(j + 1) * QBLOCK]
-            scale, inv = _tile_scale(F32(np.max(np.abs(tile))))
-            q[r, j * QBLOCK:(j + 1) * QBLOCK] = e4m3_encode((tile * inv).astype(F32))
-            sc[r, j] = scale
-    return q, sc
+    tiles = x.reshape(R, C // QBLOCK, QBLOCK)                 # tile [r, j] = x[r, 128 j : 128 (j + 1)]
+    scale, inv = _tile_scales(np.abs(tiles).max(axis=2) if R else np.zeros((0, C // QBLOCK), F32))
+    q = e4m3_encode((tiles * inv[:, :, None]).astype(F32))
+    return q.reshape(R, C), scale
 
 
 def quantize_weight_128x128(w: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
-    """Per 128x128 block: codes [R, C] uint8 and scales [R/128, C/128] fp32."""
+    """Per 128x128 block: codes [R, C] uint8 and scales [R/128, C/128] fp32.
+    Each block's codes are E4M3(fl32(w * inverse scale))."""
     w = np.asarray(w, F32)
     R, C = w.shape
     assert R % QBLOCK == 0 and C % QBLOCK == 0
-    q = np.empty((R, C), dtype=np.uint8)
-    sc = np.empty((R // QBLOCK, C // QBLOCK), dtype=F32)
-    for i in range(R // QBLOCK):
-        for j in range(C // QBLOCK):
-            blk = w[i * QBLOCK:(i + 1) * QBLOCK, j * QBLOCK:(j + 1) * QBLOCK]
-            scale, inv = _tile_scale(F32(np.max(np.abs(blk))))
-            q[i * QBLOCK:(i + 1) * QBLOCK, j * QBLOCK:(j + 1) * QBLOCK] = e4m3_encode((blk * inv).astype(F32))
-            sc[i, j] = scale
-    return q, sc
+    blocks = w.reshape(R // QBLOCK, QBLOCK, C // QBLOCK, QBLOCK)   # block [i, j] = blocks[i, :, j, :]
+    scale, inv = _tile_scales(np.abs(blocks).max(axis=(1, 3)))
+    q = e4m3_encode((blocks * inv[:, None, :, None]).astype(F32))
+    return q.reshape(R, C), scale
 
 
 def dequantize_act(q: np.ndarray, sc: np.ndarray) -> np.ndarray:
-    return e4m3_decode(q) * np.repeat(sc.astype(F64), QBLOCK, axis=1)
+    R, C = q.shape
+    return (e4m3_decode(q).reshape(R, C // QBLOCK, QBLOCK) * sc.astype(F64)[:, :, None]).reshape(R, C)
 
 
 def dequantize_weight(q: np.ndarray, sc: np.ndarray) -> np.ndarray:
-    s = np.repeat(np.repeat(sc.astype(F64), QBLOCK, axis=0), QBLOCK, axis=1)
-    return e4m3_decode(q) * s
+    R, C = q.shape
+    blocks = e4m3_decode(q).reshape(R // QBLOCK, QBLOCK, C // QBLOCK, QBLOCK)
+    return (blocks * sc.astype(F64)[:, None, :, None]).reshape(R, C)
 
 
 # --------------------------------------------------------------------------

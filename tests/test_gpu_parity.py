@@ -165,7 +165,7 @@ def test_forward_parity(name):
     routed, shared = expert_fns(inp, False)
     ref = O.layer_forward(u, E, b, cfg.top_k, routed, cfg.n_routed, shared,
                           selection=routing["topk_idx"].cpu().numpy(), fp8=cfg.fp8)
-    err = output_errors(rows_of(y), ref["y"], u, cfg.out_dtype)
+    err = output_errors(rows_of(y), ref["y"], u, cfg.out_dtype, cfg.w_dtype)
     say(f"  {err} near ties {r['near_ties']}")
     assert err["rel_to_rms"] <= TOL[cfg.w_dtype], err
 
@@ -186,7 +186,7 @@ def test_forward_trailing_experts_empty(name):
     routed, shared = expert_fns(inp, False)
     ref = O.layer_forward(u, E, b, cfg.top_k, routed, cfg.n_routed, shared,
                           selection=routing["topk_idx"].cpu().numpy(), fp8=cfg.fp8)
-    err = output_errors(rows_of(y), ref["y"], u, cfg.out_dtype)
+    err = output_errors(rows_of(y), ref["y"], u, cfg.out_dtype, cfg.w_dtype)
     say(f"  {err}")
     assert err["rel_to_rms"] <= TOL[cfg.w_dtype], err
 
@@ -240,7 +240,7 @@ def test_forward_random_shapes(cfg):
     routed, shared = expert_fns(inp, False)
     ref = O.layer_forward(u, E, b, cfg.top_k, routed, cfg.n_routed, shared,
                           selection=routing["topk_idx"].cpu().numpy(), fp8=cfg.fp8)
-    err = output_errors(rows_of(y), ref["y"], u, cfg.out_dtype)
+    err = output_errors(rows_of(y), ref["y"], u, cfg.out_dtype, cfg.w_dtype)
     say(f"  T={cfg.T} N_s={cfg.n_shared} out={cfg.out_dtype}: {err} near ties {r['near_ties']}")
     assert err["rel_to_rms"] <= TOL[cfg.w_dtype], err
 
@@ -381,7 +381,7 @@ def _sampled_forward(name, sample, first_k=False):
     ref = O.layer_forward(u[sample], E, b, cfg.top_k, routed, cfg.n_routed, shared, selection=gi[sample],
                           fp8=cfg.fp8)
     yg = rows_of(y[torch.tensor(sample, device=DEV)])
-    err = output_errors(yg, ref["y"], u[sample], cfg.out_dtype)
+    err = output_errors(yg, ref["y"], u[sample], cfg.out_dtype, cfg.w_dtype)
     say(f"  near ties {r['near_ties']}; sampled output error {err}")
     assert err["rel_to_rms"] <= TOL[cfg.w_dtype], err
     assert torch.isfinite(y).all()

@@ -377,29 +377,98 @@ def test_fp8_ffn_against_torch_float8_composition():
     wgu = rng.normal(0, 0.05, (2 * 128, 256)).astype(np.float32)
     wd = rng.normal(0, 0.05, (256, 128)).astype(np.float32)
 
-    def tq_act(a):          # 1x128 tiles
-        a = torch.from_numpy(a)
-        t = a.view(a.shape[0], -1, 128)
-        amax = t.abs().amax(-1, keepdim=True)
-        scale = amax / 448.0
-        q = (t * (448.0 / amax)).to(torch.float8_e4m3fn).to(torch.float64)
-        return (q * scale.to(torch.float64)).view_as(a).to(torch.float64)
-
-    def tq_w(w):            # 128x128 blocks
-        w = torch.from_numpy(w)
-        R, C = w.shape
-        t = w.view(R // 128, 128, C // 128, 128)
-        amax = t.abs().amax(dim=(1, 3), keepdim=True)
-        q = (t * (448.0 / amax)).to(torch.float8_e4m3fn).to(torch.float64)
-        return (q * (amax / 448.0).to(torch.float64)).view(R, C)
-
-    xd, gd, dd = tq_act(x), tq_w(wgu), tq_w(wd)
+    xd, gd, dd = _tq_act(torch.from_numpy(x)), _tq_w(torch.from_numpy(wgu)), _tq_w(torch.from_numpy(wd))
     g, u = xd @ gd[:128].T, xd @ gd[128:].T
-    h = (torch.nn.functional.silu(g) * u).to(torch.float32).numpy()
-    ref = (tq_act(h) @ dd.T).numpy()
+    h = (torch.nn.functional.silu(g) * u).to(torch.float32)
+    ref = (_tq_act(h) @ dd.T).numpy()
 
     xq, xs = O.quantize_act_1x128(x)
     gq, gs = O.quantize_weight_128x128(wgu)
     dq, ds = O.quantize_weight_128x128(wd)
     out = O.swiglu_ffn_fp8(O.dequantize_act(xq, xs), gq, gs, dq, ds)
     np.testing.assert_allclose(out, ref, rtol=1e-12, atol=1e-12)
+
+
+# ---------------------------------------------------------------- the FP8 layer, composed independently
+
+def _tq_act(a: torch.Tensor) -> torch.Tensor:
+    """1x128 tiles through torch's float8_e4m3fn cast: scale = amax / 448 and
+    codes of a * (448 / amax), in the tensor's own precision (float32 for the
+    layer; the values are scaled to at most 448, where the cast rounds to
+    nearest even like a saturating encoder).  Both quotients are
+    tensor / tensor divisions, which torch rounds correctly (its
+    scalar / tensor form multiplies by a reciprocal and can land one ulp
+    off).  Returns the dequantised values in float64."""
+    t = a.view(a.shape[0], -1, 128)
+    amax = t.abs().amax(-1, keepdim=True)
+    c448 = torch.full_like(amax, 448.0)
+    q = (t * (c448 / amax)).to(torch.float8_e4m3fn).to(torch.float64)
+    return (q * (amax / c448).to(torch.float64)).view(a.shape)
+
+
+def _tq_w(w: torch.Tensor) -> torch.Tensor:
+    """128x128 blocks through torch's float8_e4m3fn cast (float32 scales), dequantised to float64."""
+    R, C = w.shape
+    t = w.view(R // 128, 128, C // 128, 128)
+    amax = t.abs().amax(dim=(1, 3), keepdim=True)
+    c448 = torch.full_like(amax, 448.0)
+    q = (t * (c448 / amax)).to(torch.float8_e4m3fn).to(torch.float64)
+    return (q * (amax / c448).to(torch.float64)).view(R, C)
+
+
+def _torch_fp8_layer(u, E, b, k, routed, n_routed, shared, slip=None):
+    """The whole FP8 layer from torch pieces only: router and residual on the
+    bf16 u (float64 sigmoid of the float64 logits, torch.topk on s + b,
+    gates s / sum s); every expert's two GEMMs on the 1x128-quantised u and
+    the 128x128-quantised weights in float64; h rounded to float32 and
+    quantised 1x128 before the down GEMM.  ``slip`` plants one plausible
+    mistake, for the checks that the pin would catch it."""
+    u32 = torch.from_numpy(np.asarray(u, np.float32))
+    u64 = u32.double()
+    x_router = _tq_act(u32) if slip == "router_on_fp8_u" else u64
+    s = torch.sigmoid(x_router @ torch.from_numpy(np.asarray(E, np.float64)).T)
+    v = s + torch.from_numpy(np.asarray(b, np.float32)).double()
+    idx = torch.topk(v, k, dim=1).indices
+    sel = torch.gather(s, 1, idx)
+    gate = sel / sel.sum(dim=1, keepdim=True)
+    xq = _tq_act(u32)
+
+    def ffn(x, wgu, wd):
+        g = _tq_w(torch.from_numpy(np.asarray(wgu, np.float32)))
+        dn = _tq_w(torch.from_numpy(np.asarray(wd, np.float32)))
+        I = g.shape[0] // 2
+        h = torch.nn.functional.silu(x @ g[:I].T) * (x @ g[I:].T)
+        hq = _tq_act(h) if slip == "h_not_rounded_to_f32" else _tq_act(h.to(torch.float32))
+        return hq @ dn.T
+
+    y = (xq if slip == "quantised_residual" else u64).clone()
+    for wgu, wd in shared:
+        y += ffn(u64 if slip == "shared_on_bf16_u" else xq, wgu, wd)
+    for t in range(u64.shape[0]):
+        for j in range(k):
+            y[t] += gate[t, j] * ffn(xq[t:t + 1], *routed(int(idx[t, j])))[0]
+    return y.numpy(), idx.numpy()
+
+
+def test_fp8_layer_against_torch_float8_composition():
+    """layer_forward(fp8=True) against the FP8 layer composed from torch's
+    float8_e4m3fn casts (two 128-tiles along d and along I, a shared expert,
+    K = 2), and every plausible mistake in the FP8 assembly moves the
+    result by far more than the comparison's tolerance: the shared expert
+    fed the bf16 u, a quantised residual, h quantised without its fp32
+    rounding, the router on the quantised u."""
+    from moe_workloads import MoEConfig
+    cfg = MoEConfig("fp8_layer_pin", T=12, d=256, n_routed=6, n_shared=1, inter=256, top_k=2,
+                    x_dtype="bf16", w_dtype="e4m3", out_dtype="bf16", w_std=0.05, e_std=0.05, b_std=0.02,
+                    cfg_id=90)
+    inp = make_inputs(cfg, 0)
+    u, E, b, routed, shared = _np_inputs(inp)
+    r = O.layer_forward(u, E, b, cfg.top_k, routed, cfg.n_routed, shared, fp8=True)
+    assert (r["gap"] > 1e-6).all()
+    ref, idx = _torch_fp8_layer(u, E, b, cfg.top_k, routed, cfg.n_routed, shared)
+    assert (np.sort(idx, 1) == np.sort(r["idx"], 1)).all()
+    np.testing.assert_allclose(r["y"], ref, rtol=1e-12, atol=1e-12)
+    branch = float(np.abs(r["y"] - u).max())
+    for slip in ("shared_on_bf16_u", "quantised_residual", "h_not_rounded_to_f32", "router_on_fp8_u"):
+        bad, _ = _torch_fp8_layer(u, E, b, cfg.top_k, routed, cfg.n_routed, shared, slip=slip)
+        assert np.abs(bad - r["y"]).max() > 1e-9 * branch, slip

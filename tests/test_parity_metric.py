@@ -29,3 +29,16 @@ def test_error_beyond_the_rounding_is_counted():
     yg[3, 7] += 0.05                          # far beyond 2^-8 |y| at any |y| here
     e = output_errors(yg, y, u, "bf16")
     assert e["rel_to_rms"] * e["rms"] > 0.04
+
+
+def test_fp8_output_gets_no_rounding_allowance():
+    """The FP8 bound is stated for a bf16 output: the raw error is what counts."""
+    rs = np.random.RandomState(2)
+    y = rs.randn(64, 512)
+    y[0, 0] = 4.7
+    u = np.zeros_like(y)
+    e = output_errors(_bf16(y), y, u, "bf16", "e4m3")
+    assert e["rel_to_rms"] == e["raw_rel_to_rms"] == e["max_abs"] / e["rms"]
+    assert e["rel_to_rms"] > 0
+    e16 = output_errors(_bf16(y), y, u, "bf16", "bf16")
+    assert e16["rel_to_rms"] == 0.0 and e16["raw_rel_to_rms"] == e["raw_rel_to_rms"]
