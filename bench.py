@@ -205,9 +205,33 @@ def main():
         "load": {"max_over_mean": round(float(counts.max() / counts.mean()), 3), "experts_touched": touched},
     }
 
+    if cfg.zipf_s is not None:
+        result["bias_loop"] = bias_loop(cfg, shape, u, cen, ws)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_sample_tokens, result)
     print(json.dumps(result), flush=True)
+
+
+def bias_loop(cfg, shape, u, cen, ws, steps=100):
+    """The skewed batch's aux-loss-free balancing loop: from b = 0, each step
+    routes the same batch (moe_route) and updates the bias from its expert
+    counts (moe_update_bias, gamma = 0.001); reports max/mean expert load per
+    step (before that step's update)."""
+    import torch
+
+    import mixture_experts_layer_deepseekmoe_amd as moe
+
+    b = torch.zeros(cfg.n_routed, dtype=torch.float32, device="cuda")
+    routing = moe.alloc_routing(shape)
+    TK = cfg.T * cfg.top_k
+    ratios = []
+    for _ in range(steps):
+        moe.moe_route(shape, u, cen, b, out=routing, workspace=ws)
+        moe.moe_update_bias(b, routing["expert_counts"], TK, 0.001)
+        c = routing["expert_counts"].cpu().numpy()
+        ratios.append(round(float(c.max() / c.mean()), 3))
+    log(f"[bench] bias loop: max/mean load {ratios[0]} -> {ratios[-1]} over {steps} steps")
+    return {"steps": steps, "gamma": 0.001, "b0": 0.0, "load_max_over_mean_per_step": ratios}
 
 
 def cpu_baseline(cfg, inp, n_tokens, result):
@@ -224,12 +248,20 @@ def cpu_baseline(cfg, inp, n_tokens, result):
     b = inp.bias.numpy()
     routed = lambda e: (to_numpy_f32(inp.w_gate_up[e]), to_numpy_f32(inp.w_down[e]))
     shared = [(to_numpy_f32(inp.ws_gate_up[s]), to_numpy_f32(inp.ws_down[s])) for s in range(cfg.n_shared)]
-    threads = max([p.get("num_threads", 1) for p in threadpoolctl.threadpool_info()], default=1)
-    log(f"[bench] cpu baseline: oracle on {n} tokens, {threads} BLAS threads")
-    t0 = time.perf_counter()
-    O.layer_forward(u, E, b, cfg.top_k, routed, cfg.n_routed, shared, fp8=cfg.fp8)
-    dt = time.perf_counter() - t0
-    return {"value": round(n / dt, 3), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+    # The BLAS pool gets one thread per host core this process may use,
+    # capped by OMP_NUM_THREADS where the host sets one (the CPU share of
+    # one GPU on a shared node).
+    host_cores = len(os.sched_getaffinity(0))
+    cap = int(os.environ.get("OMP_NUM_THREADS", "0") or 0)
+    threads = min(host_cores, cap) if cap > 0 else host_cores
+    with threadpoolctl.threadpool_limits(limits=threads):
+        used = max([p.get("num_threads", 1) for p in threadpoolctl.threadpool_info()], default=1)
+        log(f"[bench] cpu baseline: oracle on {n} tokens, {used} BLAS threads ({host_cores} host cores visible)")
+        t0 = time.perf_counter()
+        O.layer_forward(u, E, b, cfg.top_k, routed, cfg.n_routed, shared, fp8=cfg.fp8)
+        dt = time.perf_counter() - t0
+    return {"value": round(n / dt, 3), "unit": "tokens/s", "cores": used, "kind": "oracle",
+            "host_cores_visible": host_cores, "omp_num_threads": cap or None,
             "sample": f"first {n} of the {cfg.T} tokens of the same seeded batch, full layer (fp64 NumPy; "
                       f"expert weights streamed from HBM per expert inside the timed region)",
             "seconds": round(dt, 2)}

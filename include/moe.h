@@ -150,6 +150,30 @@ int moe_route(const moe_shape* shape, const void* u, const void* centroids, cons
               const moe_routing* out, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * Where moe_forward keeps its intermediate results inside the workspace for
+ * `shape` (byte offsets from the workspace's start), for tests and tools
+ * that inspect them after a call; not an operation of the layer.
+ *   mtiles      int32x4 [max_mtiles]  the grouped GEMMs' m-tile list: (group,
+ *               first grouped row, rows, (index within its unit << 8) | unit
+ *               size); groups 0..N_r-1 are the routed experts, N_r.. the
+ *               shared ones (shared expert s holds grouped rows T*K + s*T + t)
+ *   mt_count    int32 [2 + 8]  m-tile count, then the first m-tile of each
+ *               of the 8 list segments and the count again (all -1 after the
+ *               count when the list is not cut into per-XCD segments)
+ *   h, h_scale  H [R][I] (w_dtype; fp32 scales [R][I/128] for E4M3) and
+ *   y           Y [R][d] (fp32 for F32 weights, else bf16): the gate/up and
+ *               down GEMM outputs by grouped row, R = T*K + N_s*T
+ *   tile_rows   the most rows an m-tile holds
+ *   seg_cap     the most m-tiles one list segment may hold
+ * Returns MOE_OK, or the status moe_workspace_size() would return.
+ */
+typedef struct {
+  size_t mtiles, mt_count, h, h_scale, y;
+  int32_t max_mtiles, tile_rows, seg_cap;
+} moe_workspace_map;
+int moe_workspace_layout(const moe_shape* shape, moe_workspace_map* map);
+
+/*
  * Optional per-stage timing: when a moe_trace is passed to moe_forward, the
  * library records start[i] on `stream` before stage i and stop[i] after it
  * (hipEventRecord; the events are created and owned by the caller).  A stage

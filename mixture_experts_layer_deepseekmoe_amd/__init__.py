@@ -19,5 +19,6 @@ from .binding import (  # noqa: F401
     prepare_weights,
     status_str,
     version,
+    workspace_layout,
     workspace_size,
 )

@@ -27,8 +27,8 @@ _TORCH_DT = {F32: torch.float32, BF16: torch.bfloat16}
 # moe_status
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_LAUNCH = range(5)
 
-EXPORTED = ("moe_status_str", "moe_version", "moe_workspace_size", "moe_route", "moe_forward",
-            "moe_update_bias", "moe_quantize_weight_e4m3", "moe_quantize_act_e4m3")
+EXPORTED = ("moe_status_str", "moe_version", "moe_workspace_size", "moe_workspace_layout", "moe_route",
+            "moe_forward", "moe_update_bias", "moe_quantize_weight_e4m3", "moe_quantize_act_e4m3")
 
 
 class MoEError(RuntimeError):
@@ -55,6 +55,11 @@ class Trace(ctypes.Structure):
     _fields_ = [("start", ctypes.c_void_p * NUM_STAGES), ("stop", ctypes.c_void_p * NUM_STAGES)]
 
 
+class WorkspaceMap(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_size_t) for n in ("mtiles", "mt_count", "h", "h_scale", "y")] + \
+               [(n, ctypes.c_int32) for n in ("max_mtiles", "tile_rows", "seg_cap")]
+
+
 class Routing(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in
                 ("topk_idx", "topk_gate", "expert_counts", "expert_offsets", "perm_token", "pos")]
@@ -79,6 +84,8 @@ def load_library() -> ctypes.CDLL:
     lib.moe_version.argtypes = []
     lib.moe_workspace_size.restype = ctypes.c_int
     lib.moe_workspace_size.argtypes = [ctypes.POINTER(Shape), ctypes.POINTER(sz)]
+    lib.moe_workspace_layout.restype = ctypes.c_int
+    lib.moe_workspace_layout.argtypes = [ctypes.POINTER(Shape), ctypes.POINTER(WorkspaceMap)]
     lib.moe_route.restype = ctypes.c_int
     lib.moe_route.argtypes = [ctypes.POINTER(Shape), vp, vp, vp, ctypes.POINTER(Routing), vp, sz, vp]
     lib.moe_forward.restype = ctypes.c_int
@@ -147,6 +154,14 @@ def workspace_size(shape: LayerShape) -> int:
     n = ctypes.c_size_t(0)
     _check(load_library().moe_workspace_size(ctypes.byref(shape.c()), ctypes.byref(n)), "moe_workspace_size")
     return n.value
+
+
+def workspace_layout(shape: LayerShape) -> Dict[str, int]:
+    """Byte offsets of moe_forward's intermediate results inside its workspace
+    (the m-tile list, H, Y), with the list's capacity and tile size."""
+    m = WorkspaceMap()
+    _check(load_library().moe_workspace_layout(ctypes.byref(shape.c()), ctypes.byref(m)), "moe_workspace_layout")
+    return {n: getattr(m, n) for n, _ in WorkspaceMap._fields_}
 
 
 def alloc_workspace(shape: LayerShape, device="cuda") -> torch.Tensor:

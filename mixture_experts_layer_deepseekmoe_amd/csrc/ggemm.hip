@@ -99,16 +99,19 @@ __device__ __forceinline__ void tile_coords(const int4* mtiles, int q, int nb_n,
   mt = s + in_unit;
 }
 
-// bf16: where a tile starts along K, in 64-byte K-steps (whole pairs).  The
-// n-blocks of an m-tile (which share its X rows) start 2 pairs apart, the
-// m-tiles of a unit (which share the weight block) 1 pair apart.
+// bf16: where a tile starts along K, in 64-byte K-steps (whole pairs): the
+// n-blocks of an m-tile, which share its X rows, start 2 pairs apart.  It
+// depends on the n-block only, so the order in which an output element's
+// products are summed is the same for every row, whatever else the batch
+// holds (a row's result does not depend on how many tokens share its
+// expert, nor on which of the expert's m-tiles it falls in).
 template <int FMT>
-__device__ __forceinline__ int k_rotation(int nb, int in_unit, int nk) {
+__device__ __forceinline__ int k_rotation(int nb, int nk) {
   if constexpr (FMT != FMT_BF16) {
     return 0;
   } else {
     const int np = nk / 2;
-    return 2 * ((2 * nb + in_unit) % np);
+    return 2 * ((2 * nb) % np);
   }
 }
 
@@ -350,7 +353,7 @@ __global__ __launch_bounds__(GG<FMT>::THREADS, 1) void gateup_kernel(GateUpArgs 
            },
            FMT == FMT_E4M3 ? make_rsrc(a.x_scale, static_cast<uint32_t>(a.T * kb * 4)) : make_rsrc(a.x, 0),
            [&](int r) { return static_cast<uint32_t>(token_of(r) * kb * 4); });
-    p.krot = k_rotation<FMT>(nb, in_unit, nk);
+    p.krot = k_rotation<FMT>(nb, nk);
     p.nks = nk;
     return p;
   };
@@ -483,7 +486,7 @@ __global__ __launch_bounds__(GG<FMT>::THREADS, 1) void down_kernel(DownArgs a) {
            FMT == FMT_E4M3 ? make_rsrc(a.h_scale + static_cast<size_t>(row0) * kb, static_cast<uint32_t>(rows * kb * 4))
                            : make_rsrc(a.h, 0),
            [&](int r) { return static_cast<uint32_t>((r < rows ? r : 0) * kb * 4); });
-    p.krot = k_rotation<FMT>(nb, in_unit, nk);
+    p.krot = k_rotation<FMT>(nb, nk);
     p.nks = nk;
     return p;
   };

@@ -146,6 +146,22 @@ int moe_workspace_size(const moe_shape* shape, size_t* bytes) {
   return MOE_OK;
 }
 
+int moe_workspace_layout(const moe_shape* shape, moe_workspace_map* map) {
+  if (map == nullptr) return MOE_ERR_INVALID_ARG;
+  const int rc = validate_shape(shape);
+  if (rc != MOE_OK) return rc;
+  const Layout L = make_layout(*shape);
+  map->mtiles = L.mtiles;
+  map->mt_count = L.mtcount;
+  map->h = L.h;
+  map->h_scale = L.hs;
+  map->y = L.y;
+  map->max_mtiles = L.max_mt;
+  map->tile_rows = moe::gg_bm(fmt_of(shape->w_dtype));
+  map->seg_cap = moe::seg_cap(L.max_mt);
+  return MOE_OK;
+}
+
 int moe_route(const moe_shape* shape, const void* u, const void* centroids, const float* bias,
               const moe_routing* out, void* workspace, size_t workspace_bytes, hipStream_t stream) {
   int rc = validate_shape(shape);

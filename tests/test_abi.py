@@ -160,3 +160,25 @@ def test_binding_refuses_host_tensors():
     import torch
     with pytest.raises(ValueError):
         B._ptr(torch.zeros(4))
+
+
+@pytest.mark.parametrize("name", list(CONFIGS))
+def test_workspace_layout_lies_inside_the_workspace(name):
+    cfg = CONFIGS[name]
+    shape = moe.LayerShape.from_config(cfg)
+    total = moe.workspace_size(shape)
+    lay = moe.workspace_layout(shape)
+    R = cfg.T * cfg.top_k + cfg.n_shared * cfg.T
+    es = {"f32": 4, "bf16": 2, "e4m3": 1}[cfg.w_dtype]
+    ys = 4 if cfg.w_dtype == "f32" else 2
+    spans = [(lay["mtiles"], 16 * lay["max_mtiles"]), (lay["mt_count"], 40), (lay["h"], R * cfg.inter * es),
+             (lay["y"], R * cfg.d * ys)]
+    if cfg.fp8:
+        spans.append((lay["h_scale"], R * (cfg.inter // 128) * 4))
+    for off, n in spans:
+        assert off % 256 == 0 and off + n <= total, (off, n, total)
+    spans.sort()
+    for (o0, n0), (o1, _) in zip(spans, spans[1:]):
+        assert o0 + n0 <= o1                      # no two of them overlap
+    assert lay["tile_rows"] == (256 if cfg.w_dtype == "bf16" else 128)
+    assert lay["seg_cap"] * 8 >= lay["max_mtiles"]

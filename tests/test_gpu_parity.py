@@ -3,9 +3,12 @@
 Bar: expert indices, counts, offsets, perm_token and pos bit-exact (near ties
 within 1e-6 of the K-th biased score allowed and counted); gates to fp32
 rounding; FP8 codes and scales of the quantisers bit-exact; outputs within
-max|y_gpu - y_oracle| <= 1e-2 * rms(y_oracle) (bf16 and fp32 configs) or
-4e-2 * rms(y_oracle) (FP8), beyond the final rounding of a bf16-stored output
-(at most 2^-8 |y| per element; see tests/parity.py).
+max|y_gpu - y_oracle| <= 1e-2 * rms(y_oracle) (bf16 and fp32 configs, beyond
+the final rounding of a bf16-stored output: at most 2^-8 |y| per element) or
+4e-2 * rms(y_oracle) on the raw error (FP8, whose bound is stated for a bf16
+output); see tests/parity.py.  The full-size layers compare every token
+routed to the first or last grouped row of any m-tile, and check the m-tile
+list itself.
 """
 
 import numpy as np
@@ -28,12 +31,16 @@ def _dev(inp):
 
 
 def _run_forward(cfg, inp, weights=None):
+    """One forward through the C ABI; the routing dict also keeps the call's
+    workspace (key "workspace"), for checks of the m-tile list."""
     shape = moe.LayerShape.from_config(cfg)
     u, E, b = _dev(inp)
     w = moe.prepare_weights(cfg, inp) if weights is None else weights
     routing = moe.alloc_routing(shape)
-    y = moe.moe_forward(shape, u, E, b, w, routing=routing)
+    ws = moe.alloc_workspace(shape)
+    y = moe.moe_forward(shape, u, E, b, w, routing=routing, workspace=ws)
     torch.cuda.synchronize()
+    routing["workspace"] = ws
     return y, routing, w
 
 
@@ -168,6 +175,7 @@ def test_forward_parity(name):
     err = output_errors(rows_of(y), ref["y"], u, cfg.out_dtype, cfg.w_dtype)
     say(f"  {err} near ties {r['near_ties']}")
     assert err["rel_to_rms"] <= TOL[cfg.w_dtype], err
+    check_tile_list(cfg, moe.LayerShape.from_config(cfg), routing["workspace"], routing)
 
 
 @pytest.mark.parametrize("name", ["small_bf16", "wide_router"])
@@ -183,6 +191,7 @@ def test_forward_trailing_experts_empty(name):
     check_routing(routing, u, E, b, cfg.top_k, cfg.n_routed)
     counts = routing["expert_counts"].cpu().numpy()
     assert (counts[: cfg.top_k] == cfg.T).all() and (counts[cfg.top_k:] == 0).all()
+    check_tile_list(cfg, moe.LayerShape.from_config(cfg), routing["workspace"], routing)
     routed, shared = expert_fns(inp, False)
     ref = O.layer_forward(u, E, b, cfg.top_k, routed, cfg.n_routed, shared,
                           selection=routing["topk_idx"].cpu().numpy(), fp8=cfg.fp8)
@@ -243,6 +252,7 @@ def test_forward_random_shapes(cfg):
     err = output_errors(rows_of(y), ref["y"], u, cfg.out_dtype, cfg.w_dtype)
     say(f"  T={cfg.T} N_s={cfg.n_shared} out={cfg.out_dtype}: {err} near ties {r['near_ties']}")
     assert err["rel_to_rms"] <= TOL[cfg.w_dtype], err
+    check_tile_list(cfg, moe.LayerShape.from_config(cfg), routing["workspace"], routing)
 
 
 def test_forward_replays_from_a_hip_graph():
@@ -309,6 +319,97 @@ def test_forward_deterministic_and_batch_invariant():
     assert torch.equal(y3, y1[sub.to(DEV)])
 
 
+def _check_grouping_valid(cfg, out):
+    """Counts, offsets, perm_token and pos form a valid stable grouping of
+    whatever selection the GPU made."""
+    T, K, N = cfg.T, cfg.top_k, cfg.n_routed
+    idx = out["topk_idx"].cpu().numpy()
+    assert ((idx >= 0) & (idx < N)).all()
+    assert all(len(set(row)) == K for row in idx.tolist())
+    grp = O.group_by_expert(idx, N)
+    for key, ref in (("expert_counts", grp["counts"]), ("expert_offsets", grp["offsets"]),
+                     ("perm_token", grp["perm_token"]), ("pos", grp["pos"])):
+        assert (out[key].cpu().numpy() == ref).all(), key
+
+
+NAN_ROUTE_CASES = {
+    "split_f32": CONFIGS["tiny_fp32"],                      # scores through scratch, f32 path
+    "split_bf16": PARITY_CONFIGS["small_bf16"],             # scores through scratch
+    "fused_bf16": CONFIGS["bf16_d2048"],                    # one kernel, logits in LDS
+    "ksplit_bf16": ROUTE_KSPLIT_CASES["ksplit_ragged"],     # K slices summed in order
+}
+
+
+@pytest.mark.parametrize("name", list(NAN_ROUTE_CASES))
+def test_route_nan_scores_give_k_distinct_experts(name):
+    """A NaN in a token's activations makes all its scores NaN; the router
+    still gives it K distinct in-range experts (a NaN score ranks below
+    every number, so the K lowest indices win), the grouping stays a valid
+    permutation, and every other token is routed exactly as the oracle
+    routes it."""
+    cfg = NAN_ROUTE_CASES[name]
+    say(f"case: moe_route {name} with NaN tokens")
+    inp = make_inputs(cfg, 0, with_weights=False)
+    nan_tok = sorted({0, 7, cfg.T // 2, cfg.T - 1})
+    inp.u = inp.u.clone()
+    inp.u[nan_tok, 3] = float("nan")
+    shape = moe.LayerShape.from_config(cfg)
+    u, E, b = _dev(inp)
+    out = moe.moe_route(shape, u, E, b)
+    torch.cuda.synchronize()
+    _check_grouping_valid(cfg, out)
+    idx = out["topk_idx"].cpu().numpy()
+    assert (idx[nan_tok] == np.arange(cfg.top_k)[None, :]).all(), idx[nan_tok]
+    ok = np.setdiff1d(np.arange(cfg.T), nan_tok)
+    un = to_numpy_f32(inp.u)[ok]
+    r = O.route(un, to_numpy_f32(inp.centroids), inp.bias.numpy(), cfg.top_k)
+    from tests.parity import check_selection
+    near = check_selection(r["v"], r["gap"], r["idx"], idx[ok], cfg.top_k)
+    say(f"  {len(nan_tok)} NaN tokens on experts 0..K-1; the other {len(ok)} match the oracle ({near} near ties)")
+
+
+def test_forward_nan_tokens_leave_the_others_exact():
+    """The forward with NaN tokens: no out-of-range row anywhere, and the
+    other tokens' outputs still match the oracle."""
+    cfg = PARITY_CONFIGS["small_bf16"]
+    say("case: moe_forward small_bf16 with NaN tokens")
+    inp = make_inputs(cfg, 0)
+    nan_tok = [0, 150, 299]
+    inp.u = inp.u.clone()
+    inp.u[nan_tok, 11] = float("nan")
+    y, routing, _ = _run_forward(cfg, inp)
+    _check_grouping_valid(cfg, routing)
+    ok = np.setdiff1d(np.arange(cfg.T), nan_tok)
+    u, E, b = to_numpy_f32(inp.u), to_numpy_f32(inp.centroids), inp.bias.numpy()
+    routed, shared = expert_fns(inp, False)
+    gi = routing["topk_idx"].cpu().numpy()
+    ref = O.layer_forward(u[ok], E, b, cfg.top_k, routed, cfg.n_routed, shared, selection=gi[ok])
+    err = output_errors(rows_of(y)[ok], ref["y"], u[ok], cfg.out_dtype, cfg.w_dtype)
+    say(f"  {err}")
+    assert err["rel_to_rms"] <= TOL[cfg.w_dtype], err
+
+
+def test_forward_batch_invariant_with_multi_tile_experts():
+    """At d = 2048 every expert holds ~384 rows, two m-tiles; the same tokens
+    run alone (one m-tile per expert, another router kernel with the same
+    summation order) give bit-identical outputs."""
+    cfg = CONFIGS["bf16_d2048"]
+    say("case: batch invariance bf16_d2048 (two m-tiles per expert) vs 37 tokens alone")
+    inp = make_inputs(cfg, 0, weights_device=DEV)
+    y_full, routing, w = _run_forward(cfg, inp)
+    counts = routing["expert_counts"].cpu().numpy()
+    assert counts.max() > 256          # several experts span more than one m-tile
+    sub = torch.tensor(sorted({0, 1, 5, 100, 255, 256, 511, 1000, 2047, 2048, 3001, 4094, 4095} |
+                              set(range(1200, 1224))))
+    inp_s = make_inputs(cfg, 0, with_weights=False)
+    inp_s.u = inp.u[sub].contiguous()
+    y_sub, r_sub, _ = _run_forward(cfg.replace(T=len(sub)), inp_s, w)
+    assert torch.equal(r_sub["topk_idx"], routing["topk_idx"][sub.to(DEV)])
+    assert torch.equal(y_sub, y_full[sub.to(DEV)])
+    del w
+    torch.cuda.empty_cache()
+
+
 # ------------------------------------------------------------------ bias update
 
 def test_update_bias_bitexact():
@@ -366,52 +467,151 @@ def _force_first_k(cfg, inp):
     inp.bias[: cfg.top_k] += 4.0
 
 
-def _sampled_forward(name, sample, first_k=False):
+def read_tile_list(shape, ws):
+    """The grouped GEMMs' m-tile list and its segment starts, from the
+    workspace of the last moe_forward call."""
+    lay = moe.workspace_layout(shape)
+    mt = ws[lay["mtiles"]: lay["mtiles"] + 16 * lay["max_mtiles"]].cpu().view(torch.int32).numpy().reshape(-1, 4)
+    mc = ws[lay["mt_count"]: lay["mt_count"] + 40].cpu().view(torch.int32).numpy()
+    n = int(mc[0])
+    assert 0 <= n <= lay["max_mtiles"], (n, lay)
+    return mt[:n].copy(), mc[1:10].copy(), lay
+
+
+def check_tile_list(cfg, shape, ws, routing):
+    """The m-tile list partitions every group's grouped rows into balanced
+    tiles of at most tile_rows rows, units hold consecutive tiles of one
+    group, and the segment starts (when the list is cut per XCD) are
+    monotone, cover the list and fit the grid; returns the list."""
+    tiles, seg, lay = read_tile_list(shape, ws)
+    N, S, T, K = cfg.n_routed, cfg.n_shared, cfg.T, cfg.top_k
+    bm = lay["tile_rows"]
+    counts = routing["expert_counts"].cpu().numpy()
+    offsets = routing["expert_offsets"].cpu().numpy()
+    g, r0, rows, w = tiles[:, 0], tiles[:, 1], tiles[:, 2], tiles[:, 3]
+    assert ((g >= 0) & (g < N + S)).all(), "group out of range"
+    assert ((rows >= 1) & (rows <= bm)).all(), "tile rows out of range"
+    for grp in range(N + S):
+        first, M = (int(offsets[grp]), int(counts[grp])) if grp < N else (T * K + (grp - N) * T, T)
+        idx = np.nonzero(g == grp)[0]
+        assert len(idx) == -(-M // bm), (grp, len(idx), M)
+        if M == 0:
+            continue
+        sel = tiles[idx[np.argsort(r0[idx])]]
+        assert sel[0, 1] == first and sel[-1, 1] + sel[-1, 2] == first + M, grp
+        assert (sel[:-1, 1] + sel[:-1, 2] == sel[1:, 1]).all(), grp
+        assert sel[:, 2].max() - sel[:, 2].min() <= 1, grp          # balanced split
+    idx_in, usz = w >> 8, w & 0xFF
+    i = 0
+    while i < len(tiles):
+        k = int(usz[i])
+        assert idx_in[i] == 0 and 1 <= k <= 4, i
+        assert (idx_in[i:i + k] == np.arange(k)).all() and (usz[i:i + k] == k).all() and (g[i:i + k] == g[i]).all()
+        assert (np.diff(r0[i:i + k]) > 0).all()
+        i += k
+    if seg[0] >= 0:
+        assert seg[0] == 0 and seg[8] == len(tiles) and (np.diff(seg) >= 0).all(), seg
+        assert (np.diff(seg) <= lay["seg_cap"]).all(), (seg, lay["seg_cap"])
+        where = np.searchsorted(seg, np.arange(len(tiles)), side="right") - 1
+        for grp in range(N):                                         # whole routed experts per segment
+            assert len(set(where[g == grp].tolist())) <= 1, grp
+    else:
+        assert (seg == -1).all(), seg
+    return tiles
+
+
+def boundary_tokens(cfg, tiles, routing):
+    """Tokens at the first and the last grouped row of every m-tile."""
+    perm = routing["perm_token"].cpu().numpy()
+    TK = cfg.T * cfg.top_k
+    rows = np.unique(np.concatenate([tiles[:, 1], tiles[:, 1] + tiles[:, 2] - 1]))
+    tok = np.where(rows < TK, perm[np.minimum(rows, TK - 1)] if TK else 0, (rows - TK) % max(cfg.T, 1))
+    return np.unique(tok)
+
+
+def _fp8_weight_fn(inp, n_routed, n_shared, routed_needed):
+    """The oracle's 128x128 quantisation of every needed expert, computed in
+    a thread pool (the oracle's own functions; NumPy releases the GIL) and
+    handed to layer_forward through its fp8_weights hook."""
+    import concurrent.futures
+    import os
+
+    def one(kind, e):
+        src = (inp.w_gate_up, inp.w_down) if kind == "routed" else (inp.ws_gate_up, inp.ws_down)
+        gq, gs = O.quantize_weight_128x128(to_numpy_f32(src[0][e]))
+        dq, ds = O.quantize_weight_128x128(to_numpy_f32(src[1][e]))
+        return gq, gs, dq, ds
+
+    jobs = [("routed", int(e)) for e in routed_needed] + [("shared", s) for s in range(n_shared)]
+    with concurrent.futures.ThreadPoolExecutor(max_workers=min(16, os.cpu_count() or 1)) as ex:
+        done = dict(zip(jobs, ex.map(lambda j: one(*j), jobs)))
+    return lambda kind, e: done[(kind, e)]
+
+
+def _full_forward(name, first_k=False, extra=()):
+    """A full-size layer in the launch configuration bench.py times: routing
+    parity on every token, the m-tile list checked, and the oracle's output
+    compared on the tokens at the first and last grouped row of every m-tile
+    (plus ``extra``)."""
     cfg = CONFIGS[name]
-    say(f"case: moe_forward {name} full size{' (all tokens on experts 0..K-1)' if first_k else ''}, "
-        f"oracle on tokens {sample}")
+    say(f"case: moe_forward {name} full size{' (all tokens on experts 0..K-1)' if first_k else ''}")
     inp = make_inputs(cfg, 0, weights_device=DEV)
     if first_k:
         _force_first_k(cfg, inp)
-    y, routing, w = _run_forward(cfg, inp)
+    shape = moe.LayerShape.from_config(cfg)
+    u_d, E_d, b_d = _dev(inp)
+    w = moe.prepare_weights(cfg, inp)
+    ws = moe.alloc_workspace(shape)
+    routing = moe.alloc_routing(shape)
+    y = moe.moe_forward(shape, u_d, E_d, b_d, w, routing=routing, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.isfinite(y).all()
     u, E, b = to_numpy_f32(inp.u), to_numpy_f32(inp.centroids), inp.bias.numpy()
     r = check_routing(routing, u, E, b, cfg.top_k, cfg.n_routed)
-    routed, shared = expert_fns(inp, True)
+    tiles = check_tile_list(cfg, shape, ws, routing)
+    sample = np.unique(np.concatenate([boundary_tokens(cfg, tiles, routing), np.asarray(extra, np.int64)]))
     gi = routing["topk_idx"].cpu().numpy()
+    say(f"  near ties {r['near_ties']}; {len(tiles)} m-tiles; oracle on {len(sample)} tokens "
+        f"(first and last row of every m-tile)")
+    fp8_w = None
+    routed, shared = expert_fns(inp, True)
+    if cfg.fp8:
+        fp8_w = _fp8_weight_fn(inp, cfg.n_routed, cfg.n_shared, np.unique(gi[sample]))
+        routed = lambda e: (None, None)
+        shared = [(None, None)] * cfg.n_shared
     ref = O.layer_forward(u[sample], E, b, cfg.top_k, routed, cfg.n_routed, shared, selection=gi[sample],
-                          fp8=cfg.fp8)
-    yg = rows_of(y[torch.tensor(sample, device=DEV)])
+                          fp8=cfg.fp8, fp8_weights=fp8_w)
+    yg = rows_of(y[torch.as_tensor(sample, device=DEV)])
     err = output_errors(yg, ref["y"], u[sample], cfg.out_dtype, cfg.w_dtype)
-    say(f"  near ties {r['near_ties']}; sampled output error {err}")
+    say(f"  sampled output error {err}")
     assert err["rel_to_rms"] <= TOL[cfg.w_dtype], err
-    assert torch.isfinite(y).all()
     if first_k:
         counts = routing["expert_counts"].cpu().numpy()
         assert (counts[: cfg.top_k] == cfg.T).all() and (counts[cfg.top_k:] == 0).all()
-    del w, inp
+    del w, inp, ws
     torch.cuda.empty_cache()
 
 
 def test_full_bf16_d2048():
-    _sampled_forward("bf16_d2048", [0, 1, 2047, 4095, 1234, 3000])
+    _full_forward("bf16_d2048", extra=[0, 4095])
 
 
 def test_full_bf16_d7168():
-    _sampled_forward("bf16_d7168", [0, 4097, 8191, 2500])
+    _full_forward("bf16_d7168", extra=[0, 8191])
 
 
 def test_full_bf16_d7168_trailing_experts_empty():
     # 8 experts with 8192 rows each: 256 routed m-tiles, the cost-cut segments
-    _sampled_forward("bf16_d7168", [0, 8191, 1000], first_k=True)
+    _full_forward("bf16_d7168", first_k=True)
 
 
 def test_full_fp8_d2048():
-    _sampled_forward("fp8_d2048", [0, 4095, 777])
+    _full_forward("fp8_d2048", extra=[0, 4095])
 
 
 def test_full_fp8_d7168():
-    _sampled_forward("fp8_d7168", [0, 8191, 3333])
+    _full_forward("fp8_d7168", extra=[0, 8191])
 
 
 def test_full_skew_decode_d7168():
-    _sampled_forward("skew_decode_d7168", [0, 100, 255])
+    _full_forward("skew_decode_d7168", extra=[0, 255])
