@@ -205,6 +205,26 @@ int moe_forward(const moe_shape* shape, const void* u, const void* centroids, co
                 size_t workspace_bytes, const moe_trace* trace, hipStream_t stream);
 
 /*
+ * moe_forward for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same computation and kernels, bit-identical results, with no workspace
+ * argument.  The intermediate results live in a device array of
+ * MOE_STATIC_SCRATCH_BYTES inside the library, one per device, held from the
+ * device's first call until the process ends; the call itself allocates,
+ * frees and clears nothing.  A shape whose workspace (moe_workspace_size)
+ * exceeds that returns MOE_ERR_WORKSPACE before any work is enqueued; 64 MiB
+ * holds, e.g., decode batches of up to about 400 tokens at d = 7168, I = 2048,
+ * K = 8 + 1 shared expert (bf16).  All calls on one device share its array:
+ * calls that overlap on a device (different streams, or host threads) race
+ * and must be serialised by the caller; calls on one stream are ordered.
+ * The first call on each device also looks up the array's device address.
+ */
+#define MOE_STATIC_SCRATCH_BYTES (64u << 20)
+int moe_forward_static(const moe_shape* shape, const void* u, const void* centroids, const float* bias,
+                       const moe_weights* weights, void* y, const moe_routing* routing, const moe_trace* trace,
+                       hipStream_t stream);
+
+/*
  * Aux-loss-free bias update, in place:
  *   bias[i] += gamma if n_routed * counts[i] <  total_assignments   (underloaded)
  *   bias[i] -= gamma if n_routed * counts[i] >  total_assignments   (overloaded)

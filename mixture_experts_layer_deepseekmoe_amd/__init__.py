@@ -12,6 +12,7 @@ from .binding import (  # noqa: F401
     alloc_workspace,
     load_library,
     moe_forward,
+    moe_forward_static,
     moe_quantize_act_e4m3,
     moe_quantize_weight_e4m3,
     moe_route,

@@ -28,7 +28,10 @@ _TORCH_DT = {F32: torch.float32, BF16: torch.bfloat16}
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_LAUNCH = range(5)
 
 EXPORTED = ("moe_status_str", "moe_version", "moe_workspace_size", "moe_workspace_layout", "moe_route",
-            "moe_forward", "moe_update_bias", "moe_quantize_weight_e4m3", "moe_quantize_act_e4m3")
+            "moe_forward", "moe_forward_static", "moe_update_bias", "moe_quantize_weight_e4m3",
+            "moe_quantize_act_e4m3")
+
+STATIC_SCRATCH_BYTES = 64 << 20   # MOE_STATIC_SCRATCH_BYTES
 
 
 class MoEError(RuntimeError):
@@ -91,6 +94,9 @@ def load_library() -> ctypes.CDLL:
     lib.moe_forward.restype = ctypes.c_int
     lib.moe_forward.argtypes = [ctypes.POINTER(Shape), vp, vp, vp, ctypes.POINTER(Weights), vp,
                                 ctypes.POINTER(Routing), vp, sz, ctypes.POINTER(Trace), vp]
+    lib.moe_forward_static.restype = ctypes.c_int
+    lib.moe_forward_static.argtypes = [ctypes.POINTER(Shape), vp, vp, vp, ctypes.POINTER(Weights), vp,
+                                       ctypes.POINTER(Routing), ctypes.POINTER(Trace), vp]
     lib.moe_update_bias.restype = ctypes.c_int
     lib.moe_update_bias.argtypes = [vp, vp, i32, i64, ctypes.c_float, vp]
     lib.moe_quantize_weight_e4m3.restype = ctypes.c_int
@@ -233,6 +239,22 @@ def moe_forward(shape: LayerShape, u: torch.Tensor, centroids: torch.Tensor, bia
                          ctypes.byref(weights.c()), _ptr(y), ctypes.byref(rs) if rs is not None else None,
                          _ptr(ws), ws.numel(), ctypes.byref(trace) if trace is not None else None, _stream())
     _check(rc, "moe_forward")
+    return y
+
+
+def moe_forward_static(shape: LayerShape, u: torch.Tensor, centroids: torch.Tensor, bias: torch.Tensor,
+                       weights: ExpertWeights, y: torch.Tensor, routing: Optional[Dict[str, torch.Tensor]] = None,
+                       trace: Optional[Trace] = None) -> torch.Tensor:
+    """The layer forward on the library's own per-device scratch array (no
+    workspace argument; the library allocates nothing).  ``y`` must be given
+    (this call is for callers that cannot allocate).  Calls that overlap on
+    one device race on that array."""
+    lib = load_library()
+    rs = _routing_struct(routing)
+    rc = lib.moe_forward_static(ctypes.byref(shape.c()), _ptr(u), _ptr(centroids), _ptr(bias),
+                                ctypes.byref(weights.c()), _ptr(y), ctypes.byref(rs) if rs is not None else None,
+                                ctypes.byref(trace) if trace is not None else None, _stream())
+    _check(rc, "moe_forward_static")
     return y
 
 

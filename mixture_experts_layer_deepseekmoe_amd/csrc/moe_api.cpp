@@ -5,6 +5,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
 #include "kernels.hpp"
 
 namespace {
@@ -121,6 +123,41 @@ int run_route(const moe_shape& s, const void* u, const void* cen, const float* b
   return check_launch(moe::launch_group(ga, st));
 }
 
+int validate_forward(const moe_shape* shape, const void* u, const void* centroids, const float* bias,
+                     const moe_weights* wt, const void* y);
+int run_forward(const moe_shape& s, const Layout& L, const void* u, const void* centroids, const float* bias,
+                const moe_weights* wt, void* y, const moe_routing* routing, void* workspace, const moe_trace* trace,
+                hipStream_t stream);
+
+// ---- the workspace of moe_forward_static
+//
+// A file-scope device array; every device the library runs on holds its own
+// copy (at its own address) until the process ends.  In host code `scratch`
+// names a host-side stand-in, not device memory: its device address comes
+// from hipGetSymbolAddress, taken once per device (with that device current)
+// on the device's first moe_forward_static call, and only that address is
+// ever handed to a kernel.  Nothing in the forward needs the workspace to
+// start at zero: every kernel writes what a later one reads in the same call.
+constexpr size_t kStaticScratchBytes = MOE_STATIC_SCRATCH_BYTES;
+static __device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_addr[kMaxDevices] = {};
+
+int static_scratch(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return MOE_ERR_LAUNCH;
+  if (dev < 0 || dev >= kMaxDevices) return MOE_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_addr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return MOE_ERR_LAUNCH;
+    g_scratch_addr[dev] = p;
+  }
+  *out = g_scratch_addr[dev];
+  return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -182,7 +219,33 @@ int moe_route(const moe_shape* shape, const void* u, const void* centroids, cons
 int moe_forward(const moe_shape* shape, const void* u, const void* centroids, const float* bias,
                 const moe_weights* wt, void* y, const moe_routing* routing, void* workspace, size_t workspace_bytes,
                 const moe_trace* trace, hipStream_t stream) {
-  int rc = validate_shape(shape);
+  const int rc = validate_forward(shape, u, centroids, bias, wt, y);
+  if (rc != MOE_OK) return rc;
+  const Layout L = make_layout(*shape);
+  if (workspace == nullptr || workspace_bytes < L.total) return MOE_ERR_WORKSPACE;
+  return run_forward(*shape, L, u, centroids, bias, wt, y, routing, workspace, trace, stream);
+}
+
+int moe_forward_static(const moe_shape* shape, const void* u, const void* centroids, const float* bias,
+                       const moe_weights* wt, void* y, const moe_routing* routing, const moe_trace* trace,
+                       hipStream_t stream) {
+  int rc = validate_forward(shape, u, centroids, bias, wt, y);
+  if (rc != MOE_OK) return rc;
+  const Layout L = make_layout(*shape);
+  if (L.total > kStaticScratchBytes) return MOE_ERR_WORKSPACE;
+  void* ws = nullptr;
+  rc = static_scratch(&ws);
+  if (rc != MOE_OK) return rc;
+  return run_forward(*shape, L, u, centroids, bias, wt, y, routing, ws, trace, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+int validate_forward(const moe_shape* shape, const void* u, const void* centroids, const float* bias,
+                     const moe_weights* wt, const void* y) {
+  const int rc = validate_shape(shape);
   if (rc != MOE_OK) return rc;
   const moe_shape& s = *shape;
   const bool fp8 = s.w_dtype == MOE_DTYPE_E4M3;
@@ -196,9 +259,16 @@ int moe_forward(const moe_shape* shape, const void* u, const void* centroids, co
   if (fp8 && (wt->s_gate_up == nullptr || wt->s_down == nullptr ||
               (s.n_shared > 0 && (wt->ss_gate_up == nullptr || wt->ss_down == nullptr))))
     return MOE_ERR_INVALID_ARG;
-  const Layout L = make_layout(s);
-  if (workspace == nullptr || workspace_bytes < L.total) return MOE_ERR_WORKSPACE;
+  return MOE_OK;
+}
 
+// The whole forward on a workspace of at least L.total bytes (arguments
+// already validated).
+int run_forward(const moe_shape& s, const Layout& L, const void* u, const void* centroids, const float* bias,
+                const moe_weights* wt, void* y, const moe_routing* routing, void* workspace, const moe_trace* trace,
+                hipStream_t stream) {
+  int rc = MOE_OK;
+  const bool fp8 = s.w_dtype == MOE_DTYPE_E4M3;
   moe_routing r{};
   if (routing != nullptr) r = *routing;
   int32_t* idx = r.topk_idx ? r.topk_idx : at<int32_t>(workspace, L.idx);
@@ -262,6 +332,10 @@ int moe_forward(const moe_shape* shape, const void* u, const void* centroids, co
   stg.end(MOE_STAGE_COMBINE);
   return MOE_OK;
 }
+
+}  // namespace
+
+extern "C" {
 
 int moe_update_bias(float* bias, const int32_t* counts, int32_t n_routed, int64_t total_assignments, float gamma,
                     hipStream_t stream) {
