@@ -142,7 +142,9 @@ int moe_workspace_size(const moe_shape* shape, size_t* bytes);
 
 /*
  * Routing only: affinities, biased top-K, normalised gates, and the stable
- * grouping of assignments by expert.  Computes every field of `out` (all
+ * grouping of assignments by expert.  Defined by the xyznot summary of the
+ * DeepSeek-V3 Technical Report, section 2: s_{i,t} = Sigmoid(u_t^T e_i), the
+ * top-K_r over s + b for g', and g = g' normalised over the selected experts.  Computes every field of `out` (all
  * must be non-null).  u: [T][d] x_dtype; centroids: [N_r][d] x_dtype;
  * bias: [N_r] fp32.  The affinity GEMM accumulates in fp32.
  */
@@ -194,7 +196,10 @@ typedef struct {
 } moe_trace;
 
 /*
- * The layer forward: y[T][d] (out_dtype) = h'.  `routing` may be null, and so
+ * The layer forward: y[T][d] (out_dtype) = h', the DeepSeekMoE layer output
+ * of the xyznot summary, section 2 (u_t plus the shared experts' FFNs plus
+ * the gate-weighted routed experts' FFNs; each FFN the SwiGLU operator of the
+ * report's FP8 training section).  `routing` may be null, and so
  * may any of its fields; non-null fields receive the routing results.
  * Expert outputs are accumulated in fp32 and stored in bf16 between the
  * kernels (fp32 when w_dtype is F32); the final sum is fp32.  `trace` may be
@@ -225,7 +230,9 @@ int moe_forward_static(const moe_shape* shape, const void* u, const void* centro
                        hipStream_t stream);
 
 /*
- * Aux-loss-free bias update, in place:
+ * Aux-loss-free bias update (xyznot summary, section 2: b_i is lowered by
+ * gamma for an overloaded expert and raised by gamma for an underloaded one),
+ * in place:
  *   bias[i] += gamma if n_routed * counts[i] <  total_assignments   (underloaded)
  *   bias[i] -= gamma if n_routed * counts[i] >  total_assignments   (overloaded)
  *   unchanged        if equal
@@ -237,7 +244,8 @@ int moe_update_bias(float* bias, const int32_t* counts, int32_t n_routed, int64_
                     hipStream_t stream);
 
 /*
- * FP8 weight preparation (done once, offline): quantise `n` row-major
+ * FP8 weight preparation (done once, offline; the 128x128 weight blocks of
+ * the FP8 granularity in the xyznot summary's key-ideas list): quantise `n` row-major
  * [rows][cols] matrices (src_dtype F32 or BF16) to OCP E4M3 with one fp32
  * scale per 128x128 block: scale = amax/448, code = E4M3(x * (448/amax))
  * rounded to nearest even and saturated; scale 1 and zero codes for an
@@ -248,8 +256,8 @@ int moe_quantize_weight_e4m3(const void* src, int32_t src_dtype, int64_t n, int3
                              uint8_t* codes, float* scales, hipStream_t stream);
 
 /*
- * FP8 activation quantisation, as moe_forward applies it to u: per row, per
- * 1x128 tile, scale = amax/448 and E4M3 codes (same rounding as above).
+ * FP8 activation quantisation, as moe_forward applies it to u (the 1x128
+ * activation tiles of the same key-ideas list): per row, per 1x128 tile, scale = amax/448 and E4M3 codes (same rounding as above).
  * src: [rows][cols] bf16; codes: [rows][cols]; scales: [rows][cols/128].
  */
 int moe_quantize_act_e4m3(const void* src, int32_t rows, int32_t cols, uint8_t* codes, float* scales,
