@@ -26,7 +26,10 @@ Readings taken where the pages are silent:
   weights are stored as one [2I, d] matrix, gate rows first.
 * Gate normalisation: divide the K selected (unbiased) s by their sum.
 * Top-K order: descending biased score v = s + b; exact ties go to the lower
-  expert index.  Selection is global over all N_r experts.
+  expert index.  Selection is global over all N_r experts, or, in the
+  group-limited variant (the summary's all-to-all paragraph: a token lands
+  on a median of 3.2 experts per node), confined to the topk_groups expert
+  groups with the largest sums of their ceil(K / topk_groups) best v.
 * Bias update: the load of expert i is its count over the batch of one
   routing call; it is overloaded when N_r * count_i > T * K, underloaded when
   below, unchanged at equality; b and gamma are fp32.
@@ -100,16 +103,74 @@ def select_topk(s: np.ndarray, bias: np.ndarray, k: int) -> Dict[str, np.ndarray
     return {"idx": idx, "v": v, "gap": gap}
 
 
+def group_scores(v: np.ndarray, n_groups: int, q: int) -> np.ndarray:
+    """Score of each expert group for each token: the sum of the group's q
+    largest biased scores v.  Groups are n_groups equal runs of consecutive
+    experts (group g holds experts g*S .. g*S + S - 1, S = N_r / n_groups)."""
+    T, n = v.shape
+    S = n // n_groups
+    out = np.empty((T, n_groups))
+    for t in range(T):
+        for g in range(n_groups):
+            members = np.sort(v[t, g * S:(g + 1) * S])[::-1]
+            out[t, g] = members[:q].sum()
+    return out
+
+
+def select_topk_grouped(s: np.ndarray, bias: np.ndarray, k: int, n_groups: int,
+                        topk_groups: int) -> Dict[str, np.ndarray]:
+    """Group-limited biased top-K (a token's experts come from at most
+    topk_groups of the n_groups expert groups, e.g. the devices or nodes the
+    experts live on).
+
+    Reading (the pages give only the effect, a median of 3.2 experts per
+    node, not the rule): a token ranks the groups by their score, the sum of
+    the group's q = ceil(K / topk_groups) largest biased scores (at most the
+    group size), keeps the topk_groups best groups (ties to the lower group
+    index), then takes its K largest biased scores among those groups'
+    experts, listed in descending v (ties to the lower expert index).
+    ``gap`` is v_(K) - v_(K+1) among the kept groups' experts;
+    ``group_gap`` is the margin of the last kept group's score over the
+    first one left out (inf when every group is kept)."""
+    s = np.asarray(s, F64)
+    v = s + np.asarray(bias, F32).astype(F64)[None, :]
+    T, n = v.shape
+    S = n // n_groups
+    q = min(math.ceil(k / topk_groups), S)
+    gs = group_scores(v, n_groups, q)
+    idx = np.empty((T, k), dtype=np.int32)
+    gap = np.full(T, np.inf)
+    group_gap = np.full(T, np.inf)
+    groups = np.empty((T, topk_groups), dtype=np.int32)
+    for t in range(T):
+        gorder = np.argsort(-gs[t], kind="stable")           # stable: equal scores keep group order
+        kept = np.sort(gorder[:topk_groups])
+        groups[t] = gorder[:topk_groups]
+        if topk_groups < n_groups:
+            group_gap[t] = gs[t, gorder[topk_groups - 1]] - gs[t, gorder[topk_groups]]
+        allowed = np.concatenate([np.arange(g * S, (g + 1) * S) for g in kept])   # ascending expert index
+        order = allowed[np.argsort(-v[t, allowed], kind="stable")]
+        idx[t] = order[:k]
+        if k < len(allowed):
+            gap[t] = v[t, order[k - 1]] - v[t, order[k]]
+    return {"idx": idx, "v": v, "gap": gap, "group_gap": group_gap, "groups": groups, "group_score": gs}
+
+
 def normalised_gates(s: np.ndarray, idx: np.ndarray) -> np.ndarray:
     """g_{t,k} = s_{t,idx[t,k]} / sum_k' s_{t,idx[t,k']}; the bias never enters."""
     sel = np.take_along_axis(np.asarray(s, F64), idx.astype(np.int64), axis=1)
     return sel / sel.sum(axis=1, keepdims=True)
 
 
-def route(u, centroids, bias, k: int, selection: Optional[np.ndarray] = None) -> Dict[str, np.ndarray]:
-    """Affinities, selection (or an imposed ``selection``), and gates."""
+def route(u, centroids, bias, k: int, selection: Optional[np.ndarray] = None, n_groups: int = 1,
+          topk_groups: int = 1) -> Dict[str, np.ndarray]:
+    """Affinities, selection (or an imposed ``selection``), and gates.  With
+    topk_groups < n_groups the selection is group-limited."""
     s = affinities(u, centroids)
-    r = select_topk(s, bias, k)
+    if topk_groups < n_groups:
+        r = select_topk_grouped(s, bias, k, n_groups, topk_groups)
+    else:
+        r = select_topk(s, bias, k)
     if selection is not None:
         r["idx"] = np.asarray(selection, dtype=np.int32)
     r["s"] = s
@@ -292,7 +353,8 @@ ExpertFn = Callable[[int], Tuple[np.ndarray, np.ndarray]]
 def layer_forward(u: np.ndarray, centroids: np.ndarray, bias: np.ndarray, k: int,
                   routed: ExpertFn, n_routed: int, shared: Sequence[Tuple[np.ndarray, np.ndarray]],
                   selection: Optional[np.ndarray] = None, fp8: bool = False,
-                  fp8_weights: Optional[Callable[[str, int], Tuple]] = None) -> Dict[str, np.ndarray]:
+                  fp8_weights: Optional[Callable[[str, int], Tuple]] = None, n_groups: int = 1,
+                  topk_groups: int = 1) -> Dict[str, np.ndarray]:
     """h'_t = u_t + sum_s FFN^(s)_s(u_t) + sum_k g_{t,k} FFN^(r)_{idx[t,k]}(u_t).
 
     ``routed(e)`` returns expert e's (w_gate_up [2I, d], w_down [d, I]) as
@@ -300,10 +362,11 @@ def layer_forward(u: np.ndarray, centroids: np.ndarray, bias: np.ndarray, k: int
     shared experts the same way.  With ``fp8``, the expert weights are
     quantised 128x128 here (or taken pre-quantised from ``fp8_weights(kind, e)``
     returning (gu_q, gu_s, d_q, d_s)), u is quantised 1x128 for the expert
-    GEMMs, and the router and the residual use the unquantised u.
+    GEMMs, and the router and the residual use the unquantised u.  With
+    topk_groups < n_groups the routing is group-limited (select_topk_grouped).
     """
     u64 = np.asarray(u, F64)
-    r = route(u64, centroids, bias, k, selection)
+    r = route(u64, centroids, bias, k, selection, n_groups, topk_groups)
     idx, gate = r["idx"], r["gate"]
     T, d = u64.shape
 

@@ -472,3 +472,73 @@ def test_fp8_layer_against_torch_float8_composition():
     for slip in ("shared_on_bf16_u", "quantised_residual", "h_not_rounded_to_f32", "router_on_fp8_u"):
         bad, _ = _torch_fp8_layer(u, E, b, cfg.top_k, routed, cfg.n_routed, shared, slip=slip)
         assert np.abs(bad - r["y"]).max() > 1e-9 * branch, slip
+
+
+# ---------------------------------------------------------------- group-limited routing
+
+def test_grouped_selection_hand_worked():
+    """8 experts in 4 groups of 2, K = 3.  With 2 groups kept, q = 2 and a
+    group's score is the sum of both members: groups 1 (0.5 + 0.6 = 1.1) and
+    0 (0.9 + 0.1 = 1.0) beat group 2 (0.85), so expert 4 (0.8, the second
+    best overall) is left out: [0, 3, 2].  With 3 groups kept, q = 1 (the
+    group's best member): groups 0, 2, 1 -> the global top-3 [0, 4, 3]."""
+    v = np.array([[0.9, 0.1, 0.5, 0.6, 0.8, 0.05, 0.3, 0.35]])
+    r = O.select_topk_grouped(v, np.zeros(8, np.float32), 3, 4, 2)
+    assert r["idx"][0].tolist() == [0, 3, 2]
+    np.testing.assert_allclose(r["group_score"][0], [1.0, 1.1, 0.85, 0.65], rtol=1e-15)
+    assert sorted(r["groups"][0].tolist()) == [0, 1]
+    assert r["gap"][0] == pytest.approx(0.5 - 0.1, abs=1e-15)       # best expert left in the kept groups: 1 (0.1)
+    assert r["group_gap"][0] == pytest.approx(1.0 - 0.85, abs=1e-15)
+    r3 = O.select_topk_grouped(v, np.zeros(8, np.float32), 3, 4, 3)
+    assert r3["idx"][0].tolist() == [0, 4, 3] == O.select_topk(v, np.zeros(8, np.float32), 3)["idx"][0].tolist()
+
+
+def test_grouped_selection_special_cases():
+    rng = np.random.default_rng(21)
+    s = O.sigmoid(rng.normal(0, 1, (60, 24)))
+    b = rng.normal(0, 0.05, 24).astype(np.float32)
+    full = O.select_topk(s, b, 5)
+    # every group kept: the global selection
+    allg = O.select_topk_grouped(s, b, 5, 6, 6)
+    assert (allg["idx"] == full["idx"]).all()
+    # one expert per group, at least K groups kept: q = 1, the kept groups are the best experts
+    single = O.select_topk_grouped(s, b, 5, 24, 7)
+    assert (single["idx"] == full["idx"]).all()
+
+
+def test_grouped_selection_brute_force():
+    """Tiny inputs: the kept groups maximise the total group score over all
+    subsets of topk_groups groups, and the K experts maximise the sum of v
+    over all K-subsets of the kept groups' experts; the selection spans at
+    most topk_groups groups and beats every other expert of those groups."""
+    rng = np.random.default_rng(22)
+    n, G, M, K = 12, 4, 2, 3
+    S = n // G
+    s = O.sigmoid(rng.normal(0, 1.5, (40, n)))
+    b = rng.normal(0, 0.1, n).astype(np.float32)
+    r = O.select_topk_grouped(s, b, K, G, M)
+    v = s + b.astype(np.float64)
+    q = math.ceil(K / M)
+    for t in range(40):
+        gsc = [sorted(v[t, g * S:(g + 1) * S], reverse=True)[:q] for g in range(G)]
+        gsum = [sum(x) for x in gsc]
+        best = max(itertools.combinations(range(G), M), key=lambda c: (sum(gsum[g] for g in c), tuple(-g for g in c)))
+        assert set(r["groups"][t].tolist()) == set(best)
+        allowed = [e for g in best for e in range(g * S, (g + 1) * S)]
+        pick = max(itertools.combinations(allowed, K), key=lambda c: (sum(v[t, e] for e in c), tuple(-e for e in c)))
+        assert set(r["idx"][t].tolist()) == set(pick)
+        assert len({e // S for e in r["idx"][t]}) <= M
+        rest = [e for e in allowed if e not in r["idx"][t]]
+        assert min(v[t, r["idx"][t]]) >= max(v[t, rest])
+
+
+def test_grouped_layer_matches_layer_with_the_grouped_selection():
+    cfg = PARITY_CONFIGS["small_bf16"].replace(T=20)
+    inp = make_inputs(cfg, 0)
+    u, E, b, routed, shared = _np_inputs(inp)
+    rg = O.layer_forward(u, E, b, cfg.top_k, routed, cfg.n_routed, shared, n_groups=4, topk_groups=2)
+    sel = O.select_topk_grouped(O.affinities(u, E), b, cfg.top_k, 4, 2)["idx"]
+    assert (rg["idx"] == sel).all()
+    assert all(len({e // 4 for e in row}) <= 2 for row in rg["idx"])
+    ref = O.layer_forward(u, E, b, cfg.top_k, routed, cfg.n_routed, shared, selection=sel)
+    np.testing.assert_allclose(rg["y"], ref["y"], rtol=1e-15, atol=0)
