@@ -73,6 +73,18 @@ typedef enum {
  *                    come pre-quantised per 128x128 block (moe_quantize_weight_e4m3).
  *                    The router and the residual use the unquantised bf16 u.
  *   out_dtype dtype of y: F32 or BF16
+ *   n_groups, topk_groups  group-limited (node-limited) routing: the experts
+ *             form n_groups equal runs of consecutive experts (the devices or
+ *             nodes they live on) and each token takes its experts from at
+ *             most topk_groups of them.  Groups are ranked by the sum of each
+ *             group's ceil(K / topk_groups) largest s + b (at most the group
+ *             size), ties to the lower group; the top-K is then taken over
+ *             the kept groups' experts.  A reading of the all-to-all
+ *             paragraph of the xyznot summary (a token lands on a median of
+ *             3.2 experts per node), which gives the effect but not the rule.
+ *             Off (global top-K) when n_groups is 0 or 1 or topk_groups >=
+ *             n_groups.  Otherwise n_groups divides n_routed, n_groups <= 64,
+ *             and topk_groups * n_routed / n_groups >= top_k.
  * Limits: d and inter multiples of 64 (F32: 32 is enough; E4M3: 128, and
  * at most 32768); T * top_k and (top_k + n_shared) * T below 2^31; the
  * bytes of u (T * d * size of x_dtype) and of one expert's gate/up matrix
@@ -82,6 +94,7 @@ typedef enum {
 typedef struct {
   int32_t T, d, n_routed, n_shared, inter, top_k;
   int32_t x_dtype, w_dtype, out_dtype;
+  int32_t n_groups, topk_groups;
 } moe_shape;
 
 /*

@@ -42,7 +42,8 @@ class MoEError(RuntimeError):
 
 class Shape(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in
-                ("T", "d", "n_routed", "n_shared", "inter", "top_k", "x_dtype", "w_dtype", "out_dtype")]
+                ("T", "d", "n_routed", "n_shared", "inter", "top_k", "x_dtype", "w_dtype", "out_dtype",
+                 "n_groups", "topk_groups")]
 
 
 class Weights(ctypes.Structure):
@@ -145,15 +146,18 @@ class LayerShape:
     x_dtype: str = "bf16"
     w_dtype: str = "bf16"
     out_dtype: str = "f32"
+    n_groups: int = 1        # group-limited routing: off unless 1 < topk_groups < n_groups
+    topk_groups: int = 1
 
     @classmethod
     def from_config(cls, cfg, T: Optional[int] = None) -> "LayerShape":
         return cls(cfg.T if T is None else T, cfg.d, cfg.n_routed, cfg.n_shared, cfg.inter, cfg.top_k,
-                   cfg.x_dtype, cfg.w_dtype, cfg.out_dtype)
+                   cfg.x_dtype, cfg.w_dtype, cfg.out_dtype, cfg.n_groups, cfg.topk_groups)
 
     def c(self) -> Shape:
         return Shape(self.T, self.d, self.n_routed, self.n_shared, self.inter, self.top_k,
-                     DTYPE_CODE[self.x_dtype], DTYPE_CODE[self.w_dtype], DTYPE_CODE[self.out_dtype])
+                     DTYPE_CODE[self.x_dtype], DTYPE_CODE[self.w_dtype], DTYPE_CODE[self.out_dtype],
+                     self.n_groups, self.topk_groups)
 
 
 def workspace_size(shape: LayerShape) -> int:

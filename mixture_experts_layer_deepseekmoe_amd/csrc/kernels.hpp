@@ -31,6 +31,8 @@ struct RouteArgs {
   float* gate;            // [T][K]
   float* scores;          // scratch: [T][N_r] sigmoids (route_split), [ksplit][T][N_r] partial logits (ksplit > 0)
   int ksplit;             // route_ksplit(...) of this shape: 0, or the number of K slices
+  int n_groups;           // group-limited routing: experts in n_groups equal runs, a token
+  int topk_groups;        // takes experts from at most topk_groups of them (off: topk_groups >= n_groups)
 };
 
 // Batches under 128 router blocks (T < 4096) spread the experts over blocks

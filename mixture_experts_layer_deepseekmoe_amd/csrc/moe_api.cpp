@@ -60,8 +60,20 @@ Layout make_layout(const moe_shape& s) {
   return L;
 }
 
+// Group-limited routing is on when 1 < topk_groups < n_groups; otherwise the
+// kernels get n_groups = topk_groups = 1 (global top-K).
+int groups_of(const moe_shape& s) { return s.n_groups > 1 && s.topk_groups < s.n_groups ? s.n_groups : 1; }
+int topk_groups_of(const moe_shape& s) { return s.n_groups > 1 && s.topk_groups < s.n_groups ? s.topk_groups : 1; }
+
 int validate_shape(const moe_shape* s) {
   if (s == nullptr) return MOE_ERR_INVALID_ARG;
+  if (s->n_groups < 0) return MOE_ERR_INVALID_ARG;
+  if (s->n_groups > 1) {
+    if (s->n_groups > 64) return MOE_ERR_UNSUPPORTED;
+    if (s->n_routed <= 0 || s->n_routed % s->n_groups != 0 || s->topk_groups < 1 || s->topk_groups > s->n_groups)
+      return MOE_ERR_INVALID_ARG;
+    if (static_cast<long long>(s->topk_groups) * (s->n_routed / s->n_groups) < s->top_k) return MOE_ERR_INVALID_ARG;
+  }
   if (s->T < 0 || s->d <= 0 || s->inter <= 0 || s->n_routed <= 0 || s->n_shared < 0 || s->top_k <= 0)
     return MOE_ERR_INVALID_ARG;
   if (s->top_k > s->n_routed) return MOE_ERR_INVALID_ARG;
@@ -114,7 +126,7 @@ int run_route(const moe_shape& s, const void* u, const void* cen, const float* b
               int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* pos, int32_t* hist, float* scores,
               int4* mtiles, int32_t* mtcount, hipStream_t st) {
   moe::RouteArgs ra{u,   cen,  bias,  s.T, s.d, s.n_routed, s.top_k, idx, gate, scores,
-                    moe::route_ksplit(fmt_of(s.x_dtype), s.T, s.d, s.n_routed)};
+                    moe::route_ksplit(fmt_of(s.x_dtype), s.T, s.d, s.n_routed), groups_of(s), topk_groups_of(s)};
   int rc = check_launch(moe::launch_route(fmt_of(s.x_dtype), ra, st));
   if (rc != MOE_OK) return rc;
   const int bm = moe::gg_bm(fmt_of(s.w_dtype));
@@ -173,7 +185,7 @@ const char* moe_status_str(int status) {
   }
 }
 
-const char* moe_version(void) { return "moe-mi355x 0.1 (gfx950)"; }
+const char* moe_version(void) { return "moe-mi355x 0.2 (gfx950)"; }
 
 int moe_workspace_size(const moe_shape* shape, size_t* bytes) {
   if (bytes == nullptr) return MOE_ERR_INVALID_ARG;
@@ -283,7 +295,7 @@ int run_forward(const moe_shape& s, const Layout& L, const void* u, const void* 
   Stages stg{trace, stream};
   stg.begin(MOE_STAGE_ROUTE);
   moe::RouteArgs ra{u,    centroids, bias, s.T, s.d, s.n_routed, s.top_k, idx, gate, at<float>(workspace, L.scores),
-                    moe::route_ksplit(fmt_of(s.x_dtype), s.T, s.d, s.n_routed)};
+                    moe::route_ksplit(fmt_of(s.x_dtype), s.T, s.d, s.n_routed), groups_of(s), topk_groups_of(s)};
   rc = check_launch(moe::launch_route(fmt_of(s.x_dtype), ra, stream));
   if (rc != MOE_OK) return rc;
   stg.end(MOE_STAGE_ROUTE);

@@ -25,13 +25,63 @@ namespace {
 constexpr int RBT = ROUTE_BT;
 constexpr int RCHUNK = 256;   // experts per MFMA pass
 
+// Group-limited routing (the node-limited variant: a token's experts come
+// from at most topk_groups of n_groups equal runs of consecutive experts).
+// The groups are ranked by the sum of each group's q largest keys, the
+// topk_groups best are kept (ties to the lower group), and the experts of the
+// other groups are excluded before the top-K.  Returns a bit per group, set
+// for the kept ones.  Lane g < n_groups scores group g; the keys are those of
+// the top-K (s + b, NaN ranked as -inf).
+__device__ __forceinline__ uint64_t keep_groups(const float* srow, const float* bias, int n_groups, int topk_groups,
+                                                int gsize, int q) {
+  const int lane = threadIdx.x & 63;
+  float score = -INFINITY;
+  if (lane < n_groups) {
+    // the q largest keys of the group, largest first (key, then lower index
+    // first among equal keys), summed in that order
+    float sum = 0.f, pv = INFINITY;
+    int pe = -1;
+    for (int j = 0; j < q; ++j) {
+      float bv = -INFINITY;
+      int be = 0x7fffffff;
+      for (int m = 0; m < gsize; ++m) {
+        const int e = lane * gsize + m;
+        float x = srow[e] + bias[e];
+        if (x != x) x = -INFINITY;
+        const bool after = x < pv || (x == pv && e > pe);
+        if (after && (x > bv || (x == bv && e < be))) { bv = x; be = e; }
+      }
+      sum += bv;
+      pv = bv;
+      pe = be;
+    }
+    score = sum;
+  }
+  uint64_t kept = 0;
+  for (int j = 0; j < topk_groups; ++j) {
+    const bool cand = lane < n_groups && !((kept >> lane) & 1ull);
+    float bv = cand ? score : -INFINITY;
+    int be = cand ? lane : 0x7fffffff;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      const float ov = __shfl_xor(bv, off);
+      const int oe = __shfl_xor(be, off);
+      if (ov > bv || (ov == bv && oe < be)) { bv = ov; be = oe; }
+    }
+    kept |= 1ull << be;
+  }
+  return kept;
+}
+
 // Top-K of one token by one wave: srow holds the token's N_r sigmoid scores
 // (LDS or global), bq[q] the bias of expert lane + 64 q.  Lane k < K writes
-// the k-th selected expert and its gate.
+// the k-th selected expert and its gate.  With grouped routing
+// (1 < topk_groups < n_groups) only the kept groups' experts take part.
 template <int NQ>
-__device__ __forceinline__ void select_topk(const float* srow, const float (&bq)[NQ], int n_routed, int top_k,
+__device__ __forceinline__ void select_topk(const float* srow, const float (&bq)[NQ], const RouteArgs& a,
                                             int32_t* idx_out, float* gate_out) {
   const int lane = threadIdx.x & 63;
+  const int n_routed = a.n_routed, top_k = a.top_k;
   float key[NQ];
 #pragma unroll
   for (int q = 0; q < NQ; ++q) {
@@ -43,7 +93,17 @@ __device__ __forceinline__ void select_topk(const float* srow, const float (&bq)
     }
     key[q] = v;
   }
-  uint32_t taken = 0;
+  uint32_t taken = 0;   // bit q: expert lane + 64 q is chosen or excluded
+  if (a.topk_groups < a.n_groups) {
+    const int gsize = n_routed / a.n_groups;
+    const int qg = min((top_k + a.topk_groups - 1) / a.topk_groups, gsize);
+    const uint64_t kept = keep_groups(srow, a.bias, a.n_groups, a.topk_groups, gsize, qg);
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+      const int e = lane + 64 * q;
+      if (e < n_routed && !((kept >> (e / gsize)) & 1ull)) taken |= 1u << q;
+    }
+  }
   int chosen = 0;     // lane k keeps the k-th selected expert
   float chosen_s = 0.f;
   float sum = 0.f;
@@ -176,7 +236,7 @@ __global__ __launch_bounds__(64 * RouteCfg<NRMAX>::NW) void route_kernel(RouteAr
     const int tl = w * TPW + tt;
     const int t = t0 + tl;
     if (t >= a.T) break;
-    select_topk(sbuf + tl * SSTRIDE, bq, a.n_routed, a.top_k, a.idx + static_cast<size_t>(t) * a.top_k,
+    select_topk(sbuf + tl * SSTRIDE, bq, a, a.idx + static_cast<size_t>(t) * a.top_k,
                 a.gate + static_cast<size_t>(t) * a.top_k);
   }
 }
@@ -239,8 +299,8 @@ __global__ __launch_bounds__(256) void route_topk_kernel(RouteArgs a) {
   float bq[NQ];
   load_bias(a.bias, a.n_routed, bq);
   if (t >= a.T) return;
-  select_topk(a.scores + static_cast<size_t>(t) * a.n_routed, bq, a.n_routed, a.top_k,
-              a.idx + static_cast<size_t>(t) * a.top_k, a.gate + static_cast<size_t>(t) * a.top_k);
+  select_topk(a.scores + static_cast<size_t>(t) * a.n_routed, bq, a, a.idx + static_cast<size_t>(t) * a.top_k,
+              a.gate + static_cast<size_t>(t) * a.top_k);
 }
 
 // ---- large bf16 batches: K split over blocks
@@ -324,8 +384,7 @@ __global__ __launch_bounds__(256) void route_finish_kernel(RouteArgs a) {
     }
   }
   __builtin_amdgcn_wave_barrier();
-  select_topk(srow, bq, a.n_routed, a.top_k, a.idx + static_cast<size_t>(t) * a.top_k,
-              a.gate + static_cast<size_t>(t) * a.top_k);
+  select_topk(srow, bq, a, a.idx + static_cast<size_t>(t) * a.top_k, a.gate + static_cast<size_t>(t) * a.top_k);
 }
 
 template <int FMT, int NRMAX>

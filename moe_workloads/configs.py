@@ -38,6 +38,14 @@ class MoEConfig:
     # Zipf skew of the centroid norms (decode-like load imbalance); None = off.
     zipf_s: Optional[float] = None
     cfg_id: int = 0   # folded into every seed so configs draw unrelated streams
+    # group-limited routing: experts in n_groups equal runs, at most
+    # topk_groups of them per token (off when topk_groups >= n_groups)
+    n_groups: int = 1
+    topk_groups: int = 1
+
+    @property
+    def grouped(self) -> bool:
+        return 1 < self.topk_groups < self.n_groups
 
     @property
     def fp8(self) -> bool:
@@ -78,6 +86,11 @@ CONFIGS: Dict[str, MoEConfig] = {
     "fp8_d7168": MoEConfig("fp8_d7168", T=8192, d=7168, n_routed=256, n_shared=1, inter=2048, top_k=8,
                            x_dtype="bf16", w_dtype="e4m3", out_dtype="bf16",
                            w_std=0.006, e_std=0.02, b_std=0.01, cfg_id=6),
+    # The DeepSeek-V3 layer with group-limited routing: 8 groups of 32 experts
+    # (e.g. the nodes of an expert-parallel deployment), at most 4 per token.
+    "bf16_d7168_g8": MoEConfig("bf16_d7168_g8", T=8192, d=7168, n_routed=256, n_shared=1, inter=2048, top_k=8,
+                               x_dtype="bf16", w_dtype="bf16", out_dtype="f32",
+                               w_std=0.006, e_std=0.02, b_std=0.01, cfg_id=3, n_groups=8, topk_groups=4),
     # Decode-like batch with a skewed router, used for the bias-update loop.
     "skew_decode_d7168": MoEConfig("skew_decode_d7168", T=256, d=7168, n_routed=256, n_shared=1, inter=2048,
                                    top_k=8, x_dtype="bf16", w_dtype="bf16", out_dtype="f32",

@@ -49,11 +49,51 @@ def check_selection(v: np.ndarray, gap: np.ndarray, oracle_idx: np.ndarray, gpu_
     return int(near.sum())
 
 
-def check_routing(out: dict, u: np.ndarray, E: np.ndarray, b: np.ndarray, k: int, n_routed: int) -> dict:
-    """Full routing parity.  Returns the oracle route (with the GPU's selection adopted)."""
+def check_selection_grouped(r: dict, gpu_idx: np.ndarray, k: int, n_groups: int, topk_groups: int) -> int:
+    """The group-limited selection rule; returns the number of near-tie tokens.
+
+    A token is a near tie when its K-th and (K+1)-th biased scores among the
+    kept groups' experts lie within 1e-6, or when its last kept group's score
+    lies within q * 1e-6 of the first one left out (a group score sums q fp32
+    values).  Other tokens: the GPU's set equals the oracle's.  Near ties: K
+    distinct in-range experts from at most topk_groups groups and, where the
+    kept groups are certain, the 1e-6 band of check_selection."""
+    v, T = r["v"], r["v"].shape[0]
+    n = v.shape[1]
+    S = n // n_groups
+    q = min(-(-k // topk_groups), S)
+    near_g = r["group_gap"] <= q * BAND
+    near_e = r["gap"] <= BAND
+    for t in range(T):
+        g = gpu_idx[t]
+        assert len(set(g.tolist())) == k, f"token {t}: repeated experts {g}"
+        assert ((g >= 0) & (g < n)).all(), f"token {t}: out of range {g}"
+        assert len({int(e) // S for e in g}) <= topk_groups, f"token {t}: {g} spans more than {topk_groups} groups"
+        if not near_g[t] and not near_e[t]:
+            assert set(g.tolist()) == set(r["idx"][t].tolist()), \
+                f"token {t}: gpu {sorted(g.tolist())} oracle {sorted(r['idx'][t].tolist())}"
+        elif not near_g[t]:
+            kept = set(r["groups"][t].tolist())
+            assert {int(e) // S for e in g} <= kept, f"token {t}: {g} outside the kept groups {kept}"
+            allowed = np.array([e for e in range(n) if e // S in kept])
+            vk = v[t, r["idx"][t, k - 1]]
+            must = set(allowed[v[t, allowed] > vk + BAND].tolist())
+            may = set(allowed[v[t, allowed] >= vk - BAND].tolist())
+            assert must <= set(g.tolist()) <= may, f"near-tie token {t}"
+    return int((near_g | near_e).sum())
+
+
+def check_routing(out: dict, u: np.ndarray, E: np.ndarray, b: np.ndarray, k: int, n_routed: int,
+                  n_groups: int = 1, topk_groups: int = 1) -> dict:
+    """Full routing parity (group-limited when 1 < topk_groups < n_groups).
+    Returns the oracle route (with the GPU's selection adopted)."""
     gpu_idx = out["topk_idx"].cpu().numpy()
-    r = O.route(u, E, b, k)
-    near = check_selection(r["v"], r["gap"], r["idx"], gpu_idx, k)
+    if 1 < topk_groups < n_groups:
+        r = O.route(u, E, b, k, n_groups=n_groups, topk_groups=topk_groups)
+        near = check_selection_grouped(r, gpu_idx, k, n_groups, topk_groups)
+    else:
+        r = O.route(u, E, b, k)
+        near = check_selection(r["v"], r["gap"], r["idx"], gpu_idx, k)
     r = O.route(u, E, b, k, selection=gpu_idx)
     gates = out["topk_gate"].cpu().numpy().astype(np.float64)
     np.testing.assert_allclose(gates, r["gate"], rtol=2e-6, atol=2e-7)

@@ -182,3 +182,19 @@ def test_workspace_layout_lies_inside_the_workspace(name):
         assert o0 + n0 <= o1                      # no two of them overlap
     assert lay["tile_rows"] == (256 if cfg.w_dtype == "bf16" else 128)
     assert lay["seg_cap"] * 8 >= lay["max_mtiles"]
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(n_routed=256, top_k=8, n_groups=8, topk_groups=4), B.MOE_OK),
+    (dict(n_routed=256, top_k=8, n_groups=8, topk_groups=8), B.MOE_OK),      # every group kept: global top-K
+    (dict(n_routed=256, top_k=8, n_groups=0, topk_groups=0), B.MOE_OK),      # off
+    (dict(n_routed=256, top_k=8, n_groups=7, topk_groups=3), B.MOE_ERR_INVALID_ARG),    # 7 does not divide 256
+    (dict(n_routed=256, top_k=8, n_groups=8, topk_groups=0), B.MOE_ERR_INVALID_ARG),
+    (dict(n_routed=256, top_k=8, n_groups=8, topk_groups=9), B.MOE_ERR_INVALID_ARG),
+    (dict(n_routed=32, top_k=8, n_groups=16, topk_groups=3), B.MOE_ERR_INVALID_ARG),    # 3 groups of 2 < K
+    (dict(n_routed=256, top_k=8, n_groups=128, topk_groups=8), B.MOE_ERR_UNSUPPORTED),  # more than 64 groups
+    (dict(n_routed=256, top_k=8, n_groups=-1, topk_groups=1), B.MOE_ERR_INVALID_ARG),
+])
+def test_group_limited_routing_validation(kw, code):
+    rc, _ = _ws_rc(_shape(**kw))
+    assert rc == code

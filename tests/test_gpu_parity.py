@@ -567,7 +567,7 @@ def _full_forward(name, first_k=False, extra=()):
     torch.cuda.synchronize()
     assert torch.isfinite(y).all()
     u, E, b = to_numpy_f32(inp.u), to_numpy_f32(inp.centroids), inp.bias.numpy()
-    r = check_routing(routing, u, E, b, cfg.top_k, cfg.n_routed)
+    r = check_routing(routing, u, E, b, cfg.top_k, cfg.n_routed, cfg.n_groups, cfg.topk_groups)
     tiles = check_tile_list(cfg, shape, ws, routing)
     sample = np.unique(np.concatenate([boundary_tokens(cfg, tiles, routing), np.asarray(extra, np.int64)]))
     gi = routing["topk_idx"].cpu().numpy()
@@ -615,3 +615,58 @@ def test_full_fp8_d7168():
 
 def test_full_skew_decode_d7168():
     _full_forward("skew_decode_d7168", extra=[0, 255])
+
+
+def test_full_bf16_d7168_group_limited():
+    # 8 groups of 32 experts, at most 4 per token (q = 2)
+    _full_forward("bf16_d7168_g8", extra=[0, 8191])
+
+
+# ------------------------------------------------------------------ group-limited routing, small
+
+GROUPED_CASES = {
+    "small_bf16_g4k2": PARITY_CONFIGS["small_bf16"].replace(name="small_bf16_g4k2", n_groups=4, topk_groups=2),
+    "small_bf16_ns2_g6k3": PARITY_CONFIGS["small_bf16_ns2"].replace(name="small_bf16_ns2_g6k3", n_groups=6,
+                                                                     topk_groups=3),
+    "small_fp32_g5k2": PARITY_CONFIGS["small_fp32"].replace(name="small_fp32_g5k2", n_groups=5, topk_groups=2),
+    "small_fp8_g8k3": PARITY_CONFIGS["small_fp8"].replace(name="small_fp8_g8k3", n_groups=8, topk_groups=3),
+    "wide_router_g16k4": PARITY_CONFIGS["wide_router"].replace(name="wide_router_g16k4", n_groups=16, topk_groups=4),
+    "ksplit_ragged_g8k3": ROUTE_KSPLIT_CASES["ksplit_ragged"].replace(name="ksplit_ragged_g8k3", n_groups=8,
+                                                                      topk_groups=3),
+    "fused_d2048_g8k2": CONFIGS["bf16_d2048"].replace(name="fused_d2048_g8k2", n_groups=8, topk_groups=2),
+}
+
+
+@pytest.mark.parametrize("name", list(GROUPED_CASES))
+def test_route_group_limited(name):
+    """Group-limited routing on every router path (scores through scratch,
+    the fused kernel, the K-split kernels; fp32 and bf16; 512 experts)."""
+    cfg = GROUPED_CASES[name]
+    say(f"case: moe_route {name} (groups {cfg.n_groups}, keep {cfg.topk_groups})")
+    inp = make_inputs(cfg, 0, with_weights=False)
+    shape = moe.LayerShape.from_config(cfg)
+    u, E, b = _dev(inp)
+    out = moe.moe_route(shape, u, E, b)
+    torch.cuda.synchronize()
+    r = check_routing(out, to_numpy_f32(inp.u), to_numpy_f32(inp.centroids), inp.bias.numpy(), cfg.top_k,
+                      cfg.n_routed, cfg.n_groups, cfg.topk_groups)
+    glob = O.route(to_numpy_f32(inp.u), to_numpy_f32(inp.centroids), inp.bias.numpy(), cfg.top_k)["idx"]
+    differ = int((np.sort(glob, 1) != np.sort(out["topk_idx"].cpu().numpy(), 1)).any(1).sum())
+    say(f"  near ties {r['near_ties']}; {differ} of {cfg.T} tokens select otherwise than global top-K")
+
+
+@pytest.mark.parametrize("name", ["small_bf16_g4k2", "small_fp8_g8k3", "small_fp32_g5k2"])
+def test_forward_group_limited(name):
+    cfg = GROUPED_CASES[name]
+    say(f"case: moe_forward {name}")
+    inp = make_inputs(cfg, 0)
+    y, routing, _ = _run_forward(cfg, inp)
+    u, E, b = to_numpy_f32(inp.u), to_numpy_f32(inp.centroids), inp.bias.numpy()
+    check_routing(routing, u, E, b, cfg.top_k, cfg.n_routed, cfg.n_groups, cfg.topk_groups)
+    routed, shared = expert_fns(inp, False)
+    ref = O.layer_forward(u, E, b, cfg.top_k, routed, cfg.n_routed, shared,
+                          selection=routing["topk_idx"].cpu().numpy(), fp8=cfg.fp8)
+    err = output_errors(rows_of(y), ref["y"], u, cfg.out_dtype, cfg.w_dtype)
+    say(f"  {err}")
+    assert err["rel_to_rms"] <= TOL[cfg.w_dtype], err
+    check_tile_list(cfg, moe.LayerShape.from_config(cfg), routing["workspace"], routing)
