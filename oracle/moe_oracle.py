@@ -407,6 +407,103 @@ def layer_forward(u: np.ndarray, centroids: np.ndarray, bias: np.ndarray, k: int
     return r
 
 
+# --------------------------------------------------------------------------
+# Backward pass (the report's FP8 training section, as paraphrased on
+# why-be.co.kr: the Linear operator's three GEMMs are Fprop, Dgrad and Wgrad,
+# and the inputs of the SwiGLU operator are cached and its output recomputed
+# in the backward pass).  Gradients of the forward above with the expert
+# selection held fixed (the top-K is piecewise constant); fp64 throughout.
+# --------------------------------------------------------------------------
+
+def silu_grad(a: np.ndarray) -> np.ndarray:
+    """d SiLU(a) / da = sigma(a) * (1 + a * (1 - sigma(a)))."""
+    a = np.asarray(a, F64)
+    sg = sigmoid(a)
+    return sg * (1.0 + a * (1.0 - sg))
+
+
+def swiglu_ffn_backward(x: np.ndarray, w_gate_up: np.ndarray, w_down: np.ndarray,
+                        dout: np.ndarray) -> Dict[str, np.ndarray]:
+    """Backward of FFN(x) = W_down (SiLU(G) * U), G = x W_gate^T, U = x W_up^T,
+    for the upstream gradient ``dout`` [n, d] of its n rows:
+        H = SiLU(G) * U (recomputed from the cached G, U)
+        dH = dout W_down,              dW_down = dout^T H
+        dG = dH * U * SiLU'(G),        dU = dH * SiLU(G)
+        dx = dG W_gate + dU W_up,      dW_gate = dG^T x,  dW_up = dU^T x
+    Returns dx [n, d], dW_gate_up [2I, d] (gate rows first), dW_down [d, I]."""
+    x = np.asarray(x, F64)
+    wgu = np.asarray(w_gate_up, F64)
+    wd = np.asarray(w_down, F64)
+    dout = np.asarray(dout, F64)
+    I = wgu.shape[0] // 2
+    G = x @ wgu[:I].T
+    U = x @ wgu[I:].T
+    H = silu(G) * U
+    dH = dout @ wd
+    dG = dH * U * silu_grad(G)
+    dU = dH * silu(G)
+    dGU = np.concatenate([dG, dU], axis=1)
+    return {"dx": dGU @ wgu, "dW_gate_up": dGU.T @ x, "dW_down": dout.T @ H}
+
+
+def layer_backward(u: np.ndarray, centroids: np.ndarray, bias: np.ndarray, k: int,
+                   routed: ExpertFn, n_routed: int, shared: Sequence[Tuple[np.ndarray, np.ndarray]],
+                   dy: np.ndarray, selection: Optional[np.ndarray] = None, n_groups: int = 1,
+                   topk_groups: int = 1, weight_grads: bool = True) -> Dict[str, np.ndarray]:
+    """Gradients of h' = u + sum_s FFN_s(u) + sum_k g_k FFN_{e_k}(u) for the
+    upstream gradient dy [T, d], the selection held fixed:
+      routed expert e, its rows (t, k): upstream g_{t,k} dy_t through FFN_e;
+      shared expert s: upstream dy_t through FFN_s;
+      gates g_k = s_k / S (S = sum of the selected s): dg_k = dy_t . FFN_{e_k}(u_t),
+        ds_j = (dg_j - sum_k g_k dg_k) / S, and through s = Sigmoid(z),
+        dz_j = ds_j s_j (1 - s_j), with z_j = u_t . e_j;
+      du_t = dy_t + sum_s dx_s + sum_k dx_{t,k} + sum_k dz_k e_{e_k};
+      dE_e = sum over e's rows of dz u_t.
+    Returns du [T, d], dE [N_r, d], dg and dz [T, K], and (weight_grads)
+    dW_gate_up / dW_down: dicts expert -> gradient (experts without rows
+    have zero gradients and are left out), dWs_gate_up / dWs_down: lists
+    over the shared experts."""
+    u64 = np.asarray(u, F64)
+    E64 = np.asarray(centroids, F64)
+    dy = np.asarray(dy, F64)
+    r = route(u64, E64, bias, k, selection, n_groups, topk_groups)
+    idx, gate, s = r["idx"], r["gate"], r["s"]
+    T, d = u64.shape
+    du = dy.copy()
+    dWs_gu, dWs_d = [], []
+    for wgu, wd in shared:
+        b = swiglu_ffn_backward(u64, wgu, wd, dy)
+        du += b["dx"]
+        dWs_gu.append(b["dW_gate_up"])
+        dWs_d.append(b["dW_down"])
+    dg = np.zeros((T, k))
+    dW_gu, dW_d = {}, {}
+    for e in range(n_routed):
+        tok, slot = np.nonzero(idx == e)
+        if tok.size == 0:
+            continue
+        wgu, wd = routed(e)
+        x = u64[tok]
+        ye = swiglu_ffn(x, wgu, wd)                           # FFN_e(u_t) of the rows
+        dg[tok, slot] = np.sum(dy[tok] * ye, axis=1)
+        b = swiglu_ffn_backward(x, wgu, wd, gate[tok, slot][:, None] * dy[tok])
+        du[tok] += b["dx"]
+        if weight_grads:
+            dW_gu[e] = b["dW_gate_up"]
+            dW_d[e] = b["dW_down"]
+    sel = np.take_along_axis(s, idx.astype(np.int64), axis=1)
+    S = sel.sum(axis=1, keepdims=True)
+    ds = (dg - np.sum(gate * dg, axis=1, keepdims=True)) / S
+    dz = ds * sel * (1.0 - sel)
+    dE = np.zeros((n_routed, d))
+    for t in range(T):
+        for j in range(k):
+            du[t] += dz[t, j] * E64[idx[t, j]]
+            dE[idx[t, j]] += dz[t, j] * u64[t]
+    return {"du": du, "dE": dE, "dg": dg, "dz": dz, "idx": idx, "gate": gate,
+            "dW_gate_up": dW_gu, "dW_down": dW_d, "dWs_gate_up": dWs_gu, "dWs_down": dWs_d}
+
+
 def near_tie_mask(gap: np.ndarray, band: float = 1e-6) -> np.ndarray:
     """Tokens whose K-th and (K+1)-th biased scores lie within ``band``."""
     return np.asarray(gap) <= band

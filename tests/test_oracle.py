@@ -542,3 +542,119 @@ def test_grouped_layer_matches_layer_with_the_grouped_selection():
     assert all(len({e // 4 for e in row}) <= 2 for row in rg["idx"])
     ref = O.layer_forward(u, E, b, cfg.top_k, routed, cfg.n_routed, shared, selection=sel)
     np.testing.assert_allclose(rg["y"], ref["y"], rtol=1e-15, atol=0)
+
+
+# ---------------------------------------------------------------- backward
+
+def _torch_layer(u, E, b, idx, routed, shared, n_routed):
+    """The layer as torch float64 modules with the selection fixed, for autograd."""
+    u_t = torch.tensor(u, dtype=torch.float64, requires_grad=True)
+    E_t = torch.tensor(np.asarray(E, np.float64), requires_grad=True)
+    W = {e: [torch.tensor(np.asarray(w, np.float64), requires_grad=True) for w in routed(e)] for e in range(n_routed)}
+    Ws = [[torch.tensor(np.asarray(w, np.float64), requires_grad=True) for w in sh] for sh in shared]
+    s = torch.sigmoid(u_t @ E_t.T)
+    it = torch.tensor(idx, dtype=torch.int64)
+    sel = torch.gather(s, 1, it)
+    g = sel / sel.sum(dim=1, keepdim=True)
+
+    def ffn(x, wgu, wd):
+        I = wgu.shape[0] // 2
+        return torch.nn.functional.linear(torch.nn.functional.silu(x @ wgu[:I].T) * (x @ wgu[I:].T), wd)
+
+    y = u_t
+    for wgu, wd in Ws:
+        y = y + ffn(u_t, wgu, wd)
+    for t in range(u.shape[0]):
+        for j in range(idx.shape[1]):
+            y = y + torch.nn.functional.pad(g[t, j] * ffn(u_t[t:t + 1], *W[int(idx[t, j])]),
+                                            (0, 0, t, u.shape[0] - t - 1))
+    return y, u_t, E_t, W, Ws
+
+
+def test_backward_against_torch_autograd():
+    """Every gradient of layer_backward against torch autograd in float64 on
+    the same layer (selection fixed): du, dE, each routed expert's and each
+    shared expert's dW, and zero weight gradients for experts without rows."""
+    cfg = PARITY_CONFIGS["small_bf16_ns2"].replace(T=14, d=64, inter=32, n_routed=6, top_k=2)
+    inp = make_inputs(cfg, 0)
+    u, E, b, routed, shared = _np_inputs(inp)
+    dy = np.random.default_rng(30).normal(0, 1, u.shape)
+    r = O.layer_backward(u, E, b, cfg.top_k, routed, cfg.n_routed, shared, dy)
+    y, u_t, E_t, W, Ws = _torch_layer(u, E, b, r["idx"], routed, shared, cfg.n_routed)
+    fwd = O.layer_forward(u, E, b, cfg.top_k, routed, cfg.n_routed, shared)
+    np.testing.assert_allclose(y.detach().numpy(), fwd["y"], rtol=1e-12, atol=1e-12)
+    y.backward(torch.tensor(dy))
+    np.testing.assert_allclose(r["du"], u_t.grad.numpy(), rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(r["dE"], E_t.grad.numpy(), rtol=1e-10, atol=1e-13)
+    for e in range(cfg.n_routed):
+        if e in r["dW_gate_up"]:
+            np.testing.assert_allclose(r["dW_gate_up"][e], W[e][0].grad.numpy(), rtol=1e-10, atol=1e-13)
+            np.testing.assert_allclose(r["dW_down"][e], W[e][1].grad.numpy(), rtol=1e-10, atol=1e-13)
+        else:
+            assert W[e][0].grad is None or not W[e][0].grad.any()
+    for si in range(cfg.n_shared):
+        np.testing.assert_allclose(r["dWs_gate_up"][si], Ws[si][0].grad.numpy(), rtol=1e-10, atol=1e-13)
+        np.testing.assert_allclose(r["dWs_down"][si], Ws[si][1].grad.numpy(), rtol=1e-10, atol=1e-13)
+
+
+def test_backward_finite_differences():
+    """Central differences of <dy, y> along random directions of u, of the
+    centroids and of one expert's weights (selection fixed, away from ties)."""
+    cfg = PARITY_CONFIGS["small_bf16"].replace(T=6, d=64, inter=32, n_routed=5, top_k=2)
+    inp = make_inputs(cfg, 0)
+    u, E, b, routed, shared = _np_inputs(inp)
+    rng = np.random.default_rng(31)
+    dy = rng.normal(0, 1, u.shape)
+    r = O.layer_backward(u, E, b, cfg.top_k, routed, cfg.n_routed, shared, dy)
+    sel = r["idx"]
+    eps = 1e-6
+
+    def f(uu=u, EE=E, rt=routed):
+        return float(np.sum(dy * O.layer_forward(uu, EE, b, cfg.top_k, rt, cfg.n_routed, shared, selection=sel)["y"]))
+
+    for _ in range(3):
+        v = rng.normal(0, 1, u.shape)
+        num = (f(uu=u + eps * v) - f(uu=u - eps * v)) / (2 * eps)
+        assert num == pytest.approx(float(np.sum(r["du"] * v)), rel=1e-6, abs=1e-8)
+        v = rng.normal(0, 1, E.shape)
+        num = (f(EE=E + eps * v) - f(EE=E - eps * v)) / (2 * eps)
+        assert num == pytest.approx(float(np.sum(r["dE"] * v)), rel=1e-6, abs=1e-8)
+    e = int(sel[0, 0])
+    for which in (0, 1):
+        v = rng.normal(0, 1, routed(e)[which].shape)
+
+        def rt(sign):
+            def fn(j):
+                w = list(routed(j))
+                if j == e:
+                    w[which] = w[which] + sign * eps * v
+                return tuple(w)
+            return fn
+        num = (f(rt=rt(1)) - f(rt=rt(-1))) / (2 * eps)
+        ana = float(np.sum((r["dW_gate_up"] if which == 0 else r["dW_down"])[e] * v))
+        assert num == pytest.approx(ana, rel=1e-6, abs=1e-8)
+
+
+def test_backward_single_expert_is_residual_mlp_backward():
+    """N_r = K = 1 (gate 1, so no routing gradient) and no shared expert:
+    du = dy + the plain SwiGLU MLP's input gradient (torch.func.vjp)."""
+    rng = np.random.default_rng(32)
+    u, E = rng.normal(0, 1, (9, 16)), rng.normal(0, 1, (1, 16))
+    wgu, wd = rng.normal(0, 0.3, (16, 16)), rng.normal(0, 0.3, (16, 8))
+    dy = rng.normal(0, 1, u.shape)
+    r = O.layer_backward(u, E, np.zeros(1, np.float32), 1, lambda e: (wgu, wd), 1, [], dy)
+    assert not r["dz"].any() and not r["dE"].any()
+
+    def mlp(x):
+        g, up = x @ torch.tensor(wgu[:8]).T, x @ torch.tensor(wgu[8:]).T
+        return torch.nn.functional.silu(g) * up @ torch.tensor(wd).T
+    _, vjp = torch.func.vjp(mlp, torch.tensor(u))
+    np.testing.assert_allclose(r["du"], dy + vjp(torch.tensor(dy))[0].numpy(), rtol=1e-12, atol=1e-12)
+
+
+def test_silu_grad_closed_form():
+    assert O.silu_grad(0.0) == 0.5
+    a = np.random.default_rng(33).normal(0, 3, 1000)
+    t = torch.tensor(a, requires_grad=True)
+    torch.nn.functional.silu(t).sum().backward()
+    np.testing.assert_allclose(O.silu_grad(a), t.grad.numpy(), rtol=1e-13, atol=1e-15)
