@@ -243,6 +243,47 @@ int moe_forward_static(const moe_shape* shape, const void* u, const void* centro
                        hipStream_t stream);
 
 /*
+ * Training: the layer backward, bf16 (x_dtype = w_dtype = BF16; other dtypes
+ * return MOE_ERR_UNSUPPORTED).  The report's FP8 training section (as
+ * paraphrased on why-be.co.kr) names the three GEMMs of a Linear operator,
+ * Fprop, Dgrad and Wgrad, and caches the inputs of the SwiGLU operator,
+ * recomputing its output in the backward pass; here the GEMMs run in bf16
+ * with fp32 accumulation.
+ *
+ * moe_train_workspace_size: bytes of the workspace moe_forward_train and
+ * moe_backward share for `shape` (more than moe_workspace_size: the cached
+ * SwiGLU inputs and the backward's intermediate rows).
+ *
+ * moe_forward_train: moe_forward (same y), keeping in the workspace what the
+ * backward needs: the routing, the GEMM tile list, the selected experts'
+ * sigmoid scores, the SwiGLU inputs G and U of every grouped row (bf16) and
+ * the expert outputs.
+ *
+ * moe_backward: for the upstream gradient dy [T][d] (fp32) of y, with the
+ * expert selection of the preceding moe_forward_train on this workspace (and
+ * the same u, centroids and weights) held fixed:
+ *   du          [T][d] fp32: through the residual, every expert and the router
+ *               (gates g = s / sum s of the selected sigmoids s = Sigmoid(u . e))
+ *   dcentroids  [N_r][d] fp32: through the router
+ *   grads       fp32, the layouts of moe_weights; overwritten; experts that no
+ *               token selected get zeros
+ * Every sum runs in a fixed order (bit-reproducible).
+ */
+typedef struct {
+  float* dw_gate_up;   /* [N_r][2I][d] */
+  float* dw_down;      /* [N_r][d][I] */
+  float* dws_gate_up;  /* [N_s][2I][d] (may be null when N_s = 0) */
+  float* dws_down;     /* [N_s][d][I] */
+} moe_weight_grads;
+int moe_train_workspace_size(const moe_shape* shape, size_t* bytes);
+int moe_forward_train(const moe_shape* shape, const void* u, const void* centroids, const float* bias,
+                      const moe_weights* weights, void* y, void* workspace, size_t workspace_bytes,
+                      const moe_trace* trace, hipStream_t stream);
+int moe_backward(const moe_shape* shape, const void* u, const void* centroids, const moe_weights* weights,
+                 const float* dy, float* du, float* dcentroids, const moe_weight_grads* grads, void* workspace,
+                 size_t workspace_bytes, hipStream_t stream);
+
+/*
  * Aux-loss-free bias update (xyznot summary, section 2: b_i is lowered by
  * gamma for an overloaded expert and raised by gamma for an underloaded one),
  * in place:

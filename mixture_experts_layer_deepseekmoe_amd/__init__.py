@@ -9,10 +9,14 @@ from .binding import (  # noqa: F401
     LayerShape,
     MoEError,
     alloc_routing,
+    alloc_train_workspace,
+    alloc_weight_grads,
     alloc_workspace,
     load_library,
     moe_forward,
+    moe_backward,
     moe_forward_static,
+    moe_forward_train,
     moe_quantize_act_e4m3,
     moe_quantize_weight_e4m3,
     moe_route,
@@ -21,5 +25,6 @@ from .binding import (  # noqa: F401
     status_str,
     version,
     workspace_layout,
+    train_workspace_size,
     workspace_size,
 )

@@ -28,8 +28,8 @@ _TORCH_DT = {F32: torch.float32, BF16: torch.bfloat16}
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_LAUNCH = range(5)
 
 EXPORTED = ("moe_status_str", "moe_version", "moe_workspace_size", "moe_workspace_layout", "moe_route",
-            "moe_forward", "moe_forward_static", "moe_update_bias", "moe_quantize_weight_e4m3",
-            "moe_quantize_act_e4m3")
+            "moe_forward", "moe_forward_static", "moe_train_workspace_size", "moe_forward_train", "moe_backward",
+            "moe_update_bias", "moe_quantize_weight_e4m3", "moe_quantize_act_e4m3")
 
 STATIC_SCRATCH_BYTES = 64 << 20   # MOE_STATIC_SCRATCH_BYTES
 
@@ -62,6 +62,10 @@ class Trace(ctypes.Structure):
 class WorkspaceMap(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in ("mtiles", "mt_count", "h", "h_scale", "y")] + \
                [(n, ctypes.c_int32) for n in ("max_mtiles", "tile_rows", "seg_cap")]
+
+
+class WeightGrads(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in ("dw_gate_up", "dw_down", "dws_gate_up", "dws_down")]
 
 
 class Routing(ctypes.Structure):
@@ -98,6 +102,14 @@ def load_library() -> ctypes.CDLL:
     lib.moe_forward_static.restype = ctypes.c_int
     lib.moe_forward_static.argtypes = [ctypes.POINTER(Shape), vp, vp, vp, ctypes.POINTER(Weights), vp,
                                        ctypes.POINTER(Routing), ctypes.POINTER(Trace), vp]
+    lib.moe_train_workspace_size.restype = ctypes.c_int
+    lib.moe_train_workspace_size.argtypes = [ctypes.POINTER(Shape), ctypes.POINTER(sz)]
+    lib.moe_forward_train.restype = ctypes.c_int
+    lib.moe_forward_train.argtypes = [ctypes.POINTER(Shape), vp, vp, vp, ctypes.POINTER(Weights), vp, vp, sz,
+                                      ctypes.POINTER(Trace), vp]
+    lib.moe_backward.restype = ctypes.c_int
+    lib.moe_backward.argtypes = [ctypes.POINTER(Shape), vp, vp, ctypes.POINTER(Weights), vp, vp, vp,
+                                 ctypes.POINTER(WeightGrads), vp, sz, vp]
     lib.moe_update_bias.restype = ctypes.c_int
     lib.moe_update_bias.argtypes = [vp, vp, i32, i64, ctypes.c_float, vp]
     lib.moe_quantize_weight_e4m3.restype = ctypes.c_int
@@ -260,6 +272,66 @@ def moe_forward_static(shape: LayerShape, u: torch.Tensor, centroids: torch.Tens
                                 ctypes.byref(trace) if trace is not None else None, _stream())
     _check(rc, "moe_forward_static")
     return y
+
+
+def train_workspace_size(shape: LayerShape) -> int:
+    n = ctypes.c_size_t(0)
+    _check(load_library().moe_train_workspace_size(ctypes.byref(shape.c()), ctypes.byref(n)),
+           "moe_train_workspace_size")
+    return n.value
+
+
+def alloc_train_workspace(shape: LayerShape, device="cuda") -> torch.Tensor:
+    return torch.empty(max(train_workspace_size(shape), 1), dtype=torch.uint8, device=device)
+
+
+def moe_forward_train(shape: LayerShape, u: torch.Tensor, centroids: torch.Tensor, bias: torch.Tensor,
+                      weights: ExpertWeights, workspace: torch.Tensor, y: Optional[torch.Tensor] = None,
+                      trace: Optional[Trace] = None) -> torch.Tensor:
+    """The forward for training (bf16): y, and in ``workspace`` what moe_backward needs."""
+    if y is None:
+        y = torch.empty((shape.T, shape.d), dtype=_TORCH_DT[DTYPE_CODE[shape.out_dtype]], device=u.device)
+    rc = load_library().moe_forward_train(ctypes.byref(shape.c()), _ptr(u), _ptr(centroids), _ptr(bias),
+                                          ctypes.byref(weights.c()), _ptr(y), _ptr(workspace), workspace.numel(),
+                                          ctypes.byref(trace) if trace is not None else None, _stream())
+    _check(rc, "moe_forward_train")
+    return y
+
+
+@dataclass
+class WeightGradTensors:
+    """fp32 weight gradients in the layouts of ExpertWeights."""
+    dw_gate_up: torch.Tensor
+    dw_down: torch.Tensor
+    dws_gate_up: Optional[torch.Tensor] = None
+    dws_down: Optional[torch.Tensor] = None
+
+    def c(self) -> WeightGrads:
+        f = lambda t: None if t is None or t.numel() == 0 else _ptr(t)
+        return WeightGrads(f(self.dw_gate_up), f(self.dw_down), f(self.dws_gate_up), f(self.dws_down))
+
+
+def alloc_weight_grads(shape: LayerShape, device="cuda") -> WeightGradTensors:
+    f32, I, d = torch.float32, shape.inter, shape.d
+    return WeightGradTensors(torch.empty((shape.n_routed, 2 * I, d), dtype=f32, device=device),
+                             torch.empty((shape.n_routed, d, I), dtype=f32, device=device),
+                             torch.empty((shape.n_shared, 2 * I, d), dtype=f32, device=device),
+                             torch.empty((shape.n_shared, d, I), dtype=f32, device=device))
+
+
+def moe_backward(shape: LayerShape, u: torch.Tensor, centroids: torch.Tensor, weights: ExpertWeights,
+                 dy: torch.Tensor, workspace: torch.Tensor, grads: Optional[WeightGradTensors] = None):
+    """Gradients for dy (fp32 [T, d]) after moe_forward_train on ``workspace``:
+    returns (du [T, d] fp32, dcentroids [N_r, d] fp32, weight grads)."""
+    du = torch.empty((shape.T, shape.d), dtype=torch.float32, device=u.device)
+    dE = torch.empty((shape.n_routed, shape.d), dtype=torch.float32, device=u.device)
+    grads = alloc_weight_grads(shape, u.device) if grads is None else grads
+    rc = load_library().moe_backward(ctypes.byref(shape.c()), _ptr(u) if shape.T else None, _ptr(centroids),
+                                     ctypes.byref(weights.c()), _ptr(dy) if shape.T else None,
+                                     _ptr(du) if shape.T else None, _ptr(dE), ctypes.byref(grads.c()),
+                                     _ptr(workspace), workspace.numel(), _stream())
+    _check(rc, "moe_backward")
+    return du, dE, grads
 
 
 def moe_update_bias(bias: torch.Tensor, counts: torch.Tensor, total_assignments: int, gamma: float = 0.001):

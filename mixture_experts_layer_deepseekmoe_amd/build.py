@@ -21,7 +21,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB_NAME = "libmoe_mi355x.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 
-SOURCES = ["route.hip", "group.hip", "ggemm.hip", "combine.hip", "moe_api.cpp"]
+SOURCES = ["route.hip", "group.hip", "ggemm.hip", "combine.hip", "bwd.hip", "moe_api.cpp"]
 ARCH = "gfx950"
 # measured-ceiling probes (MFMA with random / zero operands, HBM stream), a
 # standalone program run by `profiling.py peaks`

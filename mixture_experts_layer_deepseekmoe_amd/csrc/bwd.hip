@@ -1,0 +1,492 @@
+// The MoE layer backward, bf16 (the report's FP8 training section, as
+// paraphrased on why-be.co.kr: the Linear operator's Fprop, Dgrad and Wgrad
+// GEMMs; the SwiGLU inputs are cached in the forward and its output is
+// recomputed in the backward pass).  With the expert selection held fixed:
+//
+//   prep     grouped row r (token t, gate g; g = 1 for a shared expert):
+//            dY_r = g dy_t and X_r = u_t as bf16 rows, dg_{t,k} = dy_t . Y_r
+//   dz       per token: S = sum of the selected sigmoids, ds_k = (dg_k -
+//            sum_j g_j dg_j) / S, dz_k = ds_k s_k (1 - s_k)
+//   dgrad    dH = dY W_down (per group), fused with the SwiGLU backward:
+//   down     from the cached G, U: dG = dH U SiLU'(G), dU = dH SiLU(G),
+//            and H = SiLU(G) U recomputed for the down Wgrad
+//   dgrad    dX = [dG dU] W_gate_up
+//   gate/up
+//   wgrad    dW_down = dY^T H and dW_gate_up = [dG dU]^T X per group (fp32)
+//   du       du_t = dy_t + shared dX rows + routed dX rows + sum_k dz_k e_k
+//   dE       dE_e = sum over e's rows of dz u_t
+//
+// Every sum runs in a fixed order: the results are bit-reproducible.
+//
+// GEMM tiles: 256 x 256 outputs, 8 MFMA waves (2 x 4, 128 x 64 each, bf16
+// 16x16x32 MFMAs accumulating in place) and 4 load waves that move 32-K
+// stages into a ring of 4 LDS buffers by DMA.  An operand is stored either
+// K-contiguous (rows of K: the activations of Dgrad) or K-outer (rows along
+// K, its M or N index contiguous: the weights of Dgrad, both operands of
+// Wgrad).  K-outer fragments come from LDS transpose reads
+// (ds_read_b64_tr_b16): lane 16 g + c of a read points at K-row 8 g + c / 4,
+// columns 4 (c % 4) .. + 3, and receives the four K-rows 8 g .. 8 g + 3 of
+// column 4 (c / 4)' ... -- i.e. each lane gets four consecutive K values of
+// its own column; two reads give the eight a 16x16x32 MFMA operand holds.
+#include "gemm_core.hpp"
+#include "kernels.hpp"
+
+namespace moe {
+
+namespace {
+
+constexpr int BT = 256;                 // tile rows and columns
+constexpr int NSTG = 4;                 // stage buffers
+constexpr int NMW = 8;                  // MFMA waves
+constexpr int NLW = 4;                  // load waves
+constexpr int THREADS = 64 * (NMW + NLW);
+constexpr int OPB = 16384;              // bytes of one operand in a stage (256 x 32 bf16)
+constexpr int STB = 2 * OPB;            // stage bytes (A then B)
+constexpr int NLI = 4;                  // DMA instructions per operand per stage and load wave
+constexpr int NLS = 2 * NLI;            // ... for both operands
+constexpr int MI = 8, NJ = 4;           // accumulator subtiles per MFMA wave
+
+enum : int { KC = 0, KO = 1 };
+
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+
+// K-outer stage rows are 512 bytes (256 bf16); the 16-byte chunk of a row is
+// xor-ed with a function of the K-row that gives the 16 rows one transpose
+// read touches (8 g + j, g, j = 0..3) 16 different chunk positions.
+__device__ __forceinline__ int xko(int k) { return (k & 3) | (((k >> 3) & 3) << 2); }
+
+__device__ __forceinline__ i32x4 frag_kc(const uint8_t* op, int r0) {
+  const int lane = threadIdx.x & 63;
+  const int r = r0 + (lane & 15);
+  return *reinterpret_cast<const i32x4*>(op + r * 64 + (((lane >> 4) ^ swz<64>(r)) << 4));
+}
+
+__device__ __forceinline__ i32x4 frag_ko(const uint8_t* op, int c0) {
+  const int lane = threadIdx.x & 63;
+  const int g = lane >> 4, c = lane & 15;
+  const int col = c0 + 4 * (c & 3);
+  const int k0 = 8 * g + (c >> 2), k1 = k0 + 4;
+  const uint8_t* p0 = op + k0 * 512 + (((col >> 3) ^ xko(k0)) << 4) + ((col & 7) << 1);
+  const uint8_t* p1 = op + k1 * 512 + (((col >> 3) ^ xko(k1)) << 4) + ((col & 7) << 1);
+  const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(const_cast<uint8_t*>(p0)));
+  const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(const_cast<uint8_t*>(p1)));
+  const i32x2 a = __builtin_bit_cast(i32x2, lo), b = __builtin_bit_cast(i32x2, hi);
+  return i32x4{a.x, a.y, b.x, b.y};
+}
+
+// One operand's loads: a buffer resource over its valid bytes (reads past it
+// return zeros), per-lane byte offsets of the lane's NLI 16-byte pieces at
+// K-step 0, and the bytes one K-step advances.
+struct Opnd {
+  rsrc_t r;
+  uint32_t off[NLI];
+  uint32_t kstride;
+};
+
+// K-contiguous operand: tile row m at byte row_off(m) of the resource, its
+// 32-K steps 64 bytes apart.
+template <class F>
+__device__ __forceinline__ Opnd opnd_kc(rsrc_t r, F row_off) {
+  Opnd o;
+  o.r = r;
+  const int w = wave_id() - NMW, lane = threadIdx.x & 63;
+#pragma unroll
+  for (int q = 0; q < NLI; ++q) {
+    const int row = 16 * (w + NLW * q) + lane / 4;
+    o.off[q] = row_off(row) + (((lane & 3) ^ swz<64>(row)) << 4);
+  }
+  o.kstride = 64;
+  return o;
+}
+
+// K-outer operand: K-row k at byte k * ld, the tile's columns from col0; a
+// K-step is 32 rows.
+__device__ __forceinline__ Opnd opnd_ko(rsrc_t r, uint32_t ld, int col0) {
+  Opnd o;
+  o.r = r;
+  const int w = wave_id() - NMW, lane = threadIdx.x & 63;
+#pragma unroll
+  for (int q = 0; q < NLI; ++q) {
+    const int k = 2 * (w + NLW * q) + lane / 32;
+    o.off[q] = k * ld + col0 * 2 + (((lane & 31) ^ xko(k)) << 4);
+  }
+  o.kstride = 32 * ld;
+  return o;
+}
+
+__device__ __forceinline__ void issue_stage(const Opnd& a, const Opnd& b, uint8_t* st, int ks) {
+  const int w = wave_id() - NMW;
+#pragma unroll
+  for (int q = 0; q < NLI; ++q) {
+    dma16(a.r, a.off[q], ks * a.kstride, st + 1024 * (w + NLW * q));
+    dma16(b.r, b.off[q], ks * b.kstride, st + OPB + 1024 * (w + NLW * q));
+  }
+}
+
+// acc[i][j][r] = C[16 (2 i + wm) + lane % 16][64 wn + 16 j + 4 (lane / 16) + r]
+// summed over K-steps 0 .. nk-1 (A: the M side, B: the N side).  Returns on
+// every wave; one barrier per K-step keeps the roles in step:
+//   before barrier ks  stage ks has landed (the load waves waited for it);
+//   after barrier ks   nobody reads stage ks-1 any more, and the load waves
+//                      refill its buffer with stage ks + NSTG - 1.
+template <int AM, int BM>
+__device__ __forceinline__ void mainloop(uint8_t* ring, const Opnd& a, const Opnd& b, int nk,
+                                         f32x4 (&acc)[MI][NJ]) {
+  const int w = wave_id();
+  if (nk <= 0) return;
+  if (w >= NMW) {
+    const int pre = min(nk, NSTG - 1);
+    for (int s = 0; s < pre; ++s) issue_stage(a, b, ring + s * STB, s);
+    if (pre == NSTG - 1)
+      wait_vm_lgkm0<(NSTG - 2) * NLS>();
+    else
+      wait_vm_lgkm0<0>();
+    for (int ks = 0; ks < nk; ++ks) {
+      block_barrier();
+      const int kn = ks + NSTG - 1;
+      if (kn < nk) {
+        issue_stage(a, b, ring + (kn % NSTG) * STB, kn);
+        wait_vm_lgkm0<(NSTG - 2) * NLS>();   // stage ks + 1
+      } else {
+        wait_vm_lgkm0<0>();
+      }
+    }
+    return;
+  }
+  const int wm = w % 2, wn = w / 2;
+  acc_fence(acc);
+  for (int ks = 0; ks < nk; ++ks) {
+    block_barrier();
+    const uint8_t* sa = ring + (ks % NSTG) * STB;
+    const uint8_t* sb = sa + OPB;
+    i32x4 wf[NJ];
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) wf[j] = BM == KO ? frag_ko(sb, 64 * wn + 16 * j) : frag_kc(sb, 64 * wn + 16 * j);
+#pragma unroll
+    for (int i = 0; i < MI; ++i) {
+      const i32x4 xf = AM == KO ? frag_ko(sa, 16 * (2 * i + wm)) : frag_kc(sa, 16 * (2 * i + wm));
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) mfma_bf16_tied(acc[i][j], wf[j], xf);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  acc_fence(acc);
+}
+
+__device__ __forceinline__ uint2 pack4(const f32x4& v) { return make_uint2(bf16x2(v[0], v[1]), bf16x2(v[2], v[3])); }
+
+__device__ __forceinline__ void unpack4(uint2 p, float (&v)[4]) {
+  v[0] = bf16_to_f32(static_cast<uint16_t>(p.x & 0xffffu));
+  v[1] = bf16_to_f32(static_cast<uint16_t>(p.x >> 16));
+  v[2] = bf16_to_f32(static_cast<uint16_t>(p.y & 0xffffu));
+  v[3] = bf16_to_f32(static_cast<uint16_t>(p.y >> 16));
+}
+
+__device__ __forceinline__ float sigmoid_ref(float z) { return 1.0f / (1.0f + expf(-z)); }
+
+// ------------------------------------------------------------------ Dgrad
+
+// Group g's row range: routed expert g (g < N_r) or shared expert g - N_r.
+struct GroupRows {
+  int first, count;
+};
+
+// Dgrad tiles: (m-tile of the forward's list, n-block), n-block fastest.
+__device__ __forceinline__ bool dgrad_tile(const BwdArgs& a, int nb_n, int& row0, int& rows, int& g, int& n0) {
+  const int q = blockIdx.x;
+  const int mt = q / nb_n;
+  if (mt >= a.mt_count[0]) return false;
+  const int4 t = a.mtiles[mt];
+  g = t.x;
+  row0 = t.y;
+  rows = t.z;
+  n0 = (q - mt * nb_n) * BT;
+  return true;
+}
+
+// dH = dY W_down for the tile's rows, then the SwiGLU backward from the
+// cached G and U: dG, dU (into dgu) and the recomputed H (into hr).
+__global__ __launch_bounds__(THREADS, 1) void dgrad_down_kernel(BwdArgs a) {
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[NSTG * STB];
+  int row0, rows, g, n0;
+  if (!dgrad_tile(a, ceil_div(a.inter, BT), row0, rows, g, n0)) return;
+  const bool shared = g >= a.n_routed;
+  const int gs = shared ? g - a.n_routed : g;
+  const uint32_t ldy = a.d * 2, ldw = a.inter * 2;
+  const uint8_t* wd = static_cast<const uint8_t*>(shared ? a.ws_down : a.w_down) + static_cast<size_t>(gs) * a.d * ldw;
+  f32x4 acc[MI][NJ];
+  zero_acc(acc);
+  if (wave_id() >= NMW) {
+    const Opnd oa = opnd_kc(make_rsrc(reinterpret_cast<const uint8_t*>(a.dys) + static_cast<size_t>(row0) * ldy,
+                                      rows * ldy),
+                            [&](int m) { return static_cast<uint32_t>((m < rows ? m : 0) * ldy); });
+    const Opnd ob = opnd_ko(make_rsrc(wd, a.d * ldw), ldw, n0);
+    mainloop<KC, KO>(ring, oa, ob, a.d / 32, acc);
+    return;
+  }
+  mainloop<KC, KO>(ring, Opnd{}, Opnd{}, a.d / 32, acc);
+  const int w = wave_id(), lane = threadIdx.x & 63, wm = w % 2, wn = w / 2;
+#pragma unroll
+  for (int i = 0; i < MI; ++i) {
+    const int row = 16 * (2 * i + wm) + (lane & 15);
+    if (row >= rows) continue;
+    const size_t r = static_cast<size_t>(row0 + row);
+    const uint16_t* gu = a.gu + r * 2 * a.inter;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int col = n0 + 64 * wn + 16 * j + 4 * (lane >> 4);
+      if (col >= a.inter) continue;
+      float G[4], U[4], dG[4], dU[4], H[4];
+      unpack4(*reinterpret_cast<const uint2*>(gu + col), G);
+      unpack4(*reinterpret_cast<const uint2*>(gu + a.inter + col), U);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float sg = sigmoid_ref(G[e]);
+        const float silu = G[e] * sg;
+        dG[e] = acc[i][j][e] * U[e] * (sg * (1.0f + G[e] * (1.0f - sg)));
+        dU[e] = acc[i][j][e] * silu;
+        H[e] = silu * U[e];
+      }
+      uint16_t* dgu = a.dgu + r * 2 * a.inter;
+      *reinterpret_cast<uint2*>(dgu + col) = make_uint2(bf16x2(dG[0], dG[1]), bf16x2(dG[2], dG[3]));
+      *reinterpret_cast<uint2*>(dgu + a.inter + col) = make_uint2(bf16x2(dU[0], dU[1]), bf16x2(dU[2], dU[3]));
+      *reinterpret_cast<uint2*>(a.hr + r * a.inter + col) = make_uint2(bf16x2(H[0], H[1]), bf16x2(H[2], H[3]));
+    }
+  }
+}
+
+// dX = [dG dU] W_gate_up for the tile's rows (bf16 rows of dx).
+__global__ __launch_bounds__(THREADS, 1) void dgrad_gateup_kernel(BwdArgs a) {
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[NSTG * STB];
+  int row0, rows, g, n0;
+  if (!dgrad_tile(a, ceil_div(a.d, BT), row0, rows, g, n0)) return;
+  const bool shared = g >= a.n_routed;
+  const int gs = shared ? g - a.n_routed : g;
+  const uint32_t ldg = a.inter * 4, ldw = a.d * 2;
+  const uint8_t* wgu =
+      static_cast<const uint8_t*>(shared ? a.ws_gate_up : a.w_gate_up) + static_cast<size_t>(gs) * 2 * a.inter * ldw;
+  f32x4 acc[MI][NJ];
+  zero_acc(acc);
+  const int nk = 2 * a.inter / 32;
+  if (wave_id() >= NMW) {
+    const Opnd oa = opnd_kc(make_rsrc(reinterpret_cast<const uint8_t*>(a.dgu) + static_cast<size_t>(row0) * ldg,
+                                      rows * ldg),
+                            [&](int m) { return static_cast<uint32_t>((m < rows ? m : 0) * ldg); });
+    const Opnd ob = opnd_ko(make_rsrc(wgu, 2 * a.inter * ldw), ldw, n0);
+    mainloop<KC, KO>(ring, oa, ob, nk, acc);
+    return;
+  }
+  mainloop<KC, KO>(ring, Opnd{}, Opnd{}, nk, acc);
+  const int w = wave_id(), lane = threadIdx.x & 63, wm = w % 2, wn = w / 2;
+#pragma unroll
+  for (int i = 0; i < MI; ++i) {
+    const int row = 16 * (2 * i + wm) + (lane & 15);
+    if (row >= rows) continue;
+    uint16_t* dst = a.dx + static_cast<size_t>(row0 + row) * a.d;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int col = n0 + 64 * wn + 16 * j + 4 * (lane >> 4);
+      if (col < a.d) *reinterpret_cast<uint2*>(dst + col) = pack4(acc[i][j]);
+    }
+  }
+}
+
+// ------------------------------------------------------------------ Wgrad
+
+__device__ __forceinline__ GroupRows group_rows(const BwdArgs& a, int g) {
+  if (g < a.n_routed) return {a.offsets[g], a.counts[g]};
+  return {static_cast<int>(a.TK + static_cast<long long>(g - a.n_routed) * a.T), a.T};
+}
+
+// C[m][n] = sum over the group's rows r of A[r][m] B[r][n], both K-outer
+// (rows r of lda / ldb bytes), written as fp32 into dst (ldc floats per row).
+// Block q: group q / (mb_n * nb_n), then the m-block, the n-block fastest.
+__device__ __forceinline__ void wgrad_tile(const BwdArgs& a, const uint16_t* A, int M, const uint16_t* B, int N,
+                                           float* routed_dst, float* shared_dst) {
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[NSTG * STB];
+  const int mb_n = ceil_div(M, BT), nb_n = ceil_div(N, BT);
+  const int q = blockIdx.x;
+  const int g = q / (mb_n * nb_n);
+  const int rem = q - g * mb_n * nb_n;
+  const int m0 = (rem / nb_n) * BT, n0 = (rem % nb_n) * BT;
+  const GroupRows gr = group_rows(a, g);
+  const uint32_t lda = M * 2, ldb = N * 2;
+  const int nk = ceil_div(gr.count, 32);
+  f32x4 acc[MI][NJ];
+  zero_acc(acc);
+  if (wave_id() >= NMW) {
+    const Opnd oa = opnd_ko(make_rsrc(reinterpret_cast<const uint8_t*>(A) + static_cast<size_t>(gr.first) * lda,
+                                      gr.count * lda), lda, m0);
+    const Opnd ob = opnd_ko(make_rsrc(reinterpret_cast<const uint8_t*>(B) + static_cast<size_t>(gr.first) * ldb,
+                                      gr.count * ldb), ldb, n0);
+    mainloop<KO, KO>(ring, oa, ob, nk, acc);
+    return;
+  }
+  mainloop<KO, KO>(ring, Opnd{}, Opnd{}, nk, acc);
+  float* dst = g < a.n_routed ? routed_dst + static_cast<size_t>(g) * M * N
+                              : shared_dst + static_cast<size_t>(g - a.n_routed) * M * N;
+  const int w = wave_id(), lane = threadIdx.x & 63, wm = w % 2, wn = w / 2;
+#pragma unroll
+  for (int i = 0; i < MI; ++i) {
+    const int m = m0 + 16 * (2 * i + wm) + (lane & 15);
+    if (m >= M) continue;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int n = n0 + 64 * wn + 16 * j + 4 * (lane >> 4);
+      if (n < N)
+        *reinterpret_cast<float4*>(dst + static_cast<size_t>(m) * N + n) =
+            make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
+    }
+  }
+}
+
+// dW_down[c][i] = sum_r dY[r][c] H[r][i]
+__global__ __launch_bounds__(THREADS, 1) void wgrad_down_kernel(BwdArgs a) {
+  wgrad_tile(a, a.dys, a.d, a.hr, a.inter, a.dw_down, a.dws_down);
+}
+
+// dW_gate_up[j][c] = sum_r [dG dU][r][j] X[r][c]
+__global__ __launch_bounds__(THREADS, 1) void wgrad_gateup_kernel(BwdArgs a) {
+  wgrad_tile(a, a.dgu, 2 * a.inter, a.xp, a.d, a.dw_gate_up, a.dws_gate_up);
+}
+
+// ------------------------------------------------------------------ elementwise passes
+
+// One wave per grouped row: dY_r = g dy_t, X_r = u_t (bf16) and, for a routed
+// row, dg_{t,k} = dy_t . Y_r (fp32, a fixed reduction order).
+__global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a) {
+  const long long r = static_cast<long long>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (r >= a.R) return;
+  int t, k = -1;
+  float gsc = 1.f;
+  if (r < a.TK) {
+    t = a.perm_token[r];
+    for (int j = 0; j < a.top_k; ++j)
+      if (a.pos[static_cast<size_t>(t) * a.top_k + j] == r) k = j;
+    gsc = k >= 0 ? a.gate[static_cast<size_t>(t) * a.top_k + k] : 0.f;   // k is found for routing of one forward
+  } else {
+    t = static_cast<int>((r - a.TK) % a.T);
+  }
+  const float* dyt = a.dy + static_cast<size_t>(t) * a.d;
+  const uint16_t* ut = a.u + static_cast<size_t>(t) * a.d;
+  const uint16_t* yr = a.y + static_cast<size_t>(r) * a.d;
+  uint16_t* dysr = a.dys + static_cast<size_t>(r) * a.d;
+  uint16_t* xpr = a.xp + static_cast<size_t>(r) * a.d;
+  float dot = 0.f;
+  for (int c = 4 * lane; c < a.d; c += 256) {
+    const float4 dv = *reinterpret_cast<const float4*>(dyt + c);
+    *reinterpret_cast<uint2*>(dysr + c) = make_uint2(bf16x2(gsc * dv.x, gsc * dv.y), bf16x2(gsc * dv.z, gsc * dv.w));
+    *reinterpret_cast<uint2*>(xpr + c) = *reinterpret_cast<const uint2*>(ut + c);
+    if (k >= 0) {
+      float yv[4];
+      unpack4(*reinterpret_cast<const uint2*>(yr + c), yv);
+      dot = fmaf(dv.x, yv[0], dot);
+      dot = fmaf(dv.y, yv[1], dot);
+      dot = fmaf(dv.z, yv[2], dot);
+      dot = fmaf(dv.w, yv[3], dot);
+    }
+  }
+  if (k < 0) return;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) dot += __shfl_xor(dot, off);
+  if (lane == 0) a.dg[static_cast<size_t>(t) * a.top_k + k] = dot;
+}
+
+// Per token: ds_k = (dg_k - sum_j g_j dg_j) / S, dz_k = ds_k s_k (1 - s_k);
+// dz also by grouped row (for dE).
+__global__ __launch_bounds__(256) void bwd_dz_kernel(BwdArgs a) {
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  if (t >= a.T) return;
+  const size_t o = static_cast<size_t>(t) * a.top_k;
+  float S = 0.f, gd = 0.f;
+  for (int k = 0; k < a.top_k; ++k) {
+    S += a.sel_score[o + k];
+    gd = fmaf(a.gate[o + k], a.dg[o + k], gd);
+  }
+  for (int k = 0; k < a.top_k; ++k) {
+    const float s = a.sel_score[o + k];
+    const float dz = (a.dg[o + k] - gd) / S * (s * (1.f - s));
+    a.dz[o + k] = dz;
+    a.dzr[a.pos[o + k]] = dz;
+  }
+}
+
+// One wave per token: du_t = dy_t + the shared experts' dX rows + the K
+// routed dX rows + sum_k dz_k e_k, in that order (fp32).
+__global__ __launch_bounds__(256) void bwd_du_kernel(BwdArgs a) {
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (t >= a.T) return;
+  const size_t o = static_cast<size_t>(t) * a.top_k;
+  for (int c = 4 * lane; c < a.d; c += 256) {
+    float4 v = *reinterpret_cast<const float4*>(a.dy + static_cast<size_t>(t) * a.d + c);
+    float x[4];
+    for (int s = 0; s < a.n_shared; ++s) {
+      unpack4(*reinterpret_cast<const uint2*>(a.dx + static_cast<size_t>(a.TK + static_cast<long long>(s) * a.T + t) * a.d + c), x);
+      v.x += x[0]; v.y += x[1]; v.z += x[2]; v.w += x[3];
+    }
+    for (int k = 0; k < a.top_k; ++k) {
+      unpack4(*reinterpret_cast<const uint2*>(a.dx + static_cast<size_t>(a.pos[o + k]) * a.d + c), x);
+      v.x += x[0]; v.y += x[1]; v.z += x[2]; v.w += x[3];
+    }
+    for (int k = 0; k < a.top_k; ++k) {
+      const float dz = a.dz[o + k];
+      unpack4(*reinterpret_cast<const uint2*>(a.centroids + static_cast<size_t>(a.idx[o + k]) * a.d + c), x);
+      v.x = fmaf(dz, x[0], v.x); v.y = fmaf(dz, x[1], v.y); v.z = fmaf(dz, x[2], v.z); v.w = fmaf(dz, x[3], v.w);
+    }
+    *reinterpret_cast<float4*>(a.du + static_cast<size_t>(t) * a.d + c) = v;
+  }
+}
+
+// dE_e[c] = sum over expert e's grouped rows (ascending) of dz_r u_{t(r)}[c];
+// block (e, 1024-column chunk), 4 columns per thread; zero for an expert
+// without rows.
+__global__ __launch_bounds__(256) void bwd_de_kernel(BwdArgs a) {
+  const int e = blockIdx.y;
+  const int c = blockIdx.x * 1024 + 4 * threadIdx.x;
+  if (c >= a.d) return;
+  float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+  const int r1 = a.offsets[e] + a.counts[e];
+  for (int r = a.offsets[e]; r < r1; ++r) {
+    const float dz = a.dzr[r];
+    float x[4];
+    unpack4(*reinterpret_cast<const uint2*>(a.u + static_cast<size_t>(a.perm_token[r]) * a.d + c), x);
+    v.x = fmaf(dz, x[0], v.x); v.y = fmaf(dz, x[1], v.y); v.z = fmaf(dz, x[2], v.z); v.w = fmaf(dz, x[3], v.w);
+  }
+  *reinterpret_cast<float4*>(a.dcentroids + static_cast<size_t>(e) * a.d + c) = v;
+}
+
+}  // namespace
+
+hipError_t launch_backward(const BwdArgs& a, hipStream_t s) {
+  if (a.T == 0) {
+    // no tokens: every gradient is zero (no kernel writes them otherwise)
+    if (a.n_routed > 0) {
+      const dim3 gde(ceil_div(a.d, 1024), a.n_routed);
+      hipLaunchKernelGGL(bwd_de_kernel, gde, dim3(256), 0, s, a);
+    }
+    const int G = a.n_routed + a.n_shared;
+    hipLaunchKernelGGL(wgrad_down_kernel, dim3(G * ceil_div(a.d, BT) * ceil_div(a.inter, BT)), dim3(THREADS), 0, s, a);
+    hipLaunchKernelGGL(wgrad_gateup_kernel, dim3(G * ceil_div(2 * a.inter, BT) * ceil_div(a.d, BT)), dim3(THREADS), 0,
+                       s, a);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL(bwd_prep_kernel, dim3(static_cast<unsigned>(ceil_div(static_cast<int>(a.R), 4))), dim3(256), 0, s,
+                     a);
+  hipLaunchKernelGGL(bwd_dz_kernel, dim3(ceil_div(a.T, 256)), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(dgrad_down_kernel, dim3(a.max_mtiles * ceil_div(a.inter, BT)), dim3(THREADS), 0, s, a);
+  hipLaunchKernelGGL(dgrad_gateup_kernel, dim3(a.max_mtiles * ceil_div(a.d, BT)), dim3(THREADS), 0, s, a);
+  const int G = a.n_routed + a.n_shared;
+  hipLaunchKernelGGL(wgrad_down_kernel, dim3(G * ceil_div(a.d, BT) * ceil_div(a.inter, BT)), dim3(THREADS), 0, s, a);
+  hipLaunchKernelGGL(wgrad_gateup_kernel, dim3(G * ceil_div(2 * a.inter, BT) * ceil_div(a.d, BT)), dim3(THREADS), 0, s,
+                     a);
+  hipLaunchKernelGGL(bwd_du_kernel, dim3(ceil_div(a.T, 4)), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(bwd_de_kernel, dim3(ceil_div(a.d, 1024), a.n_routed), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -202,6 +202,27 @@ __device__ __forceinline__ void gateup_tile(const GateUpArgs& a, const MK& make_
   zero_acc(acc);
   gg_mainloop<FMT, NSUB, NSUBC>(make_pipe, st, nk, wr, acc, swl, kb);
   if constexpr (FMT == FMT_BF16) {
+    // Training: the SwiGLU inputs G and U of the tile, kept (bf16) for the
+    // backward pass, which recomputes H from them.
+    if (a.gu != nullptr && w < GG<FMT>::NW) {
+#pragma unroll
+      for (int i = 0; i < NSUBC; ++i) {
+        const int row = 16 * (WM * i + wm) + lr;
+        if (row < rows) {
+          uint16_t* const grow = a.gu + static_cast<size_t>(row0 + row) * 2 * a.inter;
+#pragma unroll
+          for (int jj = 0; jj < NJ2; ++jj) {
+            const int col = n0 + HW * wn + 16 * jj + 4 * lg;
+            if (col < a.inter) {
+              *reinterpret_cast<uint2*>(grow + col) =
+                  pack_bf16x4(acc[i][jj][0], acc[i][jj][1], acc[i][jj][2], acc[i][jj][3]);
+              *reinterpret_cast<uint2*>(grow + a.inter + col) =
+                  pack_bf16x4(acc[i][jj + NJ2][0], acc[i][jj + NJ2][1], acc[i][jj + NJ2][2], acc[i][jj + NJ2][3]);
+            }
+          }
+        }
+      }
+    }
     // H tile (rows x 128 columns, bf16) through LDS; every wave stores
     constexpr int PITCH = GG_HCOLS * 2 + 16;   // padded rows: the 16 rows of a subtile hit different banks
     static_assert(GG<FMT>::BM * PITCH <= GG<FMT>::NST * P::STAGE_BYTES, "output tile fits the stage ring");

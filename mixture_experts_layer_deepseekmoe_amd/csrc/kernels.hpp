@@ -33,6 +33,7 @@ struct RouteArgs {
   int ksplit;             // route_ksplit(...) of this shape: 0, or the number of K slices
   int n_groups;           // group-limited routing: experts in n_groups equal runs, a token
   int topk_groups;        // takes experts from at most topk_groups of them (off: topk_groups >= n_groups)
+  float* sel_score;       // null, or [T][K]: the selected experts' sigmoid scores s (training)
 };
 
 // Batches under 128 router blocks (T < 4096) spread the experts over blocks
@@ -90,6 +91,7 @@ struct GateUpArgs {
   int max_mtiles;
   void* h;                // [R][I]: f32 / bf16 / e4m3 codes
   float* h_scale;         // e4m3: [R][I/128]
+  uint16_t* gu;           // bf16 training only: [R][2I] the SwiGLU inputs G (columns 0..I-1) and U; else null
 };
 
 struct DownArgs {
@@ -116,7 +118,48 @@ struct CombineArgs {
   void* out;              // [T][d]
 };
 
+// The backward pass (bf16): what the training forward left in the workspace,
+// the upstream gradient, and the gradient outputs.
+struct BwdArgs {
+  int T, d, n_routed, n_shared, inter, top_k;
+  long long TK, R;                // T*K routed rows; R = T*K + N_s*T grouped rows
+  int max_mtiles;
+  const int4* mtiles;             // the forward's m-tile list
+  const int32_t* mt_count;
+  const int32_t* offsets;         // [N_r + 1]
+  const int32_t* counts;          // [N_r]
+  const int32_t* perm_token;      // [T*K]
+  const int32_t* pos;             // [T][K]
+  const int32_t* idx;             // [T][K]
+  const float* gate;              // [T][K]
+  const float* sel_score;         // [T][K] selected sigmoids
+  const uint16_t* u;              // [T][d] bf16
+  const uint16_t* centroids;      // [N_r][d] bf16
+  const uint16_t* y;              // [R][d] bf16 expert outputs Y
+  const float* dy;                // [T][d] upstream gradient
+  const void* w_gate_up;          // [N_r][2I][d] bf16
+  const void* w_down;             // [N_r][d][I]
+  const void* ws_gate_up;         // [N_s][2I][d]
+  const void* ws_down;            // [N_s][d][I]
+  const uint16_t* gu;             // [R][2I] cached G | U
+  uint16_t* dys;                  // [R][d] g dy rows
+  uint16_t* xp;                   // [R][d] gathered u rows
+  uint16_t* dgu;                  // [R][2I] dG | dU
+  uint16_t* hr;                   // [R][I] recomputed H
+  uint16_t* dx;                   // [R][d] Dgrad of the gate/up GEMM
+  float* dg;                      // [T][K]
+  float* dz;                      // [T][K]
+  float* dzr;                     // [T*K] dz by grouped row
+  float* du;                      // [T][d]
+  float* dcentroids;              // [N_r][d]
+  float* dw_gate_up;              // [N_r][2I][d]
+  float* dw_down;                 // [N_r][d][I]
+  float* dws_gate_up;             // [N_s][2I][d]
+  float* dws_down;                // [N_s][d][I]
+};
+
 hipError_t launch_route(int fmt, const RouteArgs& a, hipStream_t s);
+hipError_t launch_backward(const BwdArgs& a, hipStream_t s);
 hipError_t launch_group(const GroupArgs& a, hipStream_t s);
 hipError_t launch_quant_act(const void* x, int rows, int cols, uint8_t* q, float* scale, hipStream_t s);
 hipError_t launch_quant_weight(int fmt, const void* w, long long n, int rows, int cols, uint8_t* q, float* scale,

@@ -28,6 +28,8 @@ int fmt_of(int dt) { return dt == MOE_DTYPE_F32 ? FMT_F32 : (dt == MOE_DTYPE_BF1
 // Workspace map (byte offsets, each 256-byte aligned).
 struct Layout {
   size_t hist, idx, gate, counts, offsets, perm, pos, mtiles, mtcount, uq, us, h, hs, y, scores, total;
+  // training (moe_forward_train / moe_backward) only, after `total`
+  size_t sel, gu, dys, xp, dgu, dx, dg, dz, dzr, total_train;
   int nblk, max_mt;
   long long rows;   // grouped rows: T*K routed + N_s*T shared
 };
@@ -57,6 +59,17 @@ Layout make_layout(const moe_shape& s) {
   L.y = take(static_cast<size_t>(L.rows) * s.d * (s.w_dtype == MOE_DTYPE_F32 ? 4 : 2));
   L.scores = take(static_cast<size_t>(moe::route_scratch_floats(fmt_of(s.x_dtype), T, s.d, s.n_routed)) * 4);
   L.total = o;
+  const size_t R = static_cast<size_t>(L.rows);
+  L.sel = take(TK * 4);
+  L.gu = take(R * 2 * s.inter * 2);
+  L.dys = take(R * s.d * 2);
+  L.xp = take(R * s.d * 2);
+  L.dgu = take(R * 2 * s.inter * 2);
+  L.dx = take(R * s.d * 2);
+  L.dg = take(TK * 4);
+  L.dz = take(TK * 4);
+  L.dzr = take(TK * 4);
+  L.total_train = o;
   return L;
 }
 
@@ -139,7 +152,7 @@ int validate_forward(const moe_shape* shape, const void* u, const void* centroid
                      const moe_weights* wt, const void* y);
 int run_forward(const moe_shape& s, const Layout& L, const void* u, const void* centroids, const float* bias,
                 const moe_weights* wt, void* y, const moe_routing* routing, void* workspace, const moe_trace* trace,
-                hipStream_t stream);
+                hipStream_t stream, bool train = false);
 
 // ---- the workspace of moe_forward_static
 //
@@ -278,7 +291,7 @@ int validate_forward(const moe_shape* shape, const void* u, const void* centroid
 // already validated).
 int run_forward(const moe_shape& s, const Layout& L, const void* u, const void* centroids, const float* bias,
                 const moe_weights* wt, void* y, const moe_routing* routing, void* workspace, const moe_trace* trace,
-                hipStream_t stream) {
+                hipStream_t stream, bool train) {
   int rc = MOE_OK;
   const bool fp8 = s.w_dtype == MOE_DTYPE_E4M3;
   moe_routing r{};
@@ -295,7 +308,8 @@ int run_forward(const moe_shape& s, const Layout& L, const void* u, const void* 
   Stages stg{trace, stream};
   stg.begin(MOE_STAGE_ROUTE);
   moe::RouteArgs ra{u,    centroids, bias, s.T, s.d, s.n_routed, s.top_k, idx, gate, at<float>(workspace, L.scores),
-                    moe::route_ksplit(fmt_of(s.x_dtype), s.T, s.d, s.n_routed), groups_of(s), topk_groups_of(s)};
+                    moe::route_ksplit(fmt_of(s.x_dtype), s.T, s.d, s.n_routed), groups_of(s), topk_groups_of(s),
+                    train ? at<float>(workspace, L.sel) : nullptr};
   rc = check_launch(moe::launch_route(fmt_of(s.x_dtype), ra, stream));
   if (rc != MOE_OK) return rc;
   stg.end(MOE_STAGE_ROUTE);
@@ -324,7 +338,8 @@ int run_forward(const moe_shape& s, const Layout& L, const void* u, const void* 
   const int TK = s.T * s.top_k;
   moe::GateUpArgs ga{x, xs, perm, s.T, TK, s.n_routed, s.d, s.inter, wt->w_gate_up, wt->ws_gate_up,
                      wt->s_gate_up, wt->ss_gate_up, mtiles, mtcount, L.max_mt,
-                     at<void>(workspace, L.h), fp8 ? at<float>(workspace, L.hs) : nullptr};
+                     at<void>(workspace, L.h), fp8 ? at<float>(workspace, L.hs) : nullptr,
+                     train ? at<uint16_t>(workspace, L.gu) : nullptr};
   stg.begin(MOE_STAGE_GATE_UP);
   rc = check_launch(moe::launch_gateup(wf, ga, stream));
   if (rc != MOE_OK) return rc;
@@ -348,6 +363,91 @@ int run_forward(const moe_shape& s, const Layout& L, const void* u, const void* 
 }  // namespace
 
 extern "C" {
+
+int moe_train_workspace_size(const moe_shape* shape, size_t* bytes) {
+  if (bytes == nullptr) return MOE_ERR_INVALID_ARG;
+  const int rc = validate_shape(shape);
+  if (rc != MOE_OK) return rc;
+  if (shape->x_dtype != MOE_DTYPE_BF16 || shape->w_dtype != MOE_DTYPE_BF16) return MOE_ERR_UNSUPPORTED;
+  *bytes = make_layout(*shape).total_train;
+  return MOE_OK;
+}
+
+int moe_forward_train(const moe_shape* shape, const void* u, const void* centroids, const float* bias,
+                      const moe_weights* wt, void* y, void* workspace, size_t workspace_bytes, const moe_trace* trace,
+                      hipStream_t stream) {
+  const int rc = validate_forward(shape, u, centroids, bias, wt, y);
+  if (rc != MOE_OK) return rc;
+  if (shape->x_dtype != MOE_DTYPE_BF16 || shape->w_dtype != MOE_DTYPE_BF16) return MOE_ERR_UNSUPPORTED;
+  const Layout L = make_layout(*shape);
+  if (workspace == nullptr || workspace_bytes < L.total_train) return MOE_ERR_WORKSPACE;
+  return run_forward(*shape, L, u, centroids, bias, wt, y, nullptr, workspace, trace, stream, true);
+}
+
+int moe_backward(const moe_shape* shape, const void* u, const void* centroids, const moe_weights* wt, const float* dy,
+                 float* du, float* dcentroids, const moe_weight_grads* grads, void* workspace, size_t workspace_bytes,
+                 hipStream_t stream) {
+  const int rc = validate_shape(shape);
+  if (rc != MOE_OK) return rc;
+  const moe_shape& s = *shape;
+  if (s.x_dtype != MOE_DTYPE_BF16 || s.w_dtype != MOE_DTYPE_BF16) return MOE_ERR_UNSUPPORTED;
+  if (wt == nullptr || grads == nullptr || centroids == nullptr || dcentroids == nullptr) return MOE_ERR_INVALID_ARG;
+  if (s.T > 0 && (u == nullptr || dy == nullptr || du == nullptr || !aligned16(u) || !aligned16(dy) || !aligned16(du)))
+    return MOE_ERR_INVALID_ARG;
+  if (wt->w_gate_up == nullptr || wt->w_down == nullptr || grads->dw_gate_up == nullptr || grads->dw_down == nullptr ||
+      !aligned16(wt->w_gate_up) || !aligned16(wt->w_down) || !aligned16(grads->dw_gate_up) ||
+      !aligned16(grads->dw_down) || !aligned16(centroids) || !aligned16(dcentroids))
+    return MOE_ERR_INVALID_ARG;
+  if (s.n_shared > 0 && (wt->ws_gate_up == nullptr || wt->ws_down == nullptr || grads->dws_gate_up == nullptr ||
+                         grads->dws_down == nullptr || !aligned16(wt->ws_gate_up) || !aligned16(wt->ws_down) ||
+                         !aligned16(grads->dws_gate_up) || !aligned16(grads->dws_down)))
+    return MOE_ERR_INVALID_ARG;
+  const Layout L = make_layout(s);
+  if (workspace == nullptr || workspace_bytes < L.total_train) return MOE_ERR_WORKSPACE;
+  moe::BwdArgs a{};
+  a.T = s.T;
+  a.d = s.d;
+  a.n_routed = s.n_routed;
+  a.n_shared = s.n_shared;
+  a.inter = s.inter;
+  a.top_k = s.top_k;
+  a.TK = static_cast<long long>(s.T) * s.top_k;
+  a.R = L.rows;
+  a.max_mtiles = L.max_mt;
+  a.mtiles = at<int4>(workspace, L.mtiles);
+  a.mt_count = at<int32_t>(workspace, L.mtcount);
+  a.offsets = at<int32_t>(workspace, L.offsets);
+  a.counts = at<int32_t>(workspace, L.counts);
+  a.perm_token = at<int32_t>(workspace, L.perm);
+  a.pos = at<int32_t>(workspace, L.pos);
+  a.idx = at<int32_t>(workspace, L.idx);
+  a.gate = at<float>(workspace, L.gate);
+  a.sel_score = at<float>(workspace, L.sel);
+  a.u = static_cast<const uint16_t*>(u);
+  a.centroids = static_cast<const uint16_t*>(centroids);
+  a.y = at<uint16_t>(workspace, L.y);
+  a.dy = dy;
+  a.w_gate_up = wt->w_gate_up;
+  a.w_down = wt->w_down;
+  a.ws_gate_up = wt->ws_gate_up;
+  a.ws_down = wt->ws_down;
+  a.gu = at<uint16_t>(workspace, L.gu);
+  a.dys = at<uint16_t>(workspace, L.dys);
+  a.xp = at<uint16_t>(workspace, L.xp);
+  a.dgu = at<uint16_t>(workspace, L.dgu);
+  a.hr = at<uint16_t>(workspace, L.h);   // the forward's H is not needed any more: H is recomputed into it
+  a.dx = at<uint16_t>(workspace, L.dx);
+  a.dg = at<float>(workspace, L.dg);
+  a.dz = at<float>(workspace, L.dz);
+  a.dzr = at<float>(workspace, L.dzr);
+  a.du = du;
+  a.dcentroids = dcentroids;
+  a.dw_gate_up = grads->dw_gate_up;
+  a.dw_down = grads->dw_down;
+  a.dws_gate_up = grads->dws_gate_up;
+  a.dws_down = grads->dws_down;
+  return check_launch(moe::launch_backward(a, stream));
+}
 
 int moe_update_bias(float* bias, const int32_t* counts, int32_t n_routed, int64_t total_assignments, float gamma,
                     hipStream_t stream) {

@@ -130,6 +130,7 @@ __device__ __forceinline__ void select_topk(const float* srow, const float (&bq)
   if (lane < top_k) {
     idx_out[lane] = chosen;
     gate_out[lane] = chosen_s / sum;
+    if (a.sel_score != nullptr) a.sel_score[(idx_out - a.idx) + lane] = chosen_s;
   }
 }
 
