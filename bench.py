@@ -59,6 +59,8 @@ def main():
     ap.add_argument("--workload", default="bf16_d7168")
     ap.add_argument("--cpu-sample-tokens", type=int, default=256)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--train", action="store_true",
+                    help="time the training step instead: moe_forward_train + moe_backward (bf16)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -76,6 +78,8 @@ def main():
 
     cfg = get_config(args.workload)
     torch.cuda.set_device(0)
+    if args.train:
+        return train_bench(args, cfg)
     log(f"[bench] workload {cfg.name}: generating seeded inputs")
     inp = make_inputs(cfg, 0, weights_device="cuda")
     shape = moe.LayerShape.from_config(cfg)
@@ -210,6 +214,128 @@ def main():
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_sample_tokens, result)
     print(json.dumps(result), flush=True)
+
+
+def train_bench(args, cfg):
+    """The training step on one GPU: moe_forward_train, then moe_backward for
+    a seeded N(0, 1) upstream gradient.  Prints one JSON line; the roofline is
+    that of the slowest backward GEMM (events over the timed steps, on the
+    library's stream)."""
+    import torch
+
+    import mixture_experts_layer_deepseekmoe_amd as moe
+    from mixture_experts_layer_deepseekmoe_amd.binding import BACKWARD_STAGES, HipEvents
+    from moe_workloads import make_inputs
+
+    if cfg.w_dtype != "bf16":
+        print("the training path is bf16 only", file=sys.stderr)
+        sys.exit(2)
+    log(f"[bench] train workload {cfg.name}: generating seeded inputs")
+    inp = make_inputs(cfg, 0, weights_device="cuda")
+    shape = moe.LayerShape.from_config(cfg)
+    u, cen, bias = (t.cuda().contiguous() for t in (inp.u, inp.centroids, inp.bias))
+    weights = moe.prepare_weights(cfg, inp)
+    ws = moe.alloc_train_workspace(shape)
+    grads = moe.alloc_weight_grads(shape)
+    y = torch.empty((cfg.T, cfg.d), dtype=torch.float32 if cfg.out_dtype == "f32" else torch.bfloat16, device="cuda")
+    g = torch.Generator(device="cuda")
+    g.manual_seed(7)
+    dy = torch.randn((cfg.T, cfg.d), generator=g, device="cuda", dtype=torch.float32)
+    TK = cfg.T * cfg.top_k
+    torch.cuda.synchronize()
+
+    def step(trace_b=None):
+        moe.moe_forward_train(shape, u, cen, bias, weights, ws, y=y)
+        moe.moe_backward(shape, u, cen, weights, dy, ws, grads=grads, trace=trace_b)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [HipEvents(BACKWARD_STAGES) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(events[k].trace)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    stages = {}
+    for ev in events:
+        for name, ms in ev.elapsed_ms().items():
+            stages[name] = stages.get(name, 0.0) + ms / args.steps
+        ev.close()
+    fw = HipEvents()
+    moe.moe_forward_train(shape, u, cen, bias, weights, ws, y=y, trace=fw.trace)
+    torch.cuda.synchronize()
+    stages.update({"fwd_" + k: v for k, v in fw.elapsed_ms().items()})
+    fw.close()
+    log(f"[bench] train {elapsed / args.steps * 1e3:.3f} ms/step; stages (ms): "
+        + ", ".join(f"{k} {v:.4f}" for k, v in stages.items()))
+
+    R = TK + cfg.n_shared * cfg.T
+    d, I = cfg.d, cfg.inter
+    G = cfg.n_routed + cfg.n_shared
+    routing = moe.moe_route(shape, u, cen, bias)
+    counts = routing["expert_counts"].cpu().numpy()
+    touched = int((counts > 0).sum()) + cfg.n_shared
+    # algorithmic flops and bytes per launch of each backward GEMM
+    gemms = {
+        "bwd_dgrad_down": (2.0 * R * d * I, touched * d * I * 2 + R * d * 2 + 2 * R * 2 * I * 2 + R * I * 2),
+        "bwd_dgrad_gate_up": (2.0 * R * 2 * I * d, touched * 2 * I * d * 2 + R * 2 * I * 2 + R * d * 2),
+        "bwd_wgrad_down": (2.0 * R * d * I, R * d * 2 + R * I * 2 + G * d * I * 4),
+        "bwd_wgrad_gate_up": (2.0 * R * 2 * I * d, R * 2 * I * 2 + R * d * 2 + G * 2 * I * d * 4),
+    }
+    lines = {}
+    for name, (fl, by) in gemms.items():
+        sec = stages[name] * 1e-3
+        tf, gbs = fl / sec / 1e12, by / sec / 1e9
+        ridge = PEAK_TFLOPS["bf16"] * 1e12 / (PEAK_HBM_GBS * 1e9)
+        if fl / by < ridge:
+            bound, ach, pk, unit = "hbm", gbs, PEAK_HBM_GBS, "GB/s"
+        else:
+            bound, ach, pk, unit = "mfma", tf, PEAK_TFLOPS["bf16"], "TFLOP/s"
+        lines[name] = {"bound": bound, "achieved": round(ach, 2), "peak": pk, "unit": unit, "frac": round(ach / pk, 4),
+                       "flops_per_launch": fl, "algorithmic_bytes_per_launch": by, "avg_launch_ms": round(stages[name], 4),
+                       "mfma_frac": round(tf / PEAK_TFLOPS["bf16"], 4), "hbm_frac": round(gbs / PEAK_HBM_GBS, 4)}
+    dominant = max(gemms, key=lambda k: stages[k])
+    roofline = dict(lines[dominant], kernel=dominant, traffic=None)
+    result = {
+        "metric": "MoE-layer training step tokens/sec (forward + backward, bf16), d=7168 N_r=256 K=8, 1 GPU",
+        "value": round(cfg.T * args.steps / elapsed, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(elapsed / args.steps * 1e3, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) activations and upstream gradient, N(0,0.006) weights, random init)",
+        "config": {"workload": cfg.name, "T": cfg.T, "d": d, "n_routed": cfg.n_routed, "n_shared": cfg.n_shared,
+                   "inter": I, "top_k": cfg.top_k, "parallelism": "single GPU", "step": "forward_train + backward"},
+        "roofline": roofline, "backward_gemms": lines, "stage_ms": {k: round(v, 4) for k, v in stages.items()},
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = train_cpu_baseline(cfg, inp, dy, 32)
+    print(json.dumps(result), flush=True)
+
+
+def train_cpu_baseline(cfg, inp, dy, n_tokens):
+    """The CPU oracle's forward + backward on the first n_tokens tokens."""
+    import threadpoolctl
+
+    from moe_workloads import to_numpy_f32
+    from oracle import moe_oracle as O
+
+    n = min(n_tokens, cfg.T)
+    u, E, b = to_numpy_f32(inp.u[:n]), to_numpy_f32(inp.centroids), inp.bias.numpy()
+    routed = lambda e: (to_numpy_f32(inp.w_gate_up[e]), to_numpy_f32(inp.w_down[e]))
+    shared = [(to_numpy_f32(inp.ws_gate_up[s]), to_numpy_f32(inp.ws_down[s])) for s in range(cfg.n_shared)]
+    host_cores = len(os.sched_getaffinity(0))
+    cap = int(os.environ.get("OMP_NUM_THREADS", "0") or 0)
+    threads = min(host_cores, cap) if cap > 0 else host_cores
+    dyn = dy[:n].cpu().numpy()
+    with threadpoolctl.threadpool_limits(limits=threads):
+        used = max([p.get("num_threads", 1) for p in threadpoolctl.threadpool_info()], default=1)
+        t0 = time.perf_counter()
+        O.layer_backward(u, E, b, cfg.top_k, routed, cfg.n_routed, shared, dyn)
+        dt = time.perf_counter() - t0
+    return {"value": round(n / dt, 3), "unit": "tokens/s", "cores": used, "kind": "oracle",
+            "host_cores_visible": host_cores,
+            "sample": f"first {n} of the {cfg.T} tokens, fp64 forward + backward with every weight gradient",
+            "seconds": round(dt, 2)}
 
 
 def bias_loop(cfg, shape, u, cen, ws, steps=100):

@@ -194,14 +194,21 @@ int moe_workspace_layout(const moe_shape* shape, moe_workspace_map* map);
  * (hipEventRecord; the events are created and owned by the caller).  A stage
  * that does not run for the given dtypes gets both events back to back.
  */
-#define MOE_NUM_STAGES 6
+#define MOE_NUM_STAGES 12
 typedef enum {
   MOE_STAGE_ROUTE = 0,    /* affinity GEMM + sigmoid + bias + top-K + gates */
   MOE_STAGE_GROUP = 1,    /* expert histogram, scan, stable permutation, m-tile list */
   MOE_STAGE_QUANT = 2,    /* FP8 only: 1x128 quantisation of u */
   MOE_STAGE_GATE_UP = 3,  /* grouped gate/up GEMM with the SwiGLU epilogue */
   MOE_STAGE_DOWN = 4,     /* grouped down-projection GEMM */
-  MOE_STAGE_COMBINE = 5   /* residual + shared + gate-weighted routed sum */
+  MOE_STAGE_COMBINE = 5,  /* residual + shared + gate-weighted routed sum */
+  /* moe_backward's stages */
+  MOE_STAGE_BWD_PREP = 6,           /* scaled dy rows, gathered u rows, dg; dz */
+  MOE_STAGE_BWD_DGRAD_DOWN = 7,     /* dH = dY W_down with the SwiGLU backward */
+  MOE_STAGE_BWD_DGRAD_GATE_UP = 8,  /* dX = [dG dU] W_gate_up */
+  MOE_STAGE_BWD_WGRAD_DOWN = 9,     /* dW_down = dY^T H */
+  MOE_STAGE_BWD_WGRAD_GATE_UP = 10, /* dW_gate_up = [dG dU]^T X */
+  MOE_STAGE_BWD_COMBINE = 11        /* du and dcentroids */
 } moe_stage;
 typedef struct {
   hipEvent_t start[MOE_NUM_STAGES];
@@ -267,7 +274,8 @@ int moe_forward_static(const moe_shape* shape, const void* u, const void* centro
  *   dcentroids  [N_r][d] fp32: through the router
  *   grads       fp32, the layouts of moe_weights; overwritten; experts that no
  *               token selected get zeros
- * Every sum runs in a fixed order (bit-reproducible).
+ * Every sum runs in a fixed order (bit-reproducible).  `trace` (nullable)
+ * records the MOE_STAGE_BWD_* stages.
  */
 typedef struct {
   float* dw_gate_up;   /* [N_r][2I][d] */
@@ -281,7 +289,7 @@ int moe_forward_train(const moe_shape* shape, const void* u, const void* centroi
                       const moe_trace* trace, hipStream_t stream);
 int moe_backward(const moe_shape* shape, const void* u, const void* centroids, const moe_weights* weights,
                  const float* dy, float* du, float* dcentroids, const moe_weight_grads* grads, void* workspace,
-                 size_t workspace_bytes, hipStream_t stream);
+                 size_t workspace_bytes, const moe_trace* trace, hipStream_t stream);
 
 /*
  * Aux-loss-free bias update (xyznot summary, section 2: b_i is lowered by

@@ -51,8 +51,11 @@ class Weights(ctypes.Structure):
                 ("w_gate_up", "w_down", "ws_gate_up", "ws_down", "s_gate_up", "s_down", "ss_gate_up", "ss_down")]
 
 
-NUM_STAGES = 6
-STAGES = ("route", "group", "quant", "gate_up", "down", "combine")
+NUM_STAGES = 12
+STAGES = ("route", "group", "quant", "gate_up", "down", "combine",
+          "bwd_prep", "bwd_dgrad_down", "bwd_dgrad_gate_up", "bwd_wgrad_down", "bwd_wgrad_gate_up", "bwd_combine")
+FORWARD_STAGES = STAGES[:6]
+BACKWARD_STAGES = STAGES[6:]
 
 
 class Trace(ctypes.Structure):
@@ -109,7 +112,7 @@ def load_library() -> ctypes.CDLL:
                                       ctypes.POINTER(Trace), vp]
     lib.moe_backward.restype = ctypes.c_int
     lib.moe_backward.argtypes = [ctypes.POINTER(Shape), vp, vp, ctypes.POINTER(Weights), vp, vp, vp,
-                                 ctypes.POINTER(WeightGrads), vp, sz, vp]
+                                 ctypes.POINTER(WeightGrads), vp, sz, ctypes.POINTER(Trace), vp]
     lib.moe_update_bias.restype = ctypes.c_int
     lib.moe_update_bias.argtypes = [vp, vp, i32, i64, ctypes.c_float, vp]
     lib.moe_quantize_weight_e4m3.restype = ctypes.c_int
@@ -320,7 +323,8 @@ def alloc_weight_grads(shape: LayerShape, device="cuda") -> WeightGradTensors:
 
 
 def moe_backward(shape: LayerShape, u: torch.Tensor, centroids: torch.Tensor, weights: ExpertWeights,
-                 dy: torch.Tensor, workspace: torch.Tensor, grads: Optional[WeightGradTensors] = None):
+                 dy: torch.Tensor, workspace: torch.Tensor, grads: Optional[WeightGradTensors] = None,
+                 trace: Optional[Trace] = None):
     """Gradients for dy (fp32 [T, d]) after moe_forward_train on ``workspace``:
     returns (du [T, d] fp32, dcentroids [N_r, d] fp32, weight grads)."""
     du = torch.empty((shape.T, shape.d), dtype=torch.float32, device=u.device)
@@ -329,7 +333,8 @@ def moe_backward(shape: LayerShape, u: torch.Tensor, centroids: torch.Tensor, we
     rc = load_library().moe_backward(ctypes.byref(shape.c()), _ptr(u) if shape.T else None, _ptr(centroids),
                                      ctypes.byref(weights.c()), _ptr(dy) if shape.T else None,
                                      _ptr(du) if shape.T else None, _ptr(dE), ctypes.byref(grads.c()),
-                                     _ptr(workspace), workspace.numel(), _stream())
+                                     _ptr(workspace), workspace.numel(),
+                                     ctypes.byref(trace) if trace is not None else None, _stream())
     _check(rc, "moe_backward")
     return du, dE, grads
 
@@ -391,7 +396,7 @@ class HipEvents:
     through the HIP runtime (the same events the library records on its
     stream), with elapsed-time readout."""
 
-    def __init__(self, stages=STAGES):
+    def __init__(self, stages=FORWARD_STAGES):
         """stages: the stage names to time (the library records no event
         for the others)."""
         self.hip = ctypes.CDLL("libamdhip64.so")

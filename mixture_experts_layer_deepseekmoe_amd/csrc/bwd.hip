@@ -462,30 +462,37 @@ __global__ __launch_bounds__(256) void bwd_de_kernel(BwdArgs a) {
 
 }  // namespace
 
-hipError_t launch_backward(const BwdArgs& a, hipStream_t s) {
-  if (a.T == 0) {
-    // no tokens: every gradient is zero (no kernel writes them otherwise)
-    if (a.n_routed > 0) {
-      const dim3 gde(ceil_div(a.d, 1024), a.n_routed);
-      hipLaunchKernelGGL(bwd_de_kernel, gde, dim3(256), 0, s, a);
-    }
-    const int G = a.n_routed + a.n_shared;
-    hipLaunchKernelGGL(wgrad_down_kernel, dim3(G * ceil_div(a.d, BT) * ceil_div(a.inter, BT)), dim3(THREADS), 0, s, a);
-    hipLaunchKernelGGL(wgrad_gateup_kernel, dim3(G * ceil_div(2 * a.inter, BT) * ceil_div(a.d, BT)), dim3(THREADS), 0,
-                       s, a);
-    return hipGetLastError();
-  }
-  hipLaunchKernelGGL(bwd_prep_kernel, dim3(static_cast<unsigned>(ceil_div(static_cast<int>(a.R), 4))), dim3(256), 0, s,
-                     a);
-  hipLaunchKernelGGL(bwd_dz_kernel, dim3(ceil_div(a.T, 256)), dim3(256), 0, s, a);
-  hipLaunchKernelGGL(dgrad_down_kernel, dim3(a.max_mtiles * ceil_div(a.inter, BT)), dim3(THREADS), 0, s, a);
-  hipLaunchKernelGGL(dgrad_gateup_kernel, dim3(a.max_mtiles * ceil_div(a.d, BT)), dim3(THREADS), 0, s, a);
+hipError_t launch_backward_stage(int stage, const BwdArgs& a, hipStream_t s) {
   const int G = a.n_routed + a.n_shared;
-  hipLaunchKernelGGL(wgrad_down_kernel, dim3(G * ceil_div(a.d, BT) * ceil_div(a.inter, BT)), dim3(THREADS), 0, s, a);
-  hipLaunchKernelGGL(wgrad_gateup_kernel, dim3(G * ceil_div(2 * a.inter, BT) * ceil_div(a.d, BT)), dim3(THREADS), 0, s,
-                     a);
-  hipLaunchKernelGGL(bwd_du_kernel, dim3(ceil_div(a.T, 4)), dim3(256), 0, s, a);
-  hipLaunchKernelGGL(bwd_de_kernel, dim3(ceil_div(a.d, 1024), a.n_routed), dim3(256), 0, s, a);
+  switch (stage) {
+    case 0:   // prep, dz
+      if (a.T == 0) break;
+      hipLaunchKernelGGL(bwd_prep_kernel, dim3(static_cast<unsigned>((a.R + 3) / 4)), dim3(256), 0, s, a);
+      hipLaunchKernelGGL(bwd_dz_kernel, dim3(ceil_div(a.T, 256)), dim3(256), 0, s, a);
+      break;
+    case 1:   // Dgrad of the down GEMM, SwiGLU backward
+      if (a.T == 0) break;
+      hipLaunchKernelGGL(dgrad_down_kernel, dim3(a.max_mtiles * ceil_div(a.inter, BT)), dim3(THREADS), 0, s, a);
+      break;
+    case 2:   // Dgrad of the gate/up GEMM
+      if (a.T == 0) break;
+      hipLaunchKernelGGL(dgrad_gateup_kernel, dim3(a.max_mtiles * ceil_div(a.d, BT)), dim3(THREADS), 0, s, a);
+      break;
+    case 3:   // Wgrad of the down GEMM (every group: zeros where a group has no rows)
+      hipLaunchKernelGGL(wgrad_down_kernel, dim3(G * ceil_div(a.d, BT) * ceil_div(a.inter, BT)), dim3(THREADS), 0, s,
+                         a);
+      break;
+    case 4:   // Wgrad of the gate/up GEMM
+      hipLaunchKernelGGL(wgrad_gateup_kernel, dim3(G * ceil_div(2 * a.inter, BT) * ceil_div(a.d, BT)), dim3(THREADS),
+                         0, s, a);
+      break;
+    case 5:   // du, dcentroids (zeros for experts without rows)
+      if (a.T > 0) hipLaunchKernelGGL(bwd_du_kernel, dim3(ceil_div(a.T, 4)), dim3(256), 0, s, a);
+      if (a.n_routed > 0) hipLaunchKernelGGL(bwd_de_kernel, dim3(ceil_div(a.d, 1024), a.n_routed), dim3(256), 0, s, a);
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

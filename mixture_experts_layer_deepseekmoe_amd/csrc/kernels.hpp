@@ -159,7 +159,11 @@ struct BwdArgs {
 };
 
 hipError_t launch_route(int fmt, const RouteArgs& a, hipStream_t s);
-hipError_t launch_backward(const BwdArgs& a, hipStream_t s);
+// The backward in six stages, launched in order 0..5: prep and dz; Dgrad of
+// the down GEMM (with the SwiGLU backward); Dgrad of the gate/up GEMM; Wgrad
+// of the down GEMM; Wgrad of the gate/up GEMM; du and dcentroids.
+constexpr int BWD_STAGES = 6;
+hipError_t launch_backward_stage(int stage, const BwdArgs& a, hipStream_t s);
 hipError_t launch_group(const GroupArgs& a, hipStream_t s);
 hipError_t launch_quant_act(const void* x, int rows, int cols, uint8_t* q, float* scale, hipStream_t s);
 hipError_t launch_quant_weight(int fmt, const void* w, long long n, int rows, int cols, uint8_t* q, float* scale,

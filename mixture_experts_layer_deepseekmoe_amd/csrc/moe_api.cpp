@@ -320,7 +320,7 @@ int run_forward(const moe_shape& s, const Layout& L, const void* u, const void* 
   if (rc != MOE_OK) return rc;
   stg.end(MOE_STAGE_GROUP);
   if (s.T == 0) {
-    for (int i = MOE_STAGE_QUANT; i < MOE_NUM_STAGES; ++i) { stg.begin(i); stg.end(i); }
+    for (int i = MOE_STAGE_QUANT; i <= MOE_STAGE_COMBINE; ++i) { stg.begin(i); stg.end(i); }
     return MOE_OK;
   }
 
@@ -386,7 +386,7 @@ int moe_forward_train(const moe_shape* shape, const void* u, const void* centroi
 
 int moe_backward(const moe_shape* shape, const void* u, const void* centroids, const moe_weights* wt, const float* dy,
                  float* du, float* dcentroids, const moe_weight_grads* grads, void* workspace, size_t workspace_bytes,
-                 hipStream_t stream) {
+                 const moe_trace* trace, hipStream_t stream) {
   const int rc = validate_shape(shape);
   if (rc != MOE_OK) return rc;
   const moe_shape& s = *shape;
@@ -446,7 +446,14 @@ int moe_backward(const moe_shape* shape, const void* u, const void* centroids, c
   a.dw_down = grads->dw_down;
   a.dws_gate_up = grads->dws_gate_up;
   a.dws_down = grads->dws_down;
-  return check_launch(moe::launch_backward(a, stream));
+  Stages stg{trace, stream};
+  for (int st = 0; st < moe::BWD_STAGES; ++st) {
+    stg.begin(MOE_STAGE_BWD_PREP + st);
+    const int rc2 = check_launch(moe::launch_backward_stage(st, a, stream));
+    if (rc2 != MOE_OK) return rc2;
+    stg.end(MOE_STAGE_BWD_PREP + st);
+  }
+  return MOE_OK;
 }
 
 int moe_update_bias(float* bias, const int32_t* counts, int32_t n_routed, int64_t total_assignments, float gamma,
