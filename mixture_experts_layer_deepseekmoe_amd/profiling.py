@@ -53,15 +53,27 @@ def _run(args):
     ws = moe.alloc_workspace(shape)
     routing = moe.alloc_routing(shape)
     y = torch.empty((cfg.T, cfg.d), dtype=torch.float32 if cfg.out_dtype == "f32" else torch.bfloat16, device="cuda")
+    if args.train:
+        tws = moe.alloc_train_workspace(shape)
+        g = torch.Generator(device="cuda")
+        g.manual_seed(7)
+        dy = torch.randn((cfg.T, cfg.d), generator=g, device="cuda", dtype=torch.float32)
+        grads = moe.alloc_weight_grads(shape)
     for i in range(args.steps):
-        moe.moe_forward(shape, u, cen, bias, w, y=y, routing=routing, workspace=ws)
-        moe.moe_update_bias(bias, routing["expert_counts"], cfg.T * cfg.top_k)
+        if args.train:
+            moe.moe_forward_train(shape, u, cen, bias, w, tws, y=y)
+            moe.moe_backward(shape, u, cen, w, dy, tws, grads=grads)
+        else:
+            moe.moe_forward(shape, u, cen, bias, w, y=y, routing=routing, workspace=ws)
+            moe.moe_update_bias(bias, routing["expert_counts"], cfg.T * cfg.top_k)
         torch.cuda.synchronize()
         print(f"[profile] step {i} done", flush=True)
 
 
 def _short(name: str) -> str:
-    for key in ("gateup_kernel", "down_kernel", "route_part_kernel", "route_finish_kernel", "route_scores_kernel",
+    for key in ("dgrad_down_kernel", "dgrad_gateup_kernel", "wgrad_down_kernel", "wgrad_gateup_kernel",
+                "bwd_prep_kernel", "bwd_dz_kernel", "bwd_du_kernel", "bwd_de_kernel",
+                "gateup_kernel", "down_kernel", "route_part_kernel", "route_finish_kernel", "route_scores_kernel",
                 "route_topk_kernel", "route_kernel", "combine_kernel", "hist_kernel", "scan_kernel",
                 "permute_kernel", "quant_act_kernel", "quant_weight_kernel", "bias_update_kernel"):
         if key in name:
@@ -88,7 +100,9 @@ def _is_calibration(row) -> bool:
 
 # rocprofv3 --kernel-include-regex for counter runs: the layer's kernels and
 # the calibration stream (keeps the input generators' kernels out of the CSV)
-KERNEL_REGEX = "gateup_kernel|down_kernel|route_kernel|combine_kernel|hist_kernel|scan_kernel|permute_kernel|quant_act_kernel|bias_update_kernel|MulFunctor<double>"
+KERNEL_REGEX = ("gateup_kernel|down_kernel|route_kernel|route_part_kernel|route_finish_kernel|combine_kernel|"
+                "hist_kernel|scan_kernel|permute_kernel|quant_act_kernel|bias_update_kernel|bwd_prep_kernel|"
+                "bwd_dz_kernel|bwd_du_kernel|bwd_de_kernel|MulFunctor<double>")
 
 
 def _csvs(d, pattern):
@@ -162,6 +176,16 @@ def _summarize(args):
                 continue   # input generation, not part of the layer
             lines.append(f"| {k} | " + " | ".join(f"{v[c]:.4g}" if c in v else "" for c in names) + " |")
         lines.append("")
+        if fetch_f and write_f:
+            lines += ["HBM traffic per dispatch (FETCH_SIZE and WRITE_SIZE, KiB, scaled by the calibration):", "",
+                      "| kernel | fetch GB | write GB | total GB |", "|---|---|---|---|"]
+            for k, v in sorted(cs.items()):
+                if k.startswith("torch:") or k.startswith("__amd") or k == CALIB:
+                    continue
+                if "FETCH_SIZE" in v and "WRITE_SIZE" in v:
+                    fb, wb = v["FETCH_SIZE"] * 1024 * fetch_f, v["WRITE_SIZE"] * 1024 * write_f
+                    lines.append(f"| {k} | {fb / 1e9:.3f} | {wb / 1e9:.3f} | {(fb + wb) / 1e9:.3f} |")
+            lines.append("")
         gu = next((v for k, v in cs.items() if k.startswith("gateup_kernel")), None)
         if gu and fetch_f and write_f and "FETCH_SIZE" in gu and "WRITE_SIZE" in gu:
             traffic = gu["FETCH_SIZE"] * 1024 * fetch_f + gu["WRITE_SIZE"] * 1024 * write_f
@@ -200,6 +224,7 @@ def main():
     r = sub.add_parser("run")
     r.add_argument("--workload", default="bf16_d7168")
     r.add_argument("--steps", type=int, default=3)
+    r.add_argument("--train", action="store_true", help="training steps (moe_forward_train + moe_backward)")
     s = sub.add_parser("summarize")
     s.add_argument("--trace")
     s.add_argument("--pmc", nargs="*")
