@@ -30,13 +30,14 @@
 // its own column; two reads give the eight a 16x16x32 MFMA operand holds.
 #include "gemm_core.hpp"
 #include "kernels.hpp"
+#include "tile_map.hpp"
 
 namespace moe {
 
 namespace {
 
 constexpr int BT = 256;                 // tile rows and columns
-constexpr int NSTG = 4;                 // stage buffers
+constexpr int NSTG = 5;                 // stage buffers (5 x 32 KB: all of the LDS)
 constexpr int NMW = 8;                  // MFMA waves
 constexpr int NLW = 4;                  // load waves
 constexpr int THREADS = 64 * (NMW + NLW);
@@ -63,15 +64,27 @@ __device__ __forceinline__ i32x4 frag_kc(const uint8_t* op, int r0) {
   return *reinterpret_cast<const i32x4*>(op + r * 64 + (((lane >> 4) ^ swz<64>(r)) << 4));
 }
 
-__device__ __forceinline__ i32x4 frag_ko(const uint8_t* op, int c0) {
+// The lane's constants for K-outer fragment reads.  Lane 16 g + c reads
+// K-rows k0 = 8 g + c / 4 and k0 + 4, columns c0 + 4 (c % 4) .. + 3 of a
+// 16-column subtile at c0 (a multiple of 16): byte (col % 8) * 2 = 8 (c % 2)
+// of chunk col / 8 = c0 / 8 + (c % 4) / 2, stored at chunk position
+// (col / 8) ^ xko(k0) (xko(k0 + 4) = xko(k0)); c0 / 8 is even, so that is
+// (c0 / 8) ^ y with y = (c % 4) / 2 ^ xko(k0).
+struct KoLane {
+  int base;   // k0 * 512 + 8 (c % 2)
+  int y;
+};
+__device__ __forceinline__ KoLane ko_lane() {
   const int lane = threadIdx.x & 63;
   const int g = lane >> 4, c = lane & 15;
-  const int col = c0 + 4 * (c & 3);
-  const int k0 = 8 * g + (c >> 2), k1 = k0 + 4;
-  const uint8_t* p0 = op + k0 * 512 + (((col >> 3) ^ xko(k0)) << 4) + ((col & 7) << 1);
-  const uint8_t* p1 = op + k1 * 512 + (((col >> 3) ^ xko(k1)) << 4) + ((col & 7) << 1);
+  const int k0 = 8 * g + (c >> 2);
+  return {k0 * 512 + 8 * (c & 1), ((c & 3) >> 1) ^ xko(k0)};
+}
+
+__device__ __forceinline__ i32x4 frag_ko(const uint8_t* op, int c0, KoLane kl) {
+  const uint8_t* p0 = op + kl.base + ((((c0 >> 3) ^ kl.y)) << 4);
   const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(const_cast<uint8_t*>(p0)));
-  const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(const_cast<uint8_t*>(p1)));
+  const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(const_cast<uint8_t*>(p0 + 4 * 512)));
   const i32x2 a = __builtin_bit_cast(i32x2, lo), b = __builtin_bit_cast(i32x2, hi);
   return i32x4{a.x, a.y, b.x, b.y};
 }
@@ -128,9 +141,19 @@ __device__ __forceinline__ void issue_stage(const Opnd& a, const Opnd& b, uint8_
 // acc[i][j][r] = C[16 (2 i + wm) + lane % 16][64 wn + 16 j + 4 (lane / 16) + r]
 // summed over K-steps 0 .. nk-1 (A: the M side, B: the N side).  Returns on
 // every wave; one barrier per K-step keeps the roles in step:
-//   before barrier ks  stage ks has landed (the load waves waited for it);
+//   before barrier ks  stages ks and ks+1 have landed (the load waves waited
+//                      for them);
 //   after barrier ks   nobody reads stage ks-1 any more, and the load waves
 //                      refill its buffer with stage ks + NSTG - 1.
+// So the MFMA waves read the next stage's first fragments (its weight side
+// and first activation subtile) at the end of a stage, and within a stage
+// read each activation fragment one subtile ahead of its MFMAs: no LDS read
+// latency stands between a barrier and the first MFMA.
+template <int M>
+__device__ __forceinline__ i32x4 frag(const uint8_t* op, int at, KoLane kl) {
+  return M == KO ? frag_ko(op, at, kl) : frag_kc(op, at);
+}
+
 template <int AM, int BM>
 __device__ __forceinline__ void mainloop(uint8_t* ring, const Opnd& a, const Opnd& b, int nk,
                                          f32x4 (&acc)[MI][NJ]) {
@@ -140,7 +163,7 @@ __device__ __forceinline__ void mainloop(uint8_t* ring, const Opnd& a, const Opn
     const int pre = min(nk, NSTG - 1);
     for (int s = 0; s < pre; ++s) issue_stage(a, b, ring + s * STB, s);
     if (pre == NSTG - 1)
-      wait_vm_lgkm0<(NSTG - 2) * NLS>();
+      wait_vm_lgkm0<(NSTG - 3) * NLS>();   // stages 0 and 1
     else
       wait_vm_lgkm0<0>();
     for (int ks = 0; ks < nk; ++ks) {
@@ -148,7 +171,7 @@ __device__ __forceinline__ void mainloop(uint8_t* ring, const Opnd& a, const Opn
       const int kn = ks + NSTG - 1;
       if (kn < nk) {
         issue_stage(a, b, ring + (kn % NSTG) * STB, kn);
-        wait_vm_lgkm0<(NSTG - 2) * NLS>();   // stage ks + 1
+        wait_vm_lgkm0<(NSTG - 3) * NLS>();   // stage ks + 2
       } else {
         wait_vm_lgkm0<0>();
       }
@@ -156,21 +179,37 @@ __device__ __forceinline__ void mainloop(uint8_t* ring, const Opnd& a, const Opn
     return;
   }
   const int wm = w % 2, wn = w / 2;
+  KoLane kl = ko_lane();
+  i32x4 wf[NJ], xf;
+  block_barrier();   // stages 0 and 1 have landed
+  {
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) wf[j] = frag<BM>(ring + OPB, 64 * wn + 16 * j, kl);
+    xf = frag<AM>(ring, 16 * wm, kl);
+  }
   acc_fence(acc);
   for (int ks = 0; ks < nk; ++ks) {
-    block_barrier();
+    // the lane constants pass through an empty asm each step, so the
+    // per-subtile addresses are recomputed (one xor each) instead of being
+    // hoisted out of the loop into a register apiece
+    asm volatile("" : "+v"(kl.base), "+v"(kl.y));
     const uint8_t* sa = ring + (ks % NSTG) * STB;
-    const uint8_t* sb = sa + OPB;
-    i32x4 wf[NJ];
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) wf[j] = BM == KO ? frag_ko(sb, 64 * wn + 16 * j) : frag_kc(sb, 64 * wn + 16 * j);
+    const uint8_t* na = ring + ((ks + 1) % NSTG) * STB;   // the next stage (landed; unused past the end)
 #pragma unroll
     for (int i = 0; i < MI; ++i) {
-      const i32x4 xf = AM == KO ? frag_ko(sa, 16 * (2 * i + wm)) : frag_kc(sa, 16 * (2 * i + wm));
+      i32x4 xn;
+      if (i + 1 < MI) xn = frag<AM>(sa, 16 * (2 * (i + 1) + wm), kl);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int j = 0; j < NJ; ++j) mfma_bf16_tied(acc[i][j], wf[j], xf);
       __builtin_amdgcn_sched_barrier(0);
+      if (i + 1 < MI) xf = xn;
+    }
+    if (ks + 1 < nk) {
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) wf[j] = frag<BM>(na + OPB, 64 * wn + 16 * j, kl);
+      xf = frag<AM>(na, 16 * wm, kl);
+      block_barrier();
     }
   }
   acc_fence(acc);
@@ -194,16 +233,19 @@ struct GroupRows {
   int first, count;
 };
 
-// Dgrad tiles: (m-tile of the forward's list, n-block), n-block fastest.
+// Dgrad tiles: (m-tile of the forward's list, n-block), laid out over the
+// XCDs as the forward GEMMs lay out theirs (the list's per-XCD segments; the
+// m-tiles of a unit, which read the same weight columns, back to back).
 __device__ __forceinline__ bool dgrad_tile(const BwdArgs& a, int nb_n, int& row0, int& rows, int& g, int& n0) {
-  const int q = blockIdx.x;
-  const int mt = q / nb_n;
-  if (mt >= a.mt_count[0]) return false;
+  const int q = xcd_tile(a.mt_count, nb_n);
+  if (q < 0) return false;
+  int mt, nb, in_unit;
+  tile_coords(a.mtiles, q, nb_n, mt, nb, in_unit);
   const int4 t = a.mtiles[mt];
   g = t.x;
   row0 = t.y;
   rows = t.z;
-  n0 = (q - mt * nb_n) * BT;
+  n0 = nb * BT;
   return true;
 }
 
@@ -301,16 +343,39 @@ __device__ __forceinline__ GroupRows group_rows(const BwdArgs& a, int g) {
   return {static_cast<int>(a.TK + static_cast<long long>(g - a.n_routed) * a.T), a.T};
 }
 
+// Wgrad tiles: per group, m-blocks x n-blocks (the n-block fastest), groups
+// in order.  The routed groups' tiles are cut into NXCD contiguous chunks,
+// one per XCD, so a group's tiles (which read its rows) share one L2; the
+// shared groups' tiles, whose K runs over all T tokens, follow in chunks of
+// their own, so every XCD gets an equal share of them too.
+__device__ __forceinline__ long long wgrad_tile_index(const BwdArgs& a, long long per_g) {
+  const long long nr_t = a.n_routed * per_g, ns_t = a.n_shared * per_g;
+  const long long cr = (nr_t + NXCD - 1) / NXCD, cs = (ns_t + NXCD - 1) / NXCD;
+  const int x = blockIdx.x % NXCD;
+  const long long j = blockIdx.x / NXCD;
+  if (j < cr) {
+    const long long q = x * cr + j;
+    return q < nr_t ? q : -1;
+  }
+  if (j - cr >= cs) return -1;
+  const long long q = x * cs + (j - cr);
+  return q < ns_t ? nr_t + q : -1;
+}
+
+inline int wgrad_grid(int n_routed, int n_shared, long long per_g) {
+  return static_cast<int>(NXCD * ((n_routed * per_g + NXCD - 1) / NXCD + (n_shared * per_g + NXCD - 1) / NXCD));
+}
+
 // C[m][n] = sum over the group's rows r of A[r][m] B[r][n], both K-outer
 // (rows r of lda / ldb bytes), written as fp32 into dst (ldc floats per row).
-// Block q: group q / (mb_n * nb_n), then the m-block, the n-block fastest.
 __device__ __forceinline__ void wgrad_tile(const BwdArgs& a, const uint16_t* A, int M, const uint16_t* B, int N,
                                            float* routed_dst, float* shared_dst) {
   __shared__ __attribute__((aligned(1024))) uint8_t ring[NSTG * STB];
   const int mb_n = ceil_div(M, BT), nb_n = ceil_div(N, BT);
-  const int q = blockIdx.x;
-  const int g = q / (mb_n * nb_n);
-  const int rem = q - g * mb_n * nb_n;
+  const long long q = wgrad_tile_index(a, static_cast<long long>(mb_n) * nb_n);
+  if (q < 0) return;
+  const int g = static_cast<int>(q / (mb_n * nb_n));
+  const int rem = static_cast<int>(q - static_cast<long long>(g) * mb_n * nb_n);
   const int m0 = (rem / nb_n) * BT, n0 = (rem % nb_n) * BT;
   const GroupRows gr = group_rows(a, g);
   const uint32_t lda = M * 2, ldb = N * 2;
@@ -463,7 +528,6 @@ __global__ __launch_bounds__(256) void bwd_de_kernel(BwdArgs a) {
 }  // namespace
 
 hipError_t launch_backward_stage(int stage, const BwdArgs& a, hipStream_t s) {
-  const int G = a.n_routed + a.n_shared;
   switch (stage) {
     case 0:   // prep, dz
       if (a.T == 0) break;
@@ -472,19 +536,25 @@ hipError_t launch_backward_stage(int stage, const BwdArgs& a, hipStream_t s) {
       break;
     case 1:   // Dgrad of the down GEMM, SwiGLU backward
       if (a.T == 0) break;
-      hipLaunchKernelGGL(dgrad_down_kernel, dim3(a.max_mtiles * ceil_div(a.inter, BT)), dim3(THREADS), 0, s, a);
+      hipLaunchKernelGGL(dgrad_down_kernel, dim3(mtile_grid(a.max_mtiles, ceil_div(a.inter, BT))), dim3(THREADS), 0,
+                         s, a);
       break;
     case 2:   // Dgrad of the gate/up GEMM
       if (a.T == 0) break;
-      hipLaunchKernelGGL(dgrad_gateup_kernel, dim3(a.max_mtiles * ceil_div(a.d, BT)), dim3(THREADS), 0, s, a);
-      break;
-    case 3:   // Wgrad of the down GEMM (every group: zeros where a group has no rows)
-      hipLaunchKernelGGL(wgrad_down_kernel, dim3(G * ceil_div(a.d, BT) * ceil_div(a.inter, BT)), dim3(THREADS), 0, s,
+      hipLaunchKernelGGL(dgrad_gateup_kernel, dim3(mtile_grid(a.max_mtiles, ceil_div(a.d, BT))), dim3(THREADS), 0, s,
                          a);
       break;
+    case 3:   // Wgrad of the down GEMM (every group: zeros where a group has no rows)
+      hipLaunchKernelGGL(wgrad_down_kernel,
+                         dim3(wgrad_grid(a.n_routed, a.n_shared,
+                                         static_cast<long long>(ceil_div(a.d, BT)) * ceil_div(a.inter, BT))),
+                         dim3(THREADS), 0, s, a);
+      break;
     case 4:   // Wgrad of the gate/up GEMM
-      hipLaunchKernelGGL(wgrad_gateup_kernel, dim3(G * ceil_div(2 * a.inter, BT) * ceil_div(a.d, BT)), dim3(THREADS),
-                         0, s, a);
+      hipLaunchKernelGGL(wgrad_gateup_kernel,
+                         dim3(wgrad_grid(a.n_routed, a.n_shared,
+                                         static_cast<long long>(ceil_div(2 * a.inter, BT)) * ceil_div(a.d, BT))),
+                         dim3(THREADS), 0, s, a);
       break;
     case 5:   // du, dcentroids (zeros for experts without rows)
       if (a.T > 0) hipLaunchKernelGGL(bwd_du_kernel, dim3(ceil_div(a.T, 4)), dim3(256), 0, s, a);

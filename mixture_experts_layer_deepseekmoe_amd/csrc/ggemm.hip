@@ -22,14 +22,13 @@
 // rows.
 #include "gemm_core.hpp"
 #include "kernels.hpp"
+#include "tile_map.hpp"
 
 namespace moe {
 
 namespace {
 
 constexpr int BNW = GG_BNW;
-constexpr int NXCD = 8;
-static_assert(NXCD == MT_SEGMENTS, "one tile-list segment per XCD");
 
 template <int FMT>
 struct GG {
@@ -66,37 +65,6 @@ __device__ __forceinline__ void gg_mainloop(const MK& make_pipe, uint8_t* const 
     pipe_mainloop_ws8<P, NSUB>(make_pipe(), st, nk, wr, acc, sw_lds, sw_stride);
   else
     pipe_mainloop<P, GG<FMT>::NST, NSUB>(make_pipe(), st, nk, wr, acc, sw_lds, sw_stride);
-}
-
-// Logical tile index of this block, or -1 if the block has no work.  XCD x
-// (blocks bid with bid % 8 == x) takes the tiles of list segment x (whose
-// first m-tiles the scan kernel stores in mtc[1..9]), or, when the segments
-// do not fit the grid (mtc[1] < 0), an equal share of the tile list.
-__device__ __forceinline__ int xcd_tile(const int32_t* mtc, int nb_n) {
-  const int bid = blockIdx.x;
-  const int xcd = bid % NXCD, j = bid / NXCD;
-  if (mtc[1] < 0) {
-    const int n_tiles = mtc[0] * nb_n;
-    const int chunk = ceil_div(n_tiles, NXCD);
-    if (j >= chunk) return -1;
-    const int q = xcd * chunk + j;
-    return q < n_tiles ? q : -1;
-  }
-  const int q = mtc[1 + xcd] * nb_n + j;
-  return q < mtc[2 + xcd] * nb_n ? q : -1;
-}
-
-// Tile q -> (m-tile, n-block): within a unit of up to MT_UNIT m-tiles of one
-// group, the m-tile index runs fastest, so the tiles that read the same weight
-// block are dispatched back to back (onto the same XCD) and share its L2.
-__device__ __forceinline__ void tile_coords(const int4* mtiles, int q, int nb_n, int& mt, int& nb, int& in_unit) {
-  const int t = q / nb_n;
-  const int w = mtiles[t].w;
-  const int s = t - (w >> 8), k = w & 0xff;
-  const int local = q - s * nb_n;
-  nb = local / k;
-  in_unit = local % k;
-  mt = s + in_unit;
 }
 
 // bf16: where a tile starts along K, in 64-byte K-steps (whole pairs): the
@@ -533,10 +501,6 @@ __global__ __launch_bounds__(GG<FMT>::THREADS, 1) void down_kernel(DownArgs a) {
   });
 }
 
-// NXCD x (tiles of the largest list segment the scan may form)
-int grid_for(int max_mtiles, int nb_n) {
-  return static_cast<int>(static_cast<long long>(NXCD) * seg_cap(max_mtiles) * nb_n);
-}
 
 }  // namespace
 
@@ -545,7 +509,7 @@ int gg_bm(int fmt) {
 }
 
 hipError_t launch_gateup(int fmt, const GateUpArgs& a, hipStream_t s) {
-  const int grid = grid_for(a.max_mtiles, ceil_div(a.inter, GG_HCOLS));
+  const int grid = mtile_grid(a.max_mtiles, ceil_div(a.inter, GG_HCOLS));
   if (grid == 0) return hipSuccess;
   if (fmt == FMT_BF16)
     hipLaunchKernelGGL(gateup_kernel<FMT_BF16>, dim3(grid), dim3(GG<FMT_BF16>::THREADS), 0, s, a);
@@ -557,7 +521,7 @@ hipError_t launch_gateup(int fmt, const GateUpArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_down(int fmt, const DownArgs& a, hipStream_t s) {
-  const int grid = grid_for(a.max_mtiles, ceil_div(a.d, BNW));
+  const int grid = mtile_grid(a.max_mtiles, ceil_div(a.d, BNW));
   if (grid == 0) return hipSuccess;
   if (fmt == FMT_BF16)
     hipLaunchKernelGGL(down_kernel<FMT_BF16>, dim3(grid), dim3(GG<FMT_BF16>::THREADS), 0, s, a);
