@@ -76,18 +76,38 @@ class Routing(ctypes.Structure):
                 ("topk_idx", "topk_gate", "expert_counts", "expert_offsets", "perm_token", "pos")]
 
 
+DEBUG_LIB_PATH = os.path.join(_PKG, "libmoe_mi355x_debug.so")
+
 _lib = None
+
+
+def use_library(path: str) -> Optional[ctypes.CDLL]:
+    """Make the binding call the library at ``path`` (e.g. DEBUG_LIB_PATH,
+    the bounds-checked build); returns the previously loaded one."""
+    global _lib
+    prev = _lib
+    _lib = _open(path)
+    return prev
+
+
+def restore_library(prev: Optional[ctypes.CDLL]) -> None:
+    global _lib
+    _lib = prev
 
 
 def load_library() -> ctypes.CDLL:
     """Load the HIP library (once).  Raises if it has not been built."""
     global _lib
-    if _lib is not None:
-        return _lib
-    if not os.path.exists(LIB_PATH):
-        raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+    if _lib is None:
+        _lib = _open(LIB_PATH)
+    return _lib
+
+
+def _open(path: str) -> ctypes.CDLL:
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with "
                            "`python -m mixture_experts_layer_deepseekmoe_amd.build` (hipcc, gfx950)")
-    lib = ctypes.CDLL(LIB_PATH)
+    lib = ctypes.CDLL(path)
     vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
     lib.moe_status_str.restype = ctypes.c_char_p
     lib.moe_status_str.argtypes = [ctypes.c_int]
@@ -119,7 +139,6 @@ def load_library() -> ctypes.CDLL:
     lib.moe_quantize_weight_e4m3.argtypes = [vp, i32, i64, i32, i32, vp, vp, vp]
     lib.moe_quantize_act_e4m3.restype = ctypes.c_int
     lib.moe_quantize_act_e4m3.argtypes = [vp, i32, i32, vp, vp, vp]
-    _lib = lib
     return lib
 
 

@@ -20,6 +20,9 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB_NAME = "libmoe_mi355x.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
+# the bounds-checked build (-DMOE_DEBUG: device-side index checks, read back
+# after every call), loaded only where asked for
+DEBUG_LIB_PATH = os.path.join(PKG, "libmoe_mi355x_debug.so")
 
 SOURCES = ["route.hip", "group.hip", "ggemm.hip", "combine.hip", "bwd.hip", "moe_api.cpp"]
 ARCH = "gfx950"
@@ -44,12 +47,12 @@ def common_flags(debug: bool = False):
              # MFMA accumulators in VGPRs: with 256 live accumulator registers
              # the AGPR form makes the allocator rotate them through copies
              "-mllvm", "-amdgpu-mfma-vgpr-form"]
-    flags += ["-O1", "-g", "-DMOE_DEBUG=1"] if debug else ["-O3"]
+    flags += ["-O3", "-g", "-DMOE_DEBUG=1"] if debug else ["-O3"]
     return flags
 
 
 def _compile(src: str, debug: bool) -> str:
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+    obj = os.path.join(BUILD, ("debug_" if debug else "") + os.path.splitext(src)[0] + ".o")
     cmd = [hipcc()] + common_flags(debug) + ["-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
@@ -58,15 +61,21 @@ def _compile(src: str, debug: bool) -> str:
 
 
 def build(verbose: bool = True, debug: bool = False) -> str:
+    """Build the library (debug: the bounds-checked one, at DEBUG_LIB_PATH)."""
     os.makedirs(BUILD, exist_ok=True)
     with concurrent.futures.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
         objs = list(ex.map(lambda s: _compile(s, debug), SOURCES))
-    tmp = LIB_PATH + ".tmp"
+    path = DEBUG_LIB_PATH if debug else LIB_PATH
+    tmp = path + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"link failed:\n{res.stderr}")
-    os.replace(tmp, LIB_PATH)
+    os.replace(tmp, path)
+    if debug:
+        if verbose:
+            print(f"built {path}")
+        return path
     cmd = [hipcc()] + common_flags(debug) + ["-o", PROBES_BIN + ".tmp", PROBES_SRC]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
@@ -78,4 +87,9 @@ def build(verbose: bool = True, debug: bool = False) -> str:
 
 
 if __name__ == "__main__":
-    build(debug="--debug" in sys.argv)
+    if "--debug" in sys.argv:
+        build(debug=True)
+    else:
+        build()
+        if "--with-debug" in sys.argv:
+            build(debug=True)

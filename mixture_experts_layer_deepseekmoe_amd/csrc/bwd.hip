@@ -241,12 +241,14 @@ __device__ __forceinline__ bool dgrad_tile(const BwdArgs& a, int nb_n, int& row0
   if (q < 0) return false;
   int mt, nb, in_unit;
   tile_coords(a.mtiles, q, nb_n, mt, nb, in_unit);
+  if (!MOE_CHECK(mt >= 0 && mt < a.mt_count[0] && nb < nb_n, 501)) return false;
   const int4 t = a.mtiles[mt];
   g = t.x;
   row0 = t.y;
   rows = t.z;
   n0 = nb * BT;
-  return true;
+  return MOE_CHECK(g >= 0 && g < a.n_routed + a.n_shared && rows >= 1 && rows <= BT && row0 >= 0 &&
+                       row0 + rows <= a.R, 502);
 }
 
 // dH = dY W_down for the tile's rows, then the SwiGLU backward from the
@@ -378,6 +380,7 @@ __device__ __forceinline__ void wgrad_tile(const BwdArgs& a, const uint16_t* A, 
   const int rem = static_cast<int>(q - static_cast<long long>(g) * mb_n * nb_n);
   const int m0 = (rem / nb_n) * BT, n0 = (rem % nb_n) * BT;
   const GroupRows gr = group_rows(a, g);
+  if (!MOE_CHECK(gr.first >= 0 && gr.count >= 0 && gr.first + static_cast<long long>(gr.count) <= a.R, 504)) return;
   const uint32_t lda = M * 2, ldb = N * 2;
   const int nk = ceil_div(gr.count, 32);
   f32x4 acc[MI][NJ];
@@ -432,6 +435,7 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a) {
     t = a.perm_token[r];
     for (int j = 0; j < a.top_k; ++j)
       if (a.pos[static_cast<size_t>(t) * a.top_k + j] == r) k = j;
+    MOE_CHECK(k >= 0, 503);
     gsc = k >= 0 ? a.gate[static_cast<size_t>(t) * a.top_k + k] : 0.f;   // k is found for routing of one forward
   } else {
     t = static_cast<int>((r - a.TK) % a.T);
@@ -526,6 +530,8 @@ __global__ __launch_bounds__(256) void bwd_de_kernel(BwdArgs a) {
 }
 
 }  // namespace
+
+MOE_DEBUG_FILE(bwd)
 
 hipError_t launch_backward_stage(int stage, const BwdArgs& a, hipStream_t s) {
   switch (stage) {

@@ -45,6 +45,7 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
   if (lane < a.top_k) {
     gk = a.gate[static_cast<size_t>(t) * a.top_k + lane];
     pk = a.pos[static_cast<size_t>(t) * a.top_k + lane];
+    if (!MOE_CHECK(pk >= 0 && pk < a.TK, 401)) pk = 0;
   }
   // Broadcast the K gates and rows while every lane is still active.
   float gs[MAX_TOPK];
@@ -117,6 +118,8 @@ hipError_t launch_o(int ofmt, const CombineArgs& a, hipStream_t s) {
 }
 
 }  // namespace
+
+MOE_DEBUG_FILE(combine)
 
 hipError_t launch_combine(int xfmt, int yfmt, int ofmt, const CombineArgs& a, hipStream_t s) {
   if (a.T == 0) return hipSuccess;

@@ -311,8 +311,12 @@ __global__ __launch_bounds__(GG<FMT>::THREADS, 1) void gateup_kernel(GateUpArgs 
   if (q < 0) return;
   int mt, nb, in_unit;
   tile_coords(a.mtiles, q, nb_n, mt, nb, in_unit);
+  if (!MOE_CHECK(mt >= 0 && mt < a.mt_count[0] && nb < nb_n, 301)) return;
   const int4 tl = a.mtiles[mt];
   const int g = tl.x, row0 = tl.y, rows = tl.z;
+  if (!MOE_CHECK(g >= 0 && rows >= 1 && rows <= GG<FMT>::BM && row0 >= 0, 302)) return;
+  if (!MOE_CHECK(g < a.n_routed ? row0 + rows <= a.TK : (row0 >= a.TK && (row0 - a.TK) % a.T + rows <= a.T), 303))
+    return;
   const int n0 = nb * GG_HCOLS;
 
   const int es = FMT == FMT_F32 ? 4 : (FMT == FMT_BF16 ? 2 : 1);
@@ -325,7 +329,8 @@ __global__ __launch_bounds__(GG<FMT>::THREADS, 1) void gateup_kernel(GateUpArgs 
   auto token_of = [&](int r) -> int {
     if (r >= rows) r = 0;
     const int gr = row0 + r;
-    return shared ? gr - a.TK - gs * a.T : a.perm_token[gr];
+    const int t = shared ? gr - a.TK - gs * a.T : a.perm_token[gr];
+    return MOE_CHECK(t >= 0 && t < a.T, 304) ? t : 0;
   };
   const int kb = a.d / 128;
 
@@ -448,8 +453,10 @@ __global__ __launch_bounds__(GG<FMT>::THREADS, 1) void down_kernel(DownArgs a) {
   if (q < 0) return;
   int mt, nb, in_unit;
   tile_coords(a.mtiles, q, nb_n, mt, nb, in_unit);
+  if (!MOE_CHECK(mt >= 0 && mt < a.mt_count[0] && nb < nb_n, 305)) return;
   const int4 tl = a.mtiles[mt];
   const int g = tl.x, row0 = tl.y, rows = tl.z;
+  if (!MOE_CHECK(g >= 0 && rows >= 1 && rows <= GG<FMT>::BM && row0 >= 0, 306)) return;
   const int n0 = nb * BNW;
 
   const int es = FMT == FMT_F32 ? 4 : (FMT == FMT_BF16 ? 2 : 1);
@@ -503,6 +510,8 @@ __global__ __launch_bounds__(GG<FMT>::THREADS, 1) void down_kernel(DownArgs a) {
 
 
 }  // namespace
+
+MOE_DEBUG_FILE(ggemm)
 
 int gg_bm(int fmt) {
   return fmt == FMT_E4M3 ? GG<FMT_E4M3>::BM : (fmt == FMT_F32 ? GG<FMT_F32>::BM : GG<FMT_BF16>::BM);

@@ -24,7 +24,10 @@ __global__ __launch_bounds__(GROUP_TB) void hist_kernel(GroupArgs a) {
   __syncthreads();
   const int t = blockIdx.x * GROUP_TB + threadIdx.x;
   if (t < a.T) {
-    for (int k = 0; k < a.top_k; ++k) atomicAdd(&h[a.idx[static_cast<size_t>(t) * a.top_k + k]], 1);
+    for (int k = 0; k < a.top_k; ++k) {
+      const int e = a.idx[static_cast<size_t>(t) * a.top_k + k];
+      if (MOE_CHECK(e >= 0 && e < a.n_routed, 201)) atomicAdd(&h[e], 1);
+    }
   }
   __syncthreads();
   for (int e = threadIdx.x; e < a.n_routed; e += GROUP_TB)
@@ -225,6 +228,7 @@ __global__ __launch_bounds__(SCAN_THREADS) void scan_kernel(GroupArgs a, int nbl
   __syncthreads();
   if (tid == 0) {
     const int run = pc[np];
+    MOE_CHECK(run <= MT_SEGMENTS * a.seg_cap, 202);
     a.mt_count[0] = run;
     // the m-tile where each segment starts, for the GEMMs' XCD ranges
     // (cut by cost only: with the cut by m-tile counts, equal tile counts per
@@ -271,7 +275,7 @@ __global__ __launch_bounds__(GROUP_TB) void permute_kernel(GroupArgs a) {
   if (live) {
 #pragma unroll
     for (int k = 0; k < MAX_TOPK; ++k)
-      if (k < a.top_k) atomicOr(&mask[ev[k]][word], bit);
+      if (k < a.top_k && MOE_CHECK(ev[k] >= 0 && ev[k] < nr, 203)) atomicOr(&mask[ev[k]][word], bit);
   }
   __syncthreads();
   if (live) {
@@ -279,9 +283,11 @@ __global__ __launch_bounds__(GROUP_TB) void permute_kernel(GroupArgs a) {
     for (int k = 0; k < MAX_TOPK; ++k) {
       if (k >= a.top_k) break;
       const int e = ev[k];
+      if (!MOE_CHECK(e >= 0 && e < nr, 203)) continue;
       int rank = __popc(mask[e][word] & (bit - 1u));
       for (int wd = 0; wd < word; ++wd) rank += __popc(mask[e][wd]);
       const int p = base_s[e] + rank;
+      if (!MOE_CHECK(p >= 0 && p < static_cast<long long>(a.T) * a.top_k, 204)) continue;
       a.pos[static_cast<size_t>(t) * a.top_k + k] = p;
       a.perm_token[p] = t;
     }
@@ -389,6 +395,8 @@ __global__ void bias_update_kernel(float* bias, const int32_t* counts, int n_rou
 }
 
 }  // namespace
+
+MOE_DEBUG_FILE(group)
 
 hipError_t launch_group(const GroupArgs& a, hipStream_t s) {
   const int nblk = ceil_div(a.T, GROUP_TB);

@@ -174,6 +174,17 @@ hipError_t launch_gateup(int fmt, const GateUpArgs& a, hipStream_t s);
 hipError_t launch_down(int fmt, const DownArgs& a, hipStream_t s);
 hipError_t launch_combine(int xfmt, int yfmt, int ofmt, const CombineArgs& a, hipStream_t s);
 
+#ifdef MOE_DEBUG
+// Debug build: each kernel file's first failed index check (0: none), cleared
+// when read; -1 if it could not be read.  Check ids: 1xx route, 2xx group,
+// 3xx grouped GEMMs, 4xx combine, 5xx backward.
+int debug_take_route();
+int debug_take_group();
+int debug_take_ggemm();
+int debug_take_combine();
+int debug_take_bwd();
+#endif
+
 // Tile rows of the grouped GEMMs for a weight format (m-tiles hold at most this many rows).
 int gg_bm(int fmt);
 

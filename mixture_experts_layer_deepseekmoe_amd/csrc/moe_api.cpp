@@ -6,6 +6,9 @@
 #include <hip/hip_runtime.h>
 
 #include <mutex>
+#ifdef MOE_DEBUG
+#include <cstdio>
+#endif
 
 #include "kernels.hpp"
 
@@ -122,6 +125,28 @@ T* at(void* ws, size_t off) {
 
 int check_launch(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH; }
 
+// Debug build (-DMOE_DEBUG): after an entry point's launches, wait for the
+// stream and read every kernel file's index-check flag; a failed check turns
+// the call's status into MOE_ERR_LAUNCH and is reported on stderr.  (The
+// release build never synchronises.)
+#ifdef MOE_DEBUG
+int debug_status(int rc, hipStream_t st, const char* what) {
+  if (rc != MOE_OK) return rc;
+  if (hipStreamSynchronize(st) != hipSuccess) return MOE_ERR_LAUNCH;
+  const int flags[5] = {moe::debug_take_route(), moe::debug_take_group(), moe::debug_take_ggemm(),
+                        moe::debug_take_combine(), moe::debug_take_bwd()};
+  for (const int f : flags) {
+    if (f != 0) {
+      std::fprintf(stderr, "moe debug build: %s: index check %d failed\n", what, f);
+      return MOE_ERR_LAUNCH;
+    }
+  }
+  return MOE_OK;
+}
+#else
+inline int debug_status(int rc, hipStream_t, const char*) { return rc; }
+#endif
+
 // Optional per-stage event records on the caller's stream.
 struct Stages {
   const moe_trace* tr;
@@ -236,9 +261,10 @@ int moe_route(const moe_shape* shape, const void* u, const void* centroids, cons
   if (centroids == nullptr || bias == nullptr || !aligned16(centroids)) return MOE_ERR_INVALID_ARG;
   const Layout L = make_layout(s);
   if (workspace == nullptr || workspace_bytes < L.total) return MOE_ERR_WORKSPACE;
-  return run_route(s, u, centroids, bias, out->topk_idx, out->topk_gate, out->expert_counts, out->expert_offsets,
-                   out->perm_token, out->pos, at<int32_t>(workspace, L.hist), at<float>(workspace, L.scores),
-                   nullptr, nullptr, stream);
+  return debug_status(run_route(s, u, centroids, bias, out->topk_idx, out->topk_gate, out->expert_counts,
+                                out->expert_offsets, out->perm_token, out->pos, at<int32_t>(workspace, L.hist),
+                                at<float>(workspace, L.scores), nullptr, nullptr, stream),
+                      stream, "moe_route");
 }
 
 int moe_forward(const moe_shape* shape, const void* u, const void* centroids, const float* bias,
@@ -248,7 +274,8 @@ int moe_forward(const moe_shape* shape, const void* u, const void* centroids, co
   if (rc != MOE_OK) return rc;
   const Layout L = make_layout(*shape);
   if (workspace == nullptr || workspace_bytes < L.total) return MOE_ERR_WORKSPACE;
-  return run_forward(*shape, L, u, centroids, bias, wt, y, routing, workspace, trace, stream);
+  return debug_status(run_forward(*shape, L, u, centroids, bias, wt, y, routing, workspace, trace, stream), stream,
+                      "moe_forward");
 }
 
 int moe_forward_static(const moe_shape* shape, const void* u, const void* centroids, const float* bias,
@@ -261,7 +288,8 @@ int moe_forward_static(const moe_shape* shape, const void* u, const void* centro
   void* ws = nullptr;
   rc = static_scratch(&ws);
   if (rc != MOE_OK) return rc;
-  return run_forward(*shape, L, u, centroids, bias, wt, y, routing, ws, trace, stream);
+  return debug_status(run_forward(*shape, L, u, centroids, bias, wt, y, routing, ws, trace, stream), stream,
+                      "moe_forward_static");
 }
 
 }  // extern "C"
@@ -381,7 +409,8 @@ int moe_forward_train(const moe_shape* shape, const void* u, const void* centroi
   if (shape->x_dtype != MOE_DTYPE_BF16 || shape->w_dtype != MOE_DTYPE_BF16) return MOE_ERR_UNSUPPORTED;
   const Layout L = make_layout(*shape);
   if (workspace == nullptr || workspace_bytes < L.total_train) return MOE_ERR_WORKSPACE;
-  return run_forward(*shape, L, u, centroids, bias, wt, y, nullptr, workspace, trace, stream, true);
+  return debug_status(run_forward(*shape, L, u, centroids, bias, wt, y, nullptr, workspace, trace, stream, true),
+                      stream, "moe_forward_train");
 }
 
 int moe_backward(const moe_shape* shape, const void* u, const void* centroids, const moe_weights* wt, const float* dy,
@@ -453,7 +482,7 @@ int moe_backward(const moe_shape* shape, const void* u, const void* centroids, c
     if (rc2 != MOE_OK) return rc2;
     stg.end(MOE_STAGE_BWD_PREP + st);
   }
-  return MOE_OK;
+  return debug_status(MOE_OK, stream, "moe_backward");
 }
 
 int moe_update_bias(float* bias, const int32_t* counts, int32_t n_routed, int64_t total_assignments, float gamma,

@@ -117,4 +117,31 @@ __device__ __forceinline__ float sigmoid_f32(float z) { return 1.0f / (1.0f + ex
 
 __host__ __device__ constexpr int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
+// ---------------------------------------------------------------- debug build
+//
+// Built with -DMOE_DEBUG, MOE_CHECK(cond, id) tests an index at the points
+// where a wrong routing result or tile list would send a kernel out of
+// bounds; a failure records id (the first one) in this source file's device
+// flag and the caller skips the access.  The host reads and clears the flags
+// after each call (MOE_DEBUG_FILE below defines this file's reader).
+// Without MOE_DEBUG the checks compile to `true`.
+#ifdef MOE_DEBUG
+static __device__ int g_moe_debug_flag = 0;
+__device__ __forceinline__ bool moe_check(bool ok, int id) {
+  if (!ok) atomicCAS(&g_moe_debug_flag, 0, id);
+  return ok;
+}
+#define MOE_CHECK(cond, id) moe::moe_check(static_cast<bool>(cond), (id))
+#define MOE_DEBUG_FILE(name)                                                                     \
+  int debug_take_##name() {                                                                      \
+    int v = 0, z = 0;                                                                            \
+    if (hipMemcpyFromSymbol(&v, HIP_SYMBOL(g_moe_debug_flag), sizeof v) != hipSuccess) return -1; \
+    if (hipMemcpyToSymbol(HIP_SYMBOL(g_moe_debug_flag), &z, sizeof z) != hipSuccess) return -1;   \
+    return v;                                                                                    \
+  }
+#else
+#define MOE_CHECK(cond, id) true
+#define MOE_DEBUG_FILE(name)
+#endif
+
 }  // namespace moe

@@ -122,6 +122,7 @@ __device__ __forceinline__ void select_topk(const float* srow, const float (&bq)
       const int oe = __shfl_xor(be, off);
       if (ov > bv || (ov == bv && oe < be)) { bv = ov; be = oe; }
     }
+    if (!MOE_CHECK(be >= 0 && be < n_routed, 101)) be = 0;
     if ((be & 63) == lane) taken |= 1u << (be >> 6);
     const float s_sel = srow[be];
     sum += s_sel;
@@ -408,6 +409,8 @@ hipError_t launch_route_t(const RouteArgs& a, hipStream_t s) {
 }
 
 }  // namespace
+
+MOE_DEBUG_FILE(route)
 
 hipError_t launch_route(int fmt, const RouteArgs& a, hipStream_t s) {
   if (a.T == 0) return hipSuccess;

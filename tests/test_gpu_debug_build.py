@@ -1,0 +1,108 @@
+"""The bounds-checked build (-DMOE_DEBUG, libmoe_mi355x_debug.so): every
+index check passes on the whole path -- routing (also with NaN tokens and
+with group-limited routing), grouping, the grouped GEMMs at every size the
+other tests use, the combine, the backward -- and the results equal the
+release build's bit for bit (the checks only guard accesses)."""
+
+import numpy as np
+import pytest
+import torch
+
+import mixture_experts_layer_deepseekmoe_amd as moe
+from mixture_experts_layer_deepseekmoe_amd import binding as B
+from moe_workloads import CONFIGS, PARITY_CONFIGS, make_inputs
+from tests.parity import say
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _forward(cfg, inp, w):
+    shape = moe.LayerShape.from_config(cfg)
+    u, E, b = (t.to(DEV).contiguous() for t in (inp.u, inp.centroids, inp.bias))
+    routing = moe.alloc_routing(shape)
+    y = moe.moe_forward(shape, u, E, b, w, routing=routing)
+    torch.cuda.synchronize()
+    return y, routing
+
+
+def _both(fn):
+    """fn() under the release library, then under the debug library."""
+    rel = fn()
+    prev = B.use_library(B.DEBUG_LIB_PATH)
+    try:
+        dbg = fn()
+    finally:
+        B.restore_library(prev)
+    return rel, dbg
+
+
+CASES = [PARITY_CONFIGS[n] for n in ("small_bf16", "small_bf16_ns2", "small_fp32", "small_fp8", "one_token",
+                                     "wide_router")] + \
+        [PARITY_CONFIGS["small_bf16"].replace(name="small_bf16_g4k2", n_groups=4, topk_groups=2)]
+
+
+@pytest.mark.parametrize("cfg", CASES, ids=[c.name for c in CASES])
+def test_debug_build_forward_small(cfg):
+    say(f"case: debug build, moe_forward {cfg.name}")
+    inp = make_inputs(cfg, 0)
+    w = moe.prepare_weights(cfg, inp)
+    (y0, r0), (y1, r1) = _both(lambda: _forward(cfg, inp, w))
+    assert torch.equal(y0, y1)
+    for k in r0:
+        assert torch.equal(r0[k], r1[k]), k
+
+
+@pytest.mark.parametrize("name", ["bf16_d7168", "fp8_d7168", "skew_decode_d7168", "bf16_d2048"])
+def test_debug_build_forward_full(name):
+    cfg = CONFIGS[name]
+    say(f"case: debug build, moe_forward {name} full size")
+    inp = make_inputs(cfg, 0, weights_device=DEV)
+    w = moe.prepare_weights(cfg, inp)
+    (y0, r0), (y1, r1) = _both(lambda: _forward(cfg, inp, w))
+    assert torch.equal(y0, y1)
+    assert torch.equal(r0["topk_idx"], r1["topk_idx"]) and torch.equal(r0["pos"], r1["pos"])
+    del w, inp
+    torch.cuda.empty_cache()
+
+
+def test_debug_build_all_tokens_on_k_experts_and_nan_tokens():
+    """The degenerate routing (every token on experts 0..K-1, 256 routed
+    m-tiles at d = 7168) and NaN tokens."""
+    cfg = CONFIGS["bf16_d7168"]
+    say("case: debug build, all tokens on experts 0..K-1 at d = 7168, NaN tokens")
+    inp = make_inputs(cfg, 0, weights_device=DEV)
+    inp.bias = inp.bias.clone()
+    inp.bias[: cfg.top_k] += 4.0
+    inp.u = inp.u.clone()
+    inp.u[[0, 4000, 8191], 5] = float("nan")
+    w = moe.prepare_weights(cfg, inp)
+    (y0, r0), (y1, r1) = _both(lambda: _forward(cfg, inp, w))
+    assert torch.equal(r0["topk_idx"], r1["topk_idx"])
+    ok = torch.isfinite(y0).all(dim=1)
+    assert torch.equal(y0[ok], y1[ok]) and int((~ok).sum()) == 3
+    del w, inp
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("name", ["small_bf16_ns2", "bf16_d2048"])
+def test_debug_build_backward(name):
+    cfg = (PARITY_CONFIGS.get(name) or CONFIGS[name])
+    say(f"case: debug build, moe_forward_train + moe_backward {name}")
+    inp = make_inputs(cfg, 0)
+    w = moe.prepare_weights(cfg, inp)
+    shape = moe.LayerShape.from_config(cfg)
+    g = torch.Generator().manual_seed(5)
+    dy = torch.randn((cfg.T, cfg.d), generator=g).to(DEV)
+
+    def step():
+        u, E, b = (t.to(DEV).contiguous() for t in (inp.u, inp.centroids, inp.bias))
+        ws = moe.alloc_train_workspace(shape)
+        y = moe.moe_forward_train(shape, u, E, b, w, ws)
+        du, dE, gr = moe.moe_backward(shape, u, E, w, dy, ws)
+        torch.cuda.synchronize()
+        return y, du, dE, gr
+
+    (y0, du0, dE0, g0), (y1, du1, dE1, g1) = _both(step)
+    assert torch.equal(y0, y1) and torch.equal(du0, du1) and torch.equal(dE0, dE1)
+    assert torch.equal(g0.dw_gate_up, g1.dw_gate_up) and torch.equal(g0.dw_down, g1.dw_down)
