@@ -349,76 +349,217 @@ __device__ __forceinline__ GroupRows group_rows(const BwdArgs& a, int g) {
 // in order.  The routed groups' tiles are cut into NXCD contiguous chunks,
 // one per XCD, so a group's tiles (which read its rows) share one L2; the
 // shared groups' tiles, whose K runs over all T tokens, follow in chunks of
-// their own, so every XCD gets an equal share of them too.
-__device__ __forceinline__ long long wgrad_tile_index(const BwdArgs& a, long long per_g) {
-  const long long nr_t = a.n_routed * per_g, ns_t = a.n_shared * per_g;
-  const long long cr = (nr_t + NXCD - 1) / NXCD, cs = (ns_t + NXCD - 1) / NXCD;
-  const int x = blockIdx.x % NXCD;
-  const long long j = blockIdx.x / NXCD;
-  if (j < cr) {
-    const long long q = x * cr + j;
-    return q < nr_t ? q : -1;
+// their own, so every XCD gets an equal share of them too.  XCD x's list:
+// its routed chunk, then its shared chunk.
+//
+// The kernel is persistent: P blocks per XCD (one per CU), block l of XCD x
+// taking positions l, l + P, l + 2P, ... of x's list, so the tiles running
+// at once on an XCD are neighbours in it.  A block's K-steps over all its
+// tiles form one stream of stages: the load waves run on into the next
+// tile's first stages while the MFMA waves store the finished tile's fp32
+// gradients (a routed tile has only ~8 K-steps, and its 256 KB of stores
+// would otherwise stall the CU).
+struct WgradList {
+  long long per_g, nr_t, cr, cs, r0, nr, s0, len;
+  int l, P;
+
+  __device__ WgradList(const BwdArgs& a, long long per_group) {
+    per_g = per_group;
+    nr_t = a.n_routed * per_g;
+    const long long ns_t = a.n_shared * per_g;
+    cr = (nr_t + NXCD - 1) / NXCD;
+    cs = (ns_t + NXCD - 1) / NXCD;
+    P = gridDim.x / NXCD;
+    const int x = blockIdx.x % NXCD;
+    l = blockIdx.x / NXCD;
+    r0 = x * cr;
+    nr = max(0LL, min(r0 + cr, nr_t) - r0);
+    s0 = x * cs;
+    const long long ns = max(0LL, min(s0 + cs, ns_t) - s0);
+    len = nr + ns;
   }
-  if (j - cr >= cs) return -1;
-  const long long q = x * cs + (j - cr);
-  return q < ns_t ? nr_t + q : -1;
+  // tiles of this block
+  __device__ long long count() const { return l < len ? (len - l + P - 1) / P : 0; }
+  // the tile (index in the whole tile sequence) of this block's i-th tile
+  __device__ long long tile(long long i) const {
+    const long long p = l + i * P;
+    return p < nr ? r0 + p : nr_t + s0 + (p - nr);
+  }
+};
+
+inline int wgrad_grid() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) !=
+                                               hipSuccess || cus < NXCD)
+    cus = 256;
+  return cus / NXCD * NXCD;
 }
 
-inline int wgrad_grid(int n_routed, int n_shared, long long per_g) {
-  return static_cast<int>(NXCD * ((n_routed * per_g + NXCD - 1) / NXCD + (n_shared * per_g + NXCD - 1) / NXCD));
+// A group's rows, checked against the grouped rows (debug build: a group out
+// of range counts as empty, the same for every caller).
+__device__ __forceinline__ GroupRows checked_rows(const BwdArgs& a, int g) {
+  GroupRows gr = group_rows(a, g);
+  if (!MOE_CHECK(gr.first >= 0 && gr.count >= 0 && gr.first + static_cast<long long>(gr.count) <= a.R, 504))
+    gr = {0, 0};
+  return gr;
 }
+
+// The rows of the group of a tile, cached: a block's consecutive tiles mostly
+// share a group.
+struct GroupCache {
+  int g = -1;
+  GroupRows gr{0, 0};
+  __device__ const GroupRows& get(const BwdArgs& a, int g_new) {
+    if (g_new != g) {
+      g = g_new;
+      gr = checked_rows(a, g);
+    }
+    return gr;
+  }
+};
 
 // C[m][n] = sum over the group's rows r of A[r][m] B[r][n], both K-outer
-// (rows r of lda / ldb bytes), written as fp32 into dst (ldc floats per row).
-__device__ __forceinline__ void wgrad_tile(const BwdArgs& a, const uint16_t* A, int M, const uint16_t* B, int N,
-                                           float* routed_dst, float* shared_dst) {
+// (rows r of M and N bf16), written as fp32 into the group's gradient.
+__device__ __forceinline__ void wgrad_persistent(const BwdArgs& a, const uint16_t* A, int M, const uint16_t* B,
+                                                 int N, float* routed_dst, float* shared_dst) {
   __shared__ __attribute__((aligned(1024))) uint8_t ring[NSTG * STB];
   const int mb_n = ceil_div(M, BT), nb_n = ceil_div(N, BT);
-  const long long q = wgrad_tile_index(a, static_cast<long long>(mb_n) * nb_n);
-  if (q < 0) return;
-  const int g = static_cast<int>(q / (mb_n * nb_n));
-  const int rem = static_cast<int>(q - static_cast<long long>(g) * mb_n * nb_n);
-  const int m0 = (rem / nb_n) * BT, n0 = (rem % nb_n) * BT;
-  const GroupRows gr = group_rows(a, g);
-  if (!MOE_CHECK(gr.first >= 0 && gr.count >= 0 && gr.first + static_cast<long long>(gr.count) <= a.R, 504)) return;
+  const long long per_g = static_cast<long long>(mb_n) * nb_n;
+  const WgradList list(a, per_g);
+  const long long ntiles = list.count();
   const uint32_t lda = M * 2, ldb = N * 2;
-  const int nk = ceil_div(gr.count, 32);
-  f32x4 acc[MI][NJ];
-  zero_acc(acc);
-  if (wave_id() >= NMW) {
-    const Opnd oa = opnd_ko(make_rsrc(reinterpret_cast<const uint8_t*>(A) + static_cast<size_t>(gr.first) * lda,
-                                      gr.count * lda), lda, m0);
-    const Opnd ob = opnd_ko(make_rsrc(reinterpret_cast<const uint8_t*>(B) + static_cast<size_t>(gr.first) * ldb,
-                                      gr.count * ldb), ldb, n0);
-    mainloop<KO, KO>(ring, oa, ob, nk, acc);
+  const int w = wave_id(), lane = threadIdx.x & 63;
+
+  // stages of the block's stream: the sum of its tiles' K-steps (lanes over tiles)
+  long long total = 0;
+  for (long long i = lane; i < ntiles; i += 64) {
+    const int g = static_cast<int>(list.tile(i) / per_g);
+    const GroupRows gr = checked_rows(a, g);
+    total += gr.count > 0 ? ceil_div(gr.count, 32) : 0;
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) total += __shfl_xor(total, off);
+  // the same in every lane: say so, so that the loops over it stay scalar
+  total = static_cast<long long>(static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(total)))) |
+          static_cast<long long>(__builtin_amdgcn_readfirstlane(static_cast<int>(total >> 32))) << 32;
+
+  GroupCache gc;
+  if (w >= NMW) {
+    // ---- load waves: issue the stream NSTG - 1 stages ahead of the MFMAs
+    long long it = -1;        // tile of the next stage to issue
+    int ks = 0, nk = 0;       // that stage's K-step within it, and its K-steps
+    Opnd oa{}, ob{};
+    long long issued = 0;
+    auto issue_next = [&]() {
+      while (ks >= nk) {      // on to the next tile with rows
+        ++it;
+        const long long q = list.tile(it);
+        const int g = static_cast<int>(q / per_g);
+        const int rem = static_cast<int>(q - static_cast<long long>(g) * per_g);
+        const GroupRows& gr = gc.get(a, g);
+        nk = gr.count > 0 ? ceil_div(gr.count, 32) : 0;
+        ks = 0;
+        oa = opnd_ko(make_rsrc(reinterpret_cast<const uint8_t*>(A) + static_cast<size_t>(gr.first) * lda,
+                               gr.count * lda), lda, (rem / nb_n) * BT);
+        ob = opnd_ko(make_rsrc(reinterpret_cast<const uint8_t*>(B) + static_cast<size_t>(gr.first) * ldb,
+                               gr.count * ldb), ldb, (rem % nb_n) * BT);
+      }
+      issue_stage(oa, ob, ring + (issued % NSTG) * STB, ks);
+      ++ks;
+      ++issued;
+    };
+    const long long pre = min(total, static_cast<long long>(NSTG - 1));
+    for (long long s = 0; s < pre; ++s) issue_next();
+    if (pre == NSTG - 1)
+      wait_vm_lgkm0<(NSTG - 3) * NLS>();   // stages 0 and 1
+    else
+      wait_vm_lgkm0<0>();
+    for (long long S = 0; S < total; ++S) {
+      block_barrier();
+      if (S + NSTG - 1 < total) {
+        issue_next();
+        wait_vm_lgkm0<(NSTG - 3) * NLS>();   // stage S + 2
+      } else {
+        wait_vm_lgkm0<0>();
+      }
+    }
     return;
   }
-  mainloop<KO, KO>(ring, Opnd{}, Opnd{}, nk, acc);
-  float* dst = g < a.n_routed ? routed_dst + static_cast<size_t>(g) * M * N
-                              : shared_dst + static_cast<size_t>(g - a.n_routed) * M * N;
-  const int w = wave_id(), lane = threadIdx.x & 63, wm = w % 2, wn = w / 2;
+
+  // ---- MFMA waves
+  const int wm = w % 2, wn = w / 2;
+  KoLane kl = ko_lane();
+  f32x4 acc[MI][NJ];
+  i32x4 wf[NJ], xf;
+  long long S = 0;   // the next stage of the stream
+  if (total > 0) block_barrier();   // #0: stages 0 and 1 have landed
+  for (long long i = 0; i < ntiles; ++i) {
+    const long long q = list.tile(i);
+    const int g = static_cast<int>(q / per_g);
+    const int rem = static_cast<int>(q - static_cast<long long>(g) * per_g);
+    const int m0 = (rem / nb_n) * BT, n0 = (rem % nb_n) * BT;
+    const GroupRows& gr = gc.get(a, g);
+    const int nk = gr.count > 0 ? ceil_div(gr.count, 32) : 0;
+    zero_acc(acc);
+    if (nk > 0) {
+      {   // the tile's first stage (landed: this wave passed barrier #S)
+        const uint8_t* st = ring + (S % NSTG) * STB;
 #pragma unroll
-  for (int i = 0; i < MI; ++i) {
-    const int m = m0 + 16 * (2 * i + wm) + (lane & 15);
-    if (m >= M) continue;
+        for (int j = 0; j < NJ; ++j) wf[j] = frag_ko(st + OPB, 64 * wn + 16 * j, kl);
+        xf = frag_ko(st, 16 * wm, kl);
+      }
+      acc_fence(acc);
+      for (int k = 0; k < nk; ++k) {
+        asm volatile("" : "+v"(kl.base), "+v"(kl.y));
+        const uint8_t* sa = ring + (S % NSTG) * STB;
+        const uint8_t* na = ring + ((S + 1) % NSTG) * STB;
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      const int n = n0 + 64 * wn + 16 * j + 4 * (lane >> 4);
-      if (n < N)
-        *reinterpret_cast<float4*>(dst + static_cast<size_t>(m) * N + n) =
-            make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
+        for (int ii = 0; ii < MI; ++ii) {
+          i32x4 xn;
+          if (ii + 1 < MI) xn = frag_ko(sa, 16 * (2 * (ii + 1) + wm), kl);
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int j = 0; j < NJ; ++j) mfma_bf16_tied(acc[ii][j], wf[j], xf);
+          __builtin_amdgcn_sched_barrier(0);
+          if (ii + 1 < MI) xf = xn;
+        }
+        ++S;
+        if (k + 1 < nk) {
+#pragma unroll
+          for (int j = 0; j < NJ; ++j) wf[j] = frag_ko(na + OPB, 64 * wn + 16 * j, kl);
+          xf = frag_ko(na, 16 * wm, kl);
+          block_barrier();
+        } else if (S < total) {
+          block_barrier();   // the load waves go on into the next tile during the stores below
+        }
+      }
+      acc_fence(acc);
+    }
+    float* dst = g < a.n_routed ? routed_dst + static_cast<size_t>(g) * M * N
+                                : shared_dst + static_cast<size_t>(g - a.n_routed) * M * N;
+#pragma unroll
+    for (int ii = 0; ii < MI; ++ii) {
+      const int m = m0 + 16 * (2 * ii + wm) + (lane & 15);
+      if (m >= M) continue;
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const int n = n0 + 64 * wn + 16 * j + 4 * (lane >> 4);
+        if (n < N)
+          *reinterpret_cast<float4*>(dst + static_cast<size_t>(m) * N + n) =
+              make_float4(acc[ii][j][0], acc[ii][j][1], acc[ii][j][2], acc[ii][j][3]);
+      }
     }
   }
 }
 
 // dW_down[c][i] = sum_r dY[r][c] H[r][i]
 __global__ __launch_bounds__(THREADS, 1) void wgrad_down_kernel(BwdArgs a) {
-  wgrad_tile(a, a.dys, a.d, a.hr, a.inter, a.dw_down, a.dws_down);
+  wgrad_persistent(a, a.dys, a.d, a.hr, a.inter, a.dw_down, a.dws_down);
 }
 
 // dW_gate_up[j][c] = sum_r [dG dU][r][j] X[r][c]
 __global__ __launch_bounds__(THREADS, 1) void wgrad_gateup_kernel(BwdArgs a) {
-  wgrad_tile(a, a.dgu, 2 * a.inter, a.xp, a.d, a.dw_gate_up, a.dws_gate_up);
+  wgrad_persistent(a, a.dgu, 2 * a.inter, a.xp, a.d, a.dw_gate_up, a.dws_gate_up);
 }
 
 // ------------------------------------------------------------------ elementwise passes
@@ -551,16 +692,10 @@ hipError_t launch_backward_stage(int stage, const BwdArgs& a, hipStream_t s) {
                          a);
       break;
     case 3:   // Wgrad of the down GEMM (every group: zeros where a group has no rows)
-      hipLaunchKernelGGL(wgrad_down_kernel,
-                         dim3(wgrad_grid(a.n_routed, a.n_shared,
-                                         static_cast<long long>(ceil_div(a.d, BT)) * ceil_div(a.inter, BT))),
-                         dim3(THREADS), 0, s, a);
+      hipLaunchKernelGGL(wgrad_down_kernel, dim3(wgrad_grid()), dim3(THREADS), 0, s, a);
       break;
     case 4:   // Wgrad of the gate/up GEMM
-      hipLaunchKernelGGL(wgrad_gateup_kernel,
-                         dim3(wgrad_grid(a.n_routed, a.n_shared,
-                                         static_cast<long long>(ceil_div(2 * a.inter, BT)) * ceil_div(a.d, BT))),
-                         dim3(THREADS), 0, s, a);
+      hipLaunchKernelGGL(wgrad_gateup_kernel, dim3(wgrad_grid()), dim3(THREADS), 0, s, a);
       break;
     case 5:   // du, dcentroids (zeros for experts without rows)
       if (a.T > 0) hipLaunchKernelGGL(bwd_du_kernel, dim3(ceil_div(a.T, 4)), dim3(256), 0, s, a);
