@@ -51,6 +51,13 @@ def measured_peaks():
     return json.load(open(f)) if os.path.exists(f) else None
 
 
+def library_reference(workload):
+    """hipBLASLt timings of GEMMs of the workload's sizes (profiling.py
+    library), if stored; else None."""
+    f = os.path.join(os.path.dirname(TRAFFIC_FILE), "library_reference.json")
+    return json.load(open(f)).get(workload) if os.path.exists(f) else None
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -172,6 +179,17 @@ def main():
             roofline["measured_ceilings"] = {
                 "mfma_tflops_random_operands": m_tf, "mfma_frac": round(gu_tflops / m_tf, 4),
                 "hbm_read_gbs": m_bw, "hbm_frac": round(gu_gbs / m_bw, 4)}
+    lib = library_reference(cfg.name)
+    if lib and "gate_up_batched" in lib:
+        # the vendor library on the same products: uniform batches (one weight
+        # per expert, T K / N_r rows each) and one dense GEMM with a single weight
+        dn_tflops = dn_flops / dn_s / 1e12
+        roofline["library_reference"] = {
+            "batched_tflops": lib["gate_up_batched"]["tflops"], "dense_tflops": lib["gate_up_dense"]["tflops"],
+            "vs_batched": round(gu_tflops / lib["gate_up_batched"]["tflops"], 4),
+            "vs_dense": round(gu_tflops / lib["gate_up_dense"]["tflops"], 4),
+            "down_vs_batched": round(dn_tflops / lib["down_batched"]["tflops"], 4),
+            "down_vs_dense": round(dn_tflops / lib["down_dense"]["tflops"], 4)}
     grouped_frac = (gu_flops + dn_flops) / (gu_s + dn_s) / 1e12 / peak
 
     xs = 4 if cfg.x_dtype == "f32" else 2

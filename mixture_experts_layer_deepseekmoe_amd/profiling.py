@@ -4,6 +4,8 @@
     python -m mixture_experts_layer_deepseekmoe_amd.profiling run --workload bf16_d7168 --steps 3
     # measured ceilings (MFMA with random / zero operands, HBM stream) -> profiles/measured_peaks.json:
     python -m mixture_experts_layer_deepseekmoe_amd.profiling peaks
+    # the vendor library (hipBLASLt through torch) on GEMMs of the same sizes -> profiles/library_reference.json:
+    python -m mixture_experts_layer_deepseekmoe_amd.profiling library --workload bf16_d7168
     # turn rocprofv3's CSV output into the summaries kept under profiles/:
     python -m mixture_experts_layer_deepseekmoe_amd.profiling summarize --trace DIR --pmc DIR [DIR...] \
         --workload bf16_d7168 --out profiles
@@ -132,10 +134,11 @@ def counters(pmc_dirs):
 
 
 def source_hash():
-    """Hash of the grouped-GEMM sources, stamped on stored counter readings."""
+    """Hash of the grouped-GEMM sources (forward and backward), stamped on
+    stored counter readings."""
     csrc = os.path.join(ROOT, "mixture_experts_layer_deepseekmoe_amd", "csrc")
     h = hashlib.sha256()
-    for f in ("gemm_core.hpp", "ggemm.hip", "moe_common.hpp", "kernels.hpp"):
+    for f in ("gemm_core.hpp", "ggemm.hip", "bwd.hip", "tile_map.hpp", "moe_common.hpp", "kernels.hpp"):
         h.update(open(os.path.join(csrc, f), "rb").read())
     return h.hexdigest()[:16]
 
@@ -218,6 +221,65 @@ def _peaks(args):
     print(json.dumps(table, indent=1, sort_keys=True))
 
 
+def _library(args):
+    """Time the vendor GEMM library (hipBLASLt, called through torch) on the
+    workload's gate/up and down products, as a reference point for the
+    grouped GEMMs: one dense GEMM over all grouped rows with a single weight
+    matrix (the weight stays in cache), and a batched GEMM with one weight
+    matrix per routed expert and T K / N_r rows each (every weight read from
+    HBM, as in the layer, but uniform groups, no row gather and no shared
+    expert).  bf16 only."""
+    sys.path.insert(0, ROOT)
+    import torch
+
+    from moe_workloads import get_config
+
+    cfg = get_config(args.workload)
+    if cfg.w_dtype != "bf16":
+        raise SystemExit("library reference: bf16 workloads only")
+    dev = "cuda"
+    g = torch.Generator(device=dev).manual_seed(0)
+
+    def timeit(fn, reps=10):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s0.record()
+        for _ in range(reps):
+            fn()
+        s1.record()
+        torch.cuda.synchronize()
+        return s0.elapsed_time(s1) / reps
+
+    def randn(*shape, scale=1.0):
+        return torch.randn(*shape, device=dev, dtype=torch.bfloat16, generator=g) * scale
+
+    R = cfg.T * (cfg.top_k + cfg.n_shared)
+    per = cfg.T * cfg.top_k // cfg.n_routed
+    out = {}
+    for name, n, k in (("gate_up", 2 * cfg.inter, cfg.d), ("down", cfg.d, cfg.inter)):
+        x, w = randn(R, k), randn(n, k, scale=0.02)
+        ms = timeit(lambda: torch.nn.functional.linear(x, w))
+        out[f"{name}_dense"] = {"shape": [R, n, k], "ms": round(ms, 4), "tflops": round(2 * R * n * k / ms / 1e9, 1)}
+        del x, w
+        # the right operand [E][K][N] contiguous (no transposed view)
+        xb, wb = randn(cfg.n_routed, per, k), randn(cfg.n_routed, k, n, scale=0.02)
+        ms = timeit(lambda: torch.bmm(xb, wb))
+        out[f"{name}_batched"] = {"shape": [cfg.n_routed, per, n, k], "ms": round(ms, 4),
+                                  "tflops": round(2 * cfg.n_routed * per * n * k / ms / 1e9, 1)}
+        del xb, wb
+        torch.cuda.empty_cache()
+    out["torch"] = torch.__version__
+    out["command"] = f"python -m mixture_experts_layer_deepseekmoe_amd.profiling library --workload {cfg.name}"
+    f = os.path.join(args.out, "library_reference.json")
+    table = json.load(open(f)) if os.path.exists(f) else {}
+    table[cfg.name] = out
+    os.makedirs(args.out, exist_ok=True)
+    json.dump(table, open(f, "w"), indent=1, sort_keys=True)
+    print(json.dumps(out, indent=1, sort_keys=True))
+
+
 def main():
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -234,8 +296,11 @@ def main():
     s.add_argument("--command", nargs="*")
     pk = sub.add_parser("peaks")
     pk.add_argument("--out", default=os.path.join(ROOT, "profiles"))
+    lb = sub.add_parser("library")
+    lb.add_argument("--workload", default="bf16_d7168")
+    lb.add_argument("--out", default=os.path.join(ROOT, "profiles"))
     args = ap.parse_args()
-    {"run": _run, "summarize": _summarize, "peaks": _peaks}[args.cmd](args)
+    {"run": _run, "summarize": _summarize, "peaks": _peaks, "library": _library}[args.cmd](args)
 
 
 if __name__ == "__main__":

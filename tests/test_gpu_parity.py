@@ -398,7 +398,8 @@ def test_forward_batch_invariant_with_multi_tile_experts():
     inp = make_inputs(cfg, 0, weights_device=DEV)
     y_full, routing, w = _run_forward(cfg, inp)
     counts = routing["expert_counts"].cpu().numpy()
-    assert counts.max() > 256          # several experts span more than one m-tile
+    bm = moe.workspace_layout(moe.LayerShape.from_config(cfg))["tile_rows"]
+    assert counts.max() > bm           # several experts span more than one m-tile
     sub = torch.tensor(sorted({0, 1, 5, 100, 255, 256, 511, 1000, 2047, 2048, 3001, 4094, 4095} |
                               set(range(1200, 1224))))
     inp_s = make_inputs(cfg, 0, with_weights=False)
