@@ -154,9 +154,12 @@ __device__ __forceinline__ i32x4 frag(const uint8_t* op, int at, KoLane kl) {
   return M == KO ? frag_ko(op, at, kl) : frag_kc(op, at);
 }
 
-template <int AM, int BM>
+// NSUB: the row subtiles each MFMA wave computes (its first NSUB of MI; a
+// tile of fewer rows issues no MFMAs for the subtiles past them).
+template <int AM, int BM, int NSUB = MI>
 __device__ __forceinline__ void mainloop(uint8_t* ring, const Opnd& a, const Opnd& b, int nk,
                                          f32x4 (&acc)[MI][NJ]) {
+  static_assert(NSUB >= 1 && NSUB <= MI, "row subtiles");
   const int w = wave_id();
   if (nk <= 0) return;
   if (w >= NMW) {
@@ -196,14 +199,14 @@ __device__ __forceinline__ void mainloop(uint8_t* ring, const Opnd& a, const Opn
     const uint8_t* sa = ring + (ks % NSTG) * STB;
     const uint8_t* na = ring + ((ks + 1) % NSTG) * STB;   // the next stage (landed; unused past the end)
 #pragma unroll
-    for (int i = 0; i < MI; ++i) {
+    for (int i = 0; i < NSUB; ++i) {
       i32x4 xn;
-      if (i + 1 < MI) xn = frag<AM>(sa, 16 * (2 * (i + 1) + wm), kl);
+      if (i + 1 < NSUB) xn = frag<AM>(sa, 16 * (2 * (i + 1) + wm), kl);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int j = 0; j < NJ; ++j) mfma_bf16_tied(acc[i][j], wf[j], xf);
       __builtin_amdgcn_sched_barrier(0);
-      if (i + 1 < MI) xf = xn;
+      if (i + 1 < NSUB) xf = xn;
     }
     if (ks + 1 < nk) {
 #pragma unroll
@@ -213,6 +216,18 @@ __device__ __forceinline__ void mainloop(uint8_t* ring, const Opnd& a, const Opn
     }
   }
   acc_fence(acc);
+}
+
+// f.template operator()<NSUB>() with NSUB = the row subtiles wave row 0
+// computes for a tile of `rows` rows (two wave rows of 16-row subtiles).
+template <int N = 1, class F>
+__device__ __forceinline__ void with_row_subtiles(int rows, F&& f) {
+  if constexpr (N >= MI)
+    f.template operator()<MI>();
+  else if (rows <= 32 * N)
+    f.template operator()<N>();
+  else
+    with_row_subtiles<N + 1>(rows, f);
 }
 
 __device__ __forceinline__ uint2 pack4(const f32x4& v) { return make_uint2(bf16x2(v[0], v[1]), bf16x2(v[2], v[3])); }
@@ -266,12 +281,12 @@ __global__ __launch_bounds__(THREADS, 1) void dgrad_down_kernel(BwdArgs a) {
   if (wave_id() >= NMW) {
     const Opnd oa = opnd_kc(make_rsrc(reinterpret_cast<const uint8_t*>(a.dys) + static_cast<size_t>(row0) * ldy,
                                       rows * ldy),
-                            [&](int m) { return static_cast<uint32_t>((m < rows ? m : 0) * ldy); });
+                            [&](int m) { return static_cast<uint32_t>((m < rows ? m : rows) * ldy); });   // past the rows: zeros
     const Opnd ob = opnd_ko(make_rsrc(wd, a.d * ldw), ldw, n0);
     mainloop<KC, KO>(ring, oa, ob, a.d / 32, acc);
     return;
   }
-  mainloop<KC, KO>(ring, Opnd{}, Opnd{}, a.d / 32, acc);
+  with_row_subtiles(rows, [&]<int NS>() { mainloop<KC, KO, NS>(ring, Opnd{}, Opnd{}, a.d / 32, acc); });
   const int w = wave_id(), lane = threadIdx.x & 63, wm = w % 2, wn = w / 2;
 #pragma unroll
   for (int i = 0; i < MI; ++i) {
@@ -318,12 +333,12 @@ __global__ __launch_bounds__(THREADS, 1) void dgrad_gateup_kernel(BwdArgs a) {
   if (wave_id() >= NMW) {
     const Opnd oa = opnd_kc(make_rsrc(reinterpret_cast<const uint8_t*>(a.dgu) + static_cast<size_t>(row0) * ldg,
                                       rows * ldg),
-                            [&](int m) { return static_cast<uint32_t>((m < rows ? m : 0) * ldg); });
+                            [&](int m) { return static_cast<uint32_t>((m < rows ? m : rows) * ldg); });   // past the rows: zeros
     const Opnd ob = opnd_ko(make_rsrc(wgu, 2 * a.inter * ldw), ldw, n0);
     mainloop<KC, KO>(ring, oa, ob, nk, acc);
     return;
   }
-  mainloop<KC, KO>(ring, Opnd{}, Opnd{}, nk, acc);
+  with_row_subtiles(rows, [&]<int NS>() { mainloop<KC, KO, NS>(ring, Opnd{}, Opnd{}, nk, acc); });
   const int w = wave_id(), lane = threadIdx.x & 63, wm = w % 2, wn = w / 2;
 #pragma unroll
   for (int i = 0; i < MI; ++i) {

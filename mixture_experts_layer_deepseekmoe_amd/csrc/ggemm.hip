@@ -338,7 +338,9 @@ __global__ __launch_bounds__(GG<FMT>::THREADS, 1) void gateup_kernel(GateUpArgs 
   auto make_pipe = [&]() {
     P p;
     p.init(make_rsrc(a.x, static_cast<uint32_t>(a.T * xrow)),
-           [&](int r) { return static_cast<uint32_t>(token_of(r) * xrow); },
+           // rows past the tile's: an offset past the resource, so their
+           // loads return zeros without touching memory
+           [&](int r) { return static_cast<uint32_t>((r < rows ? token_of(r) : a.T) * xrow); },
            make_rsrc(wbase, static_cast<uint32_t>(2 * a.inter * xrow)),
            [&](int r) {
              int n = n0 + (r & 127);
@@ -472,7 +474,7 @@ __global__ __launch_bounds__(GG<FMT>::THREADS, 1) void down_kernel(DownArgs a) {
   auto make_pipe = [&]() {
     P p;
     p.init(make_rsrc(static_cast<const uint8_t*>(a.h) + static_cast<size_t>(row0) * hrow, static_cast<uint32_t>(rows * hrow)),
-           [&](int r) { return static_cast<uint32_t>((r < rows ? r : 0) * hrow); },
+           [&](int r) { return static_cast<uint32_t>((r < rows ? r : rows) * hrow); },   // past the rows: zeros
            make_rsrc(wbase, static_cast<uint32_t>(a.d * hrow)),
            [&](int r) {
              int c = n0 + r;
