@@ -37,6 +37,12 @@ Readings taken where the pages are silent:
   scale 1 and codes 0 for an all-zero tile.  Both GEMMs of every expert are
   FP8; the router stays in the activation dtype; the residual u is unquantised;
   h is quantised 1x128 along I from fl32(h).
+* FP8 backward (the Figure 6 passage: Fprop, Dgrad and Wgrad all in FP8):
+  every operand is scaled per group of 128 along its GEMM's inner dimension,
+  so the Dgrad activations (dY, [dG dU]) take 1x128 tiles along their
+  columns, both Wgrad operands take 128x1 tiles along the rows (counted from
+  each expert's first grouped row), and the weights keep their 128x128
+  blocks.  Tensors are quantised from the bf16 rows the kernels store.
 
 Everything is fp64 except where a reading fixes fp32 (scales, the bias).
 """
@@ -314,6 +320,35 @@ def quantize_weight_128x128(w: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
     return q.reshape(R, C), scale
 
 
+def quantize_act_128x1(x: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+    """Per column, per 128-row tile counted from row 0 (the last tile may be
+    short): codes [R, C] uint8 and scales [ceil(R/128), C] fp32.  The 1x128
+    tiling of x's transpose: the tiles run along the rows, the inner
+    dimension of a GEMM that contracts over them (a weight gradient)."""
+    x = np.asarray(x, F32)
+    R, C = x.shape
+    Rp = -(-R // QBLOCK) * QBLOCK
+    xt = np.zeros((C, Rp), F32)                 # zero rows do not change a tile's amax
+    xt[:, :R] = x.T
+    q, sc = quantize_act_1x128(xt)
+    return q[:, :R].T.copy(), sc.T.copy()
+
+
+def dequantize_act_128x1(q: np.ndarray, sc: np.ndarray) -> np.ndarray:
+    R, C = q.shape
+    rows = np.arange(R) // QBLOCK
+    return e4m3_decode(q) * sc.astype(F64)[rows, :]
+
+
+def round_bf16(x: np.ndarray) -> np.ndarray:
+    """Nearest bfloat16 value (ties to even) of fl32(x), as fp64: bit 16 of
+    the fp32 pattern is the kept LSB; adding 0x7FFF plus that bit and
+    clearing the low half rounds to nearest, ties to even."""
+    b = np.asarray(x, F32).view(np.uint32).astype(np.uint64)
+    b = ((b + 0x7FFF + ((b >> 16) & 1)) & 0xFFFF0000).astype(np.uint32)
+    return b.view(F32).astype(F64)
+
+
 def dequantize_act(q: np.ndarray, sc: np.ndarray) -> np.ndarray:
     R, C = q.shape
     return (e4m3_decode(q).reshape(R, C // QBLOCK, QBLOCK) * sc.astype(F64)[:, :, None]).reshape(R, C)
@@ -446,10 +481,46 @@ def swiglu_ffn_backward(x: np.ndarray, w_gate_up: np.ndarray, w_down: np.ndarray
     return {"dx": dGU @ wgu, "dW_gate_up": dGU.T @ x, "dW_down": dout.T @ H}
 
 
+def swiglu_ffn_backward_fp8(x: np.ndarray, x_deq: np.ndarray, wgu_q, wgu_s, wd_q, wd_s,
+                            dout: np.ndarray) -> Dict[str, np.ndarray]:
+    """The FP8 backward of one expert over its n rows (in grouped order): the
+    same steps as swiglu_ffn_backward with every GEMM on E4M3 operands and
+    fp64 products of the dequantised values (FP32 promotion per 128-element
+    block, exact here).  Scaling is per group of 128 along each GEMM's inner
+    dimension:
+        Dgrad  dH = q(dout) Wd            dout tiled 1x128 along d
+               dx = q([dG dU]) Wgu        [dG dU] tiled 1x128 along 2I
+        Wgrad  dW_down = q(dout)^T q(H)           both tiled 128x1 along the
+               dW_gate_up = q([dG dU])^T q(x)     rows, from the group's first
+    The weights keep their forward 128x128 blocks (read transposed).  G and U
+    are the FP8 forward's products from the dequantised input x_deq (the
+    cached SwiGLU inputs); H = SiLU(G) U is recomputed.  Every tensor is
+    quantised from bf16 (dout, [dG dU], H and x are the bf16 rows the
+    kernels store before quantising them)."""
+    wgu = dequantize_weight(wgu_q, wgu_s)
+    wd = dequantize_weight(wd_q, wd_s)
+    I = wgu.shape[0] // 2
+    x_deq = np.asarray(x_deq, F64)
+    G = x_deq @ wgu[:I].T
+    U = x_deq @ wgu[I:].T
+    dout_b = round_bf16(dout)
+    dH = dequantize_act(*quantize_act_1x128(dout_b)) @ wd
+    dG = dH * U * silu_grad(G)
+    dU = dH * silu(G)
+    dGU_b = round_bf16(np.concatenate([dG, dU], axis=1))
+    H_b = round_bf16(silu(G) * U)
+    dx = dequantize_act(*quantize_act_1x128(dGU_b)) @ wgu
+    dW_down = dequantize_act_128x1(*quantize_act_128x1(dout_b)).T @ dequantize_act_128x1(*quantize_act_128x1(H_b))
+    dW_gu = (dequantize_act_128x1(*quantize_act_128x1(dGU_b)).T
+             @ dequantize_act_128x1(*quantize_act_128x1(round_bf16(x))))
+    return {"dx": dx, "dW_gate_up": dW_gu, "dW_down": dW_down}
+
+
 def layer_backward(u: np.ndarray, centroids: np.ndarray, bias: np.ndarray, k: int,
                    routed: ExpertFn, n_routed: int, shared: Sequence[Tuple[np.ndarray, np.ndarray]],
                    dy: np.ndarray, selection: Optional[np.ndarray] = None, n_groups: int = 1,
-                   topk_groups: int = 1, weight_grads: bool = True) -> Dict[str, np.ndarray]:
+                   topk_groups: int = 1, weight_grads: bool = True, fp8: bool = False,
+                   fp8_weights: Optional[Callable[[str, int], Tuple]] = None) -> Dict[str, np.ndarray]:
     """Gradients of h' = u + sum_s FFN_s(u) + sum_k g_k FFN_{e_k}(u) for the
     upstream gradient dy [T, d], the selection held fixed:
       routed expert e, its rows (t, k): upstream g_{t,k} dy_t through FFN_e;
@@ -462,17 +533,38 @@ def layer_backward(u: np.ndarray, centroids: np.ndarray, bias: np.ndarray, k: in
     Returns du [T, d], dE [N_r, d], dg and dz [T, K], and (weight_grads)
     dW_gate_up / dW_down: dicts expert -> gradient (experts without rows
     have zero gradients and are left out), dWs_gate_up / dWs_down: lists
-    over the shared experts."""
+    over the shared experts.
+
+    With ``fp8`` the layer is the FP8 one of layer_forward (weights quantised
+    128x128 here or taken from ``fp8_weights``, u quantised 1x128 for the
+    expert GEMMs) and every expert's backward is swiglu_ffn_backward_fp8;
+    dg uses the FP8 expert outputs.  The router's gradient (dz, dE and the
+    dz e terms of du) is the same in both."""
     u64 = np.asarray(u, F64)
     E64 = np.asarray(centroids, F64)
     dy = np.asarray(dy, F64)
     r = route(u64, E64, bias, k, selection, n_groups, topk_groups)
     idx, gate, s = r["idx"], r["gate"], r["s"]
     T, d = u64.shape
+    if fp8:
+        x_deq = dequantize_act(*quantize_act_1x128(np.asarray(u, F32)))
+
+        def expert(kind, e, wgu, wd, rows, dout):
+            if fp8_weights is not None:
+                gq, gs, dq, ds = fp8_weights(kind, e)
+            else:
+                gq, gs = quantize_weight_128x128(wgu)
+                dq, ds = quantize_weight_128x128(wd)
+            ye = swiglu_ffn_fp8(x_deq[rows], gq, gs, dq, ds)
+            return ye, swiglu_ffn_backward_fp8(u64[rows], x_deq[rows], gq, gs, dq, ds, dout)
+    else:
+        def expert(kind, e, wgu, wd, rows, dout):
+            x = u64[rows]
+            return swiglu_ffn(x, wgu, wd), swiglu_ffn_backward(x, wgu, wd, dout)
     du = dy.copy()
     dWs_gu, dWs_d = [], []
-    for wgu, wd in shared:
-        b = swiglu_ffn_backward(u64, wgu, wd, dy)
+    for si, (wgu, wd) in enumerate(shared):
+        _, b = expert("shared", si, wgu, wd, np.arange(T), dy)
         du += b["dx"]
         dWs_gu.append(b["dW_gate_up"])
         dWs_d.append(b["dW_down"])
@@ -483,10 +575,9 @@ def layer_backward(u: np.ndarray, centroids: np.ndarray, bias: np.ndarray, k: in
         if tok.size == 0:
             continue
         wgu, wd = routed(e)
-        x = u64[tok]
-        ye = swiglu_ffn(x, wgu, wd)                           # FFN_e(u_t) of the rows
+        # FFN_e(u_t) of the rows, and the backward with upstream g dy
+        ye, b = expert("routed", e, wgu, wd, tok, gate[tok, slot][:, None] * dy[tok])
         dg[tok, slot] = np.sum(dy[tok] * ye, axis=1)
-        b = swiglu_ffn_backward(x, wgu, wd, gate[tok, slot][:, None] * dy[tok])
         du[tok] += b["dx"]
         if weight_grads:
             dW_gu[e] = b["dW_gate_up"]

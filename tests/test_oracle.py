@@ -658,3 +658,122 @@ def test_silu_grad_closed_form():
     t = torch.tensor(a, requires_grad=True)
     torch.nn.functional.silu(t).sum().backward()
     np.testing.assert_allclose(O.silu_grad(a), t.grad.numpy(), rtol=1e-13, atol=1e-15)
+
+
+# ------------------------------------------------------------------ FP8 backward
+
+def test_round_bf16_matches_torch():
+    """round_bf16 against torch's float32 -> bfloat16 conversion (nearest,
+    ties to even), on random values and on exact ties."""
+    rng = np.random.default_rng(40)
+    x = np.concatenate([rng.normal(0, 1, 4000), rng.normal(0, 1e-30, 100), rng.normal(0, 1e30, 100)]).astype(np.float32)
+    ties = (np.arange(1, 200, dtype=np.uint32) << 16 | 0x8000).view(np.float32)   # half-way between two bf16
+    x = np.concatenate([x, ties, -ties, np.float32([0.0, -0.0, 1.0])])
+    ref = torch.from_numpy(x).to(torch.bfloat16).to(torch.float64).numpy()
+    got = O.round_bf16(x)
+    assert np.array_equal(got, ref)
+
+
+def test_quantize_act_128x1_tiles_rows_from_row_zero():
+    """The 128x1 tiling: tile (b, c) holds rows 128 b .. 128 b + 127 of column
+    c (the last tile short); each tile is an independent 1x128 tile of the
+    transpose.  A column whose rows differ in magnitude tile by tile, a zero
+    column and a short last tile."""
+    rng = np.random.default_rng(41)
+    x = rng.normal(0, 1, (300, 5)).astype(np.float32)
+    x[:128, 1] *= 1000.0
+    x[:, 3] = 0.0
+    q, sc = O.quantize_act_128x1(x)
+    assert q.shape == x.shape and sc.shape == (3, 5)
+    for b0 in range(3):
+        rows = slice(128 * b0, min(128 * (b0 + 1), 300))
+        for c in range(5):
+            col = x[rows, c]
+            tq, ts = O.quantize_act_1x128(np.pad(col, (0, 128 - col.size))[None, :])
+            assert (q[rows, c] == tq[0, :col.size]).all() and sc[b0, c] == ts[0, 0]
+    assert sc[0, 1] > 100 * sc[1, 1]               # the scaled rows are in tile 0 only
+    assert (q[:, 3] == 0).all() and (sc[:, 3] == 1).all()
+    deq = O.dequantize_act_128x1(q, sc)
+    assert np.all(np.abs(deq - x) <= np.abs(x) * 2.0 ** -4 + sc[np.arange(300) // 128, :] * 2.0 ** -9)
+
+
+def _tq_rows(a: torch.Tensor) -> torch.Tensor:
+    """128x1 tiles (along the rows, from row 0) through torch's cast: the 1x128
+    tiling of the zero-padded transpose.  Dequantised, float64."""
+    R, C = a.shape
+    Rp = -(-R // 128) * 128
+    t = torch.zeros((C, Rp), dtype=a.dtype)
+    t[:, :R] = a.T
+    return _tq_act(t)[:, :R].T
+
+
+def _torch_fp8_expert_backward(x, wgu, wd, dout, slip=None):
+    """One FP8 expert's backward from torch pieces: float8_e4m3fn casts, torch
+    bf16 rounding, float64 products.  ``slip`` plants one plausible mistake."""
+    bf = lambda t: t.to(torch.float32).to(torch.bfloat16).to(torch.float64)
+    x32 = torch.from_numpy(np.asarray(x, np.float32))
+    g = _tq_w(torch.from_numpy(np.asarray(wgu, np.float32)))
+    dn = _tq_w(torch.from_numpy(np.asarray(wd, np.float32)))
+    I = g.shape[0] // 2
+    xq = _tq_act(x32)
+    G, U = xq @ g[:I].T, xq @ g[I:].T
+    do = torch.from_numpy(np.asarray(dout, np.float64))
+    do_b = do if slip == "no_bf16_before_quantising" else bf(do)
+    dH = _tq_act(do_b.to(torch.float32)) @ dn
+    sg = torch.sigmoid(G)
+    dG, dU = dH * U * sg * (1 + G * (1 - sg)), dH * torch.nn.functional.silu(G)
+    dGU = bf(torch.cat([dG, dU], dim=1))
+    H = bf(torch.nn.functional.silu(G) * U)
+    dx = _tq_act(dGU.to(torch.float32)) @ g
+    along_rows = (lambda t: _tq_act(t.to(torch.float32))) if slip == "wgrad_tiles_along_columns" else \
+        (lambda t: _tq_rows(t.to(torch.float32)))
+    xw = xq if slip == "wgrad_x_from_forward_codes" else x32.double()
+    dW_down = along_rows(do_b).T @ along_rows(H)
+    dW_gu = along_rows(dGU).T @ along_rows(xw)
+    return {"dx": dx.numpy(), "dW_gate_up": dW_gu.numpy(), "dW_down": dW_down.numpy()}
+
+
+def test_fp8_expert_backward_pinned_to_torch_fp8():
+    """swiglu_ffn_backward_fp8 against the same steps built from torch's
+    float8_e4m3fn and bfloat16 conversions (200 rows: one full and one short
+    128-row Wgrad tile; two 128-blocks along d and I).  Each planted slip
+    moves the torch result away from the oracle's."""
+    rng = np.random.default_rng(42)
+    n, d, I = 200, 256, 256
+    x = torch.from_numpy(rng.normal(0, 1, (n, d))).to(torch.bfloat16).double().numpy()
+    wgu = torch.from_numpy(rng.normal(0, 0.05, (2 * I, d))).to(torch.bfloat16).double().numpy()
+    wd = torch.from_numpy(rng.normal(0, 0.05, (d, I))).to(torch.bfloat16).double().numpy()
+    dout = rng.normal(0, 1, (n, d)).astype(np.float32).astype(np.float64)
+    gq, gs = O.quantize_weight_128x128(wgu)
+    dq, ds = O.quantize_weight_128x128(wd)
+    x_deq = O.dequantize_act(*O.quantize_act_1x128(x.astype(np.float32)))
+    got = O.swiglu_ffn_backward_fp8(x, x_deq, gq, gs, dq, ds, dout)
+    ref = _torch_fp8_expert_backward(x, wgu, wd, dout)
+    for key in ("dx", "dW_gate_up", "dW_down"):
+        np.testing.assert_allclose(got[key], ref[key], rtol=1e-11, atol=1e-11 * np.abs(ref[key]).max())
+    for slip, key in (("no_bf16_before_quantising", "dx"), ("wgrad_tiles_along_columns", "dW_down"),
+                      ("wgrad_x_from_forward_codes", "dW_gate_up")):
+        bad = _torch_fp8_expert_backward(x, wgu, wd, dout, slip)
+        assert np.abs(bad[key] - got[key]).max() > 1e-6 * np.abs(got[key]).max(), slip
+
+
+def test_fp8_layer_backward_close_to_exact():
+    """The FP8 backward of a small layer stays within the FP8 rounding of the
+    exact one (normwise ~2^-4 at most), on every output."""
+    cfg = PARITY_CONFIGS["small_fp8_ns2"] if "small_fp8_ns2" in PARITY_CONFIGS else CONFIGS["small_fp8"]
+    inp = make_inputs(cfg, 3)
+    u, E, b = to_numpy_f32(inp.u), to_numpy_f32(inp.centroids), inp.bias.numpy()
+    wgu_all, wd_all = to_numpy_f32(inp.w_gate_up), to_numpy_f32(inp.w_down)
+    routed = lambda e: (wgu_all[e], wd_all[e])
+    shared = [(to_numpy_f32(inp.ws_gate_up[s]), to_numpy_f32(inp.ws_down[s])) for s in range(cfg.n_shared)]
+    dy = np.random.default_rng(43).normal(0, 1, u.shape).astype(np.float32)
+    r8 = O.layer_backward(u, E, b, cfg.top_k, routed, cfg.n_routed, shared, dy, fp8=True)
+    r = O.layer_backward(u, E, b, cfg.top_k, routed, cfg.n_routed, shared, dy, selection=r8["idx"])
+    rel = lambda a, c: np.linalg.norm(a - c) / np.linalg.norm(c)
+    assert rel(r8["du"] - dy, r["du"] - dy) < 0.1
+    for e in r["dW_down"]:
+        assert rel(r8["dW_down"][e], r["dW_down"][e]) < 0.15
+        assert rel(r8["dW_gate_up"][e], r["dW_gate_up"][e]) < 0.15
+    for s in range(cfg.n_shared):
+        assert rel(r8["dWs_down"][s], r["dWs_down"][s]) < 0.15
+    assert rel(r8["dE"], r["dE"]) < 0.15
