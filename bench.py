@@ -245,14 +245,15 @@ def train_bench(args, cfg):
     from mixture_experts_layer_deepseekmoe_amd.binding import BACKWARD_STAGES, HipEvents
     from moe_workloads import make_inputs
 
-    if cfg.w_dtype != "bf16":
-        print("the training path is bf16 only", file=sys.stderr)
+    if cfg.x_dtype != "bf16" or cfg.w_dtype not in ("bf16", "e4m3"):
+        print("the training path takes bf16 activations with bf16 or e4m3 weights", file=sys.stderr)
         sys.exit(2)
+    fp8 = cfg.w_dtype == "e4m3"
     log(f"[bench] train workload {cfg.name}: generating seeded inputs")
     inp = make_inputs(cfg, 0, weights_device="cuda")
     shape = moe.LayerShape.from_config(cfg)
     u, cen, bias = (t.cuda().contiguous() for t in (inp.u, inp.centroids, inp.bias))
-    weights = moe.prepare_weights(cfg, inp)
+    weights = moe.prepare_weights(cfg, inp, train=True)
     ws = moe.alloc_train_workspace(shape)
     grads = moe.alloc_weight_grads(shape)
     y = torch.empty((cfg.T, cfg.d), dtype=torch.float32 if cfg.out_dtype == "f32" else torch.bfloat16, device="cuda")
@@ -294,32 +295,37 @@ def train_bench(args, cfg):
     routing = moe.moe_route(shape, u, cen, bias)
     counts = routing["expert_counts"].cpu().numpy()
     touched = int((counts > 0).sum()) + cfg.n_shared
-    # algorithmic flops and bytes per launch of each backward GEMM
+    # algorithmic flops and bytes per launch of each backward GEMM (operands
+    # of e bytes: 2 bf16, 1 e4m3; bf16 Dgrad outputs, fp32 weight gradients);
+    # an FP8 stage also quantises its operands (timed with it, not counted)
+    e = 1 if fp8 else 2
     gemms = {
-        "bwd_dgrad_down": (2.0 * R * d * I, touched * d * I * 2 + R * d * 2 + 2 * R * 2 * I * 2 + R * I * 2),
-        "bwd_dgrad_gate_up": (2.0 * R * 2 * I * d, touched * 2 * I * d * 2 + R * 2 * I * 2 + R * d * 2),
-        "bwd_wgrad_down": (2.0 * R * d * I, R * d * 2 + R * I * 2 + G * d * I * 4),
-        "bwd_wgrad_gate_up": (2.0 * R * 2 * I * d, R * 2 * I * 2 + R * d * 2 + G * 2 * I * d * 4),
+        "bwd_dgrad_down": (2.0 * R * d * I, touched * d * I * e + R * d * e + 2 * R * 2 * I * 2 + R * I * 2),
+        "bwd_dgrad_gate_up": (2.0 * R * 2 * I * d, touched * 2 * I * d * e + R * 2 * I * e + R * d * 2),
+        "bwd_wgrad_down": (2.0 * R * d * I, R * d * e + R * I * e + G * d * I * 4),
+        "bwd_wgrad_gate_up": (2.0 * R * 2 * I * d, R * 2 * I * e + R * d * e + G * 2 * I * d * 4),
     }
+    peak_tf = PEAK_TFLOPS["e4m3" if fp8 else "bf16"]
     lines = {}
     for name, (fl, by) in gemms.items():
         sec = stages[name] * 1e-3
         tf, gbs = fl / sec / 1e12, by / sec / 1e9
-        ridge = PEAK_TFLOPS["bf16"] * 1e12 / (PEAK_HBM_GBS * 1e9)
+        ridge = peak_tf * 1e12 / (PEAK_HBM_GBS * 1e9)
         if fl / by < ridge:
             bound, ach, pk, unit = "hbm", gbs, PEAK_HBM_GBS, "GB/s"
         else:
-            bound, ach, pk, unit = "mfma", tf, PEAK_TFLOPS["bf16"], "TFLOP/s"
+            bound, ach, pk, unit = "mfma", tf, peak_tf, "TFLOP/s"
         lines[name] = {"bound": bound, "achieved": round(ach, 2), "peak": pk, "unit": unit, "frac": round(ach / pk, 4),
                        "flops_per_launch": fl, "algorithmic_bytes_per_launch": by, "avg_launch_ms": round(stages[name], 4),
-                       "mfma_frac": round(tf / PEAK_TFLOPS["bf16"], 4), "hbm_frac": round(gbs / PEAK_HBM_GBS, 4)}
+                       "mfma_frac": round(tf / peak_tf, 4), "hbm_frac": round(gbs / PEAK_HBM_GBS, 4)}
     dominant = max(gemms, key=lambda k: stages[k])
     roofline = dict(lines[dominant], kernel=dominant, traffic=None)
     result = {
-        "metric": "MoE-layer training step tokens/sec (forward + backward, bf16), d=7168 N_r=256 K=8, 1 GPU",
+        "metric": f"MoE-layer training step tokens/sec (forward + backward, {'fp8' if fp8 else 'bf16'}), "
+                  f"d={d} N_r={cfg.n_routed} K={cfg.top_k}, 1 GPU",
         "value": round(cfg.T * args.steps / elapsed, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(elapsed / args.steps * 1e3, 4), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "scaling": "weak", "vs_baseline": None, "dtype": "e4m3" if fp8 else "bf16",
         "data": "synthetic (seeded N(0,1) activations and upstream gradient, N(0,0.006) weights, random init)",
         "config": {"workload": cfg.name, "T": cfg.T, "d": d, "n_routed": cfg.n_routed, "n_shared": cfg.n_shared,
                    "inter": I, "top_k": cfg.top_k, "parallelism": "single GPU", "step": "forward_train + backward"},
@@ -348,11 +354,12 @@ def train_cpu_baseline(cfg, inp, dy, n_tokens):
     with threadpoolctl.threadpool_limits(limits=threads):
         used = max([p.get("num_threads", 1) for p in threadpoolctl.threadpool_info()], default=1)
         t0 = time.perf_counter()
-        O.layer_backward(u, E, b, cfg.top_k, routed, cfg.n_routed, shared, dyn)
+        O.layer_backward(u, E, b, cfg.top_k, routed, cfg.n_routed, shared, dyn, fp8=cfg.w_dtype == "e4m3")
         dt = time.perf_counter() - t0
     return {"value": round(n / dt, 3), "unit": "tokens/s", "cores": used, "kind": "oracle",
             "host_cores_visible": host_cores,
-            "sample": f"first {n} of the {cfg.T} tokens, fp64 forward + backward with every weight gradient",
+            "sample": f"first {n} of the {cfg.T} tokens, fp64 forward + backward with every weight gradient"
+                      + (" (FP8 quantisation steps included)" if cfg.w_dtype == "e4m3" else ""),
             "seconds": round(dt, 2)}
 
 

@@ -109,6 +109,13 @@ typedef struct {
  *   s_down      [N_r][d/128][I/128]
  *   ss_gate_up  [N_s][2I/128][d/128]
  *   ss_down     [N_s][d/128][I/128]
+ * E4M3, moe_backward only (null otherwise): the same codes transposed, read
+ * by the FP8 Dgrad GEMMs, with their block scales transposed (a 128x128
+ * block has one scale in either orientation; moe_quantize_weight_e4m3 of the
+ * transposed matrix gives exactly these):
+ *   w_gate_up_t [N_r][d][2I]     s_gate_up_t [N_r][d/128][2I/128]
+ *   w_down_t    [N_r][I][d]      s_down_t    [N_r][I/128][d/128]
+ *   ws_gate_up_t, ws_down_t, ss_gate_up_t, ss_down_t: the shared experts'
  */
 typedef struct {
   const void* w_gate_up;
@@ -119,6 +126,14 @@ typedef struct {
   const float* s_down;
   const float* ss_gate_up;
   const float* ss_down;
+  const void* w_gate_up_t;
+  const void* w_down_t;
+  const void* ws_gate_up_t;
+  const void* ws_down_t;
+  const float* s_gate_up_t;
+  const float* s_down_t;
+  const float* ss_gate_up_t;
+  const float* ss_down_t;
 } moe_weights;
 
 /*
@@ -250,12 +265,19 @@ int moe_forward_static(const moe_shape* shape, const void* u, const void* centro
                        hipStream_t stream);
 
 /*
- * Training: the layer backward, bf16 (x_dtype = w_dtype = BF16; other dtypes
- * return MOE_ERR_UNSUPPORTED).  The report's FP8 training section (as
- * paraphrased on why-be.co.kr) names the three GEMMs of a Linear operator,
- * Fprop, Dgrad and Wgrad, and caches the inputs of the SwiGLU operator,
- * recomputing its output in the backward pass; here the GEMMs run in bf16
- * with fp32 accumulation.
+ * Training: the layer backward (x_dtype = BF16 with w_dtype = BF16 or E4M3;
+ * other dtypes return MOE_ERR_UNSUPPORTED).  The report's FP8 training
+ * section (as paraphrased on why-be.co.kr, its Figure 6 passage) runs the
+ * three GEMMs of a Linear operator, Fprop, Dgrad and Wgrad, in FP8, and
+ * caches the inputs of the SwiGLU operator, recomputing its output in the
+ * backward pass.  BF16: every GEMM in bf16 with fp32 accumulation.  E4M3:
+ * every GEMM on E4M3 operands with fp32 scales per group of 128 along its
+ * inner dimension and fp32 promotion per group -- the Dgrad inputs dY and
+ * [dG dU] in 1x128 tiles along their columns against the weights' 128x128
+ * blocks read transposed (moe_weights' *_t fields), both Wgrad operands in
+ * 128x1 tiles along the grouped rows (blocks counted from each expert's first
+ * row); the quantised tensors are the bf16 rows the backward stores.  The
+ * weight gradients are fp32 either way.
  *
  * moe_train_workspace_size: bytes of the workspace moe_forward_train and
  * moe_backward share for `shape` (more than moe_workspace_size: the cached

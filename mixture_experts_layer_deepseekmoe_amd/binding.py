@@ -46,9 +46,13 @@ class Shape(ctypes.Structure):
                  "n_groups", "topk_groups")]
 
 
+WEIGHT_FIELDS = ("w_gate_up", "w_down", "ws_gate_up", "ws_down", "s_gate_up", "s_down", "ss_gate_up", "ss_down",
+                 "w_gate_up_t", "w_down_t", "ws_gate_up_t", "ws_down_t",
+                 "s_gate_up_t", "s_down_t", "ss_gate_up_t", "ss_down_t")
+
+
 class Weights(ctypes.Structure):
-    _fields_ = [(n, ctypes.c_void_p) for n in
-                ("w_gate_up", "w_down", "ws_gate_up", "ws_down", "s_gate_up", "s_down", "ss_gate_up", "ss_down")]
+    _fields_ = [(n, ctypes.c_void_p) for n in WEIGHT_FIELDS]
 
 
 NUM_STAGES = 12
@@ -246,7 +250,8 @@ def moe_route(shape: LayerShape, u: torch.Tensor, centroids: torch.Tensor, bias:
 
 @dataclass
 class ExpertWeights:
-    """Device expert weights (bf16/f32), or e4m3 codes (uint8) plus fp32 block scales."""
+    """Device expert weights (bf16/f32), or e4m3 codes (uint8) plus fp32 block
+    scales; for the FP8 backward also the codes and scales transposed (*_t)."""
     w_gate_up: torch.Tensor
     w_down: torch.Tensor
     ws_gate_up: Optional[torch.Tensor] = None
@@ -255,11 +260,18 @@ class ExpertWeights:
     s_down: Optional[torch.Tensor] = None
     ss_gate_up: Optional[torch.Tensor] = None
     ss_down: Optional[torch.Tensor] = None
+    w_gate_up_t: Optional[torch.Tensor] = None
+    w_down_t: Optional[torch.Tensor] = None
+    ws_gate_up_t: Optional[torch.Tensor] = None
+    ws_down_t: Optional[torch.Tensor] = None
+    s_gate_up_t: Optional[torch.Tensor] = None
+    s_down_t: Optional[torch.Tensor] = None
+    ss_gate_up_t: Optional[torch.Tensor] = None
+    ss_down_t: Optional[torch.Tensor] = None
 
     def c(self) -> Weights:
         f = lambda t: None if t is None or t.numel() == 0 else _ptr(t)
-        return Weights(f(self.w_gate_up), f(self.w_down), f(self.ws_gate_up), f(self.ws_down),
-                       f(self.s_gate_up), f(self.s_down), f(self.ss_gate_up), f(self.ss_down))
+        return Weights(*[f(getattr(self, n)) for n in WEIGHT_FIELDS])
 
 
 def moe_forward(shape: LayerShape, u: torch.Tensor, centroids: torch.Tensor, bias: torch.Tensor,
@@ -310,7 +322,8 @@ def alloc_train_workspace(shape: LayerShape, device="cuda") -> torch.Tensor:
 def moe_forward_train(shape: LayerShape, u: torch.Tensor, centroids: torch.Tensor, bias: torch.Tensor,
                       weights: ExpertWeights, workspace: torch.Tensor, y: Optional[torch.Tensor] = None,
                       trace: Optional[Trace] = None) -> torch.Tensor:
-    """The forward for training (bf16): y, and in ``workspace`` what moe_backward needs."""
+    """The forward for training (bf16 activations; bf16 or e4m3 weights): y, and
+    in ``workspace`` what moe_backward needs."""
     if y is None:
         y = torch.empty((shape.T, shape.d), dtype=_TORCH_DT[DTYPE_CODE[shape.out_dtype]], device=u.device)
     rc = load_library().moe_forward_train(ctypes.byref(shape.c()), _ptr(u), _ptr(centroids), _ptr(bias),
@@ -392,22 +405,31 @@ def moe_quantize_act_e4m3(x: torch.Tensor):
     return codes, scales
 
 
-def prepare_weights(cfg, inputs) -> ExpertWeights:
-    """Device weights for moe_forward from seeded inputs (quantised on the GPU for e4m3 configs)."""
+def prepare_weights(cfg, inputs, train: bool = False) -> ExpertWeights:
+    """Device weights for moe_forward from seeded inputs (quantised on the GPU
+    for e4m3 configs).  ``train`` (e4m3): also the transposed codes and scales
+    the FP8 backward reads, quantised from the transposed matrices (the same
+    128x128 blocks)."""
     dev = torch.device("cuda")
     mv = lambda t: t.to(dev).contiguous()
     if cfg.w_dtype != "e4m3":
         return ExpertWeights(mv(inputs.w_gate_up), mv(inputs.w_down),
                              mv(inputs.ws_gate_up) if cfg.n_shared else None,
                              mv(inputs.ws_down) if cfg.n_shared else None)
-    gq, gs = moe_quantize_weight_e4m3(mv(inputs.w_gate_up))
-    dq, ds = moe_quantize_weight_e4m3(mv(inputs.w_down))
+
+    def q(t, transposed=False):
+        t = t.to(dev)
+        return moe_quantize_weight_e4m3((t.transpose(-1, -2) if transposed else t).contiguous())
+
+    names = [("w_gate_up", "s_gate_up", inputs.w_gate_up), ("w_down", "s_down", inputs.w_down)]
     if cfg.n_shared:
-        sgq, sgs = moe_quantize_weight_e4m3(mv(inputs.ws_gate_up))
-        sdq, sds = moe_quantize_weight_e4m3(mv(inputs.ws_down))
-    else:
-        sgq = sgs = sdq = sds = None
-    return ExpertWeights(gq, dq, sgq, sdq, gs, ds, sgs, sds)
+        names += [("ws_gate_up", "ss_gate_up", inputs.ws_gate_up), ("ws_down", "ss_down", inputs.ws_down)]
+    kw = {}
+    for wn, sn, t in names:
+        kw[wn], kw[sn] = q(t)
+        if train:
+            kw[wn + "_t"], kw[sn + "_t"] = q(t, True)
+    return ExpertWeights(**kw)
 
 
 class HipEvents:

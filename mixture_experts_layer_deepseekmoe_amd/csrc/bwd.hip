@@ -577,6 +577,349 @@ __global__ __launch_bounds__(THREADS, 1) void wgrad_gateup_kernel(BwdArgs a) {
   wgrad_persistent(a, a.dgu, 2 * a.inter, a.xp, a.d, a.dw_gate_up, a.dws_gate_up);
 }
 
+// ------------------------------------------------------------------ FP8 backward
+//
+// Every GEMM of the backward takes E4M3 operands with fp32 scales per group
+// of 128 along its inner dimension.  Dgrad: the 1x128 codes of dY (then of
+// [dG dU]) times the weights' codes read transposed ([N][K] arrays with the
+// same 128x128 blocks) -- the forward's FP8 row-times-weight GEMM.  Wgrad:
+// both operands tiled 128x1 along the grouped rows, stored transposed
+// ([channel][kt], group g's blocks from column koff_g) so that the GEMM reads
+// them K-contiguous; each 16x16x128 product is promoted into the fp32
+// accumulators with the row scale of A times the lane's four column scales
+// of B.
+
+__device__ __forceinline__ long long koff_of(const BwdArgs& a, int g, const GroupRows& gr) {
+  return 128LL * (gr.first / 128 + 2LL * g);
+}
+
+// SwiGLU backward on the bf16 Dgrad output dH (in hr): dG = dH U SiLU'(G),
+// dU = dH SiLU(G) into dgu, H = SiLU(G) U into hr (in place).  8 columns per
+// thread.
+__global__ __launch_bounds__(256) void swiglu_bwd_kernel(BwdArgs a) {
+  const long long idx = static_cast<long long>(blockIdx.x) * 256 + threadIdx.x;
+  const int per_row = a.inter / 8;
+  const long long r = idx / per_row;
+  if (r >= a.R) return;
+  const int c = static_cast<int>(idx - r * per_row) * 8;
+  const uint16_t* gu = a.gu + r * 2 * a.inter;
+  const uint4 dh = *reinterpret_cast<const uint4*>(a.hr + r * a.inter + c);
+  const uint4 gv = *reinterpret_cast<const uint4*>(gu + c);
+  const uint4 uv = *reinterpret_cast<const uint4*>(gu + a.inter + c);
+  const uint32_t dw[4] = {dh.x, dh.y, dh.z, dh.w}, gw[4] = {gv.x, gv.y, gv.z, gv.w}, uw[4] = {uv.x, uv.y, uv.z, uv.w};
+  uint32_t og[4], ou[4], oh[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    float dG[2], dU[2], H[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const float d = bf16_to_f32(static_cast<uint16_t>(dw[q] >> (16 * h)));
+      const float G = bf16_to_f32(static_cast<uint16_t>(gw[q] >> (16 * h)));
+      const float U = bf16_to_f32(static_cast<uint16_t>(uw[q] >> (16 * h)));
+      const float sg = sigmoid_ref(G);
+      const float silu = G * sg;
+      dG[h] = d * U * (sg * (1.0f + G * (1.0f - sg)));
+      dU[h] = d * silu;
+      H[h] = silu * U;
+    }
+    og[q] = bf16x2(dG[0], dG[1]);
+    ou[q] = bf16x2(dU[0], dU[1]);
+    oh[q] = bf16x2(H[0], H[1]);
+  }
+  uint16_t* dgu = a.dgu + r * 2 * a.inter;
+  *reinterpret_cast<uint4*>(dgu + c) = make_uint4(og[0], og[1], og[2], og[3]);
+  *reinterpret_cast<uint4*>(dgu + a.inter + c) = make_uint4(ou[0], ou[1], ou[2], ou[3]);
+  *reinterpret_cast<uint4*>(a.hr + r * a.inter + c) = make_uint4(oh[0], oh[1], oh[2], oh[3]);
+}
+
+// The group of 128-row block kb of the transposed code arrays (-1: a gap):
+// the last group whose koff is at most 128 kb, if kb falls in its blocks.
+__device__ __forceinline__ int group_of_block(const BwdArgs& a, long long kb, GroupRows& gr, int& b) {
+  int lo = 0, hi = a.n_routed + a.n_shared - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) / 2;
+    if (koff_of(a, mid, group_rows(a, mid)) <= 128 * kb) lo = mid; else hi = mid - 1;
+  }
+  gr = checked_rows(a, lo);
+  const long long k0 = koff_of(a, lo, gr) / 128;
+  if (kb < k0 || kb >= k0 + ceil_div(gr.count, 128)) return -1;
+  b = static_cast<int>(kb - k0);
+  return lo;
+}
+
+// 128x1 quantiser, transposed output: block (kb, column chunk) takes rows
+// 128 b .. 128 b + 127 of one group (b: kb's block in it; rows past the group
+// are zero) and 64 columns of src [R][C] bf16; per column, scale = amax / 448
+// and codes of x * (448 / amax) (scale 1, zero codes for an all-zero tile)
+// into dst[c][128 kb ..] and dst_s[c][kb].
+__global__ __launch_bounds__(256) void colquant_kernel(BwdArgs a, const uint16_t* __restrict__ src, int C,
+                                                       uint8_t* __restrict__ dst, float* __restrict__ dst_s) {
+  __shared__ float tile[128][65];
+  __shared__ float red[4][64];
+  GroupRows gr;
+  int b;
+  const long long kb = blockIdx.x;
+  if (group_of_block(a, kb, gr, b) < 0) return;
+  const int c0 = blockIdx.y * 64, t = threadIdx.x;
+  const int r0 = gr.first + 128 * b, nr = min(128, gr.count - 128 * b);
+  {   // 128 rows x 64 columns: thread t loads 32 columns (4 x 16 bytes) of row t / 2
+    const int rr = t >> 1, cc = (t & 1) * 32;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (rr < nr) v = *reinterpret_cast<const uint4*>(src + static_cast<size_t>(r0 + rr) * C + c0 + cc + 8 * q);
+      const uint32_t wd[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        tile[rr][cc + 8 * q + 2 * e] = bf16_to_f32(static_cast<uint16_t>(wd[e] & 0xffffu));
+        tile[rr][cc + 8 * q + 2 * e + 1] = bf16_to_f32(static_cast<uint16_t>(wd[e] >> 16));
+      }
+    }
+  }
+  __syncthreads();
+  const int c = t & 63, part = t >> 6;   // column c, rows 32 part .. 32 part + 31
+  float m = 0.f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) m = fmaxf(m, fabsf(tile[32 * part + i][c]));
+  red[part][c] = m;
+  __syncthreads();
+  m = fmaxf(fmaxf(red[0][c], red[1][c]), fmaxf(red[2][c], red[3][c]));
+  const float sc = m == 0.f ? 1.f : m / 448.f;
+  const float inv = m == 0.f ? 0.f : 448.f / m;
+  uint32_t w[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int r = 32 * part + 4 * i;
+    w[i] = e4m3x4(tile[r][c] * inv, tile[r + 1][c] * inv, tile[r + 2][c] * inv, tile[r + 3][c] * inv);
+  }
+  uint8_t* out = dst + static_cast<size_t>(c0 + c) * a.kt + 128 * kb + 32 * part;
+  *reinterpret_cast<uint4*>(out) = make_uint4(w[0], w[1], w[2], w[3]);
+  *reinterpret_cast<uint4*>(out + 16) = make_uint4(w[4], w[5], w[6], w[7]);
+  if (part == 0) dst_s[static_cast<size_t>(c0 + c) * (a.kt / 128) + kb] = sc;
+}
+
+// FP8 Wgrad tiles: 256 rows of A (M) x 128 rows of B (N), 8 MFMA waves (2 x
+// 4: 128 x 32 each) and 4 load waves; a stage is one 128-row block of the
+// group (K): A codes, B codes, A row scales, B row scales.
+constexpr int W8_BM = 256, W8_BN = 128;
+constexpr int W8_NSTG = 3;
+constexpr int W8_A = 0, W8_B = 32768, W8_AS = 49152, W8_BS = 50176;
+constexpr int W8_STB = 51200;
+constexpr int W8_NL = 8 + 4 + 2;   // DMA ops per load wave per stage
+static_assert(W8_NSTG * W8_STB <= 160 * 1024, "ring fits the LDS");
+
+struct Opnd8 {
+  rsrc_t ra, rb, rsa, rsb;
+  uint32_t oa[8], ob[4];
+  uint32_t osa, osb;
+};
+
+// A lane's byte offsets in a 16-row subtile of 128-byte rows: row lane & 15,
+// the two 16-byte chunks of K 32 (lane >> 4) .. + 31 (the swizzle depends on
+// the row modulo 16 only, so they serve every subtile).
+struct Lane8 {
+  int lo, hi;
+};
+__device__ __forceinline__ Lane8 lane8() {
+  const int lane = threadIdx.x & 63, lr = lane & 15, lg = lane >> 4;
+  return {lr * 128 + (((2 * lg) ^ swz<128>(lr)) << 4), lr * 128 + (((2 * lg + 1) ^ swz<128>(lr)) << 4)};
+}
+
+// The 32-byte fragment of the 16-row subtile at `sub` (a multiple of 16 rows).
+__device__ __forceinline__ i32x8 frag8(const uint8_t* base, int sub, Lane8 l) {
+  const i32x4 lo = *reinterpret_cast<const i32x4*>(base + sub * 128 + l.lo);
+  const i32x4 hi = *reinterpret_cast<const i32x4*>(base + sub * 128 + l.hi);
+  return i32x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+}
+
+// The load waves' operands for a tile of group g (its rows gr) at (m0, n0):
+// A = qa rows m0.., B = qb rows n0.., from column koff_g; rows past M or N
+// read past their resource (zeros).
+__device__ __forceinline__ Opnd8 opnd8(const BwdArgs& a, const uint8_t* A, const float* As, int M, const uint8_t* B,
+                                       const float* Bs, int N, long long koff, int m0, int n0) {
+  const int w = wave_id() - NMW, lane = threadIdx.x & 63;
+  const long long kt = a.kt, kbt = a.kt / 128, kb0 = koff / 128;
+  Opnd8 o;
+  o.ra = make_rsrc(A + koff, static_cast<uint32_t>(M * kt - koff));
+  o.rb = make_rsrc(B + koff, static_cast<uint32_t>(N * kt - koff));
+  o.rsa = make_rsrc(As + kb0, static_cast<uint32_t>((M * kbt - kb0) * 4));
+  o.rsb = make_rsrc(Bs + kb0, static_cast<uint32_t>((N * kbt - kb0) * 4));
+  const uint32_t far = 0x7ff00000u;   // past every resource: zeros
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const int r = 8 * (w + NLW * q) + lane / 8;
+    o.oa[q] = m0 + r < M ? static_cast<uint32_t>((m0 + r) * kt) + (((lane & 7) ^ swz<128>(r)) << 4) : far;
+  }
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int r = 8 * (w + NLW * q) + lane / 8;
+    o.ob[q] = n0 + r < N ? static_cast<uint32_t>((n0 + r) * kt) + (((lane & 7) ^ swz<128>(r)) << 4) : far;
+  }
+  const int ra = 64 * w + lane, rb = (64 * w + lane) & (W8_BN - 1);
+  o.osa = m0 + ra < M ? static_cast<uint32_t>((m0 + ra) * kbt * 4) : far;
+  o.osb = n0 + rb < N ? static_cast<uint32_t>((n0 + rb) * kbt * 4) : far;
+  return o;
+}
+
+__device__ __forceinline__ void issue8(const Opnd8& o, uint8_t* st, int ks) {
+  const int w = wave_id() - NMW;
+#pragma unroll
+  for (int q = 0; q < 8; ++q) dma16(o.ra, o.oa[q], ks * 128, st + W8_A + 1024 * (w + NLW * q));
+#pragma unroll
+  for (int q = 0; q < 4; ++q) dma16(o.rb, o.ob[q], ks * 128, st + W8_B + 1024 * (w + NLW * q));
+  dma4(o.rsa, o.osa, ks * 4, st + W8_AS + 256 * w);
+  dma4(o.rsb, o.osb, ks * 4, st + W8_BS + 256 * w);
+}
+
+// C[m][n] = sum over the group's rows r of A[r][m] B[r][n] from the 128x1
+// codes (qa: [M][kt], qb: [N][kt]), fp32 into the group's gradient.  The
+// persistent stream of the bf16 Wgrad: the load waves run into the next
+// tile's blocks while the MFMA waves store; "stage S landed" before barrier
+// #S, and barrier #S+1 frees stage S's buffer for stage S + 3.
+__device__ __forceinline__ void wgrad8_persistent(const BwdArgs& a, const uint8_t* A, const float* As, int M,
+                                                  const uint8_t* B, const float* Bs, int N, float* routed_dst,
+                                                  float* shared_dst) {
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[W8_NSTG * W8_STB];
+  const int mb_n = ceil_div(M, W8_BM), nb_n = ceil_div(N, W8_BN);
+  const long long per_g = static_cast<long long>(mb_n) * nb_n;
+  const WgradList list(a, per_g);
+  const long long ntiles = list.count();
+  const int w = wave_id(), lane = threadIdx.x & 63;
+
+  long long total = 0;
+  for (long long i = lane; i < ntiles; i += 64) {
+    const GroupRows gr = checked_rows(a, static_cast<int>(list.tile(i) / per_g));
+    total += gr.count > 0 ? ceil_div(gr.count, 128) : 0;
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) total += __shfl_xor(total, off);
+  total = static_cast<long long>(static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(total)))) |
+          static_cast<long long>(__builtin_amdgcn_readfirstlane(static_cast<int>(total >> 32))) << 32;
+
+  GroupCache gc;
+  if (w >= NMW) {
+    long long it = -1;
+    int ks = 0, nk = 0;
+    Opnd8 o{};
+    long long issued = 0;
+    auto issue_next = [&]() {
+      while (ks >= nk) {
+        ++it;
+        const long long q = list.tile(it);
+        const int g = static_cast<int>(q / per_g);
+        const int rem = static_cast<int>(q - static_cast<long long>(g) * per_g);
+        const GroupRows& gr = gc.get(a, g);
+        nk = gr.count > 0 ? ceil_div(gr.count, 128) : 0;
+        ks = 0;
+        o = opnd8(a, A, As, M, B, Bs, N, koff_of(a, g, gr), (rem / nb_n) * W8_BM, (rem % nb_n) * W8_BN);
+      }
+      issue8(o, ring + (issued % W8_NSTG) * W8_STB, ks);
+      ++ks;
+      ++issued;
+    };
+    const long long pre = min(total, 2LL);
+    for (long long s = 0; s < pre; ++s) issue_next();
+    if (pre == 2)
+      wait_vm_lgkm0<W8_NL>();   // stage 0
+    else
+      wait_vm_lgkm0<0>();
+    if (total > 0) block_barrier();   // #0
+    for (long long S = 0; S + 1 < total; ++S) {
+      if (S + 2 < total) {
+        issue_next();
+        wait_vm_lgkm0<W8_NL>();   // stage S + 1
+      } else {
+        wait_vm_lgkm0<0>();
+      }
+      block_barrier();   // #S+1
+    }
+    return;
+  }
+
+  const int wm = w % 2, wn = w / 2, lr = lane & 15, lg = lane >> 4;
+  Lane8 l8 = lane8();
+  int lsa = lr * 4, lsb = 4 * lg * 4;   // the lane's A row scale and B column scales in a stage
+  f32x4 acc[MI][2];
+  long long S = 0;
+  if (total > 0) block_barrier();   // #0
+  for (long long i = 0; i < ntiles; ++i) {
+    const long long q = list.tile(i);
+    const int g = static_cast<int>(q / per_g);
+    const int rem = static_cast<int>(q - static_cast<long long>(g) * per_g);
+    const int m0 = (rem / nb_n) * W8_BM, n0 = (rem % nb_n) * W8_BN;
+    const GroupRows& gr = gc.get(a, g);
+    const int nk = gr.count > 0 ? ceil_div(gr.count, 128) : 0;
+#pragma unroll
+    for (int ii = 0; ii < MI; ++ii) acc[ii][0] = acc[ii][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int k = 0; k < nk; ++k) {
+      // the lane constants pass through an empty asm each stage, so the
+      // per-subtile addresses stay one register plus an immediate
+      asm volatile("" : "+v"(l8.lo), "+v"(l8.hi), "+v"(lsa), "+v"(lsb));
+      const uint8_t* st = ring + (S % W8_NSTG) * W8_STB;
+      const i32x8 b0 = frag8(st + W8_B, 32 * wn, l8), b1 = frag8(st + W8_B, 32 * wn + 16, l8);
+      const f32x4 sb0 = *reinterpret_cast<const f32x4*>(st + W8_BS + 32 * wn * 4 + lsb);
+      const f32x4 sb1 = *reinterpret_cast<const f32x4*>(st + W8_BS + (32 * wn + 16) * 4 + lsb);
+      i32x8 xa = frag8(st + W8_A, 16 * wm, l8);
+      float sa = *reinterpret_cast<const float*>(st + W8_AS + 16 * wm * 4 + lsa);
+      f32x4 p0{}, p1{};
+      float psa = 0.f;
+#pragma unroll
+      for (int ii = 0; ii < MI; ++ii) {
+        i32x8 xn;
+        float sn = 0.f;
+        if (ii + 1 < MI) {   // the next row subtile's fragment, read one subtile ahead
+          xn = frag8(st + W8_A, 16 * (2 * (ii + 1) + wm), l8);
+          sn = *reinterpret_cast<const float*>(st + W8_AS + 16 * (2 * (ii + 1) + wm) * 4 + lsa);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        const f32x4 n0p = mfma_e4m3(b0, xa, f32x4{0.f, 0.f, 0.f, 0.f});
+        const f32x4 n1p = mfma_e4m3(b1, xa, f32x4{0.f, 0.f, 0.f, 0.f});
+        if (ii > 0) {   // the previous row subtile's products, while these run
+          acc[ii - 1][0] += p0 * (psa * sb0);
+          acc[ii - 1][1] += p1 * (psa * sb1);
+          // here, not sunk to the end of the stage (which would keep every
+          // product live at once)
+          asm volatile("" : "+v"(acc[ii - 1][0]), "+v"(acc[ii - 1][1]));
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        p0 = n0p;
+        p1 = n1p;
+        psa = sa;
+        if (ii + 1 < MI) {
+          xa = xn;
+          sa = sn;
+        }
+      }
+      acc[MI - 1][0] += p0 * (psa * sb0);
+      acc[MI - 1][1] += p1 * (psa * sb1);
+      ++S;
+      if (S < total) block_barrier();   // #S: this stage's buffer is free
+    }
+    float* dst = g < a.n_routed ? routed_dst + static_cast<size_t>(g) * M * N
+                                : shared_dst + static_cast<size_t>(g - a.n_routed) * M * N;
+#pragma unroll
+    for (int ii = 0; ii < MI; ++ii) {
+      const int m = m0 + 16 * (2 * ii + wm) + lr;
+      if (m >= M) continue;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int n = n0 + 32 * wn + 16 * j + 4 * lg;
+        if (n < N) *reinterpret_cast<f32x4*>(dst + static_cast<size_t>(m) * N + n) = acc[ii][j];
+      }
+    }
+  }
+}
+
+// dW_down[c][i] = sum_r dY[r][c] H[r][i]   (qa: dY codes, qb: H codes)
+__global__ __launch_bounds__(THREADS, 1) void wgrad8_down_kernel(BwdArgs a) {
+  wgrad8_persistent(a, a.qa, a.qa_s, a.d, a.qb, a.qb_s, a.inter, a.dw_down, a.dws_down);
+}
+
+// dW_gate_up[j][c] = sum_r [dG dU][r][j] X[r][c]   (qa: [dG dU] codes, qb: X codes)
+__global__ __launch_bounds__(THREADS, 1) void wgrad8_gateup_kernel(BwdArgs a) {
+  wgrad8_persistent(a, a.qa, a.qa_s, 2 * a.inter, a.qb, a.qb_s, a.d, a.dw_gate_up, a.dws_gate_up);
+}
+
 // ------------------------------------------------------------------ elementwise passes
 
 // One wave per grouped row: dY_r = g dy_t, X_r = u_t (bf16) and, for a routed
@@ -689,7 +1032,54 @@ __global__ __launch_bounds__(256) void bwd_de_kernel(BwdArgs a) {
 
 MOE_DEBUG_FILE(bwd)
 
+// FP8 stages 1-4 (a.fp8): the Dgrad GEMMs on the forward's FP8 row-times-
+// weight kernel, the Wgrad GEMMs on the 128x1 codes.
+hipError_t launch_backward_stage_fp8(int stage, const BwdArgs& a, hipStream_t s) {
+  const int R = static_cast<int>(a.R);
+  const unsigned kbt = static_cast<unsigned>(a.kt / 128);
+  hipError_t e = hipSuccess;
+  switch (stage) {
+    case 1: {   // dH = q(dY) W_down (bf16 into hr), then the SwiGLU backward
+      if (a.T == 0) break;
+      if ((e = launch_quant_act(a.dys, R, a.d, a.qr, a.qr_s, s)) != hipSuccess) return e;
+      const DownArgs da{a.qr, a.qr_s, a.n_routed, a.inter, a.d, a.w_down_t, a.ws_down_t, a.s_down_t, a.ss_down_t,
+                        a.mtiles, a.mt_count, a.max_mtiles, a.hr};
+      if ((e = launch_down(FMT_E4M3, da, s)) != hipSuccess) return e;
+      const long long n = a.R * (a.inter / 8);
+      hipLaunchKernelGGL(swiglu_bwd_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, s, a);
+      break;
+    }
+    case 2: {   // dX = q([dG dU]) W_gate_up
+      if (a.T == 0) break;
+      if ((e = launch_quant_act(a.dgu, R, 2 * a.inter, a.qr, a.qr_s, s)) != hipSuccess) return e;
+      const DownArgs da{a.qr, a.qr_s, a.n_routed, a.d, 2 * a.inter, a.w_gate_up_t, a.ws_gate_up_t, a.s_gate_up_t,
+                        a.ss_gate_up_t, a.mtiles, a.mt_count, a.max_mtiles, a.dx};
+      if ((e = launch_down(FMT_E4M3, da, s)) != hipSuccess) return e;
+      break;
+    }
+    case 3:     // dW_down from the 128x1 codes of dY and H
+      if (a.T > 0) {
+        hipLaunchKernelGGL(colquant_kernel, dim3(kbt, a.d / 64), dim3(256), 0, s, a, a.dys, a.d, a.qa, a.qa_s);
+        hipLaunchKernelGGL(colquant_kernel, dim3(kbt, a.inter / 64), dim3(256), 0, s, a, a.hr, a.inter, a.qb, a.qb_s);
+      }
+      hipLaunchKernelGGL(wgrad8_down_kernel, dim3(wgrad_grid()), dim3(THREADS), 0, s, a);
+      break;
+    case 4:     // dW_gate_up from the 128x1 codes of [dG dU] and X
+      if (a.T > 0) {
+        hipLaunchKernelGGL(colquant_kernel, dim3(kbt, 2 * a.inter / 64), dim3(256), 0, s, a, a.dgu, 2 * a.inter, a.qa,
+                           a.qa_s);
+        hipLaunchKernelGGL(colquant_kernel, dim3(kbt, a.d / 64), dim3(256), 0, s, a, a.xp, a.d, a.qb, a.qb_s);
+      }
+      hipLaunchKernelGGL(wgrad8_gateup_kernel, dim3(wgrad_grid()), dim3(THREADS), 0, s, a);
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_backward_stage(int stage, const BwdArgs& a, hipStream_t s) {
+  if (a.fp8 && stage >= 1 && stage <= 4) return launch_backward_stage_fp8(stage, a, s);
   switch (stage) {
     case 0:   // prep, dz
       if (a.T == 0) break;

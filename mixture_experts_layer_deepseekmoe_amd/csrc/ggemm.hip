@@ -153,6 +153,34 @@ __device__ __forceinline__ bool short_wave_row(int rows) {
 
 // ------------------------------------------------------------------ gate/up
 
+// Training: the SwiGLU inputs G and U of a gate/up tile (bf16, G in columns
+// 0..I-1 of a row of gu, U in I..2I-1), kept for the backward pass, which
+// recomputes H from them.  acc[i][jj] holds G and acc[i][jj + NJ/2] the
+// matching U of the wave's h columns.
+template <class P, int NSUBC, int WM, int HW>
+__device__ __forceinline__ void store_gu(const GateUpArgs& a, const f32x4 (&acc)[P::MI][P::NJ], int row0, int rows,
+                                         int n0, int wm, int wn) {
+  constexpr int NJ2 = P::NJ / 2;
+  const int lane = threadIdx.x & 63, lr = lane & 15, lg = lane >> 4;
+#pragma unroll
+  for (int i = 0; i < NSUBC; ++i) {
+    const int row = 16 * (WM * i + wm) + lr;
+    if (row < rows) {
+      uint16_t* const grow = a.gu + static_cast<size_t>(row0 + row) * 2 * a.inter;
+#pragma unroll
+      for (int jj = 0; jj < NJ2; ++jj) {
+        const int col = n0 + HW * wn + 16 * jj + 4 * lg;
+        if (col < a.inter) {
+          *reinterpret_cast<uint2*>(grow + col) =
+              pack_bf16x4(acc[i][jj][0], acc[i][jj][1], acc[i][jj][2], acc[i][jj][3]);
+          *reinterpret_cast<uint2*>(grow + a.inter + col) =
+              pack_bf16x4(acc[i][jj + NJ2][0], acc[i][jj + NJ2][1], acc[i][jj + NJ2][2], acc[i][jj + NJ2][3]);
+        }
+      }
+    }
+  }
+}
+
 template <int FMT, int NSUB, int NSUBC, class MK>
 __device__ __forceinline__ void gateup_tile(const GateUpArgs& a, const MK& make_pipe, uint8_t* const (&st)[GG<FMT>::NST],
                                             const float* swl, int kb, int nk, int row0, int rows, int n0, int nb,
@@ -170,27 +198,7 @@ __device__ __forceinline__ void gateup_tile(const GateUpArgs& a, const MK& make_
   zero_acc(acc);
   gg_mainloop<FMT, NSUB, NSUBC>(make_pipe, st, nk, wr, acc, swl, kb);
   if constexpr (FMT == FMT_BF16) {
-    // Training: the SwiGLU inputs G and U of the tile, kept (bf16) for the
-    // backward pass, which recomputes H from them.
-    if (a.gu != nullptr && w < GG<FMT>::NW) {
-#pragma unroll
-      for (int i = 0; i < NSUBC; ++i) {
-        const int row = 16 * (WM * i + wm) + lr;
-        if (row < rows) {
-          uint16_t* const grow = a.gu + static_cast<size_t>(row0 + row) * 2 * a.inter;
-#pragma unroll
-          for (int jj = 0; jj < NJ2; ++jj) {
-            const int col = n0 + HW * wn + 16 * jj + 4 * lg;
-            if (col < a.inter) {
-              *reinterpret_cast<uint2*>(grow + col) =
-                  pack_bf16x4(acc[i][jj][0], acc[i][jj][1], acc[i][jj][2], acc[i][jj][3]);
-              *reinterpret_cast<uint2*>(grow + a.inter + col) =
-                  pack_bf16x4(acc[i][jj + NJ2][0], acc[i][jj + NJ2][1], acc[i][jj + NJ2][2], acc[i][jj + NJ2][3]);
-            }
-          }
-        }
-      }
-    }
+    if (a.gu != nullptr && w < GG<FMT>::NW) store_gu<P, NSUBC, WM, HW>(a, acc, row0, rows, n0, wm, wn);
     // H tile (rows x 128 columns, bf16) through LDS; every wave stores
     constexpr int PITCH = GG_HCOLS * 2 + 16;   // padded rows: the 16 rows of a subtile hit different banks
     static_assert(GG<FMT>::BM * PITCH <= GG<FMT>::NST * P::STAGE_BYTES, "output tile fits the stage ring");
@@ -251,6 +259,7 @@ __device__ __forceinline__ void gateup_tile(const GateUpArgs& a, const MK& make_
     // lane groups, then the two waves (wn = 0, 1) that share the row.
     float hv[NSUBC][NJ2][4];
     const bool mw = w < 4;   // an MFMA wave
+    if (mw && a.gu != nullptr) store_gu<P, NSUBC, WM, HW>(a, acc, row0, rows, n0, wm, wn);
     if (mw) {
 #pragma unroll
       for (int i = 0; i < NSUBC; ++i) {

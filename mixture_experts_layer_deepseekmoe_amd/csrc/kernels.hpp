@@ -91,7 +91,7 @@ struct GateUpArgs {
   int max_mtiles;
   void* h;                // [R][I]: f32 / bf16 / e4m3 codes
   float* h_scale;         // e4m3: [R][I/128]
-  uint16_t* gu;           // bf16 training only: [R][2I] the SwiGLU inputs G (columns 0..I-1) and U; else null
+  uint16_t* gu;           // training only: [R][2I] the SwiGLU inputs G (columns 0..I-1) and U, bf16; else null
 };
 
 struct DownArgs {
@@ -156,7 +156,32 @@ struct BwdArgs {
   float* dw_down;                 // [N_r][d][I]
   float* dws_gate_up;             // [N_s][2I][d]
   float* dws_down;                // [N_s][d][I]
+  // FP8 backward (e4m3 weights; zero / null otherwise).  The weights' codes
+  // transposed (the same 128x128 blocks, so the scales are transposed too):
+  int fp8;
+  const void* w_gate_up_t;        // [N_r][d][2I] e4m3
+  const void* w_down_t;           // [N_r][I][d]
+  const void* ws_gate_up_t;       // [N_s][d][2I]
+  const void* ws_down_t;          // [N_s][I][d]
+  const float* s_gate_up_t;       // [N_r][d/128][2I/128]
+  const float* s_down_t;          // [N_r][I/128][d/128]
+  const float* ss_gate_up_t;
+  const float* ss_down_t;
+  uint8_t* qr;                    // [R][max(d, 2I)] 1x128 codes of a Dgrad input: dY, then [dG dU]
+  float* qr_s;                    // [R][max(d, 2I)/128]
+  long long kt;                   // columns of the transposed 128x1 codes (wgrad8_kt)
+  uint8_t* qa;                    // [max(d, 2I)][kt] Wgrad operand A, 128x1 codes transposed: dY, then [dG dU]
+  float* qa_s;                    // [max(d, 2I)][kt/128]
+  uint8_t* qb;                    // [max(I, d)][kt] Wgrad operand B: H, then X
+  float* qb_s;                    // [max(I, d)][kt/128]
 };
+
+// FP8 Wgrad: group g's 128-row blocks of 128x1 codes, transposed, start at
+// column koff_g = 128 (floor(first_g / 128) + 2 g) of the [channel][kt] code
+// arrays (first_g: the group's first grouped row).  Consecutive groups start
+// at least ceil(rows_g / 128) + 1 blocks apart, so each has room for its
+// blocks; kt covers the last one.
+inline long long wgrad8_kt(long long R, int n_groups) { return 128 * ((R + 127) / 128 + 2LL * n_groups + 1); }
 
 hipError_t launch_route(int fmt, const RouteArgs& a, hipStream_t s);
 // The backward in six stages, launched in order 0..5: prep and dz; Dgrad of

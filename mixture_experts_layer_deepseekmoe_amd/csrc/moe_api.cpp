@@ -32,7 +32,11 @@ int fmt_of(int dt) { return dt == MOE_DTYPE_F32 ? FMT_F32 : (dt == MOE_DTYPE_BF1
 struct Layout {
   size_t hist, idx, gate, counts, offsets, perm, pos, mtiles, mtcount, uq, us, h, hs, y, scores, total;
   // training (moe_forward_train / moe_backward) only, after `total`
-  size_t sel, gu, dys, xp, dgu, dx, dg, dz, dzr, total_train;
+  size_t sel, gu, dys, xp, dgu, dx, dg, dz, dzr;
+  size_t qr, qr_s, qa, qa_s, qb, qb_s;   // FP8 backward only (0 bytes otherwise)
+  size_t hr;                             // FP8: bf16 H rows (the forward's H holds e4m3 codes)
+  size_t total_train;
+  long long kt;                          // columns of the FP8 Wgrad codes
   int nblk, max_mt;
   long long rows;   // grouped rows: T*K routed + N_s*T shared
 };
@@ -72,6 +76,19 @@ Layout make_layout(const moe_shape& s) {
   L.dg = take(TK * 4);
   L.dz = take(TK * 4);
   L.dzr = take(TK * 4);
+  {
+    const size_t dmax = static_cast<size_t>(s.d > 2 * s.inter ? s.d : 2 * s.inter);
+    const size_t bmax = static_cast<size_t>(s.d > s.inter ? s.d : s.inter);
+    L.kt = fp8 ? moe::wgrad8_kt(L.rows, s.n_routed + s.n_shared) : 0;
+    const size_t kt = static_cast<size_t>(L.kt);
+    L.qr = take(fp8 ? R * dmax : 0);
+    L.qr_s = take(fp8 ? R * (dmax / 128) * 4 : 0);
+    L.qa = take(dmax * kt);
+    L.qa_s = take(dmax * (kt / 128) * 4);
+    L.qb = take(bmax * kt);
+    L.qb_s = take(bmax * (kt / 128) * 4);
+    L.hr = take(fp8 ? R * s.inter * 2 : 0);
+  }
   L.total_train = o;
   return L;
 }
@@ -80,6 +97,23 @@ Layout make_layout(const moe_shape& s) {
 // kernels get n_groups = topk_groups = 1 (global top-K).
 int groups_of(const moe_shape& s) { return s.n_groups > 1 && s.topk_groups < s.n_groups ? s.n_groups : 1; }
 int topk_groups_of(const moe_shape& s) { return s.n_groups > 1 && s.topk_groups < s.n_groups ? s.topk_groups : 1; }
+
+int validate_shape(const moe_shape* s);
+
+// The training entry points: bf16 activations with bf16 or E4M3 weights.
+// FP8: the Wgrad code arrays ([channel][kt], byte offsets in 32 bits, with
+// room past them for the loads of padding rows) must fit.
+int validate_train(const moe_shape& s) {
+  if (s.x_dtype != MOE_DTYPE_BF16 || (s.w_dtype != MOE_DTYPE_BF16 && s.w_dtype != MOE_DTYPE_E4M3))
+    return MOE_ERR_UNSUPPORTED;
+  if (s.w_dtype == MOE_DTYPE_E4M3) {
+    const long long R = static_cast<long long>(s.T) * (s.top_k + s.n_shared);
+    const long long kt = moe::wgrad8_kt(R, s.n_routed + s.n_shared);
+    const long long cmax = s.d > 2LL * s.inter ? s.d : 2LL * s.inter;
+    if (cmax * kt >= 0x7ff00000LL) return MOE_ERR_UNSUPPORTED;
+  }
+  return MOE_OK;
+}
 
 int validate_shape(const moe_shape* s) {
   if (s == nullptr) return MOE_ERR_INVALID_ARG;
@@ -396,7 +430,8 @@ int moe_train_workspace_size(const moe_shape* shape, size_t* bytes) {
   if (bytes == nullptr) return MOE_ERR_INVALID_ARG;
   const int rc = validate_shape(shape);
   if (rc != MOE_OK) return rc;
-  if (shape->x_dtype != MOE_DTYPE_BF16 || shape->w_dtype != MOE_DTYPE_BF16) return MOE_ERR_UNSUPPORTED;
+  const int rt = validate_train(*shape);
+  if (rt != MOE_OK) return rt;
   *bytes = make_layout(*shape).total_train;
   return MOE_OK;
 }
@@ -406,7 +441,8 @@ int moe_forward_train(const moe_shape* shape, const void* u, const void* centroi
                       hipStream_t stream) {
   const int rc = validate_forward(shape, u, centroids, bias, wt, y);
   if (rc != MOE_OK) return rc;
-  if (shape->x_dtype != MOE_DTYPE_BF16 || shape->w_dtype != MOE_DTYPE_BF16) return MOE_ERR_UNSUPPORTED;
+  const int rt = validate_train(*shape);
+  if (rt != MOE_OK) return rt;
   const Layout L = make_layout(*shape);
   if (workspace == nullptr || workspace_bytes < L.total_train) return MOE_ERR_WORKSPACE;
   return debug_status(run_forward(*shape, L, u, centroids, bias, wt, y, nullptr, workspace, trace, stream, true),
@@ -419,8 +455,16 @@ int moe_backward(const moe_shape* shape, const void* u, const void* centroids, c
   const int rc = validate_shape(shape);
   if (rc != MOE_OK) return rc;
   const moe_shape& s = *shape;
-  if (s.x_dtype != MOE_DTYPE_BF16 || s.w_dtype != MOE_DTYPE_BF16) return MOE_ERR_UNSUPPORTED;
+  const int rt = validate_train(s);
+  if (rt != MOE_OK) return rt;
+  const bool fp8 = s.w_dtype == MOE_DTYPE_E4M3;
   if (wt == nullptr || grads == nullptr || centroids == nullptr || dcentroids == nullptr) return MOE_ERR_INVALID_ARG;
+  if (fp8 && (wt->w_gate_up_t == nullptr || wt->w_down_t == nullptr || wt->s_gate_up_t == nullptr ||
+              wt->s_down_t == nullptr || !aligned16(wt->w_gate_up_t) || !aligned16(wt->w_down_t) ||
+              (s.n_shared > 0 && (wt->ws_gate_up_t == nullptr || wt->ws_down_t == nullptr ||
+                                  wt->ss_gate_up_t == nullptr || wt->ss_down_t == nullptr ||
+                                  !aligned16(wt->ws_gate_up_t) || !aligned16(wt->ws_down_t)))))
+    return MOE_ERR_INVALID_ARG;
   if (s.T > 0 && (u == nullptr || dy == nullptr || du == nullptr || !aligned16(u) || !aligned16(dy) || !aligned16(du)))
     return MOE_ERR_INVALID_ARG;
   if (wt->w_gate_up == nullptr || wt->w_down == nullptr || grads->dw_gate_up == nullptr || grads->dw_down == nullptr ||
@@ -464,7 +508,8 @@ int moe_backward(const moe_shape* shape, const void* u, const void* centroids, c
   a.dys = at<uint16_t>(workspace, L.dys);
   a.xp = at<uint16_t>(workspace, L.xp);
   a.dgu = at<uint16_t>(workspace, L.dgu);
-  a.hr = at<uint16_t>(workspace, L.h);   // the forward's H is not needed any more: H is recomputed into it
+  // the forward's H is not needed any more: bf16, H is recomputed into it
+  a.hr = at<uint16_t>(workspace, s.w_dtype == MOE_DTYPE_E4M3 ? L.hr : L.h);
   a.dx = at<uint16_t>(workspace, L.dx);
   a.dg = at<float>(workspace, L.dg);
   a.dz = at<float>(workspace, L.dz);
@@ -475,6 +520,24 @@ int moe_backward(const moe_shape* shape, const void* u, const void* centroids, c
   a.dw_down = grads->dw_down;
   a.dws_gate_up = grads->dws_gate_up;
   a.dws_down = grads->dws_down;
+  if (fp8) {
+    a.fp8 = 1;
+    a.w_gate_up_t = wt->w_gate_up_t;
+    a.w_down_t = wt->w_down_t;
+    a.ws_gate_up_t = wt->ws_gate_up_t;
+    a.ws_down_t = wt->ws_down_t;
+    a.s_gate_up_t = wt->s_gate_up_t;
+    a.s_down_t = wt->s_down_t;
+    a.ss_gate_up_t = wt->ss_gate_up_t;
+    a.ss_down_t = wt->ss_down_t;
+    a.qr = at<uint8_t>(workspace, L.qr);
+    a.qr_s = at<float>(workspace, L.qr_s);
+    a.kt = L.kt;
+    a.qa = at<uint8_t>(workspace, L.qa);
+    a.qa_s = at<float>(workspace, L.qa_s);
+    a.qb = at<uint8_t>(workspace, L.qb);
+    a.qb_s = at<float>(workspace, L.qb_s);
+  }
   Stages stg{trace, stream};
   for (int st = 0; st < moe::BWD_STAGES; ++st) {
     stg.begin(MOE_STAGE_BWD_PREP + st);

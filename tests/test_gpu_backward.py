@@ -15,6 +15,16 @@ the router's ds is a difference that can cancel).  Experts that no token
 selected must get exactly zero.  The oracle
 adopts the GPU's expert selection (its own routing is checked by the
 forward tests).
+
+FP8 (e4m3 weights): the oracle runs the same FP8 backward (the same tiles
+and codes from the same bf16 rows), so the two sides differ where a bf16 row
+they quantise differs by an ulp (the GPU's dH is rounded to bf16 before the
+SwiGLU backward, the oracle's is exact) and the element sits near an E4M3
+rounding boundary: a one-ulp move (2^-8) crosses one of the 2^-3-spaced
+boundaries with probability ~2^-5, so ~3% of such elements move by one code
+(relative 2^-3; normwise ~sqrt(0.03) 2^-3 / sqrt(3) ~ 1.3%), and three
+quantised operands lie in series on the longest path (dY -> [dG dU] -> dX);
+the bound is 4e-2 per block.
 """
 
 import numpy as np
@@ -29,6 +39,7 @@ from tests.parity import check_routing, expert_fns, say
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
 TOL = 1e-2
+TOL8 = 4e-2
 
 
 def _maxrel(got: np.ndarray, ref: np.ndarray) -> float:
@@ -93,7 +104,7 @@ def _dy(cfg):
 def _train_step(cfg, inp, dy, weights=None):
     shape = moe.LayerShape.from_config(cfg)
     u, E, b = (t.to(DEV).contiguous() for t in (inp.u, inp.centroids, inp.bias))
-    w = moe.prepare_weights(cfg, inp) if weights is None else weights
+    w = moe.prepare_weights(cfg, inp, train=True) if weights is None else weights
     ws = moe.alloc_train_workspace(shape)
     y = moe.moe_forward_train(shape, u, E, b, w, ws)
     du, dE, grads = moe.moe_backward(shape, u, E, w, dy.to(DEV).contiguous(), ws)
@@ -104,7 +115,8 @@ def _train_step(cfg, inp, dy, weights=None):
 def _compare(cfg, inp, dy_t, du, dE, grads, gi):
     u, E, b = to_numpy_f32(inp.u), to_numpy_f32(inp.centroids), inp.bias.numpy()
     routed, shared = expert_fns(inp, False)
-    ref = O.layer_backward(u, E, b, cfg.top_k, routed, cfg.n_routed, shared, dy_t.numpy(), selection=gi)
+    ref = O.layer_backward(u, E, b, cfg.top_k, routed, cfg.n_routed, shared, dy_t.numpy(), selection=gi,
+                           fp8=cfg.w_dtype == "e4m3")
     errs = {"du": _err(du.cpu().numpy(), ref["du"], 1, du.shape[1]),
             "dE": _de_err(dE.cpu().numpy(), ref, u, E, cfg.n_routed)}
     say("  max|d|/rms (information): du %.2e dE %.2e" % (_maxrel(du.cpu().numpy(), ref["du"]),
@@ -234,4 +246,72 @@ def test_backward_full_d7168_sampled():
     for k, v in errs.items():
         assert v <= TOL, (k, v)
     del w, ws, grads, inp
+    torch.cuda.empty_cache()
+
+
+# ------------------------------------------------------------------ FP8 backward
+
+FP8_CASES = {
+    "small_fp8": PARITY_CONFIGS["small_fp8"],
+    "small_fp8_ns2": PARITY_CONFIGS["small_fp8_ns2"],
+    "small_fp8_ns0": PARITY_CONFIGS["small_fp8_ns2"].replace(name="small_fp8_ns0", n_shared=0),
+}
+
+
+@pytest.mark.parametrize("name", list(FP8_CASES))
+def test_backward_fp8_parity(name):
+    """The FP8 backward (every GEMM on E4M3 operands) against the oracle's."""
+    cfg = FP8_CASES[name]
+    say(f"case: FP8 moe_forward_train + moe_backward {name}")
+    inp = make_inputs(cfg, 0)
+    dy = _dy(cfg)
+    y, du, dE, grads, ws, w = _train_step(cfg, inp, dy)
+    shape = moe.LayerShape.from_config(cfg)
+    u, E, b = (t.to(DEV).contiguous() for t in (inp.u, inp.centroids, inp.bias))
+    routing = moe.alloc_routing(shape)
+    y_inf = moe.moe_forward(shape, u, E, b, w, routing=routing)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y_inf)
+    errs, empty = _compare(cfg, inp, dy, du, dE, grads, routing["topk_idx"].cpu().numpy())
+    say("  worst block ||d||/||ref||: " + ", ".join(f"{k} {v:.2e}" for k, v in errs.items()) + f"; {empty} experts without rows")
+    for k, v in errs.items():
+        assert v <= TOL8, (k, v)
+
+
+def test_backward_fp8_transposed_weights_and_determinism():
+    """The transposed codes the FP8 Dgrad reads are the forward's codes
+    transposed (one scale per 128x128 block in either orientation), and two
+    FP8 training steps give bit-identical gradients."""
+    cfg = PARITY_CONFIGS["small_fp8_ns2"]
+    say("case: FP8 transposed weight codes, determinism")
+    inp = make_inputs(cfg, 0)
+    dy = _dy(cfg)
+    _, du1, dE1, g1, _, w = _train_step(cfg, inp, dy)
+    for a, b in ((w.w_gate_up, w.w_gate_up_t), (w.w_down, w.w_down_t), (w.ws_gate_up, w.ws_gate_up_t),
+                 (w.ws_down, w.ws_down_t), (w.s_gate_up, w.s_gate_up_t), (w.s_down, w.s_down_t)):
+        assert torch.equal(a.transpose(-1, -2), b)
+    _, du2, dE2, g2, _, _ = _train_step(cfg, inp, dy, w)
+    assert torch.equal(du1, du2) and torch.equal(dE1, dE2)
+    for a, b in ((g1.dw_gate_up, g2.dw_gate_up), (g1.dw_down, g2.dw_down), (g1.dws_gate_up, g2.dws_gate_up),
+                 (g1.dws_down, g2.dws_down)):
+        assert torch.equal(a, b)
+
+
+def test_backward_fp8_full_d2048():
+    """The FP8 d = 2048 layer (T = 4096, 64 + 2 experts, K = 6; every expert
+    spans several 128-row m-tiles and Wgrad blocks) in full: every gradient."""
+    cfg = CONFIGS["fp8_d2048"]
+    say("case: FP8 moe_backward fp8_d2048 full size, every gradient")
+    inp = make_inputs(cfg, 0)
+    dy = _dy(cfg)
+    y, du, dE, grads, ws, w = _train_step(cfg, inp, dy)
+    shape = moe.LayerShape.from_config(cfg)
+    u, E, b = (t.to(DEV).contiguous() for t in (inp.u, inp.centroids, inp.bias))
+    routing = moe.moe_route(shape, u, E, b)
+    torch.cuda.synchronize()
+    errs, empty = _compare(cfg, inp, dy, du, dE, grads, routing["topk_idx"].cpu().numpy())
+    say("  worst block ||d||/||ref||: " + ", ".join(f"{k} {v:.2e}" for k, v in errs.items()))
+    for k, v in errs.items():
+        assert v <= TOL8, (k, v)
+    del w, ws, grads
     torch.cuda.empty_cache()
