@@ -42,7 +42,8 @@ Readings taken where the pages are silent:
   so the Dgrad activations (dY, [dG dU]) take 1x128 tiles along their
   columns, both Wgrad operands take 128x1 tiles along the rows (counted from
   each expert's first grouped row), and the weights keep their 128x128
-  blocks.  Tensors are quantised from the bf16 rows the kernels store.
+  blocks.  Every row between two GEMMs (the cached G and U, dY, dH,
+  [dG dU], H, x) is bf16, and each tensor is quantised from those values.
 
 Everything is fp64 except where a reading fixes fp32 (scales, the bias).
 """
@@ -493,18 +494,19 @@ def swiglu_ffn_backward_fp8(x: np.ndarray, x_deq: np.ndarray, wgu_q, wgu_s, wd_q
         Wgrad  dW_down = q(dout)^T q(H)           both tiled 128x1 along the
                dW_gate_up = q([dG dU])^T q(x)     rows, from the group's first
     The weights keep their forward 128x128 blocks (read transposed).  G and U
-    are the FP8 forward's products from the dequantised input x_deq (the
-    cached SwiGLU inputs); H = SiLU(G) U is recomputed.  Every tensor is
-    quantised from bf16 (dout, [dG dU], H and x are the bf16 rows the
-    kernels store before quantising them)."""
+    are the FP8 forward's products from the dequantised input x_deq, cached
+    as bf16 (the cached SwiGLU inputs); H = SiLU(G) U is recomputed.  Every
+    row between two GEMMs is bf16 (dout, the Dgrad output dH, [dG dU], H and
+    x), so each quantiser decides its codes from the bf16 values the kernels
+    store."""
     wgu = dequantize_weight(wgu_q, wgu_s)
     wd = dequantize_weight(wd_q, wd_s)
     I = wgu.shape[0] // 2
     x_deq = np.asarray(x_deq, F64)
-    G = x_deq @ wgu[:I].T
-    U = x_deq @ wgu[I:].T
+    G = round_bf16(x_deq @ wgu[:I].T)
+    U = round_bf16(x_deq @ wgu[I:].T)
     dout_b = round_bf16(dout)
-    dH = dequantize_act(*quantize_act_1x128(dout_b)) @ wd
+    dH = round_bf16(dequantize_act(*quantize_act_1x128(dout_b)) @ wd)
     dG = dH * U * silu_grad(G)
     dU = dH * silu(G)
     dGU_b = round_bf16(np.concatenate([dG, dU], axis=1))

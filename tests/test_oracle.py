@@ -717,9 +717,11 @@ def _torch_fp8_expert_backward(x, wgu, wd, dout, slip=None):
     I = g.shape[0] // 2
     xq = _tq_act(x32)
     G, U = xq @ g[:I].T, xq @ g[I:].T
+    if slip != "cache_not_bf16":
+        G, U = bf(G), bf(U)
     do = torch.from_numpy(np.asarray(dout, np.float64))
     do_b = do if slip == "no_bf16_before_quantising" else bf(do)
-    dH = _tq_act(do_b.to(torch.float32)) @ dn
+    dH = bf(_tq_act(do_b.to(torch.float32)) @ dn)
     sg = torch.sigmoid(G)
     dG, dU = dH * U * sg * (1 + G * (1 - sg)), dH * torch.nn.functional.silu(G)
     dGU = bf(torch.cat([dG, dU], dim=1))
@@ -752,7 +754,7 @@ def test_fp8_expert_backward_pinned_to_torch_fp8():
     for key in ("dx", "dW_gate_up", "dW_down"):
         np.testing.assert_allclose(got[key], ref[key], rtol=1e-11, atol=1e-11 * np.abs(ref[key]).max())
     for slip, key in (("no_bf16_before_quantising", "dx"), ("wgrad_tiles_along_columns", "dW_down"),
-                      ("wgrad_x_from_forward_codes", "dW_gate_up")):
+                      ("wgrad_x_from_forward_codes", "dW_gate_up"), ("cache_not_bf16", "dW_down")):
         bad = _torch_fp8_expert_backward(x, wgu, wd, dout, slip)
         assert np.abs(bad[key] - got[key]).max() > 1e-6 * np.abs(got[key]).max(), slip
 
