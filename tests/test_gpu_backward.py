@@ -16,15 +16,14 @@ selected must get exactly zero.  The oracle
 adopts the GPU's expert selection (its own routing is checked by the
 forward tests).
 
-FP8 (e4m3 weights): the oracle runs the same FP8 backward (the same tiles
-and codes from the same bf16 rows), so the two sides differ where a bf16 row
-they quantise differs by an ulp (the GPU's dH is rounded to bf16 before the
-SwiGLU backward, the oracle's is exact) and the element sits near an E4M3
-rounding boundary: a one-ulp move (2^-8) crosses one of the 2^-3-spaced
-boundaries with probability ~2^-5, so ~3% of such elements move by one code
-(relative 2^-3; normwise ~sqrt(0.03) 2^-3 / sqrt(3) ~ 1.3%), and three
-quantised operands lie in series on the longest path (dY -> [dG dU] -> dX);
-the bound is 4e-2 per block.
+FP8 (e4m3 weights): the oracle runs the same FP8 backward -- the same
+tiles, and codes decided from the same bf16 rows (the cached G and U, dY,
+dH, [dG dU], H, x are bf16 on both sides) -- so a code differs only where
+the GPU's fp32 and the oracle's fp64 evaluation of a row land on different
+bf16 values (relative error ~1e-6 against a bf16 spacing of 2^-8: about one
+element in 4000) and that element then crosses an E4M3 boundary.  Such flips
+are rare and the rest is the fp32 accumulation and the bf16 outputs, as in
+the bf16 backward, so the same bound of 1e-2 per block applies.
 """
 
 import numpy as np
@@ -39,7 +38,7 @@ from tests.parity import check_routing, expert_fns, say
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
 TOL = 1e-2
-TOL8 = 4e-2
+TOL8 = 1e-2
 
 
 def _maxrel(got: np.ndarray, ref: np.ndarray) -> float:
