@@ -1,7 +1,7 @@
 """The bounds-checked build (-DMOE_DEBUG, libmoe_mi355x_debug.so): every
 index check passes on the whole path -- routing (also with NaN tokens and
 with group-limited routing), grouping, the grouped GEMMs at every size the
-other tests use, the combine, the backward -- and the results equal the
+other tests use, the combine, the backward (bf16 and FP8) -- and the results equal the
 release build's bit for bit (the checks only guard accesses)."""
 
 import numpy as np
@@ -85,12 +85,12 @@ def test_debug_build_all_tokens_on_k_experts_and_nan_tokens():
     torch.cuda.empty_cache()
 
 
-@pytest.mark.parametrize("name", ["small_bf16_ns2", "bf16_d2048"])
+@pytest.mark.parametrize("name", ["small_bf16_ns2", "bf16_d2048", "small_fp8_ns2", "fp8_d2048"])
 def test_debug_build_backward(name):
     cfg = (PARITY_CONFIGS.get(name) or CONFIGS[name])
     say(f"case: debug build, moe_forward_train + moe_backward {name}")
     inp = make_inputs(cfg, 0)
-    w = moe.prepare_weights(cfg, inp)
+    w = moe.prepare_weights(cfg, inp, train=True)
     shape = moe.LayerShape.from_config(cfg)
     g = torch.Generator().manual_seed(5)
     dy = torch.randn((cfg.T, cfg.d), generator=g).to(DEV)
