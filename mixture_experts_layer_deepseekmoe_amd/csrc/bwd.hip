@@ -437,7 +437,9 @@ struct GroupCache {
 // (rows r of M and N bf16), written as fp32 into the group's gradient.
 __device__ __forceinline__ void wgrad_persistent(const BwdArgs& a, const uint16_t* A, int M, const uint16_t* B,
                                                  int N, float* routed_dst, float* shared_dst) {
-  __shared__ __attribute__((aligned(1024))) uint8_t ring[NSTG * STB];
+  // 4 stage buffers, then 4 KB of store staging per MFMA wave (160 KB in all)
+  constexpr int WN = 4;
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[WN * STB + NMW * 4096];
   const int mb_n = ceil_div(M, BT), nb_n = ceil_div(N, BT);
   const long long per_g = static_cast<long long>(mb_n) * nb_n;
   const WgradList list(a, per_g);
@@ -460,7 +462,7 @@ __device__ __forceinline__ void wgrad_persistent(const BwdArgs& a, const uint16_
 
   GroupCache gc;
   if (w >= NMW) {
-    // ---- load waves: issue the stream NSTG - 1 stages ahead of the MFMAs
+    // ---- load waves: issue the stream WN - 1 stages ahead of the MFMAs
     long long it = -1;        // tile of the next stage to issue
     int ks = 0, nk = 0;       // that stage's K-step within it, and its K-steps
     Opnd oa{}, ob{};
@@ -479,21 +481,21 @@ __device__ __forceinline__ void wgrad_persistent(const BwdArgs& a, const uint16_
         ob = opnd_ko(make_rsrc(reinterpret_cast<const uint8_t*>(B) + static_cast<size_t>(gr.first) * ldb,
                                gr.count * ldb), ldb, (rem % nb_n) * BT);
       }
-      issue_stage(oa, ob, ring + (issued % NSTG) * STB, ks);
+      issue_stage(oa, ob, ring + (issued % WN) * STB, ks);
       ++ks;
       ++issued;
     };
-    const long long pre = min(total, static_cast<long long>(NSTG - 1));
+    const long long pre = min(total, static_cast<long long>(WN - 1));
     for (long long s = 0; s < pre; ++s) issue_next();
-    if (pre == NSTG - 1)
-      wait_vm_lgkm0<(NSTG - 3) * NLS>();   // stages 0 and 1
+    if (pre == WN - 1)
+      wait_vm_lgkm0<(WN - 3) * NLS>();   // stages 0 and 1
     else
       wait_vm_lgkm0<0>();
     for (long long S = 0; S < total; ++S) {
       block_barrier();
-      if (S + NSTG - 1 < total) {
+      if (S + WN - 1 < total) {
         issue_next();
-        wait_vm_lgkm0<(NSTG - 3) * NLS>();   // stage S + 2
+        wait_vm_lgkm0<(WN - 3) * NLS>();   // stage S + 2
       } else {
         wait_vm_lgkm0<0>();
       }
@@ -518,7 +520,7 @@ __device__ __forceinline__ void wgrad_persistent(const BwdArgs& a, const uint16_
     zero_acc(acc);
     if (nk > 0) {
       {   // the tile's first stage (landed: this wave passed barrier #S)
-        const uint8_t* st = ring + (S % NSTG) * STB;
+        const uint8_t* st = ring + (S % WN) * STB;
 #pragma unroll
         for (int j = 0; j < NJ; ++j) wf[j] = frag_ko(st + OPB, 64 * wn + 16 * j, kl);
         xf = frag_ko(st, 16 * wm, kl);
@@ -526,8 +528,8 @@ __device__ __forceinline__ void wgrad_persistent(const BwdArgs& a, const uint16_
       acc_fence(acc);
       for (int k = 0; k < nk; ++k) {
         asm volatile("" : "+v"(kl.base), "+v"(kl.y));
-        const uint8_t* sa = ring + (S % NSTG) * STB;
-        const uint8_t* na = ring + ((S + 1) % NSTG) * STB;
+        const uint8_t* sa = ring + (S % WN) * STB;
+        const uint8_t* na = ring + ((S + 1) % WN) * STB;
 #pragma unroll
         for (int ii = 0; ii < MI; ++ii) {
           i32x4 xn;
@@ -552,16 +554,37 @@ __device__ __forceinline__ void wgrad_persistent(const BwdArgs& a, const uint16_
     }
     float* dst = g < a.n_routed ? routed_dst + static_cast<size_t>(g) * M * N
                                 : shared_dst + static_cast<size_t>(g - a.n_routed) * M * N;
+    {
+      // each 16-row subtile through the wave's 4 KB of staging: written as
+      // the accumulators hold it (row lane & 15, 16-byte chunks 4 j + lane >> 4,
+      // chunk positions xor-ed with the row), read back 4 rows x 256 bytes per
+      // store instruction, so every store writes whole 128-byte lines, and
+      // streamed past the caches (non-temporal): the gradient is not read
+      // again here, and the group's operand rows stay in L2 for its other
+      // tiles.  (64-byte pieces straight from the accumulators left the two
+      // halves of each line to merge in L2, which the operands then lost.)
+      uint8_t* sg = ring + WN * STB + 4096 * w;
+      const int lr = lane & 15, lg = lane >> 4;
 #pragma unroll
-    for (int ii = 0; ii < MI; ++ii) {
-      const int m = m0 + 16 * (2 * ii + wm) + (lane & 15);
-      if (m >= M) continue;
+      for (int ii = 0; ii < MI; ++ii) {
 #pragma unroll
-      for (int j = 0; j < NJ; ++j) {
-        const int n = n0 + 64 * wn + 16 * j + 4 * (lane >> 4);
-        if (n < N)
-          *reinterpret_cast<float4*>(dst + static_cast<size_t>(m) * N + n) =
-              make_float4(acc[ii][j][0], acc[ii][j][1], acc[ii][j][2], acc[ii][j][3]);
+        for (int j = 0; j < NJ; ++j)
+          *reinterpret_cast<f32x4*>(sg + lr * 256 + (((4 * j + lg) ^ lr) << 4)) = acc[ii][j];
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int rr = 4 * q + (lane >> 4), c = lane & 15;
+          const f32x4 v = *reinterpret_cast<const f32x4*>(sg + rr * 256 + ((c ^ rr) << 4));
+          const int m = m0 + 16 * (2 * ii + wm) + rr, n = n0 + 64 * wn + 4 * c;
+          if (m < M && n < N) {
+            __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(dst + static_cast<size_t>(m) * N + n));
+          }
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
       }
     }
   }
@@ -706,7 +729,7 @@ constexpr int W8_NSTG = 3;
 constexpr int W8_A = 0, W8_B = 32768, W8_AS = 49152, W8_BS = 50176;
 constexpr int W8_STB = 51200;
 constexpr int W8_NL = 8 + 4 + 2;   // DMA ops per load wave per stage
-static_assert(W8_NSTG * W8_STB <= 160 * 1024, "ring fits the LDS");
+static_assert(W8_NSTG * W8_STB + NMW * 1024 <= 160 * 1024, "ring and store staging fit the LDS");
 
 struct Opnd8 {
   rsrc_t ra, rb, rsa, rsb;
@@ -779,7 +802,8 @@ __device__ __forceinline__ void issue8(const Opnd8& o, uint8_t* st, int ks) {
 __device__ __forceinline__ void wgrad8_persistent(const BwdArgs& a, const uint8_t* A, const float* As, int M,
                                                   const uint8_t* B, const float* Bs, int N, float* routed_dst,
                                                   float* shared_dst) {
-  __shared__ __attribute__((aligned(1024))) uint8_t ring[W8_NSTG * W8_STB];
+  // the stage ring, then 1 KB of store staging per MFMA wave
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[W8_NSTG * W8_STB + NMW * 1024];
   const int mb_n = ceil_div(M, W8_BM), nb_n = ceil_div(N, W8_BN);
   const long long per_g = static_cast<long long>(mb_n) * nb_n;
   const WgradList list(a, per_g);
@@ -897,14 +921,30 @@ __device__ __forceinline__ void wgrad8_persistent(const BwdArgs& a, const uint8_
     }
     float* dst = g < a.n_routed ? routed_dst + static_cast<size_t>(g) * M * N
                                 : shared_dst + static_cast<size_t>(g - a.n_routed) * M * N;
+    // each half subtile (8 rows x 128 bytes) through the wave's staging, so
+    // every store writes whole lines, streamed past the caches (as in the
+    // bf16 Wgrad)
+    uint8_t* sg = ring + W8_NSTG * W8_STB + 1024 * w;
 #pragma unroll
     for (int ii = 0; ii < MI; ++ii) {
-      const int m = m0 + 16 * (2 * ii + wm) + lr;
-      if (m >= M) continue;
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int n = n0 + 32 * wn + 16 * j + 4 * lg;
-        if (n < N) *reinterpret_cast<f32x4*>(dst + static_cast<size_t>(m) * N + n) = acc[ii][j];
+      for (int h = 0; h < 2; ++h) {
+        if ((lr >> 3) == h) {
+          const int r = lr & 7;
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+            *reinterpret_cast<f32x4*>(sg + r * 128 + (((4 * j + lg) ^ r) << 4)) = acc[ii][j];
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        const int r = lane >> 3, c = lane & 7;
+        const f32x4 v = *reinterpret_cast<const f32x4*>(sg + r * 128 + ((c ^ r) << 4));
+        const int m = m0 + 16 * (2 * ii + wm) + 8 * h + r, n = n0 + 32 * wn + 4 * c;
+        if (m < M && n < N) __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(dst + static_cast<size_t>(m) * N + n));
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
       }
     }
   }
