@@ -31,17 +31,21 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def measured_traffic(workload: str):
-    """HBM bytes per gate/up launch from the committed rocprofv3 counter runs, if
-    they were taken on the current grouped-GEMM source; else None."""
+def measured_traffic(workload: str, kernel: str = "gateup_kernel", train: bool = False):
+    """HBM bytes per launch of ``kernel`` (default: the gate/up GEMM) from the
+    committed rocprofv3 counter runs (record ``workload``, or ``workload``_train),
+    if they were taken on the current GEMM sources; else None."""
     if not os.path.exists(TRAFFIC_FILE):
         return None
     table = json.load(open(TRAFFIC_FILE))
-    rec = table.get(workload)
+    rec = table.get(workload + ("_train" if train else ""))
     from mixture_experts_layer_deepseekmoe_amd.profiling import source_hash
-    if not rec or rec.get("kernel_source_hash") != source_hash():
+    if not rec or rec.get("kernel_source_hash") != source_hash(train):
         return None
-    return rec.get("gate_up_bytes_per_launch")
+    if kernel == "gateup_kernel" and not train:
+        return rec.get("gate_up_bytes_per_launch")
+    return next((v for k, v in rec.get("bytes_per_launch", {}).items() if k == kernel or k.startswith(kernel + "<")),
+                None)
 
 
 def measured_peaks():
@@ -319,7 +323,13 @@ def train_bench(args, cfg):
                        "flops_per_launch": fl, "algorithmic_bytes_per_launch": by, "avg_launch_ms": round(stages[name], 4),
                        "mfma_frac": round(tf / peak_tf, 4), "hbm_frac": round(gbs / PEAK_HBM_GBS, 4)}
     dominant = max(gemms, key=lambda k: stages[k])
-    roofline = dict(lines[dominant], kernel=dominant, traffic=None)
+    # the dominant stage's GEMM kernel (the FP8 Dgrad runs on the forward's down kernel, not told apart)
+    kern = {"bwd_wgrad_gate_up": "wgrad8_gateup_kernel" if fp8 else "wgrad_gateup_kernel",
+            "bwd_wgrad_down": "wgrad8_down_kernel" if fp8 else "wgrad_down_kernel",
+            "bwd_dgrad_gate_up": None if fp8 else "dgrad_gateup_kernel",
+            "bwd_dgrad_down": None if fp8 else "dgrad_down_kernel"}[dominant]
+    roofline = dict(lines[dominant], kernel=dominant,
+                    traffic=measured_traffic(cfg.name, kern, train=True) if kern else None)
     result = {
         "metric": f"MoE-layer training step tokens/sec (forward + backward, {'fp8' if fp8 else 'bf16'}), "
                   f"d={d} N_r={cfg.n_routed} K={cfg.top_k}, 1 GPU",

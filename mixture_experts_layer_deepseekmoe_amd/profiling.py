@@ -51,7 +51,7 @@ def _run(args):
     inp = make_inputs(cfg, 0, weights_device="cuda")
     shape = moe.LayerShape.from_config(cfg)
     u, cen, bias = (t.cuda().contiguous() for t in (inp.u, inp.centroids, inp.bias))
-    w = moe.prepare_weights(cfg, inp)
+    w = moe.prepare_weights(cfg, inp, train=args.train)
     ws = moe.alloc_workspace(shape)
     routing = moe.alloc_routing(shape)
     y = torch.empty((cfg.T, cfg.d), dtype=torch.float32 if cfg.out_dtype == "f32" else torch.bfloat16, device="cuda")
@@ -74,6 +74,7 @@ def _run(args):
 
 def _short(name: str) -> str:
     for key in ("dgrad_down_kernel", "dgrad_gateup_kernel", "wgrad_down_kernel", "wgrad_gateup_kernel",
+                "wgrad8_down_kernel", "wgrad8_gateup_kernel", "colquant_kernel", "swiglu_bwd_kernel",
                 "bwd_prep_kernel", "bwd_dz_kernel", "bwd_du_kernel", "bwd_de_kernel",
                 "gateup_kernel", "down_kernel", "route_part_kernel", "route_finish_kernel", "route_scores_kernel",
                 "route_topk_kernel", "route_kernel", "combine_kernel", "hist_kernel", "scan_kernel",
@@ -104,7 +105,7 @@ def _is_calibration(row) -> bool:
 # the calibration stream (keeps the input generators' kernels out of the CSV)
 KERNEL_REGEX = ("gateup_kernel|down_kernel|route_kernel|route_part_kernel|route_finish_kernel|combine_kernel|"
                 "hist_kernel|scan_kernel|permute_kernel|quant_act_kernel|bias_update_kernel|bwd_prep_kernel|"
-                "bwd_dz_kernel|bwd_du_kernel|bwd_de_kernel|MulFunctor<double>")
+                "bwd_dz_kernel|bwd_du_kernel|bwd_de_kernel|colquant_kernel|swiglu_bwd_kernel|MulFunctor<double>")
 
 
 def _csvs(d, pattern):
@@ -133,12 +134,13 @@ def counters(pmc_dirs):
     return {k: {c: sum(v) / len(v) for c, v in cs.items()} for k, cs in acc.items()}
 
 
-def source_hash():
-    """Hash of the grouped-GEMM sources (forward and backward), stamped on
-    stored counter readings."""
+def source_hash(train: bool = False):
+    """Hash of the grouped-GEMM sources (with ``train``, the backward's too),
+    stamped on stored counter readings."""
     csrc = os.path.join(ROOT, "mixture_experts_layer_deepseekmoe_amd", "csrc")
     h = hashlib.sha256()
-    for f in ("gemm_core.hpp", "ggemm.hip", "bwd.hip", "tile_map.hpp", "moe_common.hpp", "kernels.hpp"):
+    files = ["gemm_core.hpp", "ggemm.hip", "tile_map.hpp", "moe_common.hpp", "kernels.hpp"]
+    for f in files + (["bwd.hip"] if train else []):
         h.update(open(os.path.join(csrc, f), "rb").read())
     return h.hexdigest()[:16]
 
@@ -195,11 +197,17 @@ def _summarize(args):
             lines += [f"gate/up HBM traffic per launch (scaled): fetch "
                       f"{gu['FETCH_SIZE'] * 1024 * fetch_f / 1e9:.3f} GB + write "
                       f"{gu['WRITE_SIZE'] * 1024 * write_f / 1e9:.3f} GB = {traffic / 1e9:.3f} GB", ""]
+            # every layer kernel's bytes per launch, for the training bench's dominant kernel
+            per_kernel = {k: v["FETCH_SIZE"] * 1024 * fetch_f + v["WRITE_SIZE"] * 1024 * write_f
+                          for k, v in cs.items() if "FETCH_SIZE" in v and "WRITE_SIZE" in v and k != CALIB
+                          and not k.startswith("torch:") and not k.startswith("__amd")}
             tf = os.path.join(args.out, "traffic_counters.json")
             table = json.load(open(tf)) if os.path.exists(tf) else {}
-            table[args.workload] = {"gate_up_bytes_per_launch": traffic, "kernel_source_hash": source_hash(),
+            train = args.workload.endswith("_train")
+            table[args.workload] = {"gate_up_bytes_per_launch": traffic, "kernel_source_hash": source_hash(train),
                                     "fetch_scale": fetch_f, "write_scale": write_f,
-                                    "gate_up_fetch_kib": gu["FETCH_SIZE"], "gate_up_write_kib": gu["WRITE_SIZE"]}
+                                    "gate_up_fetch_kib": gu["FETCH_SIZE"], "gate_up_write_kib": gu["WRITE_SIZE"],
+                                    "bytes_per_launch": per_kernel}
             json.dump(table, open(tf, "w"), indent=1, sort_keys=True)
     out = os.path.join(args.out, args.name or f"rocprof_{args.workload}.md")
     open(out, "w").write("\n".join(lines) + "\n")
