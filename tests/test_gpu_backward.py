@@ -314,3 +314,50 @@ def test_backward_fp8_full_d2048():
         assert v <= TOL8, (k, v)
     del w, ws, grads
     torch.cuda.empty_cache()
+
+
+def test_backward_fp8_full_d7168_sampled():
+    """The FP8 DeepSeek-V3 layer (T = 8192, d = 7168, 256 + 1 experts, K = 8):
+    du on sampled tokens, and dW of the shared expert and of sampled routed
+    experts (the largest, the smallest and a median one), against the
+    oracle's FP8 backward."""
+    cfg = CONFIGS["fp8_d7168"]
+    say("case: FP8 moe_backward fp8_d7168 full size, sampled")
+    inp = make_inputs(cfg, 0, weights_device=DEV)
+    dy = _dy(cfg)
+    y, du, dE, grads, ws, w = _train_step(cfg, inp, dy)
+    assert torch.isfinite(du).all() and torch.isfinite(dE).all()
+    shape = moe.LayerShape.from_config(cfg)
+    u_d, E_d, b_d = (t.to(DEV).contiguous() for t in (inp.u, inp.centroids, inp.bias))
+    routing = moe.moe_route(shape, u_d, E_d, b_d)
+    torch.cuda.synchronize()
+    gi = routing["topk_idx"].cpu().numpy()
+    counts = routing["expert_counts"].cpu().numpy()
+    u, E, b = to_numpy_f32(inp.u), to_numpy_f32(inp.centroids), inp.bias.numpy()
+    routed, shared = expert_fns(inp, True)
+    x_deq = O.dequantize_act(*O.quantize_act_1x128(u))
+
+    def expert_bwd(wgu, wd, rows, dout):
+        gq, gs = O.quantize_weight_128x128(wgu)
+        dq, ds = O.quantize_weight_128x128(wd)
+        return O.swiglu_ffn_backward_fp8(u[rows], x_deq[rows], gq, gs, dq, ds, dout)
+
+    sample = np.array([0, 1, 255, 256, 4095, 4096, 8190, 8191])
+    ref = O.layer_backward(u[sample], E, b, cfg.top_k, routed, cfg.n_routed, shared, dy.numpy()[sample],
+                           selection=gi[sample], weight_grads=False, fp8=True)
+    errs = {"du(sampled tokens)": _err(du.cpu().numpy()[sample], ref["du"], 1, cfg.d)}
+    order = np.argsort(counts)
+    for e in (int(order[-1]), int(order[0]), int(order[len(order) // 2])):
+        tok, slot = np.nonzero(gi == e)
+        r = O.route(u[tok], E, b, cfg.top_k, selection=gi[tok])
+        bb = expert_bwd(*routed(e), tok, r["gate"][np.arange(len(tok)), slot][:, None] * dy.numpy()[tok])
+        errs[f"dW_gate_up[{e}] ({len(tok)} rows)"] = _err(grads.dw_gate_up[e].cpu().numpy(), bb["dW_gate_up"])
+        errs[f"dW_down[{e}]"] = _err(grads.dw_down[e].cpu().numpy(), bb["dW_down"])
+    bs = expert_bwd(*shared[0], np.arange(cfg.T), dy.numpy())
+    errs["dWs_gate_up"] = _err(grads.dws_gate_up[0].cpu().numpy(), bs["dW_gate_up"])
+    errs["dWs_down"] = _err(grads.dws_down[0].cpu().numpy(), bs["dW_down"])
+    say("  worst block ||d||/||ref||: " + ", ".join(f"{k} {v:.2e}" for k, v in errs.items()))
+    for k, v in errs.items():
+        assert v <= TOL8, (k, v)
+    del w, ws, grads, inp
+    torch.cuda.empty_cache()
