@@ -218,6 +218,117 @@ __device__ __forceinline__ void mainloop(uint8_t* ring, const Opnd& a, const Opn
   acc_fence(acc);
 }
 
+// The Dgrad K loop (A K-contiguous, B K-outer) with the A loads paired: a
+// K-contiguous row moves 64 bytes per K-step, half a 128-byte line, and two
+// halves requested a K-step apart cost an L2 request each, while requested
+// back to back they merge into one (B's K-rows are whole lines already).  So
+// A is loaded two K-steps at a time into a ring of 3 pair buffers (32 KB),
+// B one K-step at a time into a ring of 4 (16 KB): 160 KB in all.  The
+// barrier protocol is mainloop's (stages ks and ks + 1 landed before barrier
+// ks); after barrier ks the load waves refill B's buffer of stage ks - 1 with
+// stage ks + 3 and, for even ks, A's buffer of the pair (ks - 2, ks - 1) with
+// the pair (ks + 4, ks + 5).  Loads complete in order, so the wait for stage
+// ks + 2 allows exactly the loads issued after it: this step's B and, for an
+// even ks (or the step before, for an odd one), the next A pair.
+constexpr int PA_A = 0, PA_B = 3 * 2 * OPB;   // A pair buffers, then B buffers
+static_assert(PA_B + 4 * OPB <= NSTG * STB, "paired ring fits the stage ring");
+
+__device__ __forceinline__ void issue_a_pair(const Opnd& a, uint8_t* ring, int p, int nk) {
+  const int w = wave_id() - NMW;
+  uint8_t* st = ring + PA_A + (p % 3) * 2 * OPB;
+  const int k0 = 2 * p, k1 = min(2 * p + 1, nk - 1);   // past the end: a clamped load nobody reads
+#pragma unroll
+  for (int q = 0; q < NLI; ++q) {
+    dma16(a.r, a.off[q], k0 * a.kstride, st + 1024 * (w + NLW * q));
+    dma16(a.r, a.off[q], k1 * a.kstride, st + OPB + 1024 * (w + NLW * q));
+  }
+}
+
+__device__ __forceinline__ void issue_b(const Opnd& b, uint8_t* ring, int s) {
+  const int w = wave_id() - NMW;
+#pragma unroll
+  for (int q = 0; q < NLI; ++q) dma16(b.r, b.off[q], s * b.kstride, ring + PA_B + (s % 4) * OPB + 1024 * (w + NLW * q));
+}
+
+__device__ __forceinline__ const uint8_t* pa_a(uint8_t* ring, int s) {
+  return ring + PA_A + ((s / 2) % 3) * 2 * OPB + (s % 2) * OPB;
+}
+__device__ __forceinline__ const uint8_t* pa_b(uint8_t* ring, int s) { return ring + PA_B + (s % 4) * OPB; }
+
+template <int NSUB = MI>
+__device__ __forceinline__ void mainloop_pa(uint8_t* ring, const Opnd& a, const Opnd& b, int nk,
+                                            f32x4 (&acc)[MI][NJ]) {
+  static_assert(NSUB >= 1 && NSUB <= MI, "row subtiles");
+  const int w = wave_id();
+  if (nk <= 0) return;
+  if (w >= NMW) {
+    // A pair 0, B 0, B 1, A pair 1, B 2: stages 0 and 1 first
+    issue_a_pair(a, ring, 0, nk);
+    issue_b(b, ring, 0);
+    if (nk > 1) issue_b(b, ring, 1);
+    if (nk > 2) {
+      issue_a_pair(a, ring, 1, nk);
+      issue_b(b, ring, 2);
+      wait_vm_lgkm0<3 * NLI>();   // A pair 1 and B 2 may be in flight
+    } else {
+      wait_vm_lgkm0<0>();
+    }
+    for (int ks = 0; ks < nk; ++ks) {
+      block_barrier();
+      const bool ib = ks + 3 < nk;
+      if (ib) issue_b(b, ring, ks + 3);
+      if ((ks & 1) == 0) {
+        const bool ia = ks + 4 < nk;
+        if (ia) issue_a_pair(a, ring, ks / 2 + 2, nk);
+        if (ia)
+          wait_vm_lgkm0<3 * NLI>();   // stage ks + 2; this step's B and A pair in flight
+        else if (ib)
+          wait_vm_lgkm0<NLI>();       // this step's B in flight
+        else
+          wait_vm_lgkm0<0>();
+      } else {
+        if (ib)
+          wait_vm_lgkm0<3 * NLI>();   // the previous step's A pair and this step's B in flight
+        else
+          wait_vm_lgkm0<0>();
+      }
+    }
+    return;
+  }
+  const int wm = w % 2, wn = w / 2;
+  KoLane kl = ko_lane();
+  i32x4 wf[NJ], xf;
+  block_barrier();   // stages 0 and 1 have landed
+  {
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) wf[j] = frag_ko(pa_b(ring, 0), 64 * wn + 16 * j, kl);
+    xf = frag_kc(pa_a(ring, 0), 16 * wm);
+  }
+  acc_fence(acc);
+  for (int ks = 0; ks < nk; ++ks) {
+    asm volatile("" : "+v"(kl.base), "+v"(kl.y));
+    const uint8_t* sa = pa_a(ring, ks);
+#pragma unroll
+    for (int i = 0; i < NSUB; ++i) {
+      i32x4 xn;
+      if (i + 1 < NSUB) xn = frag_kc(sa, 16 * (2 * (i + 1) + wm));
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) mfma_bf16_tied(acc[i][j], wf[j], xf);
+      __builtin_amdgcn_sched_barrier(0);
+      if (i + 1 < NSUB) xf = xn;
+    }
+    if (ks + 1 < nk) {
+      const uint8_t* nb = pa_b(ring, ks + 1);
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) wf[j] = frag_ko(nb, 64 * wn + 16 * j, kl);
+      xf = frag_kc(pa_a(ring, ks + 1), 16 * wm);
+      block_barrier();
+    }
+  }
+  acc_fence(acc);
+}
+
 // f.template operator()<NSUB>() with NSUB = the row subtiles wave row 0
 // computes for a tile of `rows` rows (two wave rows of 16-row subtiles).
 template <int N = 1, class F>
@@ -283,10 +394,10 @@ __global__ __launch_bounds__(THREADS, 1) void dgrad_down_kernel(BwdArgs a) {
                                       rows * ldy),
                             [&](int m) { return static_cast<uint32_t>((m < rows ? m : rows) * ldy); });   // past the rows: zeros
     const Opnd ob = opnd_ko(make_rsrc(wd, a.d * ldw), ldw, n0);
-    mainloop<KC, KO>(ring, oa, ob, a.d / 32, acc);
+    mainloop_pa(ring, oa, ob, a.d / 32, acc);
     return;
   }
-  with_row_subtiles(rows, [&]<int NS>() { mainloop<KC, KO, NS>(ring, Opnd{}, Opnd{}, a.d / 32, acc); });
+  with_row_subtiles(rows, [&]<int NS>() { mainloop_pa<NS>(ring, Opnd{}, Opnd{}, a.d / 32, acc); });
   const int w = wave_id(), lane = threadIdx.x & 63, wm = w % 2, wn = w / 2;
 #pragma unroll
   for (int i = 0; i < MI; ++i) {
@@ -335,10 +446,10 @@ __global__ __launch_bounds__(THREADS, 1) void dgrad_gateup_kernel(BwdArgs a) {
                                       rows * ldg),
                             [&](int m) { return static_cast<uint32_t>((m < rows ? m : rows) * ldg); });   // past the rows: zeros
     const Opnd ob = opnd_ko(make_rsrc(wgu, 2 * a.inter * ldw), ldw, n0);
-    mainloop<KC, KO>(ring, oa, ob, nk, acc);
+    mainloop_pa(ring, oa, ob, nk, acc);
     return;
   }
-  with_row_subtiles(rows, [&]<int NS>() { mainloop<KC, KO, NS>(ring, Opnd{}, Opnd{}, nk, acc); });
+  with_row_subtiles(rows, [&]<int NS>() { mainloop_pa<NS>(ring, Opnd{}, Opnd{}, nk, acc); });
   const int w = wave_id(), lane = threadIdx.x & 63, wm = w % 2, wn = w / 2;
 #pragma unroll
   for (int i = 0; i < MI; ++i) {
