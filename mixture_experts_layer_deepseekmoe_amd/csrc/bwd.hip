@@ -1,7 +1,8 @@
-// The MoE layer backward, bf16 (the report's FP8 training section, as
+// The MoE layer backward, bf16 or FP8 (the report's FP8 training section, as
 // paraphrased on why-be.co.kr: the Linear operator's Fprop, Dgrad and Wgrad
-// GEMMs; the SwiGLU inputs are cached in the forward and its output is
-// recomputed in the backward pass).  With the expert selection held fixed:
+// GEMMs, all three in FP8 in its Figure 6; the SwiGLU inputs are cached in
+// the forward and its output is recomputed in the backward pass).  With the
+// expert selection held fixed:
 //
 //   prep     grouped row r (token t, gate g; g = 1 for a shared expert):
 //            dY_r = g dy_t and X_r = u_t as bf16 rows, dg_{t,k} = dy_t . Y_r
@@ -18,9 +19,9 @@
 //
 // Every sum runs in a fixed order: the results are bit-reproducible.
 //
-// GEMM tiles: 256 x 256 outputs, 8 MFMA waves (2 x 4, 128 x 64 each, bf16
-// 16x16x32 MFMAs accumulating in place) and 4 load waves that move 32-K
-// stages into a ring of 4 LDS buffers by DMA.  An operand is stored either
+// bf16 GEMM tiles: 256 x 256 outputs, 8 MFMA waves (2 x 4, 128 x 64 each,
+// bf16 16x16x32 MFMAs accumulating in place) and 4 load waves that move 32-K
+// stages into a ring of LDS buffers by DMA.  An operand is stored either
 // K-contiguous (rows of K: the activations of Dgrad) or K-outer (rows along
 // K, its M or N index contiguous: the weights of Dgrad, both operands of
 // Wgrad).  K-outer fragments come from LDS transpose reads
@@ -144,88 +145,19 @@ __device__ __forceinline__ void issue_stage(const Opnd& a, const Opnd& b, uint8_
 //   before barrier ks  stages ks and ks+1 have landed (the load waves waited
 //                      for them);
 //   after barrier ks   nobody reads stage ks-1 any more, and the load waves
-//                      refill its buffer with stage ks + NSTG - 1.
+//                      refill its buffers.
 // So the MFMA waves read the next stage's first fragments (its weight side
 // and first activation subtile) at the end of a stage, and within a stage
 // read each activation fragment one subtile ahead of its MFMAs: no LDS read
 // latency stands between a barrier and the first MFMA.
-template <int M>
-__device__ __forceinline__ i32x4 frag(const uint8_t* op, int at, KoLane kl) {
-  return M == KO ? frag_ko(op, at, kl) : frag_kc(op, at);
-}
-
-// NSUB: the row subtiles each MFMA wave computes (its first NSUB of MI; a
-// tile of fewer rows issues no MFMAs for the subtiles past them).
-template <int AM, int BM, int NSUB = MI>
-__device__ __forceinline__ void mainloop(uint8_t* ring, const Opnd& a, const Opnd& b, int nk,
-                                         f32x4 (&acc)[MI][NJ]) {
-  static_assert(NSUB >= 1 && NSUB <= MI, "row subtiles");
-  const int w = wave_id();
-  if (nk <= 0) return;
-  if (w >= NMW) {
-    const int pre = min(nk, NSTG - 1);
-    for (int s = 0; s < pre; ++s) issue_stage(a, b, ring + s * STB, s);
-    if (pre == NSTG - 1)
-      wait_vm_lgkm0<(NSTG - 3) * NLS>();   // stages 0 and 1
-    else
-      wait_vm_lgkm0<0>();
-    for (int ks = 0; ks < nk; ++ks) {
-      block_barrier();
-      const int kn = ks + NSTG - 1;
-      if (kn < nk) {
-        issue_stage(a, b, ring + (kn % NSTG) * STB, kn);
-        wait_vm_lgkm0<(NSTG - 3) * NLS>();   // stage ks + 2
-      } else {
-        wait_vm_lgkm0<0>();
-      }
-    }
-    return;
-  }
-  const int wm = w % 2, wn = w / 2;
-  KoLane kl = ko_lane();
-  i32x4 wf[NJ], xf;
-  block_barrier();   // stages 0 and 1 have landed
-  {
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) wf[j] = frag<BM>(ring + OPB, 64 * wn + 16 * j, kl);
-    xf = frag<AM>(ring, 16 * wm, kl);
-  }
-  acc_fence(acc);
-  for (int ks = 0; ks < nk; ++ks) {
-    // the lane constants pass through an empty asm each step, so the
-    // per-subtile addresses are recomputed (one xor each) instead of being
-    // hoisted out of the loop into a register apiece
-    asm volatile("" : "+v"(kl.base), "+v"(kl.y));
-    const uint8_t* sa = ring + (ks % NSTG) * STB;
-    const uint8_t* na = ring + ((ks + 1) % NSTG) * STB;   // the next stage (landed; unused past the end)
-#pragma unroll
-    for (int i = 0; i < NSUB; ++i) {
-      i32x4 xn;
-      if (i + 1 < NSUB) xn = frag<AM>(sa, 16 * (2 * (i + 1) + wm), kl);
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int j = 0; j < NJ; ++j) mfma_bf16_tied(acc[i][j], wf[j], xf);
-      __builtin_amdgcn_sched_barrier(0);
-      if (i + 1 < NSUB) xf = xn;
-    }
-    if (ks + 1 < nk) {
-#pragma unroll
-      for (int j = 0; j < NJ; ++j) wf[j] = frag<BM>(na + OPB, 64 * wn + 16 * j, kl);
-      xf = frag<AM>(na, 16 * wm, kl);
-      block_barrier();
-    }
-  }
-  acc_fence(acc);
-}
-
+//
 // The Dgrad K loop (A K-contiguous, B K-outer) with the A loads paired: a
 // K-contiguous row moves 64 bytes per K-step, half a 128-byte line, and two
 // halves requested a K-step apart cost an L2 request each, while requested
 // back to back they merge into one (B's K-rows are whole lines already).  So
 // A is loaded two K-steps at a time into a ring of 3 pair buffers (32 KB),
-// B one K-step at a time into a ring of 4 (16 KB): 160 KB in all.  The
-// barrier protocol is mainloop's (stages ks and ks + 1 landed before barrier
-// ks); after barrier ks the load waves refill B's buffer of stage ks - 1 with
+// B one K-step at a time into a ring of 4 (16 KB): 160 KB in all.  After
+// barrier ks the load waves refill B's buffer of stage ks - 1 with
 // stage ks + 3 and, for even ks, A's buffer of the pair (ks - 2, ks - 1) with
 // the pair (ks + 4, ks + 5).  Loads complete in order, so the wait for stage
 // ks + 2 allows exactly the loads issued after it: this step's B and, for an
