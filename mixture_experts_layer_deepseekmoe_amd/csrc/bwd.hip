@@ -745,7 +745,6 @@ __device__ __forceinline__ int group_of_block(const BwdArgs& a, long long kb, Gr
 __global__ __launch_bounds__(256) void colquant_kernel(BwdArgs a, const uint16_t* __restrict__ src, int C,
                                                        uint8_t* __restrict__ dst, float* __restrict__ dst_s) {
   __shared__ float tile[128][65];
-  __shared__ float red[4][64];
   GroupRows gr;
   int b;
   const long long kb = blockIdx.x;
@@ -767,25 +766,32 @@ __global__ __launch_bounds__(256) void colquant_kernel(BwdArgs a, const uint16_t
     }
   }
   __syncthreads();
-  const int c = t & 63, part = t >> 6;   // column c, rows 32 part .. 32 part + 31
-  float m = 0.f;
+  // wave v takes columns 16 v .. 16 v + 15, two at a time: lane 8 c + k holds
+  // rows 16 k .. 16 k + 15 of column 16 v + c (then + 8), so the eight lanes
+  // of a column reduce its amax among themselves and one store instruction
+  // writes 8 columns x 128 bytes, whole lines
+  const int v = t >> 6, lane = t & 63, k = lane & 7;
 #pragma unroll
-  for (int i = 0; i < 32; ++i) m = fmaxf(m, fabsf(tile[32 * part + i][c]));
-  red[part][c] = m;
-  __syncthreads();
-  m = fmaxf(fmaxf(red[0][c], red[1][c]), fmaxf(red[2][c], red[3][c]));
-  const float sc = m == 0.f ? 1.f : m / 448.f;
-  const float inv = m == 0.f ? 0.f : 448.f / m;
-  uint32_t w[8];
+  for (int h = 0; h < 2; ++h) {
+    const int c = 16 * v + 8 * h + (lane >> 3);
+    float m = 0.f;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int r = 32 * part + 4 * i;
-    w[i] = e4m3x4(tile[r][c] * inv, tile[r + 1][c] * inv, tile[r + 2][c] * inv, tile[r + 3][c] * inv);
+    for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(tile[16 * k + i][c]));
+    m = fmaxf(m, __shfl_xor(m, 1));
+    m = fmaxf(m, __shfl_xor(m, 2));
+    m = fmaxf(m, __shfl_xor(m, 4));
+    const float sc = m == 0.f ? 1.f : m / 448.f;
+    const float inv = m == 0.f ? 0.f : 448.f / m;
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 16 * k + 4 * i;
+      w[i] = e4m3x4(tile[r][c] * inv, tile[r + 1][c] * inv, tile[r + 2][c] * inv, tile[r + 3][c] * inv);
+    }
+    *reinterpret_cast<uint4*>(dst + static_cast<size_t>(c0 + c) * a.kt + 128 * kb + 16 * k) =
+        make_uint4(w[0], w[1], w[2], w[3]);
+    if (k == 0) dst_s[static_cast<size_t>(c0 + c) * (a.kt / 128) + kb] = sc;
   }
-  uint8_t* out = dst + static_cast<size_t>(c0 + c) * a.kt + 128 * kb + 32 * part;
-  *reinterpret_cast<uint4*>(out) = make_uint4(w[0], w[1], w[2], w[3]);
-  *reinterpret_cast<uint4*>(out + 16) = make_uint4(w[4], w[5], w[6], w[7]);
-  if (part == 0) dst_s[static_cast<size_t>(c0 + c) * (a.kt / 128) + kb] = sc;
 }
 
 // FP8 Wgrad tiles: 256 rows of A (M) x 128 rows of B (N), 8 MFMA waves (2 x
