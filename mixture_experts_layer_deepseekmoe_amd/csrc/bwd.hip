@@ -1040,46 +1040,62 @@ __global__ __launch_bounds__(THREADS, 1) void wgrad8_gateup_kernel(BwdArgs a) {
 
 // ------------------------------------------------------------------ elementwise passes
 
-// One wave per grouped row: dY_r = g dy_t, X_r = u_t (bf16) and, for a routed
-// row, dg_{t,k} = dy_t . Y_r (fp32, a fixed reduction order).
+// One wave per token t, over all of its grouped rows r (the K routed rows, by
+// pos, and the N_s shared rows): dY_r = g dy_t, X_r = u_t (bf16) and, for a
+// routed row, dg_{t,k} = dy_t . Y_r (fp32; each lane sums its columns in
+// order, then a butterfly over the lanes).  dy_t and u_t are read once for
+// all of the token's rows.
 __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a) {
-  const long long r = static_cast<long long>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
-  if (r >= a.R) return;
-  int t, k = -1;
-  float gsc = 1.f;
-  if (r < a.TK) {
-    t = a.perm_token[r];
-    for (int j = 0; j < a.top_k; ++j)
-      if (a.pos[static_cast<size_t>(t) * a.top_k + j] == r) k = j;
-    MOE_CHECK(k >= 0, 503);
-    gsc = k >= 0 ? a.gate[static_cast<size_t>(t) * a.top_k + k] : 0.f;   // k is found for routing of one forward
-  } else {
-    t = static_cast<int>((r - a.TK) % a.T);
+  if (t >= a.T) return;
+  const int K = a.top_k;
+  int rk[MAX_TOPK];
+  float gk[MAX_TOPK], dot[MAX_TOPK];
+#pragma unroll
+  for (int k = 0; k < MAX_TOPK; ++k) {
+    rk[k] = -1;
+    gk[k] = 0.f;
+    dot[k] = 0.f;
+    if (k < K) {
+      const int r = a.pos[static_cast<size_t>(t) * K + k];
+      if (MOE_CHECK(r >= 0 && r < a.TK && a.perm_token[r] == t, 503)) rk[k] = r;
+      gk[k] = a.gate[static_cast<size_t>(t) * K + k];
+    }
   }
   const float* dyt = a.dy + static_cast<size_t>(t) * a.d;
   const uint16_t* ut = a.u + static_cast<size_t>(t) * a.d;
-  const uint16_t* yr = a.y + static_cast<size_t>(r) * a.d;
-  uint16_t* dysr = a.dys + static_cast<size_t>(r) * a.d;
-  uint16_t* xpr = a.xp + static_cast<size_t>(r) * a.d;
-  float dot = 0.f;
   for (int c = 4 * lane; c < a.d; c += 256) {
     const float4 dv = *reinterpret_cast<const float4*>(dyt + c);
-    *reinterpret_cast<uint2*>(dysr + c) = make_uint2(bf16x2(gsc * dv.x, gsc * dv.y), bf16x2(gsc * dv.z, gsc * dv.w));
-    *reinterpret_cast<uint2*>(xpr + c) = *reinterpret_cast<const uint2*>(ut + c);
-    if (k >= 0) {
+    const uint2 uv = *reinterpret_cast<const uint2*>(ut + c);
+#pragma unroll
+    for (int k = 0; k < MAX_TOPK; ++k) {
+      if (rk[k] < 0) continue;
+      const size_t o = static_cast<size_t>(rk[k]) * a.d + c;
+      const float g = gk[k];
+      *reinterpret_cast<uint2*>(a.dys + o) = make_uint2(bf16x2(g * dv.x, g * dv.y), bf16x2(g * dv.z, g * dv.w));
+      *reinterpret_cast<uint2*>(a.xp + o) = uv;
       float yv[4];
-      unpack4(*reinterpret_cast<const uint2*>(yr + c), yv);
-      dot = fmaf(dv.x, yv[0], dot);
-      dot = fmaf(dv.y, yv[1], dot);
-      dot = fmaf(dv.z, yv[2], dot);
-      dot = fmaf(dv.w, yv[3], dot);
+      unpack4(*reinterpret_cast<const uint2*>(a.y + o), yv);
+      dot[k] = fmaf(dv.x, yv[0], dot[k]);
+      dot[k] = fmaf(dv.y, yv[1], dot[k]);
+      dot[k] = fmaf(dv.z, yv[2], dot[k]);
+      dot[k] = fmaf(dv.w, yv[3], dot[k]);
+    }
+    for (int j = 0; j < a.n_shared; ++j) {   // shared rows: g = 1
+      const size_t o = (static_cast<size_t>(a.TK) + static_cast<size_t>(j) * a.T + t) * a.d + c;
+      *reinterpret_cast<uint2*>(a.dys + o) = make_uint2(bf16x2(dv.x, dv.y), bf16x2(dv.z, dv.w));
+      *reinterpret_cast<uint2*>(a.xp + o) = uv;
     }
   }
-  if (k < 0) return;
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) dot += __shfl_xor(dot, off);
-  if (lane == 0) a.dg[static_cast<size_t>(t) * a.top_k + k] = dot;
+  for (int k = 0; k < MAX_TOPK; ++k) {
+    if (rk[k] < 0) continue;
+    float v = dot[k];
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+    if (lane == 0) a.dg[static_cast<size_t>(t) * K + k] = v;
+  }
 }
 
 // Per token: ds_k = (dg_k - sum_j g_j dg_j) / S, dz_k = ds_k s_k (1 - s_k);
@@ -1201,7 +1217,7 @@ hipError_t launch_backward_stage(int stage, const BwdArgs& a, hipStream_t s) {
   switch (stage) {
     case 0:   // prep, dz
       if (a.T == 0) break;
-      hipLaunchKernelGGL(bwd_prep_kernel, dim3(static_cast<unsigned>((a.R + 3) / 4)), dim3(256), 0, s, a);
+      hipLaunchKernelGGL(bwd_prep_kernel, dim3(static_cast<unsigned>((a.T + 3) / 4)), dim3(256), 0, s, a);
       hipLaunchKernelGGL(bwd_dz_kernel, dim3(ceil_div(a.T, 256)), dim3(256), 0, s, a);
       break;
     case 1:   // Dgrad of the down GEMM, SwiGLU backward
