@@ -1118,46 +1118,96 @@ __global__ __launch_bounds__(256) void bwd_dz_kernel(BwdArgs a) {
 }
 
 // One wave per token: du_t = dy_t + the shared experts' dX rows + the K
-// routed dX rows + sum_k dz_k e_k, in that order (fp32).
+// routed dX rows + sum_k dz_k e_k, in that order (fp32).  Each column chunk
+// issues all of its row loads before the first add, so the wave waits on
+// memory once per chunk, not once per row.
 __global__ __launch_bounds__(256) void bwd_du_kernel(BwdArgs a) {
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (t >= a.T) return;
   const size_t o = static_cast<size_t>(t) * a.top_k;
+  const int K = a.top_k, NS = a.n_shared;
+  size_t rowk[MAX_TOPK], cenk[MAX_TOPK];
+  float dzk[MAX_TOPK];
+#pragma unroll
+  for (int k = 0; k < MAX_TOPK; ++k) {
+    rowk[k] = cenk[k] = 0;
+    dzk[k] = 0.f;
+    if (k < K) {
+      rowk[k] = static_cast<size_t>(a.pos[o + k]) * a.d;
+      cenk[k] = static_cast<size_t>(a.idx[o + k]) * a.d;
+      dzk[k] = a.dz[o + k];
+    }
+  }
   for (int c = 4 * lane; c < a.d; c += 256) {
-    float4 v = *reinterpret_cast<const float4*>(a.dy + static_cast<size_t>(t) * a.d + c);
+    const float4 dv = *reinterpret_cast<const float4*>(a.dy + static_cast<size_t>(t) * a.d + c);
+    uint2 xs[MAX_SHARED], xr[MAX_TOPK], xe[MAX_TOPK];
+#pragma unroll
+    for (int j = 0; j < MAX_SHARED; ++j)
+      if (j < NS)
+        xs[j] = *reinterpret_cast<const uint2*>(a.dx + static_cast<size_t>(a.TK + static_cast<long long>(j) * a.T + t) * a.d + c);
+#pragma unroll
+    for (int k = 0; k < MAX_TOPK; ++k)
+      if (k < K) {
+        xr[k] = *reinterpret_cast<const uint2*>(a.dx + rowk[k] + c);
+        xe[k] = *reinterpret_cast<const uint2*>(a.centroids + cenk[k] + c);
+      }
+    float4 v = dv;
     float x[4];
-    for (int s = 0; s < a.n_shared; ++s) {
-      unpack4(*reinterpret_cast<const uint2*>(a.dx + static_cast<size_t>(a.TK + static_cast<long long>(s) * a.T + t) * a.d + c), x);
-      v.x += x[0]; v.y += x[1]; v.z += x[2]; v.w += x[3];
-    }
-    for (int k = 0; k < a.top_k; ++k) {
-      unpack4(*reinterpret_cast<const uint2*>(a.dx + static_cast<size_t>(a.pos[o + k]) * a.d + c), x);
-      v.x += x[0]; v.y += x[1]; v.z += x[2]; v.w += x[3];
-    }
-    for (int k = 0; k < a.top_k; ++k) {
-      const float dz = a.dz[o + k];
-      unpack4(*reinterpret_cast<const uint2*>(a.centroids + static_cast<size_t>(a.idx[o + k]) * a.d + c), x);
-      v.x = fmaf(dz, x[0], v.x); v.y = fmaf(dz, x[1], v.y); v.z = fmaf(dz, x[2], v.z); v.w = fmaf(dz, x[3], v.w);
-    }
+#pragma unroll
+    for (int j = 0; j < MAX_SHARED; ++j)
+      if (j < NS) {
+        unpack4(xs[j], x);
+        v.x += x[0]; v.y += x[1]; v.z += x[2]; v.w += x[3];
+      }
+#pragma unroll
+    for (int k = 0; k < MAX_TOPK; ++k)
+      if (k < K) {
+        unpack4(xr[k], x);
+        v.x += x[0]; v.y += x[1]; v.z += x[2]; v.w += x[3];
+      }
+#pragma unroll
+    for (int k = 0; k < MAX_TOPK; ++k)
+      if (k < K) {
+        unpack4(xe[k], x);
+        v.x = fmaf(dzk[k], x[0], v.x); v.y = fmaf(dzk[k], x[1], v.y);
+        v.z = fmaf(dzk[k], x[2], v.z); v.w = fmaf(dzk[k], x[3], v.w);
+      }
     *reinterpret_cast<float4*>(a.du + static_cast<size_t>(t) * a.d + c) = v;
   }
 }
 
 // dE_e[c] = sum over expert e's grouped rows (ascending) of dz_r u_{t(r)}[c];
 // block (e, 1024-column chunk), 4 columns per thread; zero for an expert
-// without rows.
+// without rows.  The rows go in batches of 8 whose loads are all issued
+// before the batch's first multiply-add.
 __global__ __launch_bounds__(256) void bwd_de_kernel(BwdArgs a) {
+  constexpr int NB = 8;
   const int e = blockIdx.y;
   const int c = blockIdx.x * 1024 + 4 * threadIdx.x;
   if (c >= a.d) return;
   float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
   const int r1 = a.offsets[e] + a.counts[e];
-  for (int r = a.offsets[e]; r < r1; ++r) {
-    const float dz = a.dzr[r];
-    float x[4];
-    unpack4(*reinterpret_cast<const uint2*>(a.u + static_cast<size_t>(a.perm_token[r]) * a.d + c), x);
-    v.x = fmaf(dz, x[0], v.x); v.y = fmaf(dz, x[1], v.y); v.z = fmaf(dz, x[2], v.z); v.w = fmaf(dz, x[3], v.w);
+  for (int r = a.offsets[e]; r < r1; r += NB) {
+    float dz[NB];
+    int tok[NB];
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      dz[j] = r + j < r1 ? a.dzr[r + j] : 0.f;
+      tok[j] = r + j < r1 ? a.perm_token[r + j] : 0;
+    }
+    uint2 xv[NB];
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+      if (r + j < r1) xv[j] = *reinterpret_cast<const uint2*>(a.u + static_cast<size_t>(tok[j]) * a.d + c);
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+      if (r + j < r1) {
+        float x[4];
+        unpack4(xv[j], x);
+        v.x = fmaf(dz[j], x[0], v.x); v.y = fmaf(dz[j], x[1], v.y);
+        v.z = fmaf(dz[j], x[2], v.z); v.w = fmaf(dz[j], x[3], v.w);
+      }
   }
   *reinterpret_cast<float4*>(a.dcentroids + static_cast<size_t>(e) * a.d + c) = v;
 }
