@@ -737,11 +737,14 @@ __device__ __forceinline__ int group_of_block(const BwdArgs& a, long long kb, Gr
   return lo;
 }
 
-// 128x1 quantiser, transposed output: block (kb, column chunk) takes rows
+// 128x1 quantiser, transposed output: block (kb, column range) takes rows
 // 128 b .. 128 b + 127 of one group (b: kb's block in it; rows past the group
-// are zero) and 64 columns of src [R][C] bf16; per column, scale = amax / 448
-// and codes of x * (448 / amax) (scale 1, zero codes for an all-zero tile)
-// into dst[c][128 kb ..] and dst_s[c][kb].
+// are zero) and up to CQ_CHUNKS chunks of 64 columns of src [R][C] bf16; per
+// column, scale = amax / 448 and codes of x * (448 / amax) (scale 1, zero
+// codes for an all-zero tile) into dst[c][128 kb ..] and dst_s[c][kb].  The
+// block finds its group once, and loads the next chunk while it quantises
+// the current one.
+constexpr int CQ_CHUNKS = 8;
 __global__ __launch_bounds__(256) void colquant_kernel(BwdArgs a, const uint16_t* __restrict__ src, int C,
                                                        uint8_t* __restrict__ dst, float* __restrict__ dst_s) {
   __shared__ float tile[128][65];
@@ -749,48 +752,59 @@ __global__ __launch_bounds__(256) void colquant_kernel(BwdArgs a, const uint16_t
   int b;
   const long long kb = blockIdx.x;
   if (group_of_block(a, kb, gr, b) < 0) return;
-  const int c0 = blockIdx.y * 64, t = threadIdx.x;
+  const int t = threadIdx.x;
   const int r0 = gr.first + 128 * b, nr = min(128, gr.count - 128 * b);
-  {   // 128 rows x 64 columns: thread t loads 32 columns (4 x 16 bytes) of row t / 2
-    const int rr = t >> 1, cc = (t & 1) * 32;
+  const int ch0 = blockIdx.y * CQ_CHUNKS, nch = min(CQ_CHUNKS, C / 64 - ch0);
+  // thread t loads 32 columns (4 x 16 bytes) of row t / 2 of a chunk
+  const int rr = t >> 1, cc = (t & 1) * 32;
+  const uint16_t* srow = src + static_cast<size_t>(r0 + (rr < nr ? rr : 0)) * C + cc;
+  uint4 v[4];
+  auto load = [&](int ch) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      v[q] = rr < nr ? *reinterpret_cast<const uint4*>(srow + 64 * ch + 8 * q) : make_uint4(0, 0, 0, 0);
+  };
+  load(ch0);
+  // wave w takes columns 16 w .. 16 w + 15, two at a time: lane 8 c + k holds
+  // rows 16 k .. 16 k + 15 of column 16 w + c (then + 8), so the eight lanes
+  // of a column reduce its amax among themselves and one store instruction
+  // writes 8 columns x 128 bytes, whole lines
+  const int w = t >> 6, lane = t & 63, k = lane & 7;
+  for (int i = 0; i < nch; ++i) {
+    const int c0 = 64 * (ch0 + i);
+    if (i > 0) __syncthreads();   // the previous chunk's tile reads are done
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (rr < nr) v = *reinterpret_cast<const uint4*>(src + static_cast<size_t>(r0 + rr) * C + c0 + cc + 8 * q);
-      const uint32_t wd[4] = {v.x, v.y, v.z, v.w};
+      const uint32_t wd[4] = {v[q].x, v[q].y, v[q].z, v[q].w};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         tile[rr][cc + 8 * q + 2 * e] = bf16_to_f32(static_cast<uint16_t>(wd[e] & 0xffffu));
         tile[rr][cc + 8 * q + 2 * e + 1] = bf16_to_f32(static_cast<uint16_t>(wd[e] >> 16));
       }
     }
-  }
-  __syncthreads();
-  // wave v takes columns 16 v .. 16 v + 15, two at a time: lane 8 c + k holds
-  // rows 16 k .. 16 k + 15 of column 16 v + c (then + 8), so the eight lanes
-  // of a column reduce its amax among themselves and one store instruction
-  // writes 8 columns x 128 bytes, whole lines
-  const int v = t >> 6, lane = t & 63, k = lane & 7;
+    if (i + 1 < nch) load(ch0 + i + 1);
+    __syncthreads();
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int c = 16 * v + 8 * h + (lane >> 3);
-    float m = 0.f;
+    for (int h = 0; h < 2; ++h) {
+      const int c = 16 * w + 8 * h + (lane >> 3);
+      float m = 0.f;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(tile[16 * k + i][c]));
-    m = fmaxf(m, __shfl_xor(m, 1));
-    m = fmaxf(m, __shfl_xor(m, 2));
-    m = fmaxf(m, __shfl_xor(m, 4));
-    const float sc = m == 0.f ? 1.f : m / 448.f;
-    const float inv = m == 0.f ? 0.f : 448.f / m;
-    uint32_t w[4];
+      for (int j = 0; j < 16; ++j) m = fmaxf(m, fabsf(tile[16 * k + j][c]));
+      m = fmaxf(m, __shfl_xor(m, 1));
+      m = fmaxf(m, __shfl_xor(m, 2));
+      m = fmaxf(m, __shfl_xor(m, 4));
+      const float sc = m == 0.f ? 1.f : m / 448.f;
+      const float inv = m == 0.f ? 0.f : 448.f / m;
+      uint32_t wq[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = 16 * k + 4 * i;
-      w[i] = e4m3x4(tile[r][c] * inv, tile[r + 1][c] * inv, tile[r + 2][c] * inv, tile[r + 3][c] * inv);
+      for (int j = 0; j < 4; ++j) {
+        const int r = 16 * k + 4 * j;
+        wq[j] = e4m3x4(tile[r][c] * inv, tile[r + 1][c] * inv, tile[r + 2][c] * inv, tile[r + 3][c] * inv);
+      }
+      *reinterpret_cast<uint4*>(dst + static_cast<size_t>(c0 + c) * a.kt + 128 * kb + 16 * k) =
+          make_uint4(wq[0], wq[1], wq[2], wq[3]);
+      if (k == 0) dst_s[static_cast<size_t>(c0 + c) * (a.kt / 128) + kb] = sc;
     }
-    *reinterpret_cast<uint4*>(dst + static_cast<size_t>(c0 + c) * a.kt + 128 * kb + 16 * k) =
-        make_uint4(w[0], w[1], w[2], w[3]);
-    if (k == 0) dst_s[static_cast<size_t>(c0 + c) * (a.kt / 128) + kb] = sc;
   }
 }
 
@@ -1219,6 +1233,7 @@ MOE_DEBUG_FILE(bwd)
 // FP8 stages 1-4 (a.fp8): the Dgrad GEMMs on the forward's FP8 row-times-
 // weight kernel, the Wgrad GEMMs on the 128x1 codes.
 hipError_t launch_backward_stage_fp8(int stage, const BwdArgs& a, hipStream_t s) {
+  auto cq_grid = [](int C) { return static_cast<unsigned>(ceil_div(C / 64, CQ_CHUNKS)); };
   const int R = static_cast<int>(a.R);
   const unsigned kbt = static_cast<unsigned>(a.kt / 128);
   hipError_t e = hipSuccess;
@@ -1243,16 +1258,17 @@ hipError_t launch_backward_stage_fp8(int stage, const BwdArgs& a, hipStream_t s)
     }
     case 3:     // dW_down from the 128x1 codes of dY and H
       if (a.T > 0) {
-        hipLaunchKernelGGL(colquant_kernel, dim3(kbt, a.d / 64), dim3(256), 0, s, a, a.dys, a.d, a.qa, a.qa_s);
-        hipLaunchKernelGGL(colquant_kernel, dim3(kbt, a.inter / 64), dim3(256), 0, s, a, a.hr, a.inter, a.qb, a.qb_s);
+        hipLaunchKernelGGL(colquant_kernel, dim3(kbt, cq_grid(a.d)), dim3(256), 0, s, a, a.dys, a.d, a.qa, a.qa_s);
+        hipLaunchKernelGGL(colquant_kernel, dim3(kbt, cq_grid(a.inter)), dim3(256), 0, s, a, a.hr, a.inter, a.qb,
+                           a.qb_s);
       }
       hipLaunchKernelGGL(wgrad8_down_kernel, dim3(wgrad_grid()), dim3(THREADS), 0, s, a);
       break;
     case 4:     // dW_gate_up from the 128x1 codes of [dG dU] and X
       if (a.T > 0) {
-        hipLaunchKernelGGL(colquant_kernel, dim3(kbt, 2 * a.inter / 64), dim3(256), 0, s, a, a.dgu, 2 * a.inter, a.qa,
+        hipLaunchKernelGGL(colquant_kernel, dim3(kbt, cq_grid(2 * a.inter)), dim3(256), 0, s, a, a.dgu, 2 * a.inter, a.qa,
                            a.qa_s);
-        hipLaunchKernelGGL(colquant_kernel, dim3(kbt, a.d / 64), dim3(256), 0, s, a, a.xp, a.d, a.qb, a.qb_s);
+        hipLaunchKernelGGL(colquant_kernel, dim3(kbt, cq_grid(a.d)), dim3(256), 0, s, a, a.xp, a.d, a.qb, a.qb_s);
       }
       hipLaunchKernelGGL(wgrad8_gateup_kernel, dim3(wgrad_grid()), dim3(THREADS), 0, s, a);
       break;
