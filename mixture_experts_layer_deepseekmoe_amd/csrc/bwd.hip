@@ -739,14 +739,16 @@ __device__ __forceinline__ int group_of_block(const BwdArgs& a, long long kb, Gr
 
 // 128x1 quantiser, transposed output: block (kb, column range) takes rows
 // 128 b .. 128 b + 127 of one group (b: kb's block in it; rows past the group
-// are zero) and up to CQ_CHUNKS chunks of 64 columns of src [R][C] bf16; per
+// are zero) and up to CQ_CHUNKS chunks of 64 columns of src [R][C] bf16 (with
+// by_token, src is [T][C] and grouped row r reads the row of its token); per
 // column, scale = amax / 448 and codes of x * (448 / amax) (scale 1, zero
 // codes for an all-zero tile) into dst[c][128 kb ..] and dst_s[c][kb].  The
 // block finds its group once, and loads the next chunk while it quantises
 // the current one.
 constexpr int CQ_CHUNKS = 8;
 __global__ __launch_bounds__(256) void colquant_kernel(BwdArgs a, const uint16_t* __restrict__ src, int C,
-                                                       uint8_t* __restrict__ dst, float* __restrict__ dst_s) {
+                                                       bool by_token, uint8_t* __restrict__ dst,
+                                                       float* __restrict__ dst_s) {
   __shared__ float tile[128][65];
   GroupRows gr;
   int b;
@@ -757,7 +759,9 @@ __global__ __launch_bounds__(256) void colquant_kernel(BwdArgs a, const uint16_t
   const int ch0 = blockIdx.y * CQ_CHUNKS, nch = min(CQ_CHUNKS, C / 64 - ch0);
   // thread t loads 32 columns (4 x 16 bytes) of row t / 2 of a chunk
   const int rr = t >> 1, cc = (t & 1) * 32;
-  const uint16_t* srow = src + static_cast<size_t>(r0 + (rr < nr ? rr : 0)) * C + cc;
+  long long row = r0 + (rr < nr ? rr : 0);
+  if (by_token) row = row < a.TK ? a.perm_token[row] : (row - a.TK) % a.T;
+  const uint16_t* srow = src + static_cast<size_t>(row) * C + cc;
   uint4 v[4];
   auto load = [&](int ch) {
 #pragma unroll
@@ -1055,10 +1059,11 @@ __global__ __launch_bounds__(THREADS, 1) void wgrad8_gateup_kernel(BwdArgs a) {
 // ------------------------------------------------------------------ elementwise passes
 
 // One wave per token t, over all of its grouped rows r (the K routed rows, by
-// pos, and the N_s shared rows): dY_r = g dy_t, X_r = u_t (bf16) and, for a
-// routed row, dg_{t,k} = dy_t . Y_r (fp32; each lane sums its columns in
-// order, then a butterfly over the lanes).  dy_t and u_t are read once for
-// all of the token's rows.
+// pos, and the N_s shared rows): dY_r = g dy_t, X_r = u_t (bf16; the bf16
+// Wgrad's operand, not written for the FP8 backward, whose quantiser reads u
+// by token) and, for a routed row, dg_{t,k} = dy_t . Y_r (fp32; each lane
+// sums its columns in order, then a butterfly over the lanes).  dy_t and u_t
+// are read once for all of the token's rows.
 __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a) {
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
@@ -1088,7 +1093,7 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a) {
       const size_t o = static_cast<size_t>(rk[k]) * a.d + c;
       const float g = gk[k];
       *reinterpret_cast<uint2*>(a.dys + o) = make_uint2(bf16x2(g * dv.x, g * dv.y), bf16x2(g * dv.z, g * dv.w));
-      *reinterpret_cast<uint2*>(a.xp + o) = uv;
+      if (!a.fp8) *reinterpret_cast<uint2*>(a.xp + o) = uv;
       float yv[4];
       unpack4(*reinterpret_cast<const uint2*>(a.y + o), yv);
       dot[k] = fmaf(dv.x, yv[0], dot[k]);
@@ -1099,7 +1104,7 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a) {
     for (int j = 0; j < a.n_shared; ++j) {   // shared rows: g = 1
       const size_t o = (static_cast<size_t>(a.TK) + static_cast<size_t>(j) * a.T + t) * a.d + c;
       *reinterpret_cast<uint2*>(a.dys + o) = make_uint2(bf16x2(dv.x, dv.y), bf16x2(dv.z, dv.w));
-      *reinterpret_cast<uint2*>(a.xp + o) = uv;
+      if (!a.fp8) *reinterpret_cast<uint2*>(a.xp + o) = uv;
     }
   }
 #pragma unroll
@@ -1258,17 +1263,20 @@ hipError_t launch_backward_stage_fp8(int stage, const BwdArgs& a, hipStream_t s)
     }
     case 3:     // dW_down from the 128x1 codes of dY and H
       if (a.T > 0) {
-        hipLaunchKernelGGL(colquant_kernel, dim3(kbt, cq_grid(a.d)), dim3(256), 0, s, a, a.dys, a.d, a.qa, a.qa_s);
-        hipLaunchKernelGGL(colquant_kernel, dim3(kbt, cq_grid(a.inter)), dim3(256), 0, s, a, a.hr, a.inter, a.qb,
+        hipLaunchKernelGGL(colquant_kernel, dim3(kbt, cq_grid(a.d)), dim3(256), 0, s, a, a.dys, a.d, false, a.qa,
+                           a.qa_s);
+        hipLaunchKernelGGL(colquant_kernel, dim3(kbt, cq_grid(a.inter)), dim3(256), 0, s, a, a.hr, a.inter, false, a.qb,
                            a.qb_s);
       }
       hipLaunchKernelGGL(wgrad8_down_kernel, dim3(wgrad_grid()), dim3(THREADS), 0, s, a);
       break;
     case 4:     // dW_gate_up from the 128x1 codes of [dG dU] and X
       if (a.T > 0) {
-        hipLaunchKernelGGL(colquant_kernel, dim3(kbt, cq_grid(2 * a.inter)), dim3(256), 0, s, a, a.dgu, 2 * a.inter, a.qa,
-                           a.qa_s);
-        hipLaunchKernelGGL(colquant_kernel, dim3(kbt, cq_grid(a.d)), dim3(256), 0, s, a, a.xp, a.d, a.qb, a.qb_s);
+        hipLaunchKernelGGL(colquant_kernel, dim3(kbt, cq_grid(2 * a.inter)), dim3(256), 0, s, a, a.dgu, 2 * a.inter,
+                           false, a.qa, a.qa_s);
+        // X: the rows of u by token (the bf16 path's gathered copy is not written)
+        hipLaunchKernelGGL(colquant_kernel, dim3(kbt, cq_grid(a.d)), dim3(256), 0, s, a, a.u, a.d, true, a.qb,
+                           a.qb_s);
       }
       hipLaunchKernelGGL(wgrad8_gateup_kernel, dim3(wgrad_grid()), dim3(THREADS), 0, s, a);
       break;

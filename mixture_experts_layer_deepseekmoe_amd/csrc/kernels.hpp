@@ -143,7 +143,7 @@ struct BwdArgs {
   const void* ws_down;            // [N_s][d][I]
   const uint16_t* gu;             // [R][2I] cached G | U
   uint16_t* dys;                  // [R][d] g dy rows
-  uint16_t* xp;                   // [R][d] gathered u rows
+  uint16_t* xp;                   // [R][d] gathered u rows (bf16 backward only)
   uint16_t* dgu;                  // [R][2I] dG | dU
   uint16_t* hr;                   // [R][I] recomputed H
   uint16_t* dx;                   // [R][d] Dgrad of the gate/up GEMM
