@@ -70,7 +70,7 @@ Layout make_layout(const moe_shape& s) {
   L.sel = take(TK * 4);
   L.gu = take(R * 2 * s.inter * 2);
   L.dys = take(R * s.d * 2);
-  L.xp = take(R * s.d * 2);
+  L.xp = take(fp8 ? 0 : R * s.d * 2);   // the FP8 backward quantises u by token instead
   L.dgu = take(R * 2 * s.inter * 2);
   L.dx = take(R * s.d * 2);
   L.dg = take(TK * 4);
