@@ -254,6 +254,9 @@ FP8_CASES = {
     "small_fp8": PARITY_CONFIGS["small_fp8"],
     "small_fp8_ns2": PARITY_CONFIGS["small_fp8_ns2"],
     "small_fp8_ns0": PARITY_CONFIGS["small_fp8_ns2"].replace(name="small_fp8_ns0", n_shared=0),
+    # experts without rows and groups of one or two rows in the 128x1 code layout
+    "one_token_fp8": PARITY_CONFIGS["one_token"].replace(name="one_token_fp8", w_dtype="e4m3"),
+    "wide_router_fp8": PARITY_CONFIGS["wide_router"].replace(name="wide_router_fp8", w_dtype="e4m3"),
 }
 
 

@@ -85,9 +85,13 @@ def test_debug_build_all_tokens_on_k_experts_and_nan_tokens():
     torch.cuda.empty_cache()
 
 
-@pytest.mark.parametrize("name", ["small_bf16_ns2", "bf16_d2048", "small_fp8_ns2", "fp8_d2048"])
+# FP8 with 512 experts, most of them without rows or with one or two
+WIDE_FP8 = PARITY_CONFIGS["wide_router"].replace(name="wide_router_fp8", w_dtype="e4m3")
+
+
+@pytest.mark.parametrize("name", ["small_bf16_ns2", "bf16_d2048", "small_fp8_ns2", "fp8_d2048", "wide_router_fp8"])
 def test_debug_build_backward(name):
-    cfg = (PARITY_CONFIGS.get(name) or CONFIGS[name])
+    cfg = WIDE_FP8 if name == WIDE_FP8.name else (PARITY_CONFIGS.get(name) or CONFIGS[name])
     say(f"case: debug build, moe_forward_train + moe_backward {name}")
     inp = make_inputs(cfg, 0)
     w = moe.prepare_weights(cfg, inp, train=True)
