@@ -350,61 +350,6 @@ struct Pipe {
     }
   }
 
-  // FP8: the products of subtile i are promoted into the accumulators
-  // (acc += P * s_x * s_w) while the MFMAs of subtile i+1 run, one promotion
-  // after each MFMA.  Promoting a product right after its own MFMA waits out
-  // the MFMA's latency, and the matrix core idles meanwhile.  pp / sp: the
-  // previous subtile's products and its activation scale.
-  template <int NSUB, int I, class H>
-  __device__ __forceinline__ static void compute_fp8_from(const uint8_t* st, Frags& f, f32x4 (&acc)[MI][NJ],
-                                                          const float (&sw)[NJ], H& hook, i32x4 (&xc)[XW],
-                                                          i32x4 (&xnx)[XW], float& sc, float& snx,
-                                                          f32x4 (&pp)[NJ], float& sp) {
-    if constexpr (I <= NSUB) {
-      i32x4 xn[XW];
-      float sn = 0.f;
-      if constexpr (I < NSUB) {
-#pragma unroll
-        for (int q = 0; q < XW; ++q) xn[q] = xnx[q];
-        sn = snx;
-        if constexpr (I + 2 < NSUB) load_x(st, I + 2, xn, sn);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      f32x4 pn[NJ];
-#pragma unroll
-      for (int j = 0; j < NJ; ++j) {
-        if constexpr (I < NSUB) {
-          const i32x8 wv = {(int)f.w[2 * j].x, (int)f.w[2 * j].y, (int)f.w[2 * j].z, (int)f.w[2 * j].w,
-                            (int)f.w[2 * j + 1].x, (int)f.w[2 * j + 1].y, (int)f.w[2 * j + 1].z, (int)f.w[2 * j + 1].w};
-          const i32x8 xv = {(int)xc[0].x, (int)xc[0].y, (int)xc[0].z, (int)xc[0].w,
-                            (int)xc[1].x, (int)xc[1].y, (int)xc[1].z, (int)xc[1].w};
-          pn[j] = mfma_e4m3(wv, xv, f32x4{0.f, 0.f, 0.f, 0.f});
-        }
-        if constexpr (I > 0) acc[I - 1][j] += pp[j] * (sp * sw[j]);
-      }
-      if constexpr (I > 0 && I < NSUB) {
-#pragma unroll
-        for (int j = 0; j < NJ; ++j) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
-          __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);   // then one promotion
-        }
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      if constexpr (I < NSUB) {
-        hook.template operator()<I>();
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int q = 0; q < XW; ++q) { xc[q] = xnx[q]; xnx[q] = xn[q]; }
-#pragma unroll
-        for (int j = 0; j < NJ; ++j) pp[j] = pn[j];
-        sp = sc;
-        sc = snx;
-        snx = sn;
-      }
-      compute_fp8_from<NSUB, I + 1>(st, f, acc, sw, hook, xc, xnx, sc, snx, pp, sp);
-    }
-  }
-
   // ---- FP8, W-subtile-outer order (the wave-specialised FP8 pipeline).
   // The stage's X fragments and scales for all NSUB row subtiles are held in
   // registers; the W fragments stream two column subtiles ahead of their
@@ -498,13 +443,8 @@ struct Pipe {
     float sc = f.sx[0], snx = f.sx[1];
 #pragma unroll
     for (int q = 0; q < XW; ++q) { xc[q] = f.x[q]; xnx[q] = f.x[XW + q]; }
-    if constexpr (FMT == FMT_E4M3) {
-      f32x4 pp[NJ];
-      float sp = 0.f;
-      compute_fp8_from<NSUB, 0>(st, f, acc, sw, hook, xc, xnx, sc, snx, pp, sp);
-    } else {
-      compute_from<NSUB, 0>(st, f, acc, sw, hook, xc, xnx, sc, snx);
-    }
+    static_assert(FMT != FMT_E4M3, "FP8 tiles run in W-subtile-outer order (compute_jo)");
+    compute_from<NSUB, 0>(st, f, acc, sw, hook, xc, xnx, sc, snx);
   }
 };
 

@@ -49,15 +49,4 @@ inline int mtile_grid(int max_mtiles, int nb_n) {
   return static_cast<int>(static_cast<long long>(NXCD) * seg_cap(max_mtiles) * nb_n);
 }
 
-// A tile sequence cut into NXCD contiguous chunks, chunk x for XCD x: the
-// tile of this block, or -1.  Grid: NXCD * ceil(n_tiles / NXCD).
-__device__ __forceinline__ int xcd_chunk_tile(long long n_tiles) {
-  const int bid = blockIdx.x;
-  const long long chunk = (n_tiles + NXCD - 1) / NXCD;
-  const long long j = bid / NXCD;
-  if (j >= chunk) return -1;
-  const long long q = (bid % NXCD) * chunk + j;
-  return q < n_tiles ? static_cast<int>(q) : -1;
-}
-
 }  // namespace moe
