@@ -597,13 +597,4 @@ def layer_backward(u: np.ndarray, centroids: np.ndarray, bias: np.ndarray, k: in
             "dW_gate_up": dW_gu, "dW_down": dW_d, "dWs_gate_up": dWs_gu, "dWs_down": dWs_d}
 
 
-def near_tie_mask(gap: np.ndarray, band: float = 1e-6) -> np.ndarray:
-    """Tokens whose K-th and (K+1)-th biased scores lie within ``band``."""
-    return np.asarray(gap) <= band
-
-
-def flops_per_token(d: int, n_routed: int, inter: int, k: int, n_shared: int) -> int:
-    return 2 * d * n_routed + 6 * d * inter * (k + n_shared)
-
-
 __all__ = [n for n in dir() if not n.startswith("_") and n not in ("annotations", "math")]
