@@ -21,9 +21,13 @@ tiles, and codes decided from the same bf16 rows (the cached G and U, dY,
 dH, [dG dU], H, x are bf16 on both sides) -- so a code differs only where
 the GPU's fp32 and the oracle's fp64 evaluation of a row land on different
 bf16 values (relative error ~1e-6 against a bf16 spacing of 2^-8: about one
-element in 4000) and that element then crosses an E4M3 boundary.  Such flips
-are rare and the rest is the fp32 accumulation and the bf16 outputs, as in
-the bf16 backward, so the same bound of 1e-2 per block applies.
+element in 4000).  Such a flip moves one code, unless the element is the
+largest of its 1x128 or 128x1 tile: then the tile's scale moves and every
+code of the tile is decided afresh, each by up to one E4M3 step (2^-4).  In
+an expert with few rows one such tile is a large share of a weight
+gradient's block: the oracle against itself, with dy perturbed by 1e-7 to
+1e-6 relative (the size of fp32 evaluation error), drifts by up to 1.3e-2
+per block on the random shapes below.  The FP8 bound is 3e-2 per block.
 """
 
 import numpy as np
@@ -38,7 +42,7 @@ from tests.parity import check_routing, expert_fns, say
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
 TOL = 1e-2
-TOL8 = 1e-2
+TOL8 = 3e-2
 
 
 def _maxrel(got: np.ndarray, ref: np.ndarray) -> float:
@@ -165,6 +169,58 @@ def test_backward_parity(name):
     say("  worst block ||d||/||ref||: " + ", ".join(f"{k} {v:.2e}" for k, v in errs.items()) + f"; {empty} experts without rows")
     for k, v in errs.items():
         assert v <= TOL, (k, v)
+
+
+def _random_train_shapes(n=8, seed=77):
+    """Seeded small training shapes: bf16 or e4m3 weights, ragged T, N_r on
+    both sides of the 128-row FP8 code blocks' group count, K up to 16, 0-3
+    shared experts, d and I any multiple of 64 (bf16) or 128 (e4m3), bf16 or
+    fp32 y; sizes bounded so the fp64 oracle backward stays quick."""
+    rs = np.random.RandomState(seed)
+    out = []
+    for i in range(n):
+        w = ["bf16", "e4m3"][i % 2]
+        kmult = 64 if w == "bf16" else 128
+        n_routed = int(rs.choice([int(rs.randint(1, 40)), int(rs.randint(40, 300))]))
+        top_k = int(rs.randint(1, min(16, n_routed) + 1))
+        d = kmult * int(rs.randint(1, 768 // kmult + 1))
+        inter = kmult * int(rs.randint(1, 512 // kmult + 1))
+        while n_routed * d * inter > (1 << 23):   # keep the oracle's weights small
+            if d >= inter and d > kmult:
+                d -= kmult
+            elif inter > kmult:
+                inter -= kmult
+            else:
+                n_routed = max(top_k, n_routed // 2)
+        T = int(rs.randint(1, 600))
+        out.append(PARITY_CONFIGS["small_bf16"].replace(
+            name=f"train{i}_{w}_T{T}_d{d}_I{inter}_Nr{n_routed}_K{top_k}", T=T, d=d, n_routed=n_routed,
+            n_shared=int(rs.randint(0, 4)), inter=inter, top_k=top_k, w_dtype=w,
+            out_dtype=["f32", "bf16"][rs.randint(2)], w_std=0.03, e_std=0.05, b_std=0.02, cfg_id=200 + i))
+    return out
+
+
+RANDOM_TRAIN_SHAPES = _random_train_shapes()
+
+
+@pytest.mark.parametrize("cfg", RANDOM_TRAIN_SHAPES, ids=[c.name for c in RANDOM_TRAIN_SHAPES])
+def test_backward_random_shapes(cfg):
+    """Seeded random training shapes, bf16 and FP8, against the oracle's
+    backward (bf16 or FP8) at the same per-block bound."""
+    say(f"case: moe_forward_train + moe_backward {cfg.name}")
+    inp = make_inputs(cfg, 0)
+    dy = _dy(cfg)
+    y, du, dE, grads, ws, w = _train_step(cfg, inp, dy)
+    shape = moe.LayerShape.from_config(cfg)
+    u, E, b = (t.to(DEV).contiguous() for t in (inp.u, inp.centroids, inp.bias))
+    routing = moe.alloc_routing(shape)
+    y_inf = moe.moe_forward(shape, u, E, b, w, routing=routing)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y_inf)
+    errs, empty = _compare(cfg, inp, dy, du, dE, grads, routing["topk_idx"].cpu().numpy())
+    say("  worst block ||d||/||ref||: " + ", ".join(f"{k} {v:.2e}" for k, v in errs.items()) + f"; {empty} experts without rows")
+    for k, v in errs.items():
+        assert v <= (TOL8 if cfg.w_dtype == "e4m3" else TOL), (k, v)
 
 
 def test_backward_deterministic_and_empty_batch():
