@@ -11,6 +11,7 @@ import torch
 import mixture_experts_layer_deepseekmoe_amd as moe
 from mixture_experts_layer_deepseekmoe_amd import binding as B
 from moe_workloads import CONFIGS, PARITY_CONFIGS, make_inputs
+from tests.test_gpu_backward import RANDOM_TRAIN_SHAPES
 from tests.parity import say
 
 pytestmark = pytest.mark.gpu
@@ -85,13 +86,16 @@ def test_debug_build_all_tokens_on_k_experts_and_nan_tokens():
     torch.cuda.empty_cache()
 
 
-# FP8 with 512 experts, most of them without rows or with one or two
-WIDE_FP8 = PARITY_CONFIGS["wide_router"].replace(name="wide_router_fp8", w_dtype="e4m3")
+# FP8 with 512 experts, most of them without rows or with one or two; and
+# two of the seeded random training shapes (4 tokens over 208 experts in
+# bf16; FP8 with 226 experts)
+EXTRA = {c.name: c for c in [PARITY_CONFIGS["wide_router"].replace(name="wide_router_fp8", w_dtype="e4m3")]
+         + [c for c in RANDOM_TRAIN_SHAPES if c.name.startswith(("train4_", "train7_"))]}
 
 
-@pytest.mark.parametrize("name", ["small_bf16_ns2", "bf16_d2048", "small_fp8_ns2", "fp8_d2048", "wide_router_fp8"])
+@pytest.mark.parametrize("name", ["small_bf16_ns2", "bf16_d2048", "small_fp8_ns2", "fp8_d2048"] + list(EXTRA))
 def test_debug_build_backward(name):
-    cfg = WIDE_FP8 if name == WIDE_FP8.name else (PARITY_CONFIGS.get(name) or CONFIGS[name])
+    cfg = EXTRA.get(name) or PARITY_CONFIGS.get(name) or CONFIGS[name]
     say(f"case: debug build, moe_forward_train + moe_backward {name}")
     inp = make_inputs(cfg, 0)
     w = moe.prepare_weights(cfg, inp, train=True)
