@@ -5,7 +5,8 @@
 // expert selection held fixed:
 //
 //   prep     grouped row r (token t, gate g; g = 1 for a shared expert):
-//            dY_r = g dy_t and X_r = u_t as bf16 rows, dg_{t,k} = dy_t . Y_r
+//            dY_r = g dy_t and X_r = u_t as bf16 rows (X_r only for the bf16
+//            Wgrad: the FP8 one quantises u by token), dg_{t,k} = dy_t . Y_r
 //   dz       per token: S = sum of the selected sigmoids, ds_k = (dg_k -
 //            sum_j g_j dg_j) / S, dz_k = ds_k s_k (1 - s_k)
 //   dgrad    dH = dY W_down (per group), fused with the SwiGLU backward:
