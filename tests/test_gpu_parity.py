@@ -389,12 +389,13 @@ def test_forward_nan_tokens_leave_the_others_exact():
     assert err["rel_to_rms"] <= TOL[cfg.w_dtype], err
 
 
-def test_forward_batch_invariant_with_multi_tile_experts():
-    """At d = 2048 every expert holds ~384 rows, two m-tiles; the same tokens
-    run alone (one m-tile per expert, another router kernel with the same
-    summation order) give bit-identical outputs."""
-    cfg = CONFIGS["bf16_d2048"]
-    say("case: batch invariance bf16_d2048 (two m-tiles per expert) vs 37 tokens alone")
+@pytest.mark.parametrize("name", ["bf16_d2048", "fp8_d2048"])
+def test_forward_batch_invariant_with_multi_tile_experts(name):
+    """At d = 2048 every expert holds ~384 rows, two m-tiles (three FP8
+    ones); the same tokens run alone (one m-tile per expert, another router
+    kernel with the same summation order) give bit-identical outputs."""
+    cfg = CONFIGS[name]
+    say(f"case: batch invariance {name} (several m-tiles per expert) vs 37 tokens alone")
     inp = make_inputs(cfg, 0, weights_device=DEV)
     y_full, routing, w = _run_forward(cfg, inp)
     counts = routing["expert_counts"].cpu().numpy()
