@@ -106,6 +106,9 @@ int validate_shape(const moe_shape* s);
 int validate_train(const moe_shape& s) {
   if (s.x_dtype != MOE_DTYPE_BF16 || (s.w_dtype != MOE_DTYPE_BF16 && s.w_dtype != MOE_DTYPE_E4M3))
     return MOE_ERR_UNSUPPORTED;
+  // the Wgrad addresses one group's bf16 rows ([dG dU], G|U: up to T rows of
+  // 2I) with 32-bit byte offsets (the rows of d are covered by the check on u)
+  if (static_cast<long long>(s.T) * 4LL * s.inter >= (1LL << 32)) return MOE_ERR_UNSUPPORTED;
   if (s.w_dtype == MOE_DTYPE_E4M3) {
     const long long R = static_cast<long long>(s.T) * (s.top_k + s.n_shared);
     const long long kt = moe::wgrad8_kt(R, s.n_routed + s.n_shared);

@@ -74,6 +74,20 @@ def test_shape_validation(kw, code):
     assert rc == code
 
 
+def test_training_shape_validation():
+    def rc(shape):
+        n = ctypes.c_size_t(0)
+        return moe.load_library().moe_train_workspace_size(ctypes.byref(shape.c()), ctypes.byref(n))
+    assert rc(_shape()) == B.MOE_OK
+    assert rc(_shape(w_dtype="e4m3", inter=128)) == B.MOE_OK
+    assert rc(_shape(x_dtype="f32", w_dtype="f32")) == B.MOE_ERR_UNSUPPORTED   # training takes bf16 activations
+    # a group's [dG dU] rows (T x 2I bf16) reach 2^32 bytes, though the forward's
+    # own 32-bit offsets (u, one expert's weights) still fit
+    big = _shape(T=131_072, d=1024, inter=8192, top_k=1)
+    assert _ws_rc(big)[0] == B.MOE_OK and rc(big) == B.MOE_ERR_UNSUPPORTED
+    assert rc(_shape(T=131_071, d=1024, inter=8192, top_k=1)) == B.MOE_OK
+
+
 def test_largest_activation_within_32_bit_offsets_is_accepted():
     # T * d * 2 bytes just below 2^32
     rc, _ = _ws_rc(_shape(T=299_593, d=7168, top_k=1))
