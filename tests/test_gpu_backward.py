@@ -1,5 +1,5 @@
-"""GPU parity of the layer backward (moe_forward_train + moe_backward, bf16,
-through the C ABI) against the oracle's fp64 layer_backward.
+"""GPU parity of the layer backward (moe_forward_train + moe_backward, bf16
+and FP8, through the C ABI) against the oracle's fp64 layer_backward.
 
 Bar (the pages state none for the backward; derived from the arithmetic):
 the backward's GEMMs take bf16 operands (the scaled upstream rows, the
